@@ -1,0 +1,191 @@
+/*
+ * pagedkv.h -- PagedAttention decode for AMD Instinct MI355X (gfx950), C ABI.
+ *
+ * Page citations:
+ *   [Walkthrough] "LLM serving (vLLM, quantized inference): Visual walkthrough"
+ *   [Serving]     "How LLM Inference Serving Works: KV Cache, PagedAttention and Continuous
+ *                 Batching"
+ *
+ * Model of the cache ([Serving] "PagedAttention: Virtual Memory for the KV Cache";
+ * [Walkthrough] "Step 7"): the keys and values of every sequence live in fixed-size blocks of
+ * `bs` tokens scattered through one physical pool; a per-sequence block table maps logical
+ * block j (tokens j*bs .. j*bs+bs-1) to a physical block.  A slot is physical_block*bs + offset.
+ *
+ * Device layouts (row-major, all owned by the caller):
+ *   k_cache   [NB][Hkv][bs][D]   token-major inside each (block, KV head) tile
+ *   v_cache   [NB][Hkv][D][bs]   dim-major inside each (block, KV head) tile
+ *   k_scale, v_scale [NB][Hkv] fp32, int8 caches only (value = code * scale)
+ *   q, out    [B][Hq][D]; out is always fp32
+ *   block_tables [B][max_blocks] int32, unused entries may hold anything (e.g. -1)
+ *   seq_lens  [B] int32
+ *
+ * Conventions
+ *   - Every function returns an int status: PA_OK (0) or a negative PA_ERR_* code.  Nothing
+ *     throws across the ABI.
+ *   - Arguments are checked on the host before any HIP call; a bad argument returns
+ *     PA_ERR_INVALID (or PA_ERR_UNSUPPORTED for a valid but unimplemented combination) and
+ *     enqueues nothing.
+ *   - Device entry points enqueue on `stream` (a hipStream_t passed as void*, NULL = the null
+ *     stream) and return without synchronising.  A launch error returns PA_ERR_DEVICE.
+ *   - The library allocates no device memory.  Scratch space for pa_decode is a caller buffer
+ *     of at least pa_decode_workspace_size() bytes.
+ *   - Not checked on the device, the caller's contract: block ids in tables, slot mappings and
+ *     copy pairs lie in [0, NB); seq_lens[b] <= max_seq_len.  Kernels clamp lengths to
+ *     max_seq_len and skip table entries outside [0, NB), so a broken contract gives wrong
+ *     numbers, never an out-of-bounds access.
+ *   - Allocator handles are not thread-safe; use one handle per thread or lock around it.
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum pa_status {
+  PA_OK = 0,
+  PA_ERR_INVALID = -1,     /* bad argument (null pointer, size out of range, ...) */
+  PA_ERR_OOM = -2,         /* allocator: not enough free blocks; state left unchanged */
+  PA_ERR_DEVICE = -3,      /* a HIP call or kernel launch failed */
+  PA_ERR_UNSUPPORTED = -4, /* valid arguments, combination not implemented */
+  PA_ERR_STATE = -5        /* allocator: unknown or released sequence id */
+};
+
+enum pa_dtype { PA_F32 = 0, PA_BF16 = 1, PA_I8 = 2 };
+
+/* Static text for a status code. */
+const char* pa_status_string(int status);
+
+/* ABI version, bumped on any incompatible change. */
+int pa_abi_version(void);
+
+/* ================================================================================== */
+/* Host block allocator ([Serving] "PagedAttention: Virtual Memory for the KV Cache",   */
+/* "Sharing comes for free", "The Life of a Request"; [Walkthrough] "Step 7", "Step 8") */
+/* ================================================================================== */
+/*
+ * Blocks are handed out on demand, when a sequence's current block is full.  Blocks carry a
+ * reference count; forks share blocks; a write into a block with more than one reference first
+ * copies it (copy-on-write).  The pages fix no hand-out order; this one makes every table
+ * unique: a FIFO free list, initialised from `free_order`; allocations pop the head; a block
+ * whose count reaches zero is pushed to the tail, in the logical order of the table it leaves;
+ * batch calls serve sequences in the order given; sequence ids count up from 0 and are never
+ * reused.  Calls that run out of blocks return PA_ERR_OOM and change nothing.
+ */
+typedef struct pa_allocator pa_allocator;
+
+/* num_blocks >= 1, block_size >= 1.  free_order: NULL for 0..num_blocks-1, else a permutation
+ * of 0..num_blocks-1 (copied; anything else is PA_ERR_INVALID).  *out receives the handle. */
+int pa_alloc_create(int32_t num_blocks, int32_t block_size, const int32_t* free_order,
+                    pa_allocator** out);
+/* Releases the handle and all its host memory.  NULL is a no-op. */
+void pa_alloc_destroy(pa_allocator* a);
+
+/* New empty sequence; its id goes to *seq. */
+int pa_seq_create(pa_allocator* a, int32_t* seq);
+
+/* New sequence sharing the first n_tokens of `parent` (0 <= n_tokens <= parent length): the
+ * child's table is the parent's first ceil(n_tokens/bs) blocks, each gaining a reference. */
+int pa_seq_fork(pa_allocator* a, int32_t parent, int32_t n_tokens, int32_t* child);
+
+/* Slot of the sequence's next token.  When the write lands in a block that other sequences
+ * also hold, a fresh block replaces it in this sequence's table and *cow_src / *cow_dst name
+ * the copy that must reach the device before the write (pa_copy_blocks); otherwise both are -1.
+ * cow_src / cow_dst may be NULL only if the caller knows no copy can arise. */
+int pa_seq_append_slot(pa_allocator* a, int32_t seq, int64_t* slot, int32_t* cow_src,
+                       int32_t* cow_dst);
+
+/* n successive appends to one sequence.  slots[n] receives each slot; cow_pairs[n][2] receives
+ * the (src, dst) copies in order, *n_cow their count.  All or nothing. */
+int pa_seq_reserve(pa_allocator* a, int32_t seq, int32_t n, int64_t* slots, int32_t* cow_pairs,
+                   int32_t* n_cow);
+
+/* One decode step's appends for a batch ([Serving] "The Life of a Request": each step appends
+ * one token per request, allocating a block only when the current one fills).  For i in 0..B-1
+ * in order, one append to seqs[i]: slots[i] gets its slot; copy-on-write pairs go to
+ * cow_pairs[*n_cow][2]; table changes go to table_updates[*n_updates][3] as (i, logical block,
+ * physical block) -- a new block or a copy that replaces a shared one -- so that a device copy
+ * of the block tables can be patched with pa_update_block_tables.  Both outputs hold at most B
+ * entries; table_updates may be NULL.  All or nothing. */
+int pa_step(pa_allocator* a, const int32_t* seqs, int32_t B, int64_t* slots, int32_t* cow_pairs,
+            int32_t* n_cow, int32_t* table_updates, int32_t* n_updates);
+
+/* Drop a sequence: each of its blocks loses a reference; blocks left with none go to the tail
+ * of the free list in table order ([Serving] "The Life of a Request"). */
+int pa_seq_free(pa_allocator* a, int32_t seq);
+
+int pa_seq_len(const pa_allocator* a, int32_t seq, int32_t* len);
+/* Copies up to `cap` table entries to out; *n receives the table length. */
+int pa_seq_table(const pa_allocator* a, int32_t seq, int32_t* out, int32_t cap, int32_t* n);
+/* Host block tables [B][max_blocks] (padded with -1) and lengths [B] for the listed sequences.
+ * PA_ERR_INVALID if a table is longer than max_blocks. */
+int pa_export_block_tables(const pa_allocator* a, const int32_t* seqs, int32_t B,
+                           int32_t max_blocks, int32_t* tables, int32_t* seq_lens);
+int pa_block_refcount(const pa_allocator* a, int32_t block, int32_t* rc);
+int pa_num_free(const pa_allocator* a, int32_t* n);
+/* Free list from head to tail: up to `cap` ids to out, *n receives its length. */
+int pa_free_list(const pa_allocator* a, int32_t* out, int32_t cap, int32_t* n);
+
+/* ================================================================================== */
+/* Device entry points                                                                */
+/* ================================================================================== */
+
+/* Append one token per sequence ([Serving] "What the KV Cache Is": each decode step appends one
+ * more token's K and V; "The Life of a Request").  k_new, v_new: device [B][Hkv][D] in the
+ * cache dtype (PA_F32 or PA_BF16; int8 caches are written by their quantiser, not here).
+ * slot_mapping: device [B] int64, -1 = skip this sequence.  Writes K into k_cache[slot/bs][g]
+ * [slot%bs][:] and V into v_cache[slot/bs][g][:][slot%bs]; nothing else is touched.  Two
+ * sequences must not share a slot.  Constraints: B >= 0, Hkv >= 1, D in {64, 128}, bs == 16. */
+int pa_kv_append(const void* k_new, const void* v_new, const int64_t* slot_mapping,
+                 void* k_cache, void* v_cache, int32_t B, int32_t Hkv, int32_t D, int32_t bs,
+                 int32_t NB, int32_t kv_dtype, void* stream);
+
+/* Copy-on-write block copies ([Serving] "Sharing comes for free"; [Walkthrough] "Step 8").
+ * pairs: device [n][2] int32 (src, dst).  Copies the whole K and V tile of block src over block
+ * dst, and for PA_I8 also both scales (k_scale, v_scale must then be non-NULL).  Destinations
+ * must be distinct and no destination may be another pair's source (the allocator never
+ * produces either).  n == 0 enqueues nothing. */
+int pa_copy_blocks(void* k_cache, void* v_cache, float* k_scale, float* v_scale,
+                   const int32_t* pairs, int32_t n, int32_t Hkv, int32_t D, int32_t bs,
+                   int32_t NB, int32_t kv_dtype, void* stream);
+
+/* Patch a device block table with pa_step's table_updates: updates is device [n][3] int32
+ * (row, logical block, physical block); block_tables[row][logical] = physical.  Rows outside
+ * [0, B) or logical blocks outside [0, max_blocks) are skipped. */
+int pa_update_block_tables(int32_t* block_tables, int32_t max_blocks, int32_t B,
+                           const int32_t* updates, int32_t n, void* stream);
+
+/* Bytes of scratch that pa_decode needs for these sizes (partition_tokens as for pa_decode).
+ * Returns 0 for invalid sizes. */
+size_t pa_decode_workspace_size(int32_t B, int32_t Hq, int32_t D, int32_t max_seq_len,
+                                int32_t partition_tokens);
+
+/* Decode attention over the paged cache ([Serving] "What the KV Cache Is": the new token's
+ * query is compared with the key of every cached token and the values are mixed by those
+ * weights; "PagedAttention": the kernel follows the block table to gather K and V; grouped-query
+ * attention: query head h reads KV head h / (Hq/Hkv)).  For every b < B and h < Hq:
+ *     out[b][h] = sum_t softmax_t(scale * <q[b][h], K_t>) V_t,  t < seq_lens[b],
+ * token t at block_tables[b][t/bs], offset t%bs; int8 elements are code * scale of their
+ * (block, KV head).  seq_lens[b] == 0 gives out[b] = 0.
+ *   q_dtype:  PA_F32 or PA_BF16.  kv_dtype: PA_F32, PA_BF16 or PA_I8 (then k_scale/v_scale).
+ *   Hq % Hkv == 0, Hq/Hkv <= 16, D in {64, 128}, bs == 16.
+ *   max_seq_len: host bound on every seq_lens[b], 0 <= max_seq_len <= max_blocks*bs.
+ *   partition_tokens: 0 picks a size; else a multiple of 64 in [64, 8192].  Sequences longer
+ *     than one partition are split ("split-K") and merged with the log-sum-exp identity.
+ *   workspace: device buffer of workspace_bytes >= pa_decode_workspace_size(...).
+ * The softmax runs in fp32 with exp computed as exp2 of a log2(e)-scaled argument. */
+int pa_decode(float* out, const void* q, int32_t q_dtype, const void* k_cache,
+              const void* v_cache, int32_t kv_dtype, const float* k_scale, const float* v_scale,
+              const int32_t* block_tables, int32_t max_blocks, const int32_t* seq_lens,
+              int32_t max_seq_len, int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t bs,
+              int32_t NB, float scale, int32_t partition_tokens, void* workspace,
+              size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H */

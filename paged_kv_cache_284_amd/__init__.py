@@ -1,0 +1,351 @@
+"""Python binding of libpagedkv (PagedAttention decode for MI355X).
+
+Argument marshalling only: every computation runs in the C-ABI library (host allocator in C++,
+device work in HIP kernels).  torch is used for device memory and streams; tensors are passed by
+data pointer and the current HIP stream.  There is no fallback: if the library is not built,
+every call raises.
+
+    import paged_kv_cache_284_amd as pkv
+    a = pkv.Allocator(num_blocks, 16, free_order)
+    ...
+    pkv.kv_append(k_new, v_new, slots, k_cache, v_cache)
+    out = pkv.decode(q, k_cache, v_cache, block_tables, seq_lens, max_seq_len, scale)
+
+Layouts: k_cache [NB][Hkv][16][D], v_cache [NB][Hkv][D][16], scales [NB][Hkv] fp32,
+q [B][Hq][D] (float32 or bfloat16), out [B][Hq][D] float32.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import List, Optional, Sequence, Tuple
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpagedkv.so")
+
+PA_OK, PA_ERR_INVALID, PA_ERR_OOM, PA_ERR_DEVICE, PA_ERR_UNSUPPORTED, PA_ERR_STATE = \
+    0, -1, -2, -3, -4, -5
+PA_F32, PA_BF16, PA_I8 = 0, 1, 2
+BLOCK_SIZE = 16
+
+_i32, _i64, _sz, _vp, _f32 = C.c_int32, C.c_int64, C.c_size_t, C.c_void_p, C.c_float
+_pi32, _pi64 = C.POINTER(C.c_int32), C.POINTER(C.c_int64)
+
+# name -> (restype, argtypes); kept in the order of include/pagedkv.h
+_SIGNATURES = {
+    "pa_status_string": (C.c_char_p, [C.c_int]),
+    "pa_abi_version": (C.c_int, []),
+    "pa_alloc_create": (C.c_int, [_i32, _i32, _pi32, C.POINTER(_vp)]),
+    "pa_alloc_destroy": (None, [_vp]),
+    "pa_seq_create": (C.c_int, [_vp, _pi32]),
+    "pa_seq_fork": (C.c_int, [_vp, _i32, _i32, _pi32]),
+    "pa_seq_append_slot": (C.c_int, [_vp, _i32, _pi64, _pi32, _pi32]),
+    "pa_seq_reserve": (C.c_int, [_vp, _i32, _i32, _pi64, _pi32, _pi32]),
+    "pa_step": (C.c_int, [_vp, _pi32, _i32, _pi64, _pi32, _pi32, _pi32, _pi32]),
+    "pa_seq_free": (C.c_int, [_vp, _i32]),
+    "pa_seq_len": (C.c_int, [_vp, _i32, _pi32]),
+    "pa_seq_table": (C.c_int, [_vp, _i32, _pi32, _i32, _pi32]),
+    "pa_export_block_tables": (C.c_int, [_vp, _pi32, _i32, _i32, _pi32, _pi32]),
+    "pa_block_refcount": (C.c_int, [_vp, _i32, _pi32]),
+    "pa_num_free": (C.c_int, [_vp, _pi32]),
+    "pa_free_list": (C.c_int, [_vp, _pi32, _i32, _pi32]),
+    "pa_kv_append": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
+    "pa_copy_blocks": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
+                                 _vp]),
+    "pa_update_block_tables": (C.c_int, [_vp, _i32, _i32, _vp, _i32, _vp]),
+    "pa_decode_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32]),
+    "pa_decode": (C.c_int, [_vp, _vp, _i32, _vp, _vp, _i32, _vp, _vp, _vp, _i32, _vp, _i32,
+                            _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz, _vp]),
+}
+
+_lib_handle = None
+
+
+class PagedKVError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)} ({status})")
+
+
+class OutOfBlocks(PagedKVError):
+    pass
+
+
+def lib() -> C.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _lib_handle
+    if _lib_handle is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m paged_kv_cache_284_amd.build`")
+        h = C.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            f = getattr(h, name)
+            f.restype = res
+            f.argtypes = args
+        _lib_handle = h
+    return _lib_handle
+
+
+def status_string(status: int) -> str:
+    return lib().pa_status_string(status).decode()
+
+
+def _check(status: int, what: str) -> None:
+    if status != PA_OK:
+        if status == PA_ERR_OOM:
+            raise OutOfBlocks(status, what)
+        raise PagedKVError(status, what)
+
+
+def _i32_array(x) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(x, dtype=np.int32))
+
+
+def _p32(a: np.ndarray):
+    return a.ctypes.data_as(_pi32)
+
+
+def _p64(a: np.ndarray):
+    return a.ctypes.data_as(_pi64)
+
+
+# ------------------------------------------------------------------------------------------
+# host allocator
+# ------------------------------------------------------------------------------------------
+class Allocator:
+    """Handle on the library's block allocator (FIFO free list, refcounts, copy-on-write)."""
+
+    def __init__(self, num_blocks: int, block_size: int = BLOCK_SIZE,
+                 free_order: Optional[Sequence[int]] = None):
+        self._h = _vp()
+        order = None if free_order is None else _i32_array(free_order)
+        if order is not None and order.size != num_blocks:
+            raise ValueError("free_order must list every block once")
+        _check(lib().pa_alloc_create(num_blocks, block_size,
+                                     None if order is None else _p32(order), C.byref(self._h)),
+               "pa_alloc_create")
+        self.num_blocks, self.block_size = num_blocks, block_size
+
+    def close(self) -> None:
+        if self._h:
+            lib().pa_alloc_destroy(self._h)
+            self._h = _vp()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def create(self) -> int:
+        s = _i32()
+        _check(lib().pa_seq_create(self._h, C.byref(s)), "pa_seq_create")
+        return s.value
+
+    def fork(self, parent: int, n_tokens: int) -> int:
+        c = _i32()
+        _check(lib().pa_seq_fork(self._h, parent, n_tokens, C.byref(c)), "pa_seq_fork")
+        return c.value
+
+    def append_slot(self, seq: int) -> Tuple[int, int, int]:
+        slot, src, dst = _i64(), _i32(), _i32()
+        _check(lib().pa_seq_append_slot(self._h, seq, C.byref(slot), C.byref(src), C.byref(dst)),
+               "pa_seq_append_slot")
+        return slot.value, src.value, dst.value
+
+    def reserve(self, seq: int, n: int):
+        slots = np.zeros(max(n, 1), np.int64)
+        pairs = np.zeros((max(n, 1), 2), np.int32)
+        k = _i32()
+        _check(lib().pa_seq_reserve(self._h, seq, n, _p64(slots), _p32(pairs), C.byref(k)),
+               "pa_seq_reserve")
+        return slots[:n].tolist(), [tuple(p) for p in pairs[:k.value].tolist()]
+
+    def step_arrays(self, seqs) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+        """One append per listed sequence: (slots int64 [B], cow pairs int32 [n][2],
+        table updates int32 [m][3])."""
+        s = _i32_array(seqs)
+        B = s.size
+        slots = np.zeros(max(B, 1), np.int64)
+        pairs = np.zeros((max(B, 1), 2), np.int32)
+        upd = np.zeros((max(B, 1), 3), np.int32)
+        k, u = _i32(), _i32()
+        _check(lib().pa_step(self._h, _p32(s), B, _p64(slots), _p32(pairs), C.byref(k),
+                             _p32(upd), C.byref(u)), "pa_step")
+        return slots[:B], pairs[:k.value], upd[:u.value]
+
+    def step(self, seqs):
+        slots, pairs, _ = self.step_arrays(seqs)
+        return slots.tolist(), [tuple(p) for p in pairs.tolist()]
+
+    def release(self, seq: int) -> None:
+        _check(lib().pa_seq_free(self._h, seq), "pa_seq_free")
+
+    def length(self, seq: int) -> int:
+        n = _i32()
+        _check(lib().pa_seq_len(self._h, seq, C.byref(n)), "pa_seq_len")
+        return n.value
+
+    def table(self, seq: int) -> List[int]:
+        n = _i32()
+        _check(lib().pa_seq_table(self._h, seq, None, 0, C.byref(n)), "pa_seq_table")
+        out = np.zeros(max(n.value, 1), np.int32)
+        _check(lib().pa_seq_table(self._h, seq, _p32(out), n.value, C.byref(n)), "pa_seq_table")
+        return out[:n.value].tolist()
+
+    def export(self, seqs, max_blocks: int) -> Tuple[np.ndarray, np.ndarray]:
+        s = _i32_array(seqs)
+        tables = np.zeros((s.size, max(max_blocks, 1)), np.int32)[:, :max_blocks].copy()
+        lens = np.zeros(max(s.size, 1), np.int32)
+        _check(lib().pa_export_block_tables(self._h, _p32(s), s.size, max_blocks,
+                                            _p32(tables) if tables.size else None, _p32(lens)),
+               "pa_export_block_tables")
+        return tables, lens[:s.size]
+
+    def refcount(self, block: int) -> int:
+        rc = _i32()
+        _check(lib().pa_block_refcount(self._h, block, C.byref(rc)), "pa_block_refcount")
+        return rc.value
+
+    def num_free(self) -> int:
+        n = _i32()
+        _check(lib().pa_num_free(self._h, C.byref(n)), "pa_num_free")
+        return n.value
+
+    def free_list(self) -> List[int]:
+        n = _i32()
+        _check(lib().pa_free_list(self._h, None, 0, C.byref(n)), "pa_free_list")
+        out = np.zeros(max(n.value, 1), np.int32)
+        _check(lib().pa_free_list(self._h, _p32(out), n.value, C.byref(n)), "pa_free_list")
+        return out[:n.value].tolist()
+
+
+def run_script(alloc: Allocator, ops) -> dict:
+    """Apply a set-up script of ("create"|"reserve"|"fork"|"free", ...) ops (see
+    inputs.setup_script); returns the map from script names to sequence ids."""
+    ids = {}
+    for op in ops:
+        if op[0] == "create":
+            ids[op[1]] = alloc.create()
+        elif op[0] == "reserve":
+            alloc.reserve(ids[op[1]], op[2])
+        elif op[0] == "fork":
+            ids[op[3]] = alloc.fork(ids[op[1]], op[2])
+        elif op[0] == "free":
+            alloc.release(ids.pop(op[1]))
+        else:
+            raise ValueError(op)
+    return ids
+
+
+# ------------------------------------------------------------------------------------------
+# device entry points (torch tensors in, nothing computed here)
+# ------------------------------------------------------------------------------------------
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    m = {torch.float32: PA_F32, torch.bfloat16: PA_BF16, torch.int8: PA_I8}
+    if t.dtype not in m:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return m[t.dtype]
+
+
+def _dev(t, name, dtype=None):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _stream(stream=None):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def kv_append(k_new, v_new, slot_mapping, k_cache, v_cache, stream=None) -> None:
+    """Write each sequence's new K/V [B][Hkv][D] at its slot (int64 [B], -1 skips)."""
+    torch = _torch()
+    NB, Hkv, bs, D = k_cache.shape
+    B = k_new.shape[0]
+    if tuple(k_new.shape) != (B, Hkv, D) or tuple(v_new.shape) != (B, Hkv, D):
+        raise ValueError("k_new/v_new must be [B][Hkv][D]")
+    if tuple(v_cache.shape) != (NB, Hkv, D, bs) or tuple(slot_mapping.shape) != (B,):
+        raise ValueError("v_cache must be [NB][Hkv][D][bs], slot_mapping [B]")
+    if k_new.dtype != k_cache.dtype or v_new.dtype != k_cache.dtype or v_cache.dtype != k_cache.dtype:
+        raise TypeError("k_new, v_new, k_cache and v_cache must share one dtype")
+    _check(lib().pa_kv_append(_dev(k_new, "k_new"), _dev(v_new, "v_new"),
+                              _dev(slot_mapping, "slot_mapping", torch.int64),
+                              _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), B, Hkv, D, bs,
+                              NB, _dtype_code(k_cache), _stream(stream)), "pa_kv_append")
+
+
+def copy_blocks(k_cache, v_cache, pairs, k_scale=None, v_scale=None, stream=None) -> None:
+    """Copy whole blocks (K, V and int8 scales) for each (src, dst) row of pairs int32 [n][2]."""
+    torch = _torch()
+    NB, Hkv, bs, D = k_cache.shape
+    n = pairs.shape[0]
+    if n and tuple(pairs.shape) != (n, 2):
+        raise ValueError("pairs must be [n][2]")
+    _check(lib().pa_copy_blocks(_dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+                                _dev(k_scale, "k_scale", torch.float32),
+                                _dev(v_scale, "v_scale", torch.float32),
+                                _dev(pairs, "pairs", torch.int32) if n else None, n, Hkv, D, bs,
+                                NB, _dtype_code(k_cache), _stream(stream)), "pa_copy_blocks")
+
+
+def update_block_tables(block_tables, updates, stream=None) -> None:
+    """Apply (row, logical, physical) rows of updates int32 [n][3] to block_tables [B][MB]."""
+    torch = _torch()
+    B, MB = block_tables.shape
+    n = updates.shape[0]
+    _check(lib().pa_update_block_tables(_dev(block_tables, "block_tables", torch.int32), MB, B,
+                                        _dev(updates, "updates", torch.int32) if n else None, n,
+                                        _stream(stream)), "pa_update_block_tables")
+
+
+def decode_workspace_size(B: int, Hq: int, D: int, max_seq_len: int,
+                          partition_tokens: int = 0) -> int:
+    return int(lib().pa_decode_workspace_size(B, Hq, D, max_seq_len, partition_tokens))
+
+
+def decode(q, k_cache, v_cache, block_tables, seq_lens, max_seq_len: int, scale: float,
+           k_scale=None, v_scale=None, out=None, workspace=None, partition_tokens: int = 0,
+           stream=None):
+    """Paged decode attention; returns out [B][Hq][D] float32."""
+    torch = _torch()
+    B, Hq, D = q.shape
+    NB, Hkv, bs, Dk = k_cache.shape
+    if Dk != D or tuple(v_cache.shape) != (NB, Hkv, D, bs):
+        raise ValueError("cache shapes do not match q")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or tuple(seq_lens.shape) != (B,):
+        raise ValueError("block_tables must be [B][max_blocks] and seq_lens [B]")
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+    elif tuple(out.shape) != (B, Hq, D):
+        raise ValueError("out must be [B][Hq][D]")
+    need = decode_workspace_size(B, Hq, D, max_seq_len, partition_tokens)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    _check(lib().pa_decode(_dev(out, "out", torch.float32), _dev(q, "q"), _dtype_code(q),
+                           _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+                           _dtype_code(k_cache), _dev(k_scale, "k_scale", torch.float32),
+                           _dev(v_scale, "v_scale", torch.float32),
+                           _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
+                           _dev(seq_lens, "seq_lens", torch.int32), max_seq_len, B, Hq, Hkv, D,
+                           bs, NB, float(scale), partition_tokens, _dev(workspace, "workspace"),
+                           workspace.numel() * workspace.element_size(), _stream(stream)),
+           "pa_decode")
+    return out

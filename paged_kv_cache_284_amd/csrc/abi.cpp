@@ -1,0 +1,158 @@
+// C-ABI device entry points: host-side argument checks, then dispatch to the kernels.
+// Nothing here touches the device before every argument has been checked.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "internal.h"
+#include "pagedkv.h"
+
+namespace {
+
+int elem_bytes(int32_t dtype) {
+  switch (dtype) {
+    case PA_F32: return 4;
+    case PA_BF16: return 2;
+    case PA_I8: return 1;
+    default: return 0;
+  }
+}
+
+int status_of(hipError_t e) {
+  if (e == hipSuccess) return PA_OK;
+  if (e == hipErrorNotSupported) return PA_ERR_UNSUPPORTED;
+  return PA_ERR_DEVICE;
+}
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+}  // namespace
+
+namespace pa {
+
+// Long sequences are split so that the grid holds several workgroups per compute unit even for
+// small batches; short ones stay whole (no merge pass).  Depends only on sizes the workspace
+// query also sees.
+int32_t auto_partition(int32_t B, int32_t Hq, int32_t max_seq_len) {
+  (void)B;
+  (void)Hq;
+  (void)max_seq_len;
+  return 512;
+}
+
+}  // namespace pa
+
+extern "C" {
+
+int pa_kv_append(const void* k_new, const void* v_new, const int64_t* slot_mapping,
+                 void* k_cache, void* v_cache, int32_t B, int32_t Hkv, int32_t D, int32_t bs,
+                 int32_t NB, int32_t kv_dtype, void* stream) {
+  if (B < 0 || Hkv < 1 || NB < 1 || (D != 64 && D != 128)) return PA_ERR_INVALID;
+  if (bs != pa::kBlockSize) return PA_ERR_UNSUPPORTED;
+  if (kv_dtype != PA_F32 && kv_dtype != PA_BF16) {
+    return kv_dtype == PA_I8 ? PA_ERR_UNSUPPORTED : PA_ERR_INVALID;
+  }
+  if (B == 0) return PA_OK;
+  if (!k_new || !v_new || !slot_mapping || !k_cache || !v_cache) return PA_ERR_INVALID;
+  return status_of(pa::launch_kv_append(k_new, v_new, slot_mapping, k_cache, v_cache, B, Hkv, D,
+                                        NB, elem_bytes(kv_dtype),
+                                        static_cast<hipStream_t>(stream)));
+}
+
+int pa_copy_blocks(void* k_cache, void* v_cache, float* k_scale, float* v_scale,
+                   const int32_t* pairs, int32_t n, int32_t Hkv, int32_t D, int32_t bs,
+                   int32_t NB, int32_t kv_dtype, void* stream) {
+  if (n < 0 || Hkv < 1 || NB < 1 || (D != 64 && D != 128)) return PA_ERR_INVALID;
+  if (bs != pa::kBlockSize) return PA_ERR_UNSUPPORTED;
+  const int eb = elem_bytes(kv_dtype);
+  if (eb == 0) return PA_ERR_INVALID;
+  if (n == 0) return PA_OK;
+  if (!k_cache || !v_cache || !pairs) return PA_ERR_INVALID;
+  if (kv_dtype == PA_I8 && (!k_scale || !v_scale)) return PA_ERR_INVALID;
+  if (kv_dtype != PA_I8) k_scale = v_scale = nullptr;
+  return status_of(pa::launch_copy_blocks(k_cache, v_cache, k_scale, v_scale, pairs, n, Hkv, D,
+                                          NB, eb, static_cast<hipStream_t>(stream)));
+}
+
+int pa_update_block_tables(int32_t* block_tables, int32_t max_blocks, int32_t B,
+                           const int32_t* updates, int32_t n, void* stream) {
+  if (n < 0 || B < 0 || max_blocks < 0) return PA_ERR_INVALID;
+  if (n == 0) return PA_OK;
+  if (!block_tables || !updates) return PA_ERR_INVALID;
+  return status_of(pa::launch_update_tables(block_tables, max_blocks, B, updates, n,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+size_t pa_decode_workspace_size(int32_t B, int32_t Hq, int32_t D, int32_t max_seq_len,
+                                int32_t partition_tokens) {
+  if (B < 0 || Hq < 1 || D < 1 || max_seq_len < 0 || partition_tokens < 0) return 0;
+  const int32_t P =
+      partition_tokens ? partition_tokens : pa::auto_partition(B, Hq, max_seq_len);
+  const int64_t np = (static_cast<int64_t>(max_seq_len) + P - 1) / P;
+  if (np <= 1) return 256;  // nothing is staged; keep the query non-zero and aligned
+  const int64_t rows = static_cast<int64_t>(B) * Hq * np;
+  const int64_t bytes = rows * (D + 2) * 4;
+  return static_cast<size_t>((bytes + 255) / 256 * 256 + 3 * 256);
+}
+
+int pa_decode(float* out, const void* q, int32_t q_dtype, const void* k_cache,
+              const void* v_cache, int32_t kv_dtype, const float* k_scale, const float* v_scale,
+              const int32_t* block_tables, int32_t max_blocks, const int32_t* seq_lens,
+              int32_t max_seq_len, int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t bs,
+              int32_t NB, float scale, int32_t partition_tokens, void* workspace,
+              size_t workspace_bytes, void* stream) {
+  if (B < 0 || Hq < 1 || Hkv < 1 || NB < 1 || max_blocks < 0 || max_seq_len < 0)
+    return PA_ERR_INVALID;
+  if (Hq % Hkv != 0 || (D != 64 && D != 128)) return PA_ERR_INVALID;
+  if (Hq / Hkv > 16) return PA_ERR_UNSUPPORTED;
+  if (bs != pa::kBlockSize) return PA_ERR_UNSUPPORTED;
+  if (q_dtype != PA_F32 && q_dtype != PA_BF16) return PA_ERR_INVALID;
+  if (elem_bytes(kv_dtype) == 0) return PA_ERR_INVALID;
+  if (static_cast<int64_t>(max_seq_len) > static_cast<int64_t>(max_blocks) * bs)
+    return PA_ERR_INVALID;
+  if (partition_tokens != 0 &&
+      (partition_tokens < 64 || partition_tokens > 8192 || partition_tokens % 64 != 0))
+    return PA_ERR_INVALID;
+  if (!(scale == scale)) return PA_ERR_INVALID;
+  if (B == 0) return PA_OK;
+  if (!out || !q || !k_cache || !v_cache || !seq_lens || (max_blocks > 0 && !block_tables))
+    return PA_ERR_INVALID;
+  if (kv_dtype == PA_I8 && (!k_scale || !v_scale)) return PA_ERR_INVALID;
+
+  pa::DecodeArgs a{};
+  a.out = out;
+  a.q = q;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.tables = block_tables;
+  a.seq_lens = seq_lens;
+  a.max_blocks = max_blocks;
+  a.max_seq_len = max_seq_len;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.D = D;
+  a.NB = NB;
+  a.partition = partition_tokens ? partition_tokens : pa::auto_partition(B, Hq, max_seq_len);
+  const int64_t np = (static_cast<int64_t>(max_seq_len) + a.partition - 1) / a.partition;
+  a.np_max = static_cast<int32_t>(np < 1 ? 1 : np);
+  a.scale_log2 = scale * kLog2e;
+  if (a.np_max > 1) {
+    const size_t need = pa_decode_workspace_size(B, Hq, D, max_seq_len, a.partition);
+    if (!workspace || workspace_bytes < need) return PA_ERR_INVALID;
+    const int64_t rows = static_cast<int64_t>(B) * Hq * a.np_max;
+    char* base = static_cast<char*>(workspace);
+    const int64_t ml_bytes = (rows * 4 + 255) / 256 * 256;
+    a.ws_m = reinterpret_cast<float*>(base);
+    a.ws_l = reinterpret_cast<float*>(base + ml_bytes);
+    a.ws_o = reinterpret_cast<float*>(base + 2 * ml_bytes);
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = pa::launch_decode_generic(a, q_dtype, kv_dtype, s);
+  if (e != hipSuccess) return status_of(e);
+  return status_of(pa::launch_splitk_reduce(a, s));
+}
+
+}  // extern "C"

@@ -1,0 +1,118 @@
+// Writes into the paged cache: token append, copy-on-write block copies, block-table patches.
+//
+// Append ("How LLM Inference Serving Works", "What the KV Cache Is, and How Big It Gets": every
+// decode step appends one token's K and V; "The Life of a Request": into the request's current
+// block).  Copy-on-write ("Sharing comes for free": a shared block is copied only when a branch
+// writes to it).  All three are bit copies; they move a few KiB to a few MiB per step and are
+// bound by launch latency, so they favour simple, fully coalesced addressing over occupancy
+// tuning.
+#include "internal.h"
+
+namespace pa {
+namespace {
+
+// One thread per element of k_new / v_new.  K rows are contiguous in the tile; V is dim-major,
+// so consecutive d land 32 B (bf16) apart -- the write is small enough for that not to matter.
+template <typename T>
+__global__ void __launch_bounds__(256) kv_append_kernel(const T* __restrict__ k_new,
+                                                        const T* __restrict__ v_new,
+                                                        const int64_t* __restrict__ slots,
+                                                        T* __restrict__ k_cache,
+                                                        T* __restrict__ v_cache, int32_t B,
+                                                        int32_t Hkv, int32_t D, int32_t NB) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t total = static_cast<int64_t>(B) * Hkv * D;
+  if (i >= total) return;
+  const int32_t d = static_cast<int32_t>(i % D);
+  const int32_t g = static_cast<int32_t>((i / D) % Hkv);
+  const int32_t b = static_cast<int32_t>(i / (static_cast<int64_t>(D) * Hkv));
+  const int64_t slot = slots[b];
+  if (slot < 0 || slot >= static_cast<int64_t>(NB) * kBlockSize) return;
+  const int64_t blk = slot / kBlockSize;
+  const int32_t off = static_cast<int32_t>(slot % kBlockSize);
+  const int64_t tile = (blk * Hkv + g);
+  k_cache[(tile * kBlockSize + off) * D + d] = k_new[i];
+  v_cache[(tile * D + d) * kBlockSize + off] = v_new[i];
+}
+
+// One workgroup per pair; its threads stride over the 16-byte chunks of the K and V tiles.
+__global__ void __launch_bounds__(256) copy_blocks_kernel(uint4* __restrict__ k_cache,
+                                                          uint4* __restrict__ v_cache,
+                                                          float* __restrict__ k_scale,
+                                                          float* __restrict__ v_scale,
+                                                          const int32_t* __restrict__ pairs,
+                                                          int32_t chunks, int32_t Hkv,
+                                                          int32_t NB) {
+  const int32_t src = pairs[2 * blockIdx.x];
+  const int32_t dst = pairs[2 * blockIdx.x + 1];
+  if (src < 0 || src >= NB || dst < 0 || dst >= NB) return;
+  const int64_t s0 = static_cast<int64_t>(src) * chunks;
+  const int64_t d0 = static_cast<int64_t>(dst) * chunks;
+  for (int32_t c = threadIdx.x; c < chunks; c += blockDim.x) {
+    k_cache[d0 + c] = k_cache[s0 + c];
+    v_cache[d0 + c] = v_cache[s0 + c];
+  }
+  if (k_scale) {
+    for (int32_t g = threadIdx.x; g < Hkv; g += blockDim.x) {
+      k_scale[static_cast<int64_t>(dst) * Hkv + g] = k_scale[static_cast<int64_t>(src) * Hkv + g];
+      v_scale[static_cast<int64_t>(dst) * Hkv + g] = v_scale[static_cast<int64_t>(src) * Hkv + g];
+    }
+  }
+}
+
+__global__ void __launch_bounds__(256) update_tables_kernel(int32_t* __restrict__ tables,
+                                                            int32_t max_blocks, int32_t B,
+                                                            const int32_t* __restrict__ upd,
+                                                            int32_t n) {
+  const int32_t i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const int32_t row = upd[3 * i], j = upd[3 * i + 1], blk = upd[3 * i + 2];
+  if (row < 0 || row >= B || j < 0 || j >= max_blocks) return;
+  tables[static_cast<int64_t>(row) * max_blocks + j] = blk;
+}
+
+}  // namespace
+
+hipError_t launch_kv_append(const void* k_new, const void* v_new, const int64_t* slots,
+                            void* k_cache, void* v_cache, int32_t B, int32_t Hkv, int32_t D,
+                            int32_t NB, int32_t elem_bytes, hipStream_t stream) {
+  const int64_t total = static_cast<int64_t>(B) * Hkv * D;
+  if (total == 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>((total + 255) / 256));
+  if (elem_bytes == 4) {
+    hipLaunchKernelGGL(kv_append_kernel<uint32_t>, grid, dim3(256), 0, stream,
+                       static_cast<const uint32_t*>(k_new), static_cast<const uint32_t*>(v_new),
+                       slots, static_cast<uint32_t*>(k_cache), static_cast<uint32_t*>(v_cache),
+                       B, Hkv, D, NB);
+  } else if (elem_bytes == 2) {
+    hipLaunchKernelGGL(kv_append_kernel<uint16_t>, grid, dim3(256), 0, stream,
+                       static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new),
+                       slots, static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache),
+                       B, Hkv, D, NB);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_blocks(void* k_cache, void* v_cache, float* k_scale, float* v_scale,
+                              const int32_t* pairs, int32_t n, int32_t Hkv, int32_t D,
+                              int32_t NB, int32_t elem_bytes, hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  const int64_t tile_bytes = static_cast<int64_t>(Hkv) * kBlockSize * D * elem_bytes;
+  const int32_t chunks = static_cast<int32_t>(tile_bytes / 16);
+  hipLaunchKernelGGL(copy_blocks_kernel, dim3(n), dim3(256), 0, stream,
+                     static_cast<uint4*>(k_cache), static_cast<uint4*>(v_cache), k_scale, v_scale,
+                     pairs, chunks, Hkv, NB);
+  return hipGetLastError();
+}
+
+hipError_t launch_update_tables(int32_t* tables, int32_t max_blocks, int32_t B,
+                                const int32_t* updates, int32_t n, hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(update_tables_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, tables,
+                     max_blocks, B, updates, n);
+  return hipGetLastError();
+}
+
+}  // namespace pa

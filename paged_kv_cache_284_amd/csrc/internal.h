@@ -1,0 +1,50 @@
+// Internal declarations shared by the device translation units of libpagedkv.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+namespace pa {
+
+constexpr int kBlockSize = 16;  // tokens per KV block (the only size the kernels take)
+
+// Everything one decode launch needs.  Pointers are device pointers.
+struct DecodeArgs {
+  float* out;                 // [B][Hq][D]
+  const void* q;              // [B][Hq][D]
+  const void* k;              // [NB][Hkv][bs][D]
+  const void* v;              // [NB][Hkv][D][bs]
+  const float* k_scale;       // [NB][Hkv] (int8)
+  const float* v_scale;       // [NB][Hkv] (int8)
+  const int32_t* tables;      // [B][max_blocks]
+  const int32_t* seq_lens;    // [B]
+  float* ws_m;                // [B][Hq][np_max]  running max (log2 domain)
+  float* ws_l;                // [B][Hq][np_max]  running sum
+  float* ws_o;                // [B][Hq][np_max][D] normalised partial outputs
+  int32_t max_blocks, max_seq_len;
+  int32_t B, Hq, Hkv, D, NB;
+  int32_t partition;          // tokens per partition (multiple of 64)
+  int32_t np_max;             // ceil(max_seq_len / partition), >= 1
+  float scale_log2;           // softmax scale * log2(e)
+};
+
+// Partition length the library picks when the caller passes 0.
+int32_t auto_partition(int32_t B, int32_t Hq, int32_t max_seq_len);
+
+hipError_t launch_kv_append(const void* k_new, const void* v_new, const int64_t* slots,
+                            void* k_cache, void* v_cache, int32_t B, int32_t Hkv, int32_t D,
+                            int32_t NB, int32_t elem_bytes, hipStream_t stream);
+hipError_t launch_copy_blocks(void* k_cache, void* v_cache, float* k_scale, float* v_scale,
+                              const int32_t* pairs, int32_t n, int32_t Hkv, int32_t D,
+                              int32_t NB, int32_t elem_bytes, hipStream_t stream);
+hipError_t launch_update_tables(int32_t* tables, int32_t max_blocks, int32_t B,
+                                const int32_t* updates, int32_t n, hipStream_t stream);
+
+// Returns hipErrorNotSupported when no kernel of this family takes the combination.
+hipError_t launch_decode_generic(const DecodeArgs& a, int q_dtype, int kv_dtype,
+                                 hipStream_t stream);
+hipError_t launch_splitk_reduce(const DecodeArgs& a, hipStream_t stream);
+
+}  // namespace pa

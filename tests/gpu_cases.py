@@ -1,0 +1,151 @@
+"""Scaffolding for the GPU parity tests: one workload, run side by side through the library
+(allocator + HIP kernels) and through the oracle, on the same seeded inputs.
+
+The library side and the oracle side each keep their own allocator and their own copy of the
+pools; the only shared things are the seeded draws from ``inputs`` and, for the oracle's host
+pools, a poisoning of every slot that holds no token (NaN for float caches, -128 for int8) so
+that any unmasked read on the device shows up as a NaN or a large error.
+"""
+from __future__ import annotations
+
+import sys
+import time
+
+import numpy as np
+import torch
+
+import inputs
+import paged_kv_cache_284_amd as pkv
+from oracle import attention, cache_ops
+from oracle.allocator import PyAllocator, run_script
+
+TOL = {"f32": 1e-5, "bf16": 8e-3, "i8": 2e-2}
+TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16, "i8": torch.int8}
+
+
+def say(msg: str) -> None:
+    print(f"[gpu-case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def to_device(a: np.ndarray, dtype: str) -> torch.Tensor:
+    a = np.ascontiguousarray(a)
+    if dtype == "bf16":
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to("cuda")
+    return torch.from_numpy(a).to("cuda")
+
+
+def from_device_bits(t: torch.Tensor) -> np.ndarray:
+    t = t.detach().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def poison_unused(pool: dict, w, tables, lens) -> None:
+    """Overwrite every slot that holds no token of any sequence (host pools, in place)."""
+    used = np.zeros((w.NB, w.bs), bool)
+    for row, L in zip(tables, lens):
+        for j in range((int(L) + w.bs - 1) // w.bs):
+            n = min(w.bs, int(L) - j * w.bs)
+            used[row[j], :n] = True
+    blk, slot = np.nonzero(~used)
+    if w.kv_dtype == "i8":
+        pv = inputs.POISON_I8
+    elif w.kv_dtype == "bf16":
+        pv = inputs.POISON_BF16
+    else:
+        pv = np.float32(np.nan)
+    pool["k"][blk, :, slot, :] = pv
+    pool["v"][blk, :, :, slot] = pv
+
+
+class Case:
+    def __init__(self, w, poison: bool = True, steps_ahead: int = None):
+        t0 = time.time()
+        self.w = w
+        order = inputs.free_order(w)
+        ops = inputs.setup_script(w)
+        self.py = PyAllocator(w.NB, w.bs, order)
+        ids = run_script(self.py, ops)
+        self.lib = pkv.Allocator(w.NB, w.bs, order)
+        ids_l = pkv.run_script(self.lib, ops)
+        assert ids == ids_l
+        self.seqs = [ids[b] for b in range(w.B)]
+        steps = w.steps if steps_ahead is None else steps_ahead
+        self.MB = (w.max_len_after(steps) + w.bs - 1) // w.bs + 1
+        self.host = inputs.pool(w)
+        tables, lens = self.py.export(self.seqs, self.MB)
+        if poison:
+            poison_unused(self.host, w, tables, lens)
+        dt = w.kv_dtype
+        self.k = to_device(self.host["k"], dt)
+        self.v = to_device(self.host["v"], dt)
+        self.ks = self.vs = None
+        if dt == "i8":
+            self.ks = torch.from_numpy(self.host["k_scale"]).cuda()
+            self.vs = torch.from_numpy(self.host["v_scale"]).cuda()
+        t_l, _ = self.lib.export(self.seqs, self.MB)
+        assert np.array_equal(t_l, np.array(tables))
+        self.tables = torch.from_numpy(t_l).cuda()
+        self.step_index = 0
+        say(f"{w.describe()} set up in {time.time() - t0:.1f}s")
+
+    # one pass of the path: allocator step, CoW copies, table patch, append, decode
+    def step(self, partition_tokens: int = 0, check_pool: bool = True):
+        w, s = self.w, self.step_index
+        if w.append:
+            slots, pairs, upd = self.lib.step_arrays(self.seqs)
+            slots_p, pairs_p = self.py.step(self.seqs)
+            assert slots.tolist() == slots_p, "slot mapping differs from the oracle allocator"
+            assert [tuple(p) for p in pairs.tolist()] == pairs_p
+            k_new, v_new = inputs.new_tokens(w, s)
+            if len(pairs):
+                pkv.copy_blocks(self.k, self.v, torch.from_numpy(pairs).cuda(), self.ks, self.vs)
+            if len(upd):
+                pkv.update_block_tables(self.tables, torch.from_numpy(upd).cuda())
+            pkv.kv_append(to_device(k_new, w.kv_dtype), to_device(v_new, w.kv_dtype),
+                          torch.from_numpy(slots).cuda(), self.k, self.v)
+            kh, vh, _, _ = cache_ops.copy_blocks(self.host["k"], self.host["v"], pairs_p)
+            self.host["k"], self.host["v"] = cache_ops.append(kh, vh, k_new, v_new, slots_p, w.bs)
+        tables_p, lens_p = self.py.export(self.seqs, self.MB)
+        tables_p = np.array(tables_p, np.int32)
+        lens_p = np.array(lens_p, np.int32)
+        dev_tables = self.tables.cpu().numpy()
+        live = tables_p >= 0
+        assert np.array_equal(dev_tables[live], tables_p[live]), "device block tables differ"
+        if check_pool and w.append:
+            assert np.array_equal(from_device_bits(self.k).view(np.uint8),
+                                  np.ascontiguousarray(self.host["k"]).view(np.uint8))
+            assert np.array_equal(from_device_bits(self.v).view(np.uint8),
+                                  np.ascontiguousarray(self.host["v"]).view(np.uint8))
+        q = inputs.queries(w, s)
+        lens_d = torch.from_numpy(lens_p).cuda()
+        max_len = int(lens_p.max())
+        out = pkv.decode(to_device(q, w.q_dtype), self.k, self.v, self.tables, lens_d, max_len,
+                         w.scale, self.ks, self.vs, partition_tokens=partition_tokens)
+        torch.cuda.synchronize()
+        self.step_index += 1
+        return q, out.cpu().numpy(), tables_p, lens_p
+
+    def oracle(self, q, tables, lens, heads=None):
+        w = self.w
+        return attention.decode_paged(q, w.q_dtype, self.host["k"], self.host["v"], w.kv_dtype,
+                                      tables, lens, w.bs, w.scale, self.host.get("k_scale"),
+                                      self.host.get("v_scale"), heads=heads)
+
+
+def max_err(out, ref, heads=None):
+    if heads is None:
+        return float(np.max(np.abs(out.astype(np.float64) - ref)))
+    return max(float(np.max(np.abs(out[b, h].astype(np.float64) - ref[b, h]))) for b, h in heads)
+
+
+def sample_heads(w, lens, n, seed=0):
+    """Sampled (b, h) rows: the longest and shortest sequences in full, plus random rows."""
+    rng = np.random.default_rng(seed)
+    picks = {(int(np.argmax(lens)), h) for h in range(w.Hq)}
+    picks |= {(int(np.argmin(lens)), h) for h in range(0, w.Hq, max(1, w.G))}
+    for _ in range(n):
+        picks.add((int(rng.integers(w.B)), int(rng.integers(w.Hq))))
+    return sorted(picks)
