@@ -1,0 +1,309 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark for the paged KV cache on one MI355X.
+
+One step is one pass of the whole hot path over the batch:
+  host allocator step (slot of each new token, copy-on-write pairs, table changes)
+  -> one pinned H2D copy of that step's small arrays
+  -> copy_blocks (if any copy-on-write) -> block-table patch -> kv_append -> decode (+ merge).
+Inputs (pools, queries, new tokens) are resident in HBM before the timed region starts.
+
+Prints one JSON line: whole-job tokens/s (B decode tokens per step), the decode kernel's achieved
+HBM GB/s against the MI355X peak (algorithmic bytes / mean launch time from HIP events on the
+launch stream), and the CPU oracle timed on the host cores.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload llama8b_decode]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import subprocess
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0
+METRIC = "paged decode attn: tokens/s + achieved HBM GB/s (% of MI355X peak)"
+KV_BYTES = {"f32": 4, "bf16": 2, "i8": 1}
+
+
+def algorithmic_bytes(w, lens) -> int:
+    """Bytes a decode launch must move at minimum: K/V of every cached token, the int8 scales of
+    every touched (block, KV head) tile, q, out, the table entries in use and the lengths."""
+    lens = np.asarray(lens, np.int64)
+    blocks = (lens + w.bs - 1) // w.bs
+    kv = int(lens.sum()) * w.Hkv * w.D * 2 * KV_BYTES[w.kv_dtype]
+    scales = int(blocks.sum()) * w.Hkv * 2 * 4 if w.kv_dtype == "i8" else 0
+    q = w.B * w.Hq * w.D * KV_BYTES[w.q_dtype]
+    out = w.B * w.Hq * w.D * 4
+    return kv + scales + q + out + int(blocks.sum()) * 4 + w.B * 4
+
+
+def build_workload(name: str, total_steps: int):
+    import inputs
+    if name == "llama8b_decode":
+        return inputs.llama8b_decode(steps=total_steps)
+    if name == "shared_prefix_batch":
+        return inputs.shared_prefix_batch(steps=total_steps)
+    if name == "long_context":
+        return inputs.long_context()
+    if name == "int8_mha":
+        return inputs.int8_mha()
+    if name == "tiny_fp32":
+        return inputs.tiny_fp32()
+    raise SystemExit(f"unknown workload {name}")
+
+
+class StepRunner:
+    """Holds the device state of one workload and runs decode steps through the library."""
+
+    def __init__(self, w, total_steps: int, partition: int = 0):
+        import torch
+        import inputs
+        import paged_kv_cache_284_amd as pkv
+        self.torch, self.pkv, self.w = torch, pkv, w
+        self.partition = partition
+        order = inputs.free_order(w)
+        self.alloc = pkv.Allocator(w.NB, w.bs, order)
+        ids = pkv.run_script(self.alloc, inputs.setup_script(w))
+        self.seqs = np.array([ids[b] for b in range(w.B)], np.int32)
+        steps_len = total_steps if w.append else 0
+        self.MB = (int(w.cached_lengths.max()) + steps_len + w.bs - 1) // w.bs + 1
+        tables, lens = self.alloc.export(self.seqs, self.MB)
+        self.lens = lens.astype(np.int32)
+        pool = inputs.pool(w)
+        dev = "cuda"
+
+        def up(a, dt):
+            a = np.ascontiguousarray(a)
+            if dt == "bf16":
+                return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+            return torch.from_numpy(a).to(dev)
+        self.k = up(pool["k"], w.kv_dtype)
+        self.v = up(pool["v"], w.kv_dtype)
+        self.ks = self.vs = None
+        if w.kv_dtype == "i8":
+            self.ks = up(pool["k_scale"], "f32")
+            self.vs = up(pool["v_scale"], "f32")
+        del pool
+        self.tables = torch.from_numpy(tables).to(dev)
+        # per-step inputs, resident before timing
+        n_inputs = max(total_steps, 1)
+        self.q = [up(inputs.queries(w, s), w.q_dtype) for s in range(n_inputs)]
+        self.new = []
+        if w.append:
+            for s in range(n_inputs):
+                kn, vn = inputs.new_tokens(w, s)
+                self.new.append((up(kn, w.kv_dtype), up(vn, w.kv_dtype)))
+        max_len = int(self.lens.max()) + (total_steps if w.append else 0)
+        self.ws = torch.empty(pkv.decode_workspace_size(w.B, w.Hq, w.D, max_len, partition),
+                              dtype=torch.uint8, device=dev)
+        self.out = torch.empty((w.B, w.Hq, w.D), dtype=torch.float32, device=dev)
+        # staging for the per-step host arrays: slots int64[B] | pairs i32[B][2] |
+        # updates i32[B][3] | seq_lens i32[B]; two pinned buffers used in turn
+        B = w.B
+        self.off = [0, 8 * B, 8 * B + 8 * B, 8 * B + 8 * B + 12 * B]
+        nbytes = self.off[3] + 4 * B
+        self.pinned = [torch.empty(nbytes, dtype=torch.uint8, pin_memory=True) for _ in range(2)]
+        self.pin_ready = [None, None]
+        self.stage = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        self.step_no = 0
+        self.ev = []
+
+    def step(self, time_decode: bool = False):
+        torch, pkv, w = self.torch, self.pkv, self.w
+        s = self.step_no
+        n_cow = n_upd = 0
+        if w.append:
+            slots, pairs, upd = self.alloc.step_arrays(self.seqs)
+            self.lens += 1
+            n_cow, n_upd = len(pairs), len(upd)
+            i = s % 2
+            if self.pin_ready[i] is not None:
+                self.pin_ready[i].synchronize()
+            buf = self.pinned[i].numpy()
+            B = w.B
+            buf[self.off[0]:self.off[0] + 8 * B].view(np.int64)[:] = slots
+            if n_cow:
+                buf[self.off[1]:self.off[1] + 8 * n_cow].view(np.int32)[:] = pairs.reshape(-1)
+            if n_upd:
+                buf[self.off[2]:self.off[2] + 12 * n_upd].view(np.int32)[:] = upd.reshape(-1)
+            buf[self.off[3]:self.off[3] + 4 * B].view(np.int32)[:] = self.lens
+            self.stage.copy_(self.pinned[i], non_blocking=True)
+            ev = torch.cuda.Event()
+            ev.record()
+            self.pin_ready[i] = ev
+            st = self.stage
+            slots_d = st[self.off[0]:self.off[0] + 8 * B].view(torch.int64)
+            if n_cow:
+                pkv.copy_blocks(self.k, self.v, st[self.off[1]:self.off[1] + 8 * n_cow]
+                                .view(torch.int32).view(n_cow, 2), self.ks, self.vs)
+            if n_upd:
+                pkv.update_block_tables(self.tables, st[self.off[2]:self.off[2] + 12 * n_upd]
+                                        .view(torch.int32).view(n_upd, 3))
+            kn, vn = self.new[s % len(self.new)]
+            pkv.kv_append(kn, vn, slots_d, self.k, self.v)
+            lens_d = st[self.off[3]:self.off[3] + 4 * B].view(torch.int32)
+        else:
+            if s == 0:
+                self.lens_dev = torch.from_numpy(self.lens).cuda()
+            lens_d = self.lens_dev
+        max_len = int(self.lens.max())
+        if time_decode:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+        pkv.decode(self.q[s % len(self.q)], self.k, self.v, self.tables, lens_d, max_len, w.scale,
+                   self.ks, self.vs, out=self.out, workspace=self.ws,
+                   partition_tokens=self.partition)
+        if time_decode:
+            e1.record()
+            self.ev.append((e0, e1, self.lens.copy()))
+        self.step_no += 1
+
+
+def cpu_baseline(name: str, min_seconds: float = 10.0) -> dict:
+    """Time the fp64 oracle on one decode step of the same workload, one thread, in a child
+    process (input generation excluded)."""
+    env = dict(os.environ, OMP_NUM_THREADS="1", OPENBLAS_NUM_THREADS="1", MKL_NUM_THREADS="1")
+    code = f"""
+import sys, time, json, numpy as np
+sys.path.insert(0, {ROOT!r})
+import inputs
+from oracle import attention
+from oracle.allocator import PyAllocator, run_script
+from bench import build_workload
+w = build_workload({name!r}, 1)
+a = PyAllocator(w.NB, w.bs, inputs.free_order(w))
+ids = run_script(a, inputs.setup_script(w))
+seqs = [ids[b] for b in range(w.B)]
+if w.append:
+    a.step(seqs)
+tables, lens = a.export(seqs, max(len(a.table(s)) for s in seqs))
+pool = inputs.pool(w)
+q = inputs.queries(w, 0)
+reps, t0 = 0, time.perf_counter()
+while True:
+    attention.decode_paged(q, w.q_dtype, pool["k"], pool["v"], w.kv_dtype, tables, lens, w.bs,
+                           w.scale, pool.get("k_scale"), pool.get("v_scale"))
+    reps += 1
+    el = time.perf_counter() - t0
+    if el >= {min_seconds}:
+        break
+print(json.dumps({{"reps": reps, "seconds": el, "B": w.B}}))
+"""
+    r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True,
+                       cwd=ROOT)
+    if r.returncode != 0:
+        return {"value": None, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+                "sample": f"failed: {r.stderr[-300:]}"}
+    d = json.loads(r.stdout.strip().splitlines()[-1])
+    tps = d["B"] * d["reps"] / d["seconds"]
+    return {"value": round(tps, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{d['reps']} full decode step(s) of the workload (B={d['B']}, all heads, "
+                      f"fp64 numpy, 1 thread) in {d['seconds']:.1f} s"}
+
+
+def traffic_from_profiles(kernel_src_hash: str):
+    """HBM bytes per decode launch from the committed counter summary, when it was taken on the
+    current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", "decode_traffic.json")
+    try:
+        with open(path) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if d.get("kernel_sources_sha256") != kernel_src_hash:
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def kernel_sources_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "paged_kv_cache_284_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h", ".cpp")):
+            with open(os.path.join(csrc, f), "rb") as fh:
+                h.update(f.encode() + fh.read())
+    return h.hexdigest()
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llama8b_decode")
+    ap.add_argument("--partition", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the decode path shards by sequence or KV head with no "
+              "exchange, and this build runs and reports a single MI355X only.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        raise SystemExit("no GPU visible")
+    import paged_kv_cache_284_amd as pkv
+    pkv.lib()
+
+    total = args.warmup + args.steps
+    w = build_workload(args.workload, total)
+    runner = StepRunner(w, total, args.partition)
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        runner.step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        runner.step(time_decode=True)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    ms = [e0.elapsed_time(e1) for e0, e1, _ in runner.ev]
+    byts = [algorithmic_bytes(w, lens) for _, _, lens in runner.ev]
+    mean_ms = float(np.mean(ms))
+    achieved = float(np.mean(byts)) / (mean_ms * 1e-3) / 1e9
+    tokens_per_s = w.B * args.steps / elapsed
+    traffic = traffic_from_profiles(kernel_sources_hash())
+
+    rec = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"bf16": "bf16", "f32": "f32", "i8": "i8"}[w.kv_dtype],
+        "data": "synthetic (seeded N(0,1) K/V/q, shapes of the workload; no weights)",
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "head_dim": w.D,
+                   "block_size": w.bs, "kv_dtype": w.kv_dtype, "q_dtype": w.q_dtype,
+                   "context_tokens_first_step": int(w.lengths.sum()), "pool_blocks": w.NB,
+                   "partition_tokens": args.partition or "auto"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
+                     "traffic": traffic},
+        "decode_ms_mean": round(mean_ms, 5),
+        "decode_ms_p10_p90": [round(float(np.percentile(ms, 10)), 5),
+                              round(float(np.percentile(ms, 90)), 5)],
+        "decode_algorithmic_bytes_mean": int(np.mean(byts)),
+        "decode_tokens_per_s": round(w.B / (mean_ms * 1e-3), 1),
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -150,7 +150,11 @@ int pa_decode(float* out, const void* q, int32_t q_dtype, const void* k_cache,
     a.ws_o = reinterpret_cast<float*>(base + 2 * ml_bytes);
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = pa::launch_decode_generic(a, q_dtype, kv_dtype, s);
+  const int G = Hq / Hkv;
+  const bool mfma = q_dtype == PA_BF16 && kv_dtype == PA_BF16 &&
+                    (G == 1 || G == 2 || G == 4 || G == 8 || G == 16);
+  hipError_t e = mfma ? pa::launch_decode_mfma(a, s)
+                      : pa::launch_decode_generic(a, q_dtype, kv_dtype, s);
   if (e != hipSuccess) return status_of(e);
   return status_of(pa::launch_splitk_reduce(a, s));
 }
