@@ -2,9 +2,10 @@
 """Decode-step benchmark for the paged KV cache on one MI355X.
 
 One step is one pass of the whole hot path over the batch:
-  host allocator step (slot of each new token, copy-on-write pairs, table changes)
-  -> one pinned H2D copy of that step's small arrays
-  -> copy_blocks (if any copy-on-write) -> block-table patch -> kv_append -> decode (+ merge).
+  host allocator step (slot of each new token, lengths, table changes, copy-on-write pairs)
+  written straight into pinned memory -> one H2D copy of those arrays
+  -> copy_blocks (only when a copy-on-write arose) -> fused append + block-table patch
+  -> decode (+ merge of split segments).
 Inputs (pools, queries, new tokens) are resident in HBM before the timed region starts.
 
 Prints one JSON line: whole-job tokens/s (B decode tokens per step), the decode kernel's achieved
@@ -43,6 +44,44 @@ def algorithmic_bytes(w, lens) -> int:
     q = w.B * w.Hq * w.D * KV_BYTES[w.q_dtype]
     out = w.B * w.Hq * w.D * 4
     return kv + scales + q + out + int(blocks.sum()) * 4 + w.B * 4
+
+
+class HipEvents:
+    """HIP events created with hipEventDisableSystemFence: recording them costs no system-scope
+    cache writeback / invalidation, so they time the stream without stretching it (a default
+    event adds a ~6 us bubble before the next launch on MI355X)."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self):
+        import ctypes as C
+        self.C = C
+        self.hip = C.CDLL("libamdhip64.so.7")  # the runtime torch already loaded
+        self.hip.hipEventCreateWithFlags.argtypes = [C.POINTER(C.c_void_p), C.c_uint]
+        self.hip.hipEventRecord.argtypes = [C.c_void_p, C.c_void_p]
+        self.hip.hipEventSynchronize.argtypes = [C.c_void_p]
+        self.hip.hipEventElapsedTime.argtypes = [C.POINTER(C.c_float), C.c_void_p, C.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [C.c_void_p]
+
+    def create(self):
+        e = self.C.c_void_p()
+        if self.hip.hipEventCreateWithFlags(self.C.byref(e), self.DISABLE_SYSTEM_FENCE) != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed")
+        return e
+
+    def record(self, e, stream):
+        if self.hip.hipEventRecord(e, stream) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def sync(self, e):
+        if self.hip.hipEventSynchronize(e) != 0:
+            raise RuntimeError("hipEventSynchronize failed")
+
+    def elapsed_ms(self, e0, e1) -> float:
+        ms = self.C.c_float()
+        if self.hip.hipEventElapsedTime(self.C.byref(ms), e0, e1) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
 
 
 def build_workload(name: str, total_steps: int):
@@ -102,69 +141,95 @@ class StepRunner:
                 kn, vn = inputs.new_tokens(w, s)
                 self.new.append((up(kn, w.kv_dtype), up(vn, w.kv_dtype)))
         max_len = int(self.lens.max()) + (total_steps if w.append else 0)
-        self.ws = torch.empty(pkv.decode_workspace_size(w.B, w.Hq, w.D, max_len, partition),
+        self.ws = torch.empty(pkv.decode_workspace_size(w.B, w.Hq, w.Hkv, w.D, max_len, partition),
                               dtype=torch.uint8, device=dev)
         self.out = torch.empty((w.B, w.Hq, w.D), dtype=torch.float32, device=dev)
-        # staging for the per-step host arrays: slots int64[B] | pairs i32[B][2] |
-        # updates i32[B][3] | seq_lens i32[B]; two pinned buffers used in turn
+        # staging for the per-step host arrays, written by pa_step straight into pinned memory:
+        # slots int64[B] | seq_lens int32[B] | table_index int32[B] | cow pairs int32[B][2];
+        # two pinned buffers used in turn, one device copy
         B = w.B
-        self.off = [0, 8 * B, 8 * B + 8 * B, 8 * B + 8 * B + 12 * B]
-        nbytes = self.off[3] + 4 * B
+        self.off = [0, 8 * B, 12 * B, 16 * B]
+        nbytes = 24 * B
         self.pinned = [torch.empty(nbytes, dtype=torch.uint8, pin_memory=True) for _ in range(2)]
-        self.pin_ready = [None, None]
+        self.hev = HipEvents()
+        # decode timing events, recorded before / after each decode; the one before step s's
+        # decode also marks its staging copy done, which guards pinned buffer s % 2
+        self.n_ev = total_steps + 2
+        self.ev_before = [self.hev.create() for _ in range(self.n_ev)]
+        self.ev_after = [self.hev.create() for _ in range(self.n_ev)]
+        self.timed = []
         self.stage = torch.empty(nbytes, dtype=torch.uint8, device=dev)
         self.step_no = 0
-        self.ev = []
+        self.max_len = int(self.lens.max())
+        # ctypes arguments that do not change from step to step
+        import ctypes as C
+        self.C = C
+        L = pkv.lib()
+        self.L = L
+        self.n_cow = C.c_int32()
+        self.seqs_p = self.seqs.ctypes.data_as(C.POINTER(C.c_int32))
+        self.hp = [[C.cast(pb.data_ptr() + o, C.POINTER(C.c_int64 if j == 0 else C.c_int32))
+                    for j, o in enumerate(self.off)] for pb in self.pinned]
+        sd = self.stage.data_ptr()
+        self.d_slots, self.d_lens, self.d_tidx, self.d_pairs = (sd + o for o in self.off)
+        self.kv_code = {"f32": pkv.PA_F32, "bf16": pkv.PA_BF16, "i8": pkv.PA_I8}[w.kv_dtype]
+        self.q_code = {"f32": pkv.PA_F32, "bf16": pkv.PA_BF16}[w.q_dtype]
+        self.stream = torch.cuda.current_stream().cuda_stream
+        self.ks_p = self.ks.data_ptr() if self.ks is not None else None
+        self.vs_p = self.vs.data_ptr() if self.vs is not None else None
+        if not w.append:
+            self.lens_dev = torch.from_numpy(self.lens).to(dev)
 
     def step(self, time_decode: bool = False):
-        torch, pkv, w = self.torch, self.pkv, self.w
+        """One decode step through the C ABI: allocator step into pinned memory, one H2D copy,
+        copy-on-write copies (if any), fused append + table patch, decode."""
+        torch, pkv, w, L = self.torch, self.pkv, self.w, self.L
         s = self.step_no
-        n_cow = n_upd = 0
         if w.append:
-            slots, pairs, upd = self.alloc.step_arrays(self.seqs)
-            self.lens += 1
-            n_cow, n_upd = len(pairs), len(upd)
             i = s % 2
-            if self.pin_ready[i] is not None:
-                self.pin_ready[i].synchronize()
-            buf = self.pinned[i].numpy()
-            B = w.B
-            buf[self.off[0]:self.off[0] + 8 * B].view(np.int64)[:] = slots
-            if n_cow:
-                buf[self.off[1]:self.off[1] + 8 * n_cow].view(np.int32)[:] = pairs.reshape(-1)
-            if n_upd:
-                buf[self.off[2]:self.off[2] + 12 * n_upd].view(np.int32)[:] = upd.reshape(-1)
-            buf[self.off[3]:self.off[3] + 4 * B].view(np.int32)[:] = self.lens
+            if s >= 2:
+                self.hev.sync(self.ev_before[s - 2])
+            hp = self.hp[i]
+            st = L.pa_step(self.alloc._h, self.seqs_p, w.B, hp[0], hp[1], hp[2], hp[3],
+                           self.C.byref(self.n_cow))
+            if st != 0:
+                raise pkv.PagedKVError(st, "pa_step")
             self.stage.copy_(self.pinned[i], non_blocking=True)
-            ev = torch.cuda.Event()
-            ev.record()
-            self.pin_ready[i] = ev
-            st = self.stage
-            slots_d = st[self.off[0]:self.off[0] + 8 * B].view(torch.int64)
+            self.max_len += 1
+            n_cow = self.n_cow.value
             if n_cow:
-                pkv.copy_blocks(self.k, self.v, st[self.off[1]:self.off[1] + 8 * n_cow]
-                                .view(torch.int32).view(n_cow, 2), self.ks, self.vs)
-            if n_upd:
-                pkv.update_block_tables(self.tables, st[self.off[2]:self.off[2] + 12 * n_upd]
-                                        .view(torch.int32).view(n_upd, 3))
+                st = L.pa_copy_blocks(self.k.data_ptr(), self.v.data_ptr(), self.ks_p, self.vs_p,
+                                      self.d_pairs, n_cow, w.Hkv, w.D, w.bs, w.NB, self.kv_code,
+                                      self.stream)
+                if st != 0:
+                    raise pkv.PagedKVError(st, "pa_copy_blocks")
             kn, vn = self.new[s % len(self.new)]
-            pkv.kv_append(kn, vn, slots_d, self.k, self.v)
-            lens_d = st[self.off[3]:self.off[3] + 4 * B].view(torch.int32)
+            st = L.pa_append_step(kn.data_ptr(), vn.data_ptr(), self.d_slots, self.d_tidx,
+                                  self.k.data_ptr(), self.v.data_ptr(), self.tables.data_ptr(),
+                                  self.MB, w.B, w.Hkv, w.D, w.bs, w.NB, self.kv_code, self.stream)
+            if st != 0:
+                raise pkv.PagedKVError(st, "pa_append_step")
+            lens_d = self.d_lens
+            self.lens += 1
         else:
-            if s == 0:
-                self.lens_dev = torch.from_numpy(self.lens).cuda()
-            lens_d = self.lens_dev
-        max_len = int(self.lens.max())
+            lens_d = self.lens_dev.data_ptr()
+        self.hev.record(self.ev_before[s], self.stream)
+        st = L.pa_decode(self.out.data_ptr(), self.q[s % len(self.q)].data_ptr(), self.q_code,
+                         self.k.data_ptr(), self.v.data_ptr(), self.kv_code, self.ks_p, self.vs_p,
+                         self.tables.data_ptr(), self.MB, lens_d, self.max_len, w.B, w.Hq, w.Hkv,
+                         w.D, w.bs, w.NB, w.scale, self.partition, self.ws.data_ptr(),
+                         self.ws.numel(), self.stream)
+        if st != 0:
+            raise pkv.PagedKVError(st, "pa_decode")
+        self.hev.record(self.ev_after[s], self.stream)
         if time_decode:
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-        pkv.decode(self.q[s % len(self.q)], self.k, self.v, self.tables, lens_d, max_len, w.scale,
-                   self.ks, self.vs, out=self.out, workspace=self.ws,
-                   partition_tokens=self.partition)
-        if time_decode:
-            e1.record()
-            self.ev.append((e0, e1, self.lens.copy()))
+            self.timed.append((s, self.lens.copy()))
         self.step_no += 1
+
+    def decode_ms(self):
+        """(ms, lengths) of every timed decode launch (after the stream has drained)."""
+        return [(self.hev.elapsed_ms(self.ev_before[s], self.ev_after[s]), lens)
+                for s, lens in self.timed]
 
 
 def cpu_baseline(name: str, min_seconds: float = 10.0) -> dict:
@@ -267,8 +332,9 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
-    ms = [e0.elapsed_time(e1) for e0, e1, _ in runner.ev]
-    byts = [algorithmic_bytes(w, lens) for _, _, lens in runner.ev]
+    timed = runner.decode_ms()
+    ms = [t for t, _ in timed]
+    byts = [algorithmic_bytes(w, lens) for _, lens in timed]
     mean_ms = float(np.mean(ms))
     achieved = float(np.mean(byts)) / (mean_ms * 1e-3) / 1e9
     tokens_per_s = w.B * args.steps / elapsed

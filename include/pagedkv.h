@@ -105,13 +105,18 @@ int pa_seq_reserve(pa_allocator* a, int32_t seq, int32_t n, int64_t* slots, int3
 
 /* One decode step's appends for a batch ([Serving] "The Life of a Request": each step appends
  * one token per request, allocating a block only when the current one fills).  For i in 0..B-1
- * in order, one append to seqs[i]: slots[i] gets its slot; copy-on-write pairs go to
- * cow_pairs[*n_cow][2]; table changes go to table_updates[*n_updates][3] as (i, logical block,
- * physical block) -- a new block or a copy that replaces a shared one -- so that a device copy
- * of the block tables can be patched with pa_update_block_tables.  Both outputs hold at most B
- * entries; table_updates may be NULL.  All or nothing. */
-int pa_step(pa_allocator* a, const int32_t* seqs, int32_t B, int64_t* slots, int32_t* cow_pairs,
-            int32_t* n_cow, int32_t* table_updates, int32_t* n_updates);
+ * in order, one append to seqs[i]:
+ *   slots[i]        its slot;
+ *   seq_lens[i]     (may be NULL) the sequence length after the append;
+ *   table_index[i]  (may be NULL) the logical block whose table entry now holds slots[i]/bs --
+ *                   a new block or the copy that replaced a shared one -- or -1, so that a device
+ *                   copy of the block tables can be patched (pa_update_block_tables,
+ *                   pa_append_step);
+ *   cow_pairs[*n_cow][2]  the (src, dst) copies, in batch order, that must reach the device
+ *                   before any of the step's writes (pa_copy_blocks).  At most B entries.
+ * All or nothing. */
+int pa_step(pa_allocator* a, const int32_t* seqs, int32_t B, int64_t* slots, int32_t* seq_lens,
+            int32_t* table_index, int32_t* cow_pairs, int32_t* n_cow);
 
 /* Drop a sequence: each of its blocks loses a reference; blocks left with none go to the tail
  * of the free list in table order ([Serving] "The Life of a Request"). */
@@ -152,16 +157,25 @@ int pa_copy_blocks(void* k_cache, void* v_cache, float* k_scale, float* v_scale,
                    const int32_t* pairs, int32_t n, int32_t Hkv, int32_t D, int32_t bs,
                    int32_t NB, int32_t kv_dtype, void* stream);
 
-/* Patch a device block table with pa_step's table_updates: updates is device [n][3] int32
- * (row, logical block, physical block); block_tables[row][logical] = physical.  Rows outside
- * [0, B) or logical blocks outside [0, max_blocks) are skipped. */
-int pa_update_block_tables(int32_t* block_tables, int32_t max_blocks, int32_t B,
-                           const int32_t* updates, int32_t n, void* stream);
+/* Patch a device block table after pa_step: for every i < B with table_index[i] >= 0,
+ * block_tables[i][table_index[i]] = slots[i] / bs.  slots (int64) and table_index (int32) are
+ * device [B] arrays; entries outside [0, max_blocks) are skipped. */
+int pa_update_block_tables(int32_t* block_tables, int32_t max_blocks, const int64_t* slots,
+                           const int32_t* table_index, int32_t B, int32_t bs, void* stream);
 
-/* Bytes of scratch that pa_decode needs for these sizes (partition_tokens as for pa_decode).
- * Returns 0 for invalid sizes. */
-size_t pa_decode_workspace_size(int32_t B, int32_t Hq, int32_t D, int32_t max_seq_len,
-                                int32_t partition_tokens);
+/* pa_kv_append and pa_update_block_tables in one launch: the cache writes of a decode step once
+ * its copy-on-write copies (pa_copy_blocks) are enqueued.  Arguments as for those two calls;
+ * table_index may be NULL (no table changes). */
+int pa_append_step(const void* k_new, const void* v_new, const int64_t* slot_mapping,
+                   const int32_t* table_index, void* k_cache, void* v_cache,
+                   int32_t* block_tables, int32_t max_blocks, int32_t B, int32_t Hkv, int32_t D,
+                   int32_t bs, int32_t NB, int32_t kv_dtype, void* stream);
+
+/* Bytes of scratch that pa_decode needs for these sizes (same partition_tokens as the decode
+ * call).  Returns 0 for invalid sizes.  The size does not depend on the lengths themselves, so a
+ * buffer sized once for the largest max_seq_len serves every step. */
+size_t pa_decode_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                                int32_t max_seq_len, int32_t partition_tokens);
 
 /* Decode attention over the paged cache ([Serving] "What the KV Cache Is": the new token's
  * query is compared with the key of every cached token and the values are mixed by those
@@ -173,9 +187,13 @@ size_t pa_decode_workspace_size(int32_t B, int32_t Hq, int32_t D, int32_t max_se
  *   q_dtype:  PA_F32 or PA_BF16.  kv_dtype: PA_F32, PA_BF16 or PA_I8 (then k_scale/v_scale).
  *   Hq % Hkv == 0, Hq/Hkv <= 16, D in {64, 128}, bs == 16.
  *   max_seq_len: host bound on every seq_lens[b], 0 <= max_seq_len <= max_blocks*bs.
- *   partition_tokens: 0 picks a size; else a multiple of 64 in [64, 8192].  Sequences longer
- *     than one partition are split ("split-K") and merged with the log-sum-exp identity.
- *   workspace: device buffer of workspace_bytes >= pa_decode_workspace_size(...).
+ *   partition_tokens: 0 = balanced schedule: the block pairs of all (sequence, KV head)
+ *     segments are split into equal spans, one per resident workgroup, whatever the length mix
+ *     (bf16 caches; other dtypes fall back to fixed 512-token partitions).  Otherwise a multiple
+ *     of 64 in [64, 8192]: one workgroup per partition of that many tokens.  Either way a
+ *     segment cut into several pieces ("split-K") is merged with the log-sum-exp identity.
+ *   workspace: device buffer of workspace_bytes >= pa_decode_workspace_size(...); its contents
+ *     need no initialisation and are scratch after the call.
  * The softmax runs in fp32 with exp computed as exp2 of a log2(e)-scaled argument. */
 int pa_decode(float* out, const void* q, int32_t q_dtype, const void* k_cache,
               const void* v_cache, int32_t kv_dtype, const float* k_scale, const float* v_scale,

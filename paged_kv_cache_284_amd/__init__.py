@@ -54,8 +54,10 @@ _SIGNATURES = {
     "pa_kv_append": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
     "pa_copy_blocks": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                                  _vp]),
-    "pa_update_block_tables": (C.c_int, [_vp, _i32, _i32, _vp, _i32, _vp]),
-    "pa_decode_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32]),
+    "pa_update_block_tables": (C.c_int, [_vp, _i32, _vp, _vp, _i32, _i32, _vp]),
+    "pa_append_step": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                                 _i32, _i32, _vp]),
+    "pa_decode_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "pa_decode": (C.c_int, [_vp, _vp, _i32, _vp, _vp, _i32, _vp, _vp, _vp, _i32, _vp, _i32,
                             _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz, _vp]),
 }
@@ -80,6 +82,10 @@ def lib() -> C.CDLL:
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is missing: build it with "
                                "`python -m paged_kv_cache_284_amd.build`")
+        try:  # let torch bring in its HIP runtime first, so the process holds exactly one
+            import torch  # noqa: F401
+        except ImportError:
+            pass
         h = C.CDLL(LIB_PATH)
         for name, (res, args) in _SIGNATURES.items():
             f = getattr(h, name)
@@ -164,21 +170,22 @@ class Allocator:
                "pa_seq_reserve")
         return slots[:n].tolist(), [tuple(p) for p in pairs[:k.value].tolist()]
 
-    def step_arrays(self, seqs) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
-        """One append per listed sequence: (slots int64 [B], cow pairs int32 [n][2],
-        table updates int32 [m][3])."""
+    def step_arrays(self, seqs):
+        """One append per listed sequence: (slots int64 [B], lengths after the append int32 [B],
+        table_index int32 [B] (-1 = no table change), cow pairs int32 [n][2])."""
         s = _i32_array(seqs)
         B = s.size
         slots = np.zeros(max(B, 1), np.int64)
+        lens = np.zeros(max(B, 1), np.int32)
+        tidx = np.zeros(max(B, 1), np.int32)
         pairs = np.zeros((max(B, 1), 2), np.int32)
-        upd = np.zeros((max(B, 1), 3), np.int32)
-        k, u = _i32(), _i32()
-        _check(lib().pa_step(self._h, _p32(s), B, _p64(slots), _p32(pairs), C.byref(k),
-                             _p32(upd), C.byref(u)), "pa_step")
-        return slots[:B], pairs[:k.value], upd[:u.value]
+        k = _i32()
+        _check(lib().pa_step(self._h, _p32(s), B, _p64(slots), _p32(lens), _p32(tidx), _p32(pairs),
+                             C.byref(k)), "pa_step")
+        return slots[:B], lens[:B], tidx[:B], pairs[:k.value]
 
     def step(self, seqs):
-        slots, pairs, _ = self.step_arrays(seqs)
+        slots, _, _, pairs = self.step_arrays(seqs)
         return slots.tolist(), [tuple(p) for p in pairs.tolist()]
 
     def release(self, seq: int) -> None:
@@ -306,19 +313,44 @@ def copy_blocks(k_cache, v_cache, pairs, k_scale=None, v_scale=None, stream=None
                                 NB, _dtype_code(k_cache), _stream(stream)), "pa_copy_blocks")
 
 
-def update_block_tables(block_tables, updates, stream=None) -> None:
-    """Apply (row, logical, physical) rows of updates int32 [n][3] to block_tables [B][MB]."""
+def update_block_tables(block_tables, slots, table_index, stream=None) -> None:
+    """For every i with table_index[i] >= 0: block_tables[i][table_index[i]] = slots[i] // 16."""
     torch = _torch()
     B, MB = block_tables.shape
-    n = updates.shape[0]
-    _check(lib().pa_update_block_tables(_dev(block_tables, "block_tables", torch.int32), MB, B,
-                                        _dev(updates, "updates", torch.int32) if n else None, n,
-                                        _stream(stream)), "pa_update_block_tables")
+    if tuple(slots.shape) != (B,) or tuple(table_index.shape) != (B,):
+        raise ValueError("slots and table_index must be [B]")
+    _check(lib().pa_update_block_tables(_dev(block_tables, "block_tables", torch.int32), MB,
+                                        _dev(slots, "slots", torch.int64),
+                                        _dev(table_index, "table_index", torch.int32), B,
+                                        BLOCK_SIZE, _stream(stream)), "pa_update_block_tables")
 
 
-def decode_workspace_size(B: int, Hq: int, D: int, max_seq_len: int,
+def append_step(k_new, v_new, slot_mapping, table_index, k_cache, v_cache, block_tables,
+                stream=None) -> None:
+    """kv_append and update_block_tables in one launch."""
+    torch = _torch()
+    NB, Hkv, bs, D = k_cache.shape
+    B = k_new.shape[0]
+    if tuple(k_new.shape) != (B, Hkv, D) or tuple(v_new.shape) != (B, Hkv, D):
+        raise ValueError("k_new/v_new must be [B][Hkv][D]")
+    if tuple(v_cache.shape) != (NB, Hkv, D, bs) or tuple(slot_mapping.shape) != (B,):
+        raise ValueError("v_cache must be [NB][Hkv][D][bs], slot_mapping [B]")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be [B][max_blocks]")
+    if k_new.dtype != k_cache.dtype or v_new.dtype != k_cache.dtype or v_cache.dtype != k_cache.dtype:
+        raise TypeError("k_new, v_new, k_cache and v_cache must share one dtype")
+    _check(lib().pa_append_step(_dev(k_new, "k_new"), _dev(v_new, "v_new"),
+                                _dev(slot_mapping, "slot_mapping", torch.int64),
+                                _dev(table_index, "table_index", torch.int32),
+                                _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+                                _dev(block_tables, "block_tables", torch.int32),
+                                block_tables.shape[1], B, Hkv, D, bs, NB, _dtype_code(k_cache),
+                                _stream(stream)), "pa_append_step")
+
+
+def decode_workspace_size(B: int, Hq: int, Hkv: int, D: int, max_seq_len: int,
                           partition_tokens: int = 0) -> int:
-    return int(lib().pa_decode_workspace_size(B, Hq, D, max_seq_len, partition_tokens))
+    return int(lib().pa_decode_workspace_size(B, Hq, Hkv, D, max_seq_len, partition_tokens))
 
 
 def decode(q, k_cache, v_cache, block_tables, seq_lens, max_seq_len: int, scale: float,
@@ -336,7 +368,7 @@ def decode(q, k_cache, v_cache, block_tables, seq_lens, max_seq_len: int, scale:
         out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
     elif tuple(out.shape) != (B, Hq, D):
         raise ValueError("out must be [B][Hq][D]")
-    need = decode_workspace_size(B, Hq, D, max_seq_len, partition_tokens)
+    need = decode_workspace_size(B, Hq, Hkv, D, max_seq_len, partition_tokens)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     _check(lib().pa_decode(_dev(out, "out", torch.float32), _dev(q, "q"), _dtype_code(q),

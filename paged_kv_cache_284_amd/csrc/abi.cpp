@@ -55,8 +55,26 @@ int pa_kv_append(const void* k_new, const void* v_new, const int64_t* slot_mappi
   if (B == 0) return PA_OK;
   if (!k_new || !v_new || !slot_mapping || !k_cache || !v_cache) return PA_ERR_INVALID;
   return status_of(pa::launch_kv_append(k_new, v_new, slot_mapping, k_cache, v_cache, B, Hkv, D,
-                                        NB, elem_bytes(kv_dtype),
+                                        NB, elem_bytes(kv_dtype), nullptr, nullptr, 0,
                                         static_cast<hipStream_t>(stream)));
+}
+
+int pa_append_step(const void* k_new, const void* v_new, const int64_t* slot_mapping,
+                   const int32_t* table_index, void* k_cache, void* v_cache,
+                   int32_t* block_tables, int32_t max_blocks, int32_t B, int32_t Hkv, int32_t D,
+                   int32_t bs, int32_t NB, int32_t kv_dtype, void* stream) {
+  if (B < 0 || Hkv < 1 || NB < 1 || max_blocks < 0 || (D != 64 && D != 128))
+    return PA_ERR_INVALID;
+  if (bs != pa::kBlockSize) return PA_ERR_UNSUPPORTED;
+  if (kv_dtype != PA_F32 && kv_dtype != PA_BF16) {
+    return kv_dtype == PA_I8 ? PA_ERR_UNSUPPORTED : PA_ERR_INVALID;
+  }
+  if (B == 0) return PA_OK;
+  if (!k_new || !v_new || !slot_mapping || !k_cache || !v_cache) return PA_ERR_INVALID;
+  if (table_index && !block_tables) return PA_ERR_INVALID;
+  return status_of(pa::launch_kv_append(k_new, v_new, slot_mapping, k_cache, v_cache, B, Hkv, D,
+                                        NB, elem_bytes(kv_dtype), table_index, block_tables,
+                                        max_blocks, static_cast<hipStream_t>(stream)));
 }
 
 int pa_copy_blocks(void* k_cache, void* v_cache, float* k_scale, float* v_scale,
@@ -74,25 +92,64 @@ int pa_copy_blocks(void* k_cache, void* v_cache, float* k_scale, float* v_scale,
                                           NB, eb, static_cast<hipStream_t>(stream)));
 }
 
-int pa_update_block_tables(int32_t* block_tables, int32_t max_blocks, int32_t B,
-                           const int32_t* updates, int32_t n, void* stream) {
-  if (n < 0 || B < 0 || max_blocks < 0) return PA_ERR_INVALID;
-  if (n == 0) return PA_OK;
-  if (!block_tables || !updates) return PA_ERR_INVALID;
-  return status_of(pa::launch_update_tables(block_tables, max_blocks, B, updates, n,
+int pa_update_block_tables(int32_t* block_tables, int32_t max_blocks, const int64_t* slots,
+                           const int32_t* table_index, int32_t B, int32_t bs, void* stream) {
+  if (B < 0 || max_blocks < 0) return PA_ERR_INVALID;
+  if (bs != pa::kBlockSize) return PA_ERR_UNSUPPORTED;
+  if (B == 0) return PA_OK;
+  if (!block_tables || !slots || !table_index) return PA_ERR_INVALID;
+  return status_of(pa::launch_update_tables(block_tables, max_blocks, slots, table_index, B,
                                             static_cast<hipStream_t>(stream)));
 }
 
-size_t pa_decode_workspace_size(int32_t B, int32_t Hq, int32_t D, int32_t max_seq_len,
-                                int32_t partition_tokens) {
-  if (B < 0 || Hq < 1 || D < 1 || max_seq_len < 0 || partition_tokens < 0) return 0;
+}  // extern "C"
+
+namespace {
+
+int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
+
+// Fixed partitions: m, l [B][Hq][np] and o [B][Hq][np][D].
+int64_t fixed_bytes(int32_t B, int32_t Hq, int32_t D, int64_t np) {
+  if (np <= 1) return 0;
+  const int64_t rows = static_cast<int64_t>(B) * Hq * np;
+  return 2 * align256(rows * 4) + align256(rows * D * 4);
+}
+
+// Balanced schedule: m, l [nw][2][G], o [nw][2][G][D], prefix sums [B + 1].
+int64_t balanced_bytes(int32_t B, int32_t G, int32_t D, int64_t nw) {
+  const int64_t rows = nw * 2 * G;
+  return 2 * align256(rows * 4) + align256(rows * D * 4) + align256((B + 1) * 4);
+}
+
+int cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < 64 && cached[dev] > 0) return cached[dev];
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (dev < 64) cached[dev] = n;
+  return n;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t pa_decode_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                                int32_t max_seq_len, int32_t partition_tokens) {
+  if (B < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || D < 1 || max_seq_len < 0 ||
+      partition_tokens < 0)
+    return 0;
   const int32_t P =
       partition_tokens ? partition_tokens : pa::auto_partition(B, Hq, max_seq_len);
   const int64_t np = (static_cast<int64_t>(max_seq_len) + P - 1) / P;
-  if (np <= 1) return 256;  // nothing is staged; keep the query non-zero and aligned
-  const int64_t rows = static_cast<int64_t>(B) * Hq * np;
-  const int64_t bytes = rows * (D + 2) * 4;
-  return static_cast<size_t>((bytes + 255) / 256 * 256 + 3 * 256);
+  int64_t bytes = fixed_bytes(B, Hq, D, np);
+  if (partition_tokens == 0 && B <= pa::kMaxBalancedBatch) {
+    const int64_t bal = balanced_bytes(B, Hq / Hkv, D, pa::kMaxBalancedWorkgroups);
+    bytes = bytes > bal ? bytes : bal;
+  }
+  return static_cast<size_t>(bytes < 256 ? 256 : bytes);
 }
 
 int pa_decode(float* out, const void* q, int32_t q_dtype, const void* k_cache,
@@ -139,23 +196,42 @@ int pa_decode(float* out, const void* q, int32_t q_dtype, const void* k_cache,
   const int64_t np = (static_cast<int64_t>(max_seq_len) + a.partition - 1) / a.partition;
   a.np_max = static_cast<int32_t>(np < 1 ? 1 : np);
   a.scale_log2 = scale * kLog2e;
-  if (a.np_max > 1) {
-    const size_t need = pa_decode_workspace_size(B, Hq, D, max_seq_len, a.partition);
-    if (!workspace || workspace_bytes < need) return PA_ERR_INVALID;
-    const int64_t rows = static_cast<int64_t>(B) * Hq * a.np_max;
-    char* base = static_cast<char*>(workspace);
-    const int64_t ml_bytes = (rows * 4 + 255) / 256 * 256;
-    a.ws_m = reinterpret_cast<float*>(base);
-    a.ws_l = reinterpret_cast<float*>(base + ml_bytes);
-    a.ws_o = reinterpret_cast<float*>(base + 2 * ml_bytes);
-  }
-  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!workspace || workspace_bytes < pa_decode_workspace_size(B, Hq, Hkv, D, max_seq_len,
+                                                               partition_tokens))
+    return PA_ERR_INVALID;
+
   const int G = Hq / Hkv;
   const bool mfma = q_dtype == PA_BF16 && kv_dtype == PA_BF16 &&
                     (G == 1 || G == 2 || G == 4 || G == 8 || G == 16);
+  const bool balanced = mfma && partition_tokens == 0 && B <= pa::kMaxBalancedBatch;
+  char* base = static_cast<char*>(workspace);
+  if (balanced) {
+    const int cus = cu_count();
+    if (cus <= 0) return PA_ERR_DEVICE;
+    int64_t nw = static_cast<int64_t>(cus) * pa::mfma_workgroups_per_cu();
+    if (nw > pa::kMaxBalancedWorkgroups) nw = pa::kMaxBalancedWorkgroups;
+    const int64_t units = static_cast<int64_t>(Hkv) * B * ((max_seq_len + 31) / 32);
+    if (nw > units) nw = units;
+    if (nw >= 8) nw -= nw % 8;
+    if (nw < 1) nw = 1;
+    a.nw = static_cast<int32_t>(nw);
+    const int64_t rows = nw * 2 * G;
+    a.ws_m = reinterpret_cast<float*>(base);
+    a.ws_l = reinterpret_cast<float*>(base + align256(rows * 4));
+    a.ws_o = reinterpret_cast<float*>(base + 2 * align256(rows * 4));
+    a.ws_cum = reinterpret_cast<int32_t*>(base + 2 * align256(rows * 4) +
+                                          align256(rows * D * 4));
+  } else if (a.np_max > 1) {
+    const int64_t rows = static_cast<int64_t>(B) * Hq * a.np_max;
+    a.ws_m = reinterpret_cast<float*>(base);
+    a.ws_l = reinterpret_cast<float*>(base + align256(rows * 4));
+    a.ws_o = reinterpret_cast<float*>(base + 2 * align256(rows * 4));
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = mfma ? pa::launch_decode_mfma(a, s)
                       : pa::launch_decode_generic(a, q_dtype, kv_dtype, s);
   if (e != hipSuccess) return status_of(e);
+  if (balanced) return PA_OK;
   return status_of(pa::launch_splitk_reduce(a, s));
 }
 

@@ -205,15 +205,14 @@ int pa_seq_reserve(pa_allocator* a, int32_t seq, int32_t n, int64_t* slots, int3
   return PA_OK;
 }
 
-int pa_step(pa_allocator* a, const int32_t* seqs, int32_t B, int64_t* slots, int32_t* cow_pairs,
-            int32_t* n_cow, int32_t* table_updates, int32_t* n_updates) {
+int pa_step(pa_allocator* a, const int32_t* seqs, int32_t B, int64_t* slots, int32_t* seq_lens,
+            int32_t* table_index, int32_t* cow_pairs, int32_t* n_cow) {
   if (!a || B < 0 || (B > 0 && (!seqs || !slots || !cow_pairs)) || !n_cow) return PA_ERR_INVALID;
-  if (table_updates && !n_updates) return PA_ERR_INVALID;
   for (int32_t i = 0; i < B; ++i)
     if (!a->valid_seq(seqs[i])) return PA_ERR_STATE;
   std::vector<LogEntry> log;
   log.reserve(B);
-  int32_t k = 0, u = 0;
+  int32_t k = 0;
   for (int32_t i = 0; i < B; ++i) {
     AppendResult r;
     if (!a->append_one(seqs[i], &r, &log)) {
@@ -226,15 +225,10 @@ int pa_step(pa_allocator* a, const int32_t* seqs, int32_t B, int64_t* slots, int
       cow_pairs[2 * k + 1] = r.dst;
       ++k;
     }
-    if (table_updates && r.logical >= 0) {
-      table_updates[3 * u] = i;
-      table_updates[3 * u + 1] = r.logical;
-      table_updates[3 * u + 2] = a->seqs[seqs[i]].table[r.logical];
-      ++u;
-    }
+    if (table_index) table_index[i] = r.logical;
+    if (seq_lens) seq_lens[i] = a->seqs[seqs[i]].len;
   }
   *n_cow = k;
-  if (n_updates) *n_updates = u;
   return PA_OK;
 }
 

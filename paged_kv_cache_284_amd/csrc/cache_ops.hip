@@ -13,13 +13,18 @@ namespace {
 
 // One thread per element of k_new / v_new.  K rows are contiguous in the tile; V is dim-major,
 // so consecutive d land 32 B (bf16) apart -- the write is small enough for that not to matter.
+// With a table (the fused step), the first thread of each sequence also patches its block-table
+// entry when the step gave the sequence a new or copied block.
 template <typename T>
 __global__ void __launch_bounds__(256) kv_append_kernel(const T* __restrict__ k_new,
                                                         const T* __restrict__ v_new,
                                                         const int64_t* __restrict__ slots,
                                                         T* __restrict__ k_cache,
                                                         T* __restrict__ v_cache, int32_t B,
-                                                        int32_t Hkv, int32_t D, int32_t NB) {
+                                                        int32_t Hkv, int32_t D, int32_t NB,
+                                                        const int32_t* __restrict__ table_index,
+                                                        int32_t* __restrict__ tables,
+                                                        int32_t max_blocks) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   const int64_t total = static_cast<int64_t>(B) * Hkv * D;
   if (i >= total) return;
@@ -33,6 +38,11 @@ __global__ void __launch_bounds__(256) kv_append_kernel(const T* __restrict__ k_
   const int64_t tile = (blk * Hkv + g);
   k_cache[(tile * kBlockSize + off) * D + d] = k_new[i];
   v_cache[(tile * D + d) * kBlockSize + off] = v_new[i];
+  if (tables && g == 0 && d == 0) {
+    const int32_t j = table_index[b];
+    if (j >= 0 && j < max_blocks)
+      tables[static_cast<int64_t>(b) * max_blocks + j] = static_cast<int32_t>(blk);
+  }
 }
 
 // One workgroup per pair; its threads stride over the 16-byte chunks of the K and V tiles.
@@ -61,34 +71,38 @@ __global__ void __launch_bounds__(256) copy_blocks_kernel(uint4* __restrict__ k_
 }
 
 __global__ void __launch_bounds__(256) update_tables_kernel(int32_t* __restrict__ tables,
-                                                            int32_t max_blocks, int32_t B,
-                                                            const int32_t* __restrict__ upd,
-                                                            int32_t n) {
+                                                            int32_t max_blocks,
+                                                            const int64_t* __restrict__ slots,
+                                                            const int32_t* __restrict__ table_index,
+                                                            int32_t B) {
   const int32_t i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= n) return;
-  const int32_t row = upd[3 * i], j = upd[3 * i + 1], blk = upd[3 * i + 2];
-  if (row < 0 || row >= B || j < 0 || j >= max_blocks) return;
-  tables[static_cast<int64_t>(row) * max_blocks + j] = blk;
+  if (i >= B) return;
+  const int32_t j = table_index[i];
+  const int64_t slot = slots[i];
+  if (j < 0 || j >= max_blocks || slot < 0) return;
+  tables[static_cast<int64_t>(i) * max_blocks + j] = static_cast<int32_t>(slot / kBlockSize);
 }
 
 }  // namespace
 
 hipError_t launch_kv_append(const void* k_new, const void* v_new, const int64_t* slots,
                             void* k_cache, void* v_cache, int32_t B, int32_t Hkv, int32_t D,
-                            int32_t NB, int32_t elem_bytes, hipStream_t stream) {
+                            int32_t NB, int32_t elem_bytes, const int32_t* table_index,
+                            int32_t* tables, int32_t max_blocks, hipStream_t stream) {
   const int64_t total = static_cast<int64_t>(B) * Hkv * D;
   if (total == 0) return hipSuccess;
+  if (!table_index) tables = nullptr;
   const dim3 grid(static_cast<unsigned>((total + 255) / 256));
   if (elem_bytes == 4) {
     hipLaunchKernelGGL(kv_append_kernel<uint32_t>, grid, dim3(256), 0, stream,
                        static_cast<const uint32_t*>(k_new), static_cast<const uint32_t*>(v_new),
                        slots, static_cast<uint32_t*>(k_cache), static_cast<uint32_t*>(v_cache),
-                       B, Hkv, D, NB);
+                       B, Hkv, D, NB, table_index, tables, max_blocks);
   } else if (elem_bytes == 2) {
     hipLaunchKernelGGL(kv_append_kernel<uint16_t>, grid, dim3(256), 0, stream,
                        static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new),
                        slots, static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache),
-                       B, Hkv, D, NB);
+                       B, Hkv, D, NB, table_index, tables, max_blocks);
   } else {
     return hipErrorInvalidValue;
   }
@@ -107,11 +121,11 @@ hipError_t launch_copy_blocks(void* k_cache, void* v_cache, float* k_scale, floa
   return hipGetLastError();
 }
 
-hipError_t launch_update_tables(int32_t* tables, int32_t max_blocks, int32_t B,
-                                const int32_t* updates, int32_t n, hipStream_t stream) {
-  if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(update_tables_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, tables,
-                     max_blocks, B, updates, n);
+hipError_t launch_update_tables(int32_t* tables, int32_t max_blocks, const int64_t* slots,
+                                const int32_t* table_index, int32_t B, hipStream_t stream) {
+  if (B == 0) return hipSuccess;
+  hipLaunchKernelGGL(update_tables_kernel, dim3((B + 255) / 256), dim3(256), 0, stream, tables,
+                     max_blocks, slots, table_index, B);
   return hipGetLastError();
 }
 

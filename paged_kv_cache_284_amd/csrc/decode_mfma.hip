@@ -11,10 +11,18 @@
 // possible on everything else; the two small contractions run on MFMA so the vector ALUs only do
 // the softmax.
 //
-// Work split.  One workgroup = 4 waves = one (partition, KV head, sequence).  A partition is a
-// run of whole blocks; the waves take its block *pairs* (32 tokens) in turn and keep private
-// softmax state; the workgroup merges the 4 states in LDS at the end.  Long sequences span
-// several partitions whose normalised outputs are merged by splitk_reduce_kernel.
+// Work split.  The unit of work is a block *pair* (32 tokens) of one (KV head, sequence) segment.
+// A workgroup (4 waves) processes a run of pairs of one segment -- a "piece": its waves take the
+// pairs in turn with private softmax state and merge the 4 states in LDS at the end.  Two
+// schedules decide the pieces:
+//   balanced (default): all segments are laid end to end (KV-head-major, then sequence) and the
+//     unit range is cut into equal contiguous spans, one per resident workgroup, so every
+//     workgroup moves the same number of bytes whatever the length mix.  A span starts and ends
+//     inside at most two segments; those partial pieces are merged by streamk_reduce_kernel.
+//     Workgroups are numbered so that each XCD (blockIdx % 8) takes one contiguous eighth of the
+//     range: sequences that share prefix blocks meet in the same L2.
+//   fixed partitions (caller-given length): one workgroup per (partition, KV head, sequence),
+//     merged by splitk_reduce_kernel.
 //
 // One pair (blocks A, B of one KV head) per wave iteration, v_mfma_f32_16x16x32_bf16 throughout:
 //   scores  S = K . q^T as two 16(token) x 16(head) tiles, K tiles token-major in HBM (each lane
@@ -38,7 +46,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
 constexpr int kPair = 2 * kBlockSize;  // tokens per wave iteration
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
@@ -57,23 +65,18 @@ struct PairRegs {
   int32_t blk_a, blk_b;  // physical blocks, -1 when masked
 };
 
-template <int G, int D>
-__global__ void __launch_bounds__(64 * kWaves) decode_mfma_kernel(DecodeArgs a) {
+template <int G, int D, bool kStream>
+__global__ void __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
+decode_mfma_kernel(DecodeArgs a) {
   using Regs = PairRegs<D>;
   constexpr int kSteps = Regs::kSteps;
   constexpr int kTiles = Regs::kTiles;
 
+  extern __shared__ int32_t cum_s[];  // balanced schedule: pair-count prefix sums, B + 1 entries
   __shared__ float m_s[kWaves][G];
   __shared__ float l_s[kWaves][G];
   __shared__ float o_s[kWaves][G][D];
-
-  const int p = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int L = min(max(a.seq_lens[b], 0), a.max_seq_len);
-  const int nparts = max(1, (L + a.partition - 1) / a.partition);
-  if (p >= nparts) return;
-  const int start = p * a.partition;
-  const int end = min(start + a.partition, L);
-  const int n_pairs = (end - start + kPair - 1) / kPair;
+  __shared__ int32_t wave_tot[kWaves];
 
   const int lane = threadIdx.x % 64;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
@@ -82,17 +85,7 @@ __global__ void __launch_bounds__(64 * kWaves) decode_mfma_kernel(DecodeArgs a) 
 
   const uint16_t* __restrict__ kc = static_cast<const uint16_t*>(a.k);
   const uint16_t* __restrict__ vc = static_cast<const uint16_t*>(a.v);
-  const int32_t* __restrict__ table = a.tables + static_cast<int64_t>(b) * a.max_blocks;
   const int NB = a.NB, Hkv = a.Hkv;
-
-  // q^T operand: lane holds q[head (r % G)][dims 32 s + 8 qg .. +8] for each k-step s
-  u32x4 qv[kSteps];
-  {
-    const uint16_t* q = static_cast<const uint16_t*>(a.q) +
-                        (static_cast<int64_t>(b) * a.Hq + static_cast<int64_t>(g) * G + r % G) * D;
-#pragma unroll
-    for (int s = 0; s < kSteps; ++s) qv[s] = load16(q + 32 * s + 8 * qg);
-  }
 
   // token rows of the two score tiles, relative to the pair start
   const int tok1 = (r / 8) * 16 + ((r / 4) % 2) * 8 + (r % 4);
@@ -100,193 +93,352 @@ __global__ void __launch_bounds__(64 * kWaves) decode_mfma_kernel(DecodeArgs a) 
   const int vblk_sel = qg / 2;         // which block of the pair this lane's P.V tokens are in
   const int vtok = 8 * (qg % 2);       // first of its 8 tokens inside that block
 
-  auto load_pair = [&](int i, Regs& R) {
-    const int tok0 = start + i * kPair;
-    const int j = tok0 / kBlockSize;
-    int32_t ba = table[j];
-    int32_t bb = (tok0 + kBlockSize < end) ? table[j + 1] : -1;
-    ba = (ba >= 0 && ba < NB) ? ba : -1;
-    bb = (bb >= 0 && bb < NB) ? bb : -1;
-    R.blk_a = ba;
-    R.blk_b = bb;
-    const int64_t tile_a = (static_cast<int64_t>(ba < 0 ? 0 : ba) * Hkv + g) * (kBlockSize * D);
-    const int64_t tile_b = (static_cast<int64_t>(bb < 0 ? 0 : bb) * Hkv + g) * (kBlockSize * D);
-    const uint16_t* k1 = kc + (tok1 < 16 ? tile_a : tile_b) + (tok1 % 16) * D + 8 * qg;
-    const uint16_t* k2 = kc + (tok2 < 16 ? tile_a : tile_b) + (tok2 % 16) * D + 8 * qg;
-#pragma unroll
-    for (int s = 0; s < kSteps; ++s) {
-      R.k1[s] = load16(k1 + 32 * s);
-      R.k2[s] = load16(k2 + 32 * s);
-    }
-    const uint16_t* v = vc + (vblk_sel ? tile_b : tile_a) + r * kBlockSize + vtok;
-#pragma unroll
-    for (int n = 0; n < kTiles; ++n) R.v[n] = load16(v + 16 * n * kBlockSize);
-  };
+  // One piece: pairs [i0, i1) of KV head g of sequence b (L tokens).  Every thread of the
+  // workgroup calls it with the same arguments.  dest: 0 = final output, 1 = fixed-partition
+  // slot `part`, 2 = balanced-schedule slot `part`.
+  auto run_piece = [&](int b, int g, int L, int i0, int i1, int dest, int64_t part) {
+    const int32_t* __restrict__ table = a.tables + static_cast<int64_t>(b) * a.max_blocks;
+    const int end = L;
 
-  float m_run = -INFINITY;  // running max (log2 domain) of head r % G
-  float l_run = 0.f;        // lane-partial running sum over this lane's tokens
-  f32x4 acc[kTiles];
+    u32x4 qv[kSteps];
+    {
+      const uint16_t* q = static_cast<const uint16_t*>(a.q) +
+                          (static_cast<int64_t>(b) * a.Hq + static_cast<int64_t>(g) * G + r % G) * D;
 #pragma unroll
-  for (int n = 0; n < kTiles; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int s = 0; s < kSteps; ++s) qv[s] = load16(q + 32 * s + 8 * qg);
+    }
 
-  auto compute_pair = [&](int i, Regs& R) {
-    const int tok0 = start + i * kPair;
-    // scores
-    f32x4 s1 = {0.f, 0.f, 0.f, 0.f}, s2 = {0.f, 0.f, 0.f, 0.f};
+    auto load_pair = [&](int i, Regs& R) {
+      const int tok0 = i * kPair;
+      const int j = tok0 / kBlockSize;
+      int32_t ba = table[j];
+      int32_t bb = (tok0 + kBlockSize < end) ? table[j + 1] : -1;
+      ba = (ba >= 0 && ba < NB) ? ba : -1;
+      bb = (bb >= 0 && bb < NB) ? bb : -1;
+      R.blk_a = ba;
+      R.blk_b = bb;
+      const int64_t tile_a = (static_cast<int64_t>(ba < 0 ? 0 : ba) * Hkv + g) * (kBlockSize * D);
+      const int64_t tile_b = (static_cast<int64_t>(bb < 0 ? 0 : bb) * Hkv + g) * (kBlockSize * D);
+      const uint16_t* k1 = kc + (tok1 < 16 ? tile_a : tile_b) + (tok1 % 16) * D + 8 * qg;
+      const uint16_t* k2 = kc + (tok2 < 16 ? tile_a : tile_b) + (tok2 % 16) * D + 8 * qg;
 #pragma unroll
-    for (int s = 0; s < kSteps; ++s) {
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(R.k1[s]), as_bf16x8(qv[s]), s1, 0, 0, 0);
-      s2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(R.k2[s]), as_bf16x8(qv[s]), s2, 0, 0, 0);
-    }
-    // this lane's 8 tokens: pair tokens 8 qg + e, e = 0..7
-    const int t_first = tok0 + 8 * qg;
-    const int32_t my_blk = vblk_sel ? R.blk_b : R.blk_a;
-    const bool tail = (tok0 + kPair > end) || R.blk_b < 0 || R.blk_a < 0;
-    float sc[8];
+      for (int s = 0; s < kSteps; ++s) {
+        R.k1[s] = load16(k1 + 32 * s);
+        R.k2[s] = load16(k2 + 32 * s);
+      }
+      const uint16_t* v = vc + (vblk_sel ? tile_b : tile_a) + r * kBlockSize + vtok;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      sc[e] = s1[e] * a.scale_log2;
-      sc[4 + e] = s2[e] * a.scale_log2;
-    }
-    if (tail) {
+      for (int n = 0; n < kTiles; ++n) R.v[n] = load16(v + 16 * n * kBlockSize);
+    };
+
+    float m_run = -INFINITY;  // running max (log2 domain) of head r % G
+    float l_run = 0.f;        // lane-partial running sum over this lane's tokens
+    f32x4 acc[kTiles];
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (t_first + e >= end || my_blk < 0) sc[e] = -INFINITY;
-      // masked tokens must not reach P.V even with p = 0 (their V may be anything)
-      uint32_t keep[4];
+    for (int n = 0; n < kTiles; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    auto compute_pair = [&](int i, Regs& R) {
+      const int tok0 = i * kPair;
+      f32x4 s1 = {0.f, 0.f, 0.f, 0.f}, s2 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < kSteps; ++s) {
+        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(R.k1[s]), as_bf16x8(qv[s]), s1, 0, 0, 0);
+        s2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(R.k2[s]), as_bf16x8(qv[s]), s2, 0, 0, 0);
+      }
+      // this lane's 8 tokens: pair tokens 8 qg + e, e = 0..7
+      const int t_first = tok0 + 8 * qg;
+      const int32_t my_blk = vblk_sel ? R.blk_b : R.blk_a;
+      const bool tail = (tok0 + kPair > end) || R.blk_b < 0 || R.blk_a < 0;
+      float sc[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sc[e] = s1[e] * a.scale_log2;
+        sc[4 + e] = s2[e] * a.scale_log2;
+      }
+      if (tail) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (t_first + e >= end || my_blk < 0) sc[e] = -INFINITY;
+        // masked tokens must not reach P.V even with p = 0 (their V may be anything)
+        uint32_t keep[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const bool k0 = my_blk >= 0 && t_first + 2 * c < end;
+          const bool k1 = my_blk >= 0 && t_first + 2 * c + 1 < end;
+          keep[c] = (k0 ? 0x0000ffffu : 0u) | (k1 ? 0xffff0000u : 0u);
+        }
+#pragma unroll
+        for (int n = 0; n < kTiles; ++n)
+#pragma unroll
+          for (int c = 0; c < 4; ++c) R.v[n][c] &= keep[c];
+      }
+      float bmax = sc[0];
+#pragma unroll
+      for (int e = 1; e < 8; ++e) bmax = fmaxf(bmax, sc[e]);
+      bmax = fmaxf(bmax, __shfl_xor(bmax, 16, 64));
+      bmax = fmaxf(bmax, __shfl_xor(bmax, 32, 64));
+      const float m_new = fmaxf(m_run, bmax);
+      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+      m_run = m_new;
+      f32x8 pv;
+      float psum = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        pv[e] = __builtin_amdgcn_exp2f(sc[e] - m_use);
+        psum += pv[e];
+      }
+      l_run = l_run * alpha + psum;
+      // rescale the accumulators: rows 4 qg + j hold head (4 qg + j) % G
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float aj;
+        if constexpr (G <= 4) {
+          aj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), j % G));
+        } else {
+          aj = __shfl(alpha, (4 * qg + j) % G, 64);
+        }
+#pragma unroll
+        for (int n = 0; n < kTiles; ++n) acc[n][j] *= aj;
+      }
+      // P as bf16 hi + lo
+      const bf16x8 p_hi = __builtin_convertvector(pv, bf16x8);
+      const u32x4 hi_bits = __builtin_bit_cast(u32x4, p_hi);
+      f32x8 rest;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const bool k0 = my_blk >= 0 && t_first + 2 * c < end;
-        const bool k1 = my_blk >= 0 && t_first + 2 * c + 1 < end;
-        keep[c] = (k0 ? 0x0000ffffu : 0u) | (k1 ? 0xffff0000u : 0u);
+        rest[2 * c] = pv[2 * c] - __uint_as_float(hi_bits[c] << 16);
+        rest[2 * c + 1] = pv[2 * c + 1] - __uint_as_float(hi_bits[c] & 0xffff0000u);
       }
+      const bf16x8 p_lo = __builtin_convertvector(rest, bf16x8);
 #pragma unroll
-      for (int n = 0; n < kTiles; ++n)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) R.v[n][c] &= keep[c];
+      for (int n = 0; n < kTiles; ++n) {
+        acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(p_hi, as_bf16x8(R.v[n]), acc[n], 0, 0, 0);
+        acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(p_lo, as_bf16x8(R.v[n]), acc[n], 0, 0, 0);
+      }
+    };
+
+    // software pipeline: the next pair's loads are in flight while the current one is computed
+    {
+      Regs ra, rb;
+      int i = i0 + w;
+      if (i < i1) load_pair(i, ra);
+      while (i < i1) {
+        if (i + kWaves < i1) load_pair(i + kWaves, rb);
+        compute_pair(i, ra);
+        i += kWaves;
+        if (i >= i1) break;
+        if (i + kWaves < i1) load_pair(i + kWaves, ra);
+        compute_pair(i, rb);
+        i += kWaves;
+      }
     }
-    float bmax = sc[0];
-#pragma unroll
-    for (int e = 1; e < 8; ++e) bmax = fmaxf(bmax, sc[e]);
-    bmax = fmaxf(bmax, __shfl_xor(bmax, 16, 64));
-    bmax = fmaxf(bmax, __shfl_xor(bmax, 32, 64));
-    const float m_new = fmaxf(m_run, bmax);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-    m_run = m_new;
-    f32x8 pv;
-    float psum = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      pv[e] = __builtin_amdgcn_exp2f(sc[e] - m_use);
-      psum += pv[e];
+
+    // per-wave state -> LDS
+    float l_tot = l_run + __shfl_xor(l_run, 16, 64);
+    l_tot += __shfl_xor(l_tot, 32, 64);
+    if (qg == 0 && r < G) {
+      m_s[w][r] = m_run;
+      l_s[w][r] = l_tot;
     }
-    l_run = l_run * alpha + psum;
-    // rescale the accumulators: rows 4 qg + j hold head (4 qg + j) % G
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      float aj;
-      if constexpr (G <= 4) {
-        aj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), j % G));
+      const int h = 4 * qg + j;
+      if (h < G) {
+#pragma unroll
+        for (int n = 0; n < kTiles; ++n) o_s[w][h][16 * n + r] = acc[n][j];
+      }
+    }
+    __syncthreads();
+
+    // merge the waves and write
+    for (int idx = threadIdx.x; idx < G * D; idx += 64 * kWaves) {
+      const int h = idx / D, d = idx % D;
+      float M = -INFINITY;
+#pragma unroll
+      for (int v = 0; v < kWaves; ++v) M = fmaxf(M, m_s[v][h]);
+      float num = 0.f, den = 0.f;
+      if (M != -INFINITY) {
+#pragma unroll
+        for (int v = 0; v < kWaves; ++v) {
+          const float f = __builtin_amdgcn_exp2f(m_s[v][h] - M);
+          num += f * o_s[v][h][d];
+          den += f * l_s[v][h];
+        }
+      }
+      const float o = den > 0.f ? num / den : 0.f;
+      const int64_t row = static_cast<int64_t>(b) * a.Hq + static_cast<int64_t>(g) * G + h;
+      int64_t slot;
+      if (dest == 0) {
+        a.out[row * D + d] = o;
+        continue;
+      } else if (dest == 1) {
+        slot = row * a.np_max + part;
       } else {
-        aj = __shfl(alpha, (4 * qg + j) % G, 64);
+        slot = part * G + h;
       }
-#pragma unroll
-      for (int n = 0; n < kTiles; ++n) acc[n][j] *= aj;
-    }
-    // P as bf16 hi + lo
-    const bf16x8 p_hi = __builtin_convertvector(pv, bf16x8);
-    const u32x4 hi_bits = __builtin_bit_cast(u32x4, p_hi);
-    f32x8 rest;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      rest[2 * c] = pv[2 * c] - __uint_as_float(hi_bits[c] << 16);
-      rest[2 * c + 1] = pv[2 * c + 1] - __uint_as_float(hi_bits[c] & 0xffff0000u);
-    }
-    const bf16x8 p_lo = __builtin_convertvector(rest, bf16x8);
-#pragma unroll
-    for (int n = 0; n < kTiles; ++n) {
-      acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(p_hi, as_bf16x8(R.v[n]), acc[n], 0, 0, 0);
-      acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(p_lo, as_bf16x8(R.v[n]), acc[n], 0, 0, 0);
-    }
-  };
-
-  // software pipeline: the next pair's loads are in flight while the current one is computed
-  {
-    Regs ra, rb;
-    int i = w;
-    if (i < n_pairs) load_pair(i, ra);
-    while (i < n_pairs) {
-      if (i + kWaves < n_pairs) load_pair(i + kWaves, rb);
-      compute_pair(i, ra);
-      i += kWaves;
-      if (i >= n_pairs) break;
-      if (i + kWaves < n_pairs) load_pair(i + kWaves, ra);
-      compute_pair(i, rb);
-      i += kWaves;
-    }
-  }
-
-  // per-wave state -> LDS
-  float l_tot = l_run + __shfl_xor(l_run, 16, 64);
-  l_tot += __shfl_xor(l_tot, 32, 64);
-  if (qg == 0 && r < G) {
-    m_s[w][r] = m_run;
-    l_s[w][r] = l_tot;
-  }
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int h = 4 * qg + j;
-    if (h < G) {
-#pragma unroll
-      for (int n = 0; n < kTiles; ++n) o_s[w][h][16 * n + r] = acc[n][j];
-    }
-  }
-  __syncthreads();
-
-  // merge the waves and write
-  for (int idx = threadIdx.x; idx < G * D; idx += 64 * kWaves) {
-    const int h = idx / D, d = idx % D;
-    float M = -INFINITY;
-#pragma unroll
-    for (int v = 0; v < kWaves; ++v) M = fmaxf(M, m_s[v][h]);
-    float num = 0.f, den = 0.f;
-    if (M != -INFINITY) {
-#pragma unroll
-      for (int v = 0; v < kWaves; ++v) {
-        const float f = __builtin_amdgcn_exp2f(m_s[v][h] - M);
-        num += f * o_s[v][h][d];
-        den += f * l_s[v][h];
-      }
-    }
-    const float o = den > 0.f ? num / den : 0.f;
-    const int64_t row = static_cast<int64_t>(b) * a.Hq + static_cast<int64_t>(g) * G + h;
-    if (nparts == 1) {
-      a.out[row * D + d] = o;
-    } else {
-      const int64_t slot = row * a.np_max + p;
       a.ws_o[slot * D + d] = o;
       if (d == 0) {
         a.ws_m[slot] = M;
         a.ws_l[slot] = den;
       }
     }
+    __syncthreads();  // LDS is reused by the next piece
+  };
+
+  if constexpr (!kStream) {
+    const int p = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    const int L = min(max(a.seq_lens[b], 0), a.max_seq_len);
+    const int nparts = max(1, (L + a.partition - 1) / a.partition);
+    if (p >= nparts) return;
+    const int ppp = a.partition / kPair;  // pairs per partition
+    const int n_b = (L + kPair - 1) / kPair;
+    run_piece(b, g, L, p * ppp, min(n_b, (p + 1) * ppp), nparts == 1 ? 0 : 1, p);
+  } else {
+    // pair counts -> prefix sums cum_s[0..B]
+    const int B = a.B;
+    int carry = 0;
+    for (int base = 0; base < B; base += 64 * kWaves) {
+      const int i = base + threadIdx.x;
+      const int L = i < B ? min(max(a.seq_lens[i], 0), a.max_seq_len) : 0;
+      int x = (L + kPair - 1) / kPair;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(x, o, 64);
+        if (lane >= o) x += y;
+      }
+      if (lane == 63) wave_tot[w] = x;
+      __syncthreads();
+      int add = carry;
+      for (int v = 0; v < w; ++v) add += wave_tot[v];
+      if (i < B) cum_s[i + 1] = add + x;
+      int tot = 0;
+      for (int v = 0; v < kWaves; ++v) tot += wave_tot[v];
+      __syncthreads();
+      carry += tot;
+    }
+    if (threadIdx.x == 0) cum_s[0] = 0;
+    __syncthreads();
+    const int64_t T = carry;              // pairs per KV head
+    const int64_t U = T * Hkv;            // all units
+    const int NW = a.nw;
+    const int wl = (NW % 8 == 0) ? (blockIdx.x % 8) * (NW / 8) + blockIdx.x / 8 : blockIdx.x;
+    if (wl == 0)
+      for (int i = threadIdx.x; i <= B; i += 64 * kWaves) a.ws_cum[i] = cum_s[i];
+    // empty sequences produce zeros
+    for (int b = wl; b < B; b += NW) {
+      if (cum_s[b + 1] != cum_s[b]) continue;
+      for (int i = threadIdx.x; i < a.Hq * D; i += 64 * kWaves)
+        a.out[static_cast<int64_t>(b) * a.Hq * D + i] = 0.f;
+    }
+    const int64_t u0 = U * wl / NW, u1 = U * (wl + 1) / NW;
+    int64_t u = u0;
+    while (u < u1) {
+      const int g = static_cast<int>(u / T);
+      const int rem = static_cast<int>(u - static_cast<int64_t>(g) * T);
+      // first sequence b with cum_s[b + 1] > rem
+      int lo = 0, hi = B - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi) / 2;
+        if (cum_s[mid + 1] > rem) hi = mid; else lo = mid + 1;
+      }
+      const int b = lo;
+      const int n_b = cum_s[b + 1] - cum_s[b];
+      const int i0 = rem - cum_s[b];
+      const int take = static_cast<int>(min(static_cast<int64_t>(n_b - i0), u1 - u));
+      const int L = min(max(a.seq_lens[b], 0), a.max_seq_len);
+      const bool whole = (i0 == 0 && take == n_b);
+      run_piece(b, g, L, i0, i0 + take, whole ? 0 : 2,
+                static_cast<int64_t>(wl) * 2 + (u == u0 ? 0 : 1));
+      u += take;
+    }
   }
+}
+
+// Merge the partial pieces of each (sequence, KV head) segment of the balanced schedule.  The
+// pieces are found from the same span arithmetic the decode kernel used: workgroup w (logical)
+// covers units [U w / NW, U (w + 1) / NW); a piece sits in slot 0 of its workgroup when it
+// starts that workgroup's span, else in slot 1.
+template <int G, int D>
+__global__ void __launch_bounds__(256) streamk_reduce_kernel(DecodeArgs a) {
+  __shared__ int32_t slot_s[kMaxBalancedWorkgroups];
+  const int b = blockIdx.x, g = blockIdx.y;
+  const int32_t* cum = a.ws_cum;
+  const int64_t T = cum[a.B];
+  const int n_b = cum[b + 1] - cum[b];
+  if (n_b == 0) return;
+  const int64_t U = T * a.Hkv;
+  const int64_t NW = a.nw;
+  const int64_t s0 = static_cast<int64_t>(g) * T + cum[b], s1 = s0 + n_b;
+  const int64_t wa = ((s0 + 1) * NW + U - 1) / U - 1;
+  const int64_t wb = (s1 * NW + U - 1) / U - 1;
+  if (wa == wb) return;
+  // slot of each piece, -1 for workgroups whose span is empty (fewer units than workgroups)
+  const int np = static_cast<int>(wb - wa + 1);
+  for (int k = threadIdx.x; k < np; k += blockDim.x) {
+    const int64_t wv = wa + k;
+    const int64_t st = U * wv / NW;
+    const bool empty = st == U * (wv + 1) / NW;
+    slot_s[k] = empty ? -1 : static_cast<int32_t>(wv * 2 + (k == 0 && st < s0 ? 1 : 0));
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < G * D; idx += blockDim.x) {
+    const int h = idx / D, d = idx % D;
+    float M = -INFINITY;
+    for (int k = 0; k < np; ++k)
+      if (slot_s[k] >= 0) M = fmaxf(M, a.ws_m[static_cast<int64_t>(slot_s[k]) * G + h]);
+    float num = 0.f, den = 0.f;
+    if (M != -INFINITY) {
+      for (int k = 0; k < np; ++k) {
+        if (slot_s[k] < 0) continue;
+        const int64_t slot = static_cast<int64_t>(slot_s[k]) * G + h;
+        const float f = a.ws_l[slot] * __builtin_amdgcn_exp2f(a.ws_m[slot] - M);
+        den += f;
+        num += f * a.ws_o[slot * D + d];
+      }
+    }
+    const int64_t row = static_cast<int64_t>(b) * a.Hq + static_cast<int64_t>(g) * G + h;
+    a.out[row * D + d] = den > 0.f ? num / den : 0.f;
+  }
+}
+
+template <int G, int D>
+hipError_t launch_gd(const DecodeArgs& a, hipStream_t stream) {
+  if (a.nw == 0) {
+    const dim3 grid(a.np_max, a.Hkv, a.B);
+    hipLaunchKernelGGL((decode_mfma_kernel<G, D, false>), grid, dim3(64 * kWaves), 0, stream, a);
+    return hipGetLastError();
+  }
+  const size_t lds = static_cast<size_t>(a.B + 1) * sizeof(int32_t);
+  hipLaunchKernelGGL((decode_mfma_kernel<G, D, true>), dim3(a.nw), dim3(64 * kWaves), lds, stream,
+                     a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((streamk_reduce_kernel<G, D>), dim3(a.B, a.Hkv), dim3(256), 0, stream, a);
+  return hipGetLastError();
 }
 
 template <int G>
 hipError_t launch_g(const DecodeArgs& a, hipStream_t stream) {
-  const dim3 grid(a.np_max, a.Hkv, a.B);
-  if (a.D == 128)
-    hipLaunchKernelGGL((decode_mfma_kernel<G, 128>), grid, dim3(64 * kWaves), 0, stream, a);
-  else if (a.D == 64)
-    hipLaunchKernelGGL((decode_mfma_kernel<G, 64>), grid, dim3(64 * kWaves), 0, stream, a);
-  else
-    return hipErrorNotSupported;
-  return hipGetLastError();
+  if (a.D == 128) return launch_gd<G, 128>(a, stream);
+  if (a.D == 64) return launch_gd<G, 64>(a, stream);
+  return hipErrorNotSupported;
 }
 
 }  // namespace
+
+int mfma_workgroups_per_cu() {
+  static int cached = 0;
+  if (cached == 0) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_mfma_kernel<4, 128, true>,
+                                                     64 * kWaves, 1024) != hipSuccess ||
+        n < 1)
+      n = 1;
+    cached = n;
+  }
+  return cached;
+}
 
 hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream) {
   switch (a.Hq / a.Hkv) {

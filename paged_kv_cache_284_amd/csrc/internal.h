@@ -27,20 +27,31 @@ struct DecodeArgs {
   int32_t B, Hq, Hkv, D, NB;
   int32_t partition;          // tokens per partition (multiple of 64)
   int32_t np_max;             // ceil(max_seq_len / partition), >= 1
+  int32_t nw;                 // balanced schedule: workgroups (0 = fixed partitions)
+  int32_t* ws_cum;            // balanced schedule: pair-count prefix sums [B + 1]
   float scale_log2;           // softmax scale * log2(e)
 };
+
+// Upper bound on balanced-schedule workgroups; sizes the workspace.
+constexpr int kMaxBalancedWorkgroups = 1024;
+// Largest batch the balanced schedule takes (its prefix sums live in LDS).
+constexpr int kMaxBalancedBatch = 8192;
+// Resident workgroups of the balanced MFMA kernel per compute unit.
+int mfma_workgroups_per_cu();
 
 // Partition length the library picks when the caller passes 0.
 int32_t auto_partition(int32_t B, int32_t Hq, int32_t max_seq_len);
 
+// table_index / tables may be NULL; otherwise the launch also patches the block tables.
 hipError_t launch_kv_append(const void* k_new, const void* v_new, const int64_t* slots,
                             void* k_cache, void* v_cache, int32_t B, int32_t Hkv, int32_t D,
-                            int32_t NB, int32_t elem_bytes, hipStream_t stream);
+                            int32_t NB, int32_t elem_bytes, const int32_t* table_index,
+                            int32_t* tables, int32_t max_blocks, hipStream_t stream);
 hipError_t launch_copy_blocks(void* k_cache, void* v_cache, float* k_scale, float* v_scale,
                               const int32_t* pairs, int32_t n, int32_t Hkv, int32_t D,
                               int32_t NB, int32_t elem_bytes, hipStream_t stream);
-hipError_t launch_update_tables(int32_t* tables, int32_t max_blocks, int32_t B,
-                                const int32_t* updates, int32_t n, hipStream_t stream);
+hipError_t launch_update_tables(int32_t* tables, int32_t max_blocks, const int64_t* slots,
+                                const int32_t* table_index, int32_t B, hipStream_t stream);
 
 // Returns hipErrorNotSupported when no kernel of this family takes the combination.
 hipError_t launch_decode_generic(const DecodeArgs& a, int q_dtype, int kv_dtype,

@@ -61,9 +61,10 @@ def poison_unused(pool: dict, w, tables, lens) -> None:
 
 
 class Case:
-    def __init__(self, w, poison: bool = True, steps_ahead: int = None):
+    def __init__(self, w, poison: bool = True, steps_ahead: int = None, fused: bool = True):
         t0 = time.time()
         self.w = w
+        self.fused = fused
         order = inputs.free_order(w)
         ops = inputs.setup_script(w)
         self.py = PyAllocator(w.NB, w.bs, order)
@@ -95,17 +96,26 @@ class Case:
     def step(self, partition_tokens: int = 0, check_pool: bool = True):
         w, s = self.w, self.step_index
         if w.append:
-            slots, pairs, upd = self.lib.step_arrays(self.seqs)
+            slots, lens_after, tidx, pairs = self.lib.step_arrays(self.seqs)
             slots_p, pairs_p = self.py.step(self.seqs)
             assert slots.tolist() == slots_p, "slot mapping differs from the oracle allocator"
             assert [tuple(p) for p in pairs.tolist()] == pairs_p
+            assert lens_after.tolist() == [self.py.length(q) for q in self.seqs]
+            for i, j in enumerate(tidx.tolist()):     # table_index names exactly the new entries
+                if j >= 0:
+                    assert self.py.table(self.seqs[i])[j] == slots_p[i] // w.bs
             k_new, v_new = inputs.new_tokens(w, s)
             if len(pairs):
                 pkv.copy_blocks(self.k, self.v, torch.from_numpy(pairs).cuda(), self.ks, self.vs)
-            if len(upd):
-                pkv.update_block_tables(self.tables, torch.from_numpy(upd).cuda())
-            pkv.kv_append(to_device(k_new, w.kv_dtype), to_device(v_new, w.kv_dtype),
-                          torch.from_numpy(slots).cuda(), self.k, self.v)
+            slots_d = torch.from_numpy(slots).cuda()
+            tidx_d = torch.from_numpy(tidx).cuda()
+            if self.fused:
+                pkv.append_step(to_device(k_new, w.kv_dtype), to_device(v_new, w.kv_dtype),
+                                slots_d, tidx_d, self.k, self.v, self.tables)
+            else:
+                pkv.update_block_tables(self.tables, slots_d, tidx_d)
+                pkv.kv_append(to_device(k_new, w.kv_dtype), to_device(v_new, w.kv_dtype), slots_d,
+                              self.k, self.v)
             kh, vh, _, _ = cache_ops.copy_blocks(self.host["k"], self.host["v"], pairs_p)
             self.host["k"], self.host["v"] = cache_ops.append(kh, vh, k_new, v_new, slots_p, w.bs)
         tables_p, lens_p = self.py.export(self.seqs, self.MB)

@@ -20,10 +20,10 @@ SMALL = ["tiny_fp32", "llama8b_decode", "long_context", "shared_prefix_batch", "
 
 
 @pytest.mark.parametrize("name", SMALL)
-@pytest.mark.parametrize("partition", [0, 64, 192])
-def test_small_workload_all_steps(name, partition):
+@pytest.mark.parametrize("partition,fused", [(0, True), (64, False), (192, True)])
+def test_small_workload_all_steps(name, partition, fused):
     w = inputs.small(name)
-    case = Case(w)
+    case = Case(w, fused=fused)
     for s in range(w.steps):
         say(f"{w.name} step {s} partition {partition}")
         q, out, tables, lens = case.step(partition_tokens=partition)

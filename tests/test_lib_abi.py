@@ -68,7 +68,7 @@ def _decode(**kw):
     (dict(part=100), pkv.PA_ERR_INVALID),
     (dict(part=16384), pkv.PA_ERR_INVALID),
     (dict(B=-1), pkv.PA_ERR_INVALID),
-    (dict(ws=None), pkv.PA_ERR_INVALID),               # split needed, no workspace
+    (dict(ws=None), pkv.PA_ERR_INVALID),               # no workspace
     (dict(ws_bytes=16), pkv.PA_ERR_INVALID),
     (dict(scale=float("nan")), pkv.PA_ERR_INVALID),
 ])
@@ -100,12 +100,21 @@ def test_append_and_copy_reject_on_host():
         == pkv.PA_ERR_INVALID
     assert L.pa_copy_blocks(None, None, None, None, None, 0, 8, 128, 16, 10, pkv.PA_BF16, None) \
         == pkv.PA_OK
-    assert L.pa_update_block_tables(None, 8, 2, FAKE, 3, None) == pkv.PA_ERR_INVALID
+    assert L.pa_update_block_tables(None, 8, FAKE, FAKE, 2, 16, None) == pkv.PA_ERR_INVALID
+    assert L.pa_update_block_tables(FAKE, 8, FAKE, FAKE, 2, 32, None) == pkv.PA_ERR_UNSUPPORTED
+    assert L.pa_update_block_tables(None, 8, None, None, 0, 16, None) == pkv.PA_OK
+    assert L.pa_append_step(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 8, 4, 8, 128, 16, 10,
+                            pkv.PA_BF16, None) == pkv.PA_ERR_INVALID   # table_index, no table
+    assert L.pa_append_step(FAKE, FAKE, FAKE, None, FAKE, FAKE, None, 8, 4, 8, 128, 16, 10,
+                            pkv.PA_I8, None) == pkv.PA_ERR_UNSUPPORTED
 
 
 def test_workspace_size():
     L = pkv.lib()
-    assert L.pa_decode_workspace_size(4, 32, 128, 512, 512) == 256          # one partition
-    n = L.pa_decode_workspace_size(4, 32, 128, 131072, 512)
+    assert L.pa_decode_workspace_size(4, 32, 8, 128, 512, 512) == 256       # one partition
+    n = L.pa_decode_workspace_size(4, 32, 8, 128, 131072, 512)
     assert n >= 4 * 32 * 256 * 130 * 4 and n % 256 == 0
-    assert L.pa_decode_workspace_size(-1, 32, 128, 10, 0) == 0
+    bal = L.pa_decode_workspace_size(64, 32, 8, 128, 4096, 0)               # balanced schedule
+    assert bal >= 1024 * 2 * 4 * 130 * 4
+    assert L.pa_decode_workspace_size(-1, 32, 8, 128, 10, 0) == 0
+    assert L.pa_decode_workspace_size(4, 30, 8, 128, 10, 0) == 0

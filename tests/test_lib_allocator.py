@@ -38,13 +38,21 @@ def test_workload_setup_and_steps_match(name):
     t_p, l_p = py.export(seqs, mb)
     assert np.array_equal(t_l, np.array(t_p)) and np.array_equal(l_l, np.array(l_p))
     for _ in range(w.steps if w.append else 0):
-        slots_l, pairs_l, upd = lib.step_arrays(seqs)
+        before = {s: py.table(s) for s in seqs}
+        slots_l, lens_l, tidx, pairs_l = lib.step_arrays(seqs)
         slots_p, pairs_p = py.step(seqs)
         assert slots_l.tolist() == slots_p
         assert [tuple(p) for p in pairs_l.tolist()] == pairs_p
+        assert lens_l.tolist() == [py.length(s) for s in seqs]
         same_state(lib, py, seqs)
-        for i, j, blk in upd.tolist():                 # updates name exactly the changed entries
-            assert py.table(seqs[i])[j] == blk
+        for i, s in enumerate(seqs):                   # table_index names exactly the changes
+            after = py.table(s)
+            changed = [j for j in range(len(after))
+                       if j >= len(before[s]) or after[j] != before[s][j]]
+            if tidx[i] >= 0:
+                assert changed == [tidx[i]] and after[tidx[i]] == slots_p[i] // 16
+            else:
+                assert changed == []
 
 
 @pytest.mark.parametrize("name", ["llama8b_decode", "shared_prefix_batch"])
@@ -61,7 +69,7 @@ def test_full_workload_setup_matches(name):
     t_p, l_p = py.export(seqs, mb)
     assert np.array_equal(t_l, np.array(t_p)) and np.array_equal(l_l, np.array(l_p))
     assert lib.free_list() == py.free_list()
-    sl, pl, _ = lib.step_arrays(seqs)
+    sl, _, _, pl = lib.step_arrays(seqs)
     sp, pp = py.step(seqs)
     assert sl.tolist() == sp and [tuple(p) for p in pl.tolist()] == pp
     if name == "shared_prefix_batch":
