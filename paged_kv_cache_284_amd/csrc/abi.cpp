@@ -201,7 +201,7 @@ int pa_decode(float* out, const void* q, int32_t q_dtype, const void* k_cache,
     return PA_ERR_INVALID;
 
   const int G = Hq / Hkv;
-  const bool mfma = q_dtype == PA_BF16 && kv_dtype == PA_BF16 &&
+  const bool mfma = q_dtype == PA_BF16 && (kv_dtype == PA_BF16 || kv_dtype == PA_I8) &&
                     (G == 1 || G == 2 || G == 4 || G == 8 || G == 16);
   const bool balanced = mfma && partition_tokens == 0 && B <= pa::kMaxBalancedBatch;
   char* base = static_cast<char*>(workspace);
@@ -228,7 +228,7 @@ int pa_decode(float* out, const void* q, int32_t q_dtype, const void* k_cache,
     a.ws_o = reinterpret_cast<float*>(base + 2 * align256(rows * 4));
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = mfma ? pa::launch_decode_mfma(a, s)
+  hipError_t e = mfma ? pa::launch_decode_mfma(a, kv_dtype == PA_I8, s)
                       : pa::launch_decode_generic(a, q_dtype, kv_dtype, s);
   if (e != hipSuccess) return status_of(e);
   if (balanced) return PA_OK;

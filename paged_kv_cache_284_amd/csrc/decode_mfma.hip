@@ -34,6 +34,7 @@
 // (l%16)%G): softmax and P.V need no cross-lane transposition.  P is fed as a bf16 hi/lo pair
 // (p = hi + lo to ~16 bits) so the rounding of P stays far below the bf16 tolerance.
 #include <cmath>
+#include <type_traits>
 
 #include "internal.h"
 #include "pagedkv.h"
@@ -45,6 +46,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWaves = 8;
 constexpr int kPair = 2 * kBlockSize;  // tokens per wave iteration
@@ -65,16 +67,42 @@ struct PairRegs {
   int32_t blk_a, blk_b;  // physical blocks, -1 when masked
 };
 
-template <int G, int D, bool kStream>
+// int8 cache: the same tiles at one byte per element, plus the (block, head) scales.
+template <int D>
+struct PairRegsI8 {
+  static constexpr int kSteps = D / 32;
+  static constexpr int kTiles = D / 16;
+  u32x4 k1[kSteps / 2];  // 16 dims per load = two k-steps
+  u32x4 k2[kSteps / 2];
+  u32x2 v[kTiles];       // 8 tokens x 1 dim per tile
+  int32_t blk_a, blk_b;
+  float ks_a, ks_b, vs_a, vs_b;
+};
+
+// Eight int8 codes c -> eight bf16 values of u = c + 128 (0..255, exact in bf16).  The +128
+// offset is taken out of the dot products by the caller.
+__device__ __forceinline__ bf16x8 codes_to_bf16(uint32_t x0, uint32_t x1) {
+  const uint32_t u0 = x0 ^ 0x80808080u, u1 = x1 ^ 0x80808080u;
+  f32x8 f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    f[e] = static_cast<float>((u0 >> (8 * e)) & 0xffu);
+    f[4 + e] = static_cast<float>((u1 >> (8 * e)) & 0xffu);
+  }
+  return __builtin_convertvector(f, bf16x8);
+}
+
+template <int G, int D, bool kStream, bool kI8>
 __global__ void __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
 decode_mfma_kernel(DecodeArgs a) {
-  using Regs = PairRegs<D>;
-  constexpr int kSteps = Regs::kSteps;
-  constexpr int kTiles = Regs::kTiles;
+  using Regs = std::conditional_t<kI8, PairRegsI8<D>, PairRegs<D>>;
+  constexpr int kSteps = D / 32;
+  constexpr int kTiles = D / 16;
 
   extern __shared__ int32_t cum_s[];  // balanced schedule: pair-count prefix sums, B + 1 entries
   __shared__ float m_s[kWaves][G];
   __shared__ float l_s[kWaves][G];
+  __shared__ float c_s[kWaves][G];  // int8: sum of the P operand, to take the +128 offset out
   __shared__ float o_s[kWaves][G][D];
   __shared__ int32_t wave_tot[kWaves];
 
@@ -85,6 +113,8 @@ decode_mfma_kernel(DecodeArgs a) {
 
   const uint16_t* __restrict__ kc = static_cast<const uint16_t*>(a.k);
   const uint16_t* __restrict__ vc = static_cast<const uint16_t*>(a.v);
+  const uint8_t* __restrict__ kc8 = static_cast<const uint8_t*>(a.k);
+  const uint8_t* __restrict__ vc8 = static_cast<const uint8_t*>(a.v);
   const int NB = a.NB, Hkv = a.Hkv;
 
   // token rows of the two score tiles, relative to the pair start
@@ -100,12 +130,29 @@ decode_mfma_kernel(DecodeArgs a) {
     const int32_t* __restrict__ table = a.tables + static_cast<int64_t>(b) * a.max_blocks;
     const int end = L;
 
+    // q^T operand, head (r % G).  bf16 cache: step s covers dims 32 s + 8 qg .. +8.  int8
+    // cache: step s covers dims 16 (qg + 4 (s / 2)) + 8 (s % 2) .. +8, matching the 16-byte K
+    // loads (16 dims of a row serve two steps).
     u32x4 qv[kSteps];
+    float qsum = 0.f;  // int8: sum of this head's q, reduced over the four lane groups
     {
       const uint16_t* q = static_cast<const uint16_t*>(a.q) +
                           (static_cast<int64_t>(b) * a.Hq + static_cast<int64_t>(g) * G + r % G) * D;
 #pragma unroll
-      for (int s = 0; s < kSteps; ++s) qv[s] = load16(q + 32 * s + 8 * qg);
+      for (int s = 0; s < kSteps; ++s) {
+        if constexpr (kI8) {
+          qv[s] = load16(q + 16 * (qg + 4 * (s / 2)) + 8 * (s % 2));
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            qsum += __uint_as_float(qv[s][c] << 16) + __uint_as_float(qv[s][c] & 0xffff0000u);
+        } else {
+          qv[s] = load16(q + 32 * s + 8 * qg);
+        }
+      }
+      if constexpr (kI8) {
+        qsum += __shfl_xor(qsum, 16, 64);
+        qsum += __shfl_xor(qsum, 32, 64);
+      }
     }
 
     auto load_pair = [&](int i, Regs& R) {
@@ -117,22 +164,43 @@ decode_mfma_kernel(DecodeArgs a) {
       bb = (bb >= 0 && bb < NB) ? bb : -1;
       R.blk_a = ba;
       R.blk_b = bb;
-      const int64_t tile_a = (static_cast<int64_t>(ba < 0 ? 0 : ba) * Hkv + g) * (kBlockSize * D);
-      const int64_t tile_b = (static_cast<int64_t>(bb < 0 ? 0 : bb) * Hkv + g) * (kBlockSize * D);
-      const uint16_t* k1 = kc + (tok1 < 16 ? tile_a : tile_b) + (tok1 % 16) * D + 8 * qg;
-      const uint16_t* k2 = kc + (tok2 < 16 ? tile_a : tile_b) + (tok2 % 16) * D + 8 * qg;
+      const int64_t ta = static_cast<int64_t>(ba < 0 ? 0 : ba) * Hkv + g;  // (block, head) tiles
+      const int64_t tb = static_cast<int64_t>(bb < 0 ? 0 : bb) * Hkv + g;
+      const int64_t tile_a = ta * (kBlockSize * D);
+      const int64_t tile_b = tb * (kBlockSize * D);
+      if constexpr (kI8) {
+        R.ks_a = a.k_scale[ta];
+        R.ks_b = a.k_scale[tb];
+        R.vs_a = a.v_scale[ta];
+        R.vs_b = a.v_scale[tb];
+        const uint8_t* k1 = kc8 + (tok1 < 16 ? tile_a : tile_b) + (tok1 % 16) * D + 16 * qg;
+        const uint8_t* k2 = kc8 + (tok2 < 16 ? tile_a : tile_b) + (tok2 % 16) * D + 16 * qg;
 #pragma unroll
-      for (int s = 0; s < kSteps; ++s) {
-        R.k1[s] = load16(k1 + 32 * s);
-        R.k2[s] = load16(k2 + 32 * s);
+        for (int c = 0; c < kSteps / 2; ++c) {
+          R.k1[c] = *reinterpret_cast<const u32x4*>(k1 + 64 * c);
+          R.k2[c] = *reinterpret_cast<const u32x4*>(k2 + 64 * c);
+        }
+        const uint8_t* v = vc8 + (vblk_sel ? tile_b : tile_a) + r * kBlockSize + vtok;
+#pragma unroll
+        for (int n = 0; n < kTiles; ++n)
+          R.v[n] = *reinterpret_cast<const u32x2*>(v + 16 * n * kBlockSize);
+      } else {
+        const uint16_t* k1 = kc + (tok1 < 16 ? tile_a : tile_b) + (tok1 % 16) * D + 8 * qg;
+        const uint16_t* k2 = kc + (tok2 < 16 ? tile_a : tile_b) + (tok2 % 16) * D + 8 * qg;
+#pragma unroll
+        for (int s = 0; s < kSteps; ++s) {
+          R.k1[s] = load16(k1 + 32 * s);
+          R.k2[s] = load16(k2 + 32 * s);
+        }
+        const uint16_t* v = vc + (vblk_sel ? tile_b : tile_a) + r * kBlockSize + vtok;
+#pragma unroll
+        for (int n = 0; n < kTiles; ++n) R.v[n] = load16(v + 16 * n * kBlockSize);
       }
-      const uint16_t* v = vc + (vblk_sel ? tile_b : tile_a) + r * kBlockSize + vtok;
-#pragma unroll
-      for (int n = 0; n < kTiles; ++n) R.v[n] = load16(v + 16 * n * kBlockSize);
     };
 
     float m_run = -INFINITY;  // running max (log2 domain) of head r % G
     float l_run = 0.f;        // lane-partial running sum over this lane's tokens
+    float c_run = 0.f;        // int8: lane-partial running sum of the (scaled) P operand
     f32x4 acc[kTiles];
 #pragma unroll
     for (int n = 0; n < kTiles; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -140,26 +208,54 @@ decode_mfma_kernel(DecodeArgs a) {
     auto compute_pair = [&](int i, Regs& R) {
       const int tok0 = i * kPair;
       f32x4 s1 = {0.f, 0.f, 0.f, 0.f}, s2 = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (kI8) {
 #pragma unroll
-      for (int s = 0; s < kSteps; ++s) {
-        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(R.k1[s]), as_bf16x8(qv[s]), s1, 0, 0, 0);
-        s2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(R.k2[s]), as_bf16x8(qv[s]), s2, 0, 0, 0);
+        for (int c = 0; c < kSteps / 2; ++c) {
+          s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(codes_to_bf16(R.k1[c][0], R.k1[c][1]),
+                                                        as_bf16x8(qv[2 * c]), s1, 0, 0, 0);
+          s2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(codes_to_bf16(R.k2[c][0], R.k2[c][1]),
+                                                        as_bf16x8(qv[2 * c]), s2, 0, 0, 0);
+          s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(codes_to_bf16(R.k1[c][2], R.k1[c][3]),
+                                                        as_bf16x8(qv[2 * c + 1]), s1, 0, 0, 0);
+          s2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(codes_to_bf16(R.k2[c][2], R.k2[c][3]),
+                                                        as_bf16x8(qv[2 * c + 1]), s2, 0, 0, 0);
+        }
+      } else {
+#pragma unroll
+        for (int s = 0; s < kSteps; ++s) {
+          s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(R.k1[s]), as_bf16x8(qv[s]), s1, 0, 0, 0);
+          s2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(R.k2[s]), as_bf16x8(qv[s]), s2, 0, 0, 0);
+        }
       }
       // this lane's 8 tokens: pair tokens 8 qg + e, e = 0..7
       const int t_first = tok0 + 8 * qg;
       const int32_t my_blk = vblk_sel ? R.blk_b : R.blk_a;
       const bool tail = (tok0 + kPair > end) || R.blk_b < 0 || R.blk_a < 0;
       float sc[8];
+      if constexpr (kI8) {
+        // score = k_scale * sum_d q_d (u_d - 128), u = code + 128
+        const float f = (vblk_sel ? R.ks_b : R.ks_a) * a.scale_log2;
+        const float off = 128.f * qsum;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        sc[e] = s1[e] * a.scale_log2;
-        sc[4 + e] = s2[e] * a.scale_log2;
+        for (int e = 0; e < 4; ++e) {
+          sc[e] = (s1[e] - off) * f;
+          sc[4 + e] = (s2[e] - off) * f;
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          sc[e] = s1[e] * a.scale_log2;
+          sc[4 + e] = s2[e] * a.scale_log2;
+        }
       }
       if (tail) {
 #pragma unroll
         for (int e = 0; e < 8; ++e)
           if (t_first + e >= end || my_blk < 0) sc[e] = -INFINITY;
-        // masked tokens must not reach P.V even with p = 0 (their V may be anything)
+      }
+      if (tail && !kI8) {
+        // masked tokens must not reach P.V even with p = 0 (their V may be anything); int8
+        // codes always convert to finite values, so there p = 0 is enough
         uint32_t keep[4];
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
@@ -167,10 +263,12 @@ decode_mfma_kernel(DecodeArgs a) {
           const bool k1 = my_blk >= 0 && t_first + 2 * c + 1 < end;
           keep[c] = (k0 ? 0x0000ffffu : 0u) | (k1 ? 0xffff0000u : 0u);
         }
+        if constexpr (!kI8) {
 #pragma unroll
-        for (int n = 0; n < kTiles; ++n)
+          for (int n = 0; n < kTiles; ++n)
 #pragma unroll
-          for (int c = 0; c < 4; ++c) R.v[n][c] &= keep[c];
+            for (int c = 0; c < 4; ++c) R.v[n][c] &= keep[c];
+        }
       }
       float bmax = sc[0];
 #pragma unroll
@@ -189,6 +287,17 @@ decode_mfma_kernel(DecodeArgs a) {
         psum += pv[e];
       }
       l_run = l_run * alpha + psum;
+      if constexpr (kI8) {
+        // fold this block's V scale into P; keep the sum of P to take out the +128 offset
+        const float vs = vblk_sel ? R.vs_b : R.vs_a;
+        float csum = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          pv[e] *= vs;
+          csum += pv[e];
+        }
+        c_run = c_run * alpha + csum;
+      }
       // rescale the accumulators: rows 4 qg + j hold head (4 qg + j) % G
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -213,8 +322,14 @@ decode_mfma_kernel(DecodeArgs a) {
       const bf16x8 p_lo = __builtin_convertvector(rest, bf16x8);
 #pragma unroll
       for (int n = 0; n < kTiles; ++n) {
-        acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(p_hi, as_bf16x8(R.v[n]), acc[n], 0, 0, 0);
-        acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(p_lo, as_bf16x8(R.v[n]), acc[n], 0, 0, 0);
+        bf16x8 vop;
+        if constexpr (kI8) {
+          vop = codes_to_bf16(R.v[n][0], R.v[n][1]);
+        } else {
+          vop = as_bf16x8(R.v[n]);
+        }
+        acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(p_hi, vop, acc[n], 0, 0, 0);
+        acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(p_lo, vop, acc[n], 0, 0, 0);
       }
     };
 
@@ -237,9 +352,15 @@ decode_mfma_kernel(DecodeArgs a) {
     // per-wave state -> LDS
     float l_tot = l_run + __shfl_xor(l_run, 16, 64);
     l_tot += __shfl_xor(l_tot, 32, 64);
+    float c_tot = 0.f;
+    if constexpr (kI8) {
+      c_tot = c_run + __shfl_xor(c_run, 16, 64);
+      c_tot += __shfl_xor(c_tot, 32, 64);
+    }
     if (qg == 0 && r < G) {
       m_s[w][r] = m_run;
       l_s[w][r] = l_tot;
+      c_s[w][r] = c_tot;
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -262,7 +383,7 @@ decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
         for (int v = 0; v < kWaves; ++v) {
           const float f = __builtin_amdgcn_exp2f(m_s[v][h] - M);
-          num += f * o_s[v][h][d];
+          num += f * (kI8 ? o_s[v][h][d] - 128.f * c_s[v][h] : o_s[v][h][d]);
           den += f * l_s[v][h];
         }
       }
@@ -402,27 +523,40 @@ __global__ void __launch_bounds__(256) streamk_reduce_kernel(DecodeArgs a) {
   }
 }
 
-template <int G, int D>
+template <int G, int D, bool kI8>
 hipError_t launch_gd(const DecodeArgs& a, hipStream_t stream) {
   if (a.nw == 0) {
     const dim3 grid(a.np_max, a.Hkv, a.B);
-    hipLaunchKernelGGL((decode_mfma_kernel<G, D, false>), grid, dim3(64 * kWaves), 0, stream, a);
+    hipLaunchKernelGGL((decode_mfma_kernel<G, D, false, kI8>), grid, dim3(64 * kWaves), 0, stream,
+                       a);
     return hipGetLastError();
   }
   const size_t lds = static_cast<size_t>(a.B + 1) * sizeof(int32_t);
-  hipLaunchKernelGGL((decode_mfma_kernel<G, D, true>), dim3(a.nw), dim3(64 * kWaves), lds, stream,
-                     a);
+  hipLaunchKernelGGL((decode_mfma_kernel<G, D, true, kI8>), dim3(a.nw), dim3(64 * kWaves), lds,
+                     stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((streamk_reduce_kernel<G, D>), dim3(a.B, a.Hkv), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
-template <int G>
+template <int G, bool kI8>
 hipError_t launch_g(const DecodeArgs& a, hipStream_t stream) {
-  if (a.D == 128) return launch_gd<G, 128>(a, stream);
-  if (a.D == 64) return launch_gd<G, 64>(a, stream);
+  if (a.D == 128) return launch_gd<G, 128, kI8>(a, stream);
+  if (a.D == 64) return launch_gd<G, 64, kI8>(a, stream);
   return hipErrorNotSupported;
+}
+
+template <bool kI8>
+hipError_t launch_kv(const DecodeArgs& a, hipStream_t stream) {
+  switch (a.Hq / a.Hkv) {
+    case 1: return launch_g<1, kI8>(a, stream);
+    case 2: return launch_g<2, kI8>(a, stream);
+    case 4: return launch_g<4, kI8>(a, stream);
+    case 8: return launch_g<8, kI8>(a, stream);
+    case 16: return launch_g<16, kI8>(a, stream);
+    default: return hipErrorNotSupported;
+  }
 }
 
 }  // namespace
@@ -431,7 +565,7 @@ int mfma_workgroups_per_cu() {
   static int cached = 0;
   if (cached == 0) {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_mfma_kernel<4, 128, true>,
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_mfma_kernel<4, 128, true, false>,
                                                      64 * kWaves, 1024) != hipSuccess ||
         n < 1)
       n = 1;
@@ -440,15 +574,8 @@ int mfma_workgroups_per_cu() {
   return cached;
 }
 
-hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream) {
-  switch (a.Hq / a.Hkv) {
-    case 1: return launch_g<1>(a, stream);
-    case 2: return launch_g<2>(a, stream);
-    case 4: return launch_g<4>(a, stream);
-    case 8: return launch_g<8>(a, stream);
-    case 16: return launch_g<16>(a, stream);
-    default: return hipErrorNotSupported;
-  }
+hipError_t launch_decode_mfma(const DecodeArgs& a, bool int8_cache, hipStream_t stream) {
+  return int8_cache ? launch_kv<true>(a, stream) : launch_kv<false>(a, stream);
 }
 
 }  // namespace pa

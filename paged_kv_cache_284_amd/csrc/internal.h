@@ -56,8 +56,9 @@ hipError_t launch_update_tables(int32_t* tables, int32_t max_blocks, const int64
 // Returns hipErrorNotSupported when no kernel of this family takes the combination.
 hipError_t launch_decode_generic(const DecodeArgs& a, int q_dtype, int kv_dtype,
                                  hipStream_t stream);
-// bf16 query and cache, D 64/128, group size 1, 2, 4, 8 or 16.
-hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream);
+// bf16 query; bf16 or int8 cache (int8: k_scale / v_scale set); D 64/128; group size 1, 2, 4,
+// 8 or 16.
+hipError_t launch_decode_mfma(const DecodeArgs& a, bool int8_cache, hipStream_t stream);
 hipError_t launch_splitk_reduce(const DecodeArgs& a, hipStream_t stream);
 
 }  // namespace pa

@@ -58,13 +58,15 @@ def _ragged_case(kv="bf16", G=4, D=128, lens=(0, 1, 15, 16, 17, 63, 64, 65, 200,
     w = inputs.llama8b_decode(B=len(lens), lo=1, hi=2, cid=40, name="edges")
     w.lengths = np.array(lens, np.int64)
     w.Hkv, w.Hq, w.D, w.kv_dtype, w.q_dtype = 2, 2 * G, D, kv, ("f32" if kv == "f32" else "bf16")
+    w.cid = 40 + D + G
     w.NB = int(sum((L + 15) // 16 for L in lens)) + 8
     w.append = False
     return w
 
 
 @pytest.mark.parametrize("kv,G,D", [("bf16", 4, 128), ("bf16", 1, 64), ("f32", 2, 64),
-                                    ("f32", 16, 128), ("bf16", 8, 128)])
+                                    ("f32", 16, 128), ("bf16", 8, 128), ("i8", 1, 128),
+                                    ("i8", 4, 64), ("bf16", 16, 128)])
 @pytest.mark.parametrize("partition", [0, 64])
 def test_edge_lengths(kv, G, D, partition):
     """Empty, single-token, block-boundary and partition-boundary lengths, several group sizes."""
