@@ -307,6 +307,9 @@ def main():
     ap.add_argument("--partition", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-reference", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB five times (calibrates the "
+                         "FETCH_SIZE / WRITE_SIZE counters against known bytes) and exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the decode path shards by sequence or KV head with no "
@@ -316,6 +319,17 @@ def main():
     import torch
     if not torch.cuda.is_available():
         raise SystemExit("no GPU visible")
+    if args.copy_reference:
+        n = args.copy_reference << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_reference_bytes_read": n, "copy_reference_bytes_written": n,
+                          "launches": 5}))
+        return
+
     import paged_kv_cache_284_amd as pkv
     pkv.lib()
 
