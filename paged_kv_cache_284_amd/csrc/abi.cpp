@@ -145,7 +145,7 @@ size_t pa_decode_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
       partition_tokens ? partition_tokens : pa::auto_partition(B, Hq, max_seq_len);
   const int64_t np = (static_cast<int64_t>(max_seq_len) + P - 1) / P;
   int64_t bytes = fixed_bytes(B, Hq, D, np);
-  if (partition_tokens == 0 && B <= pa::kMaxBalancedBatch) {
+  if (partition_tokens == 0 && B <= pa::kMaxBalancedBatch && Hq / Hkv <= pa::kMaxBalancedGroup) {
     const int64_t bal = balanced_bytes(B, Hq / Hkv, D, pa::kMaxBalancedWorkgroups);
     bytes = bytes > bal ? bytes : bal;
   }
@@ -203,7 +203,8 @@ int pa_decode(float* out, const void* q, int32_t q_dtype, const void* k_cache,
   const int G = Hq / Hkv;
   const bool mfma = q_dtype == PA_BF16 && (kv_dtype == PA_BF16 || kv_dtype == PA_I8) &&
                     (G == 1 || G == 2 || G == 4 || G == 8 || G == 16);
-  const bool balanced = mfma && partition_tokens == 0 && B <= pa::kMaxBalancedBatch;
+  const bool balanced = mfma && partition_tokens == 0 && B <= pa::kMaxBalancedBatch &&
+                        G <= pa::kMaxBalancedGroup;
   char* base = static_cast<char*>(workspace);
   if (balanced) {
     const int cus = cu_count();

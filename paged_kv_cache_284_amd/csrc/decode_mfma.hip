@@ -99,11 +99,15 @@ decode_mfma_kernel(DecodeArgs a) {
   constexpr int kSteps = D / 32;
   constexpr int kTiles = D / 16;
 
+  // Per-wave softmax states waiting to be merged: one slot per wave for the fixed schedule (the
+  // piece the whole workgroup shares), two for the balanced one (the first and the last piece of
+  // the wave's span, when a neighbouring wave holds the rest of it).  o holds acc - 128 c (the
+  // int8 offset already taken out).
+  constexpr int kSlots = kStream ? 2 : 1;
   extern __shared__ int32_t cum_s[];  // balanced schedule: pair-count prefix sums, B + 1 entries
-  __shared__ float m_s[kWaves][G];
-  __shared__ float l_s[kWaves][G];
-  __shared__ float c_s[kWaves][G];  // int8: sum of the P operand, to take the +128 offset out
-  __shared__ float o_s[kWaves][G][D];
+  __shared__ float m_s[kWaves][kSlots][G];
+  __shared__ float l_s[kWaves][kSlots][G];
+  __shared__ float o_s[kWaves][kSlots][G][D];
   __shared__ int32_t wave_tot[kWaves];
 
   const int lane = threadIdx.x % 64;
@@ -123,10 +127,15 @@ decode_mfma_kernel(DecodeArgs a) {
   const int vblk_sel = qg / 2;         // which block of the pair this lane's P.V tokens are in
   const int vtok = 8 * (qg % 2);       // first of its 8 tokens inside that block
 
-  // One piece: pairs [i0, i1) of KV head g of sequence b (L tokens).  Every thread of the
-  // workgroup calls it with the same arguments.  dest: 0 = final output, 1 = fixed-partition
-  // slot `part`, 2 = balanced-schedule slot `part`.
-  auto run_piece = [&](int b, int g, int L, int i0, int i1, int dest, int64_t part) {
+  // One piece: pairs [i0, i1) of KV head g of sequence b (L tokens).
+  //   solo = false: every wave of the workgroup calls it with the same arguments, the waves take
+  //     the pairs in turn and merge in LDS; dest 0 = final output, 1 = fixed-partition slot
+  //     `part`.
+  //   solo = true: the calling wave takes every pair itself; with lds_slot >= 0 it leaves its
+  //     state in LDS slot (w, lds_slot), otherwise it writes the result: dest 0 = final output,
+  //     2 = balanced-schedule slot `part`.
+  auto run_piece = [&](int b, int g, int L, int i0, int i1, bool solo, int dest, int64_t part,
+                       int lds_slot) {
     const int32_t* __restrict__ table = a.tables + static_cast<int64_t>(b) * a.max_blocks;
     const int end = L;
 
@@ -335,21 +344,22 @@ decode_mfma_kernel(DecodeArgs a) {
 
     // software pipeline: the next pair's loads are in flight while the current one is computed
     {
+      const int step = solo ? 1 : kWaves;
       Regs ra, rb;
-      int i = i0 + w;
+      int i = solo ? i0 : i0 + w;
       if (i < i1) load_pair(i, ra);
       while (i < i1) {
-        if (i + kWaves < i1) load_pair(i + kWaves, rb);
+        if (i + step < i1) load_pair(i + step, rb);
         compute_pair(i, ra);
-        i += kWaves;
+        i += step;
         if (i >= i1) break;
-        if (i + kWaves < i1) load_pair(i + kWaves, ra);
+        if (i + step < i1) load_pair(i + step, ra);
         compute_pair(i, rb);
-        i += kWaves;
+        i += step;
       }
     }
 
-    // per-wave state -> LDS
+    // reduce the lane partials over the four lane groups: l_tot, c_tot belong to head r % G
     float l_tot = l_run + __shfl_xor(l_run, 16, 64);
     l_tot += __shfl_xor(l_tot, 32, 64);
     float c_tot = 0.f;
@@ -357,47 +367,78 @@ decode_mfma_kernel(DecodeArgs a) {
       c_tot = c_run + __shfl_xor(c_run, 16, 64);
       c_tot += __shfl_xor(c_tot, 32, 64);
     }
-    if (qg == 0 && r < G) {
-      m_s[w][r] = m_run;
-      l_s[w][r] = l_tot;
-      c_s[w][r] = c_tot;
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int h = 4 * qg + j;
-      if (h < G) {
-#pragma unroll
-        for (int n = 0; n < kTiles; ++n) o_s[w][h][16 * n + r] = acc[n][j];
+    // accumulator rows 4 qg + j hold head (4 qg + j) % G; the copy with 4 qg + j < G is written
+    auto to_lds = [&](int slot) {
+      if (qg == 0 && r < G) {
+        m_s[w][slot][r] = m_run;
+        l_s[w][slot][r] = l_tot;
       }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int h = 4 * qg + j;
+        const float cj = kI8 ? __shfl(c_tot, h % G, 64) : 0.f;
+        if (h < G) {
+#pragma unroll
+          for (int n = 0; n < kTiles; ++n) o_s[w][slot][h][16 * n + r] = acc[n][j] - 128.f * cj;
+        }
+      }
+    };
+    if (solo) {
+      if (lds_slot >= 0) {
+        to_lds(lds_slot);
+        return;
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int h = 4 * qg + j;
+        const float lj = __shfl(l_tot, h % G, 64);
+        const float mj = __shfl(m_run, h % G, 64);
+        const float cj = kI8 ? __shfl(c_tot, h % G, 64) : 0.f;
+        if (h < G) {
+          const int64_t row = static_cast<int64_t>(b) * a.Hq + static_cast<int64_t>(g) * G + h;
+          const int64_t slot = part * G + h;
+#pragma unroll
+          for (int n = 0; n < kTiles; ++n) {
+            const float o = lj > 0.f ? (acc[n][j] - 128.f * cj) / lj : 0.f;
+            if (dest == 0) {
+              a.out[row * D + 16 * n + r] = o;
+            } else {
+              a.ws_o[slot * D + 16 * n + r] = o;
+            }
+          }
+          if (dest != 0 && r == 0) {
+            a.ws_m[slot] = mj;
+            a.ws_l[slot] = lj;
+          }
+        }
+      }
+      return;
     }
-    __syncthreads();
 
+    to_lds(0);
+    __syncthreads();
     // merge the waves and write
     for (int idx = threadIdx.x; idx < G * D; idx += 64 * kWaves) {
       const int h = idx / D, d = idx % D;
       float M = -INFINITY;
 #pragma unroll
-      for (int v = 0; v < kWaves; ++v) M = fmaxf(M, m_s[v][h]);
+      for (int v = 0; v < kWaves; ++v) M = fmaxf(M, m_s[v][0][h]);
       float num = 0.f, den = 0.f;
       if (M != -INFINITY) {
 #pragma unroll
         for (int v = 0; v < kWaves; ++v) {
-          const float f = __builtin_amdgcn_exp2f(m_s[v][h] - M);
-          num += f * (kI8 ? o_s[v][h][d] - 128.f * c_s[v][h] : o_s[v][h][d]);
-          den += f * l_s[v][h];
+          const float f = __builtin_amdgcn_exp2f(m_s[v][0][h] - M);
+          num += f * o_s[v][0][h][d];
+          den += f * l_s[v][0][h];
         }
       }
       const float o = den > 0.f ? num / den : 0.f;
       const int64_t row = static_cast<int64_t>(b) * a.Hq + static_cast<int64_t>(g) * G + h;
-      int64_t slot;
       if (dest == 0) {
         a.out[row * D + d] = o;
         continue;
-      } else if (dest == 1) {
-        slot = row * a.np_max + part;
-      } else {
-        slot = part * G + h;
       }
+      const int64_t slot = row * a.np_max + part;
       a.ws_o[slot * D + d] = o;
       if (d == 0) {
         a.ws_m[slot] = M;
@@ -414,7 +455,7 @@ decode_mfma_kernel(DecodeArgs a) {
     if (p >= nparts) return;
     const int ppp = a.partition / kPair;  // pairs per partition
     const int n_b = (L + kPair - 1) / kPair;
-    run_piece(b, g, L, p * ppp, min(n_b, (p + 1) * ppp), nparts == 1 ? 0 : 1, p);
+    run_piece(b, g, L, p * ppp, min(n_b, (p + 1) * ppp), false, nparts == 1 ? 0 : 1, p, -1);
   } else {
     // pair counts -> prefix sums cum_s[0..B]
     const int B = a.B;
@@ -443,7 +484,7 @@ decode_mfma_kernel(DecodeArgs a) {
     const int64_t T = carry;              // pairs per KV head
     const int64_t U = T * Hkv;            // all units
     const int NW = a.nw;
-    const int wl = (NW % 8 == 0) ? (blockIdx.x % 8) * (NW / 8) + blockIdx.x / 8 : blockIdx.x;
+    const int wl = blockIdx.x;
     if (wl == 0)
       for (int i = threadIdx.x; i <= B; i += 64 * kWaves) a.ws_cum[i] = cum_s[i];
     // empty sequences produce zeros
@@ -452,9 +493,14 @@ decode_mfma_kernel(DecodeArgs a) {
       for (int i = threadIdx.x; i < a.Hq * D; i += 64 * kWaves)
         a.out[static_cast<int64_t>(b) * a.Hq * D + i] = 0.f;
     }
+    // workgroup span [u0, u1); wave w streams its own eighth [v0, v1) of it with no barriers
     const int64_t u0 = U * wl / NW, u1 = U * (wl + 1) / NW;
-    int64_t u = u0;
-    while (u < u1) {
+    const int64_t v0 = u0 + (u1 - u0) * w / kWaves, v1 = u0 + (u1 - u0) * (w + 1) / kWaves;
+    __shared__ int64_t tag_s[kWaves][2];   // workgroup piece (first unit) held in each LDS slot
+    __shared__ int32_t info_s[kWaves][2][4];  // its b, g, destination, partial slot
+    if (lane < 2) tag_s[w][lane] = -1;
+    int64_t u = v0;
+    while (u < v1) {
       const int g = static_cast<int>(u / T);
       const int rem = static_cast<int>(u - static_cast<int64_t>(g) * T);
       // first sequence b with cum_s[b + 1] > rem
@@ -466,12 +512,79 @@ decode_mfma_kernel(DecodeArgs a) {
       const int b = lo;
       const int n_b = cum_s[b + 1] - cum_s[b];
       const int i0 = rem - cum_s[b];
-      const int take = static_cast<int>(min(static_cast<int64_t>(n_b - i0), u1 - u));
+      const int take = static_cast<int>(min(static_cast<int64_t>(n_b - i0), v1 - u));
       const int L = min(max(a.seq_lens[b], 0), a.max_seq_len);
-      const bool whole = (i0 == 0 && take == n_b);
-      run_piece(b, g, L, i0, i0 + take, whole ? 0 : 2,
-                static_cast<int64_t>(wl) * 2 + (u == u0 ? 0 : 1));
+      const int64_t s0 = static_cast<int64_t>(g) * T + cum_s[b], s1 = s0 + n_b;
+      const int64_t p0 = max(s0, u0), p1 = min(s1, u1);  // this workgroup's piece of the segment
+      const bool whole = (p0 == s0 && p1 == s1);
+      const int dest = whole ? 0 : 2;
+      const int64_t part = static_cast<int64_t>(wl) * 2 + (p0 == u0 ? 0 : 1);
+      int slot = -1;
+      if (p0 != u || p1 != u + take) {
+        // shared with a neighbouring wave: the wave's first or last piece
+        slot = (u == v0) ? 0 : 1;
+        if (lane == 0) {
+          tag_s[w][slot] = p0;
+          info_s[w][slot][0] = b;
+          info_s[w][slot][1] = g;
+          info_s[w][slot][2] = dest;
+          info_s[w][slot][3] = static_cast<int32_t>(part);
+        }
+      }
+      run_piece(b, g, L, i0, i0 + take, true, dest, part, slot);
       u += take;
+    }
+    __syncthreads();
+    // merge the pieces that waves share: entries (wave, slot) in order; equal tags form a group
+    __shared__ int32_t grp_s[2 * kWaves + 1][2];
+    __shared__ int32_t ngrp_s;
+    if (threadIdx.x == 0) {
+      int n = 0;
+      int64_t cur = -2;
+      for (int e = 0; e < 2 * kWaves; ++e) {
+        const int64_t t = tag_s[e / 2][e % 2];
+        if (t < 0) continue;
+        if (t != cur) {
+          grp_s[n][0] = e;
+          ++n;
+          cur = t;
+        }
+        grp_s[n - 1][1] = e;
+      }
+      ngrp_s = n;
+    }
+    __syncthreads();
+    for (int q = 0; q < ngrp_s; ++q) {
+      const int e0 = grp_s[q][0], e1 = grp_s[q][1];
+      const int* inf = info_s[e0 / 2][e0 % 2];
+      const int b = inf[0], g = inf[1], dest = inf[2], part = inf[3];
+      for (int idx = threadIdx.x; idx < G * D; idx += 64 * kWaves) {
+        const int h = idx / D, d = idx % D;
+        float M = -INFINITY;
+        for (int e = e0; e <= e1; ++e)
+          if (tag_s[e / 2][e % 2] >= 0) M = fmaxf(M, m_s[e / 2][e % 2][h]);
+        float num = 0.f, den = 0.f;
+        if (M != -INFINITY) {
+          for (int e = e0; e <= e1; ++e) {
+            if (tag_s[e / 2][e % 2] < 0) continue;
+            const float f = __builtin_amdgcn_exp2f(m_s[e / 2][e % 2][h] - M);
+            num += f * o_s[e / 2][e % 2][h][d];
+            den += f * l_s[e / 2][e % 2][h];
+          }
+        }
+        const float o = den > 0.f ? num / den : 0.f;
+        const int64_t row = static_cast<int64_t>(b) * a.Hq + static_cast<int64_t>(g) * G + h;
+        if (dest == 0) {
+          a.out[row * D + d] = o;
+        } else {
+          const int64_t slot = static_cast<int64_t>(part) * G + h;
+          a.ws_o[slot * D + d] = o;
+          if (d == 0) {
+            a.ws_m[slot] = M;
+            a.ws_l[slot] = den;
+          }
+        }
+      }
     }
   }
 }
@@ -525,14 +638,15 @@ __global__ void __launch_bounds__(256) streamk_reduce_kernel(DecodeArgs a) {
 
 template <int G, int D, bool kI8>
 hipError_t launch_gd(const DecodeArgs& a, hipStream_t stream) {
-  if (a.nw == 0) {
+  if (a.nw == 0 || G > kMaxBalancedGroup) {
     const dim3 grid(a.np_max, a.Hkv, a.B);
     hipLaunchKernelGGL((decode_mfma_kernel<G, D, false, kI8>), grid, dim3(64 * kWaves), 0, stream,
                        a);
     return hipGetLastError();
   }
+  constexpr int Gb = G <= kMaxBalancedGroup ? G : kMaxBalancedGroup;  // never launched for G > 8
   const size_t lds = static_cast<size_t>(a.B + 1) * sizeof(int32_t);
-  hipLaunchKernelGGL((decode_mfma_kernel<G, D, true, kI8>), dim3(a.nw), dim3(64 * kWaves), lds,
+  hipLaunchKernelGGL((decode_mfma_kernel<Gb, D, true, kI8>), dim3(a.nw), dim3(64 * kWaves), lds,
                      stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -34,8 +34,10 @@ struct DecodeArgs {
 
 // Upper bound on balanced-schedule workgroups; sizes the workspace.
 constexpr int kMaxBalancedWorkgroups = 1024;
-// Largest batch the balanced schedule takes (its prefix sums live in LDS).
+// Largest batch / group size the balanced schedule takes (its prefix sums and per-wave states
+// live in LDS).
 constexpr int kMaxBalancedBatch = 8192;
+constexpr int kMaxBalancedGroup = 8;
 // Resident workgroups of the balanced MFMA kernel per compute unit.
 int mfma_workgroups_per_cu();
 
