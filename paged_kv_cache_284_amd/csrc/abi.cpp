@@ -115,10 +115,10 @@ int64_t fixed_bytes(int32_t B, int32_t Hq, int32_t D, int64_t np) {
   return 2 * align256(rows * 4) + align256(rows * D * 4);
 }
 
-// Balanced schedule: m, l [nw][2][G], o [nw][2][G][D], prefix sums [B + 1].
-int64_t balanced_bytes(int32_t B, int32_t G, int32_t D, int64_t nw) {
+// Balanced schedule: m, l [nw][2][G], o [nw][2][G][D], merge records [nw][4].
+int64_t balanced_bytes(int32_t G, int32_t D, int64_t nw) {
   const int64_t rows = nw * 2 * G;
-  return 2 * align256(rows * 4) + align256(rows * D * 4) + align256((B + 1) * 4);
+  return 2 * align256(rows * 4) + align256(rows * D * 4) + align256(nw * 16);
 }
 
 int cu_count() {
@@ -146,7 +146,7 @@ size_t pa_decode_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
   const int64_t np = (static_cast<int64_t>(max_seq_len) + P - 1) / P;
   int64_t bytes = fixed_bytes(B, Hq, D, np);
   if (partition_tokens == 0 && B <= pa::kMaxBalancedBatch && Hq / Hkv <= pa::kMaxBalancedGroup) {
-    const int64_t bal = balanced_bytes(B, Hq / Hkv, D, pa::kMaxBalancedWorkgroups);
+    const int64_t bal = balanced_bytes(Hq / Hkv, D, pa::kMaxBalancedWorkgroups);
     bytes = bytes > bal ? bytes : bal;
   }
   return static_cast<size_t>(bytes < 256 ? 256 : bytes);
@@ -220,8 +220,8 @@ int pa_decode(float* out, const void* q, int32_t q_dtype, const void* k_cache,
     a.ws_m = reinterpret_cast<float*>(base);
     a.ws_l = reinterpret_cast<float*>(base + align256(rows * 4));
     a.ws_o = reinterpret_cast<float*>(base + 2 * align256(rows * 4));
-    a.ws_cum = reinterpret_cast<int32_t*>(base + 2 * align256(rows * 4) +
-                                          align256(rows * D * 4));
+    a.ws_merge = reinterpret_cast<int32_t*>(base + 2 * align256(rows * 4) +
+                                            align256(rows * D * 4));
   } else if (a.np_max > 1) {
     const int64_t rows = static_cast<int64_t>(B) * Hq * a.np_max;
     a.ws_m = reinterpret_cast<float*>(base);

@@ -12,17 +12,16 @@
 // the softmax.
 //
 // Work split.  The unit of work is a block *pair* (32 tokens) of one (KV head, sequence) segment.
-// A workgroup (4 waves) processes a run of pairs of one segment -- a "piece": its waves take the
-// pairs in turn with private softmax state and merge the 4 states in LDS at the end.  Two
-// schedules decide the pieces:
+// A workgroup has 8 waves, two per SIMD.  Two schedules decide who takes which pairs:
 //   balanced (default): all segments are laid end to end (KV-head-major, then sequence) and the
 //     unit range is cut into equal contiguous spans, one per resident workgroup, so every
-//     workgroup moves the same number of bytes whatever the length mix.  A span starts and ends
-//     inside at most two segments; those partial pieces are merged by streamk_reduce_kernel.
-//     Workgroups are numbered so that each XCD (blockIdx % 8) takes one contiguous eighth of the
-//     range: sequences that share prefix blocks meet in the same L2.
+//     workgroup moves the same number of bytes whatever the length mix.  Each wave streams its
+//     own contiguous eighth of the span with no barriers, keeping one softmax state per segment
+//     it walks through and writing it out directly when it holds the whole segment; states of
+//     segments it shares with other waves are merged in LDS at the end.  A segment cut by a
+//     span boundary leaves a partial state per workgroup, merged by streamk_reduce_kernel.
 //   fixed partitions (caller-given length): one workgroup per (partition, KV head, sequence),
-//     merged by splitk_reduce_kernel.
+//     its waves taking the pairs in turn, merged by splitk_reduce_kernel.
 //
 // One pair (blocks A, B of one KV head) per wave iteration, v_mfma_f32_16x16x32_bf16 throughout:
 //   scores  S = K . q^T as two 16(token) x 16(head) tiles, K tiles token-major in HBM (each lane
@@ -485,8 +484,6 @@ decode_mfma_kernel(DecodeArgs a) {
     const int64_t U = T * Hkv;            // all units
     const int NW = a.nw;
     const int wl = blockIdx.x;
-    if (wl == 0)
-      for (int i = threadIdx.x; i <= B; i += 64 * kWaves) a.ws_cum[i] = cum_s[i];
     // empty sequences produce zeros
     for (int b = wl; b < B; b += NW) {
       if (cum_s[b + 1] != cum_s[b]) continue;
@@ -495,6 +492,32 @@ decode_mfma_kernel(DecodeArgs a) {
     }
     // workgroup span [u0, u1); wave w streams its own eighth [v0, v1) of it with no barriers
     const int64_t u0 = U * wl / NW, u1 = U * (wl + 1) / NW;
+    // Merge record for the reduce kernel: the segment that starts in this span and runs past
+    // its end (at most one), as {b, g, last workgroup holding a piece, slot of the piece here}.
+    // An empty span marks its slot 0 as holding nothing.
+    if (threadIdx.x == 0) {
+      int4 rec = {-1, 0, 0, 0};
+      if (u0 < u1) {
+        const int g = static_cast<int>((u1 - 1) / T);
+        const int rem = static_cast<int>(u1 - 1 - static_cast<int64_t>(g) * T);
+        int lo = 0, hi = B - 1;
+        while (lo < hi) {
+          const int mid = (lo + hi) / 2;
+          if (cum_s[mid + 1] > rem) hi = mid; else lo = mid + 1;
+        }
+        const int64_t s0 = static_cast<int64_t>(g) * T + cum_s[lo];
+        const int64_t s1 = s0 + (cum_s[lo + 1] - cum_s[lo]);
+        if (s0 >= u0 && s1 > u1) {
+          const int64_t wb = (s1 * NW + U - 1) / U - 1;  // workgroup holding unit s1 - 1
+          rec = int4{lo, g, static_cast<int>(wb), s0 == u0 ? 0 : 1};
+        }
+      }
+      reinterpret_cast<int4*>(a.ws_merge)[wl] = rec;
+    }
+    if (u0 == u1 && threadIdx.x < G) {
+      a.ws_m[static_cast<int64_t>(wl) * 2 * G + threadIdx.x] = -INFINITY;
+      a.ws_l[static_cast<int64_t>(wl) * 2 * G + threadIdx.x] = 0.f;
+    }
     const int64_t v0 = u0 + (u1 - u0) * w / kWaves, v1 = u0 + (u1 - u0) * (w + 1) / kWaves;
     __shared__ int64_t tag_s[kWaves][2];   // workgroup piece (first unit) held in each LDS slot
     __shared__ int32_t info_s[kWaves][2][4];  // its b, g, destination, partial slot
@@ -589,47 +612,30 @@ decode_mfma_kernel(DecodeArgs a) {
   }
 }
 
-// Merge the partial pieces of each (sequence, KV head) segment of the balanced schedule.  The
-// pieces are found from the same span arithmetic the decode kernel used: workgroup w (logical)
-// covers units [U w / NW, U (w + 1) / NW); a piece sits in slot 0 of its workgroup when it
-// starts that workgroup's span, else in slot 1.
+// Merge the partial pieces of the segments the balanced schedule cut: one workgroup per decode
+// workgroup wa, reading the record wa left.  The pieces sit in slot `first` of wa and in slot 0
+// of wa + 1 .. wb (an empty span's slot 0 holds l = 0 and is skipped).  Pieces are combined in
+// workgroup order, so the result does not depend on timing.
 template <int G, int D>
 __global__ void __launch_bounds__(256) streamk_reduce_kernel(DecodeArgs a) {
-  __shared__ int32_t slot_s[kMaxBalancedWorkgroups];
-  const int b = blockIdx.x, g = blockIdx.y;
-  const int32_t* cum = a.ws_cum;
-  const int64_t T = cum[a.B];
-  const int n_b = cum[b + 1] - cum[b];
-  if (n_b == 0) return;
-  const int64_t U = T * a.Hkv;
-  const int64_t NW = a.nw;
-  const int64_t s0 = static_cast<int64_t>(g) * T + cum[b], s1 = s0 + n_b;
-  const int64_t wa = ((s0 + 1) * NW + U - 1) / U - 1;
-  const int64_t wb = (s1 * NW + U - 1) / U - 1;
-  if (wa == wb) return;
-  // slot of each piece, -1 for workgroups whose span is empty (fewer units than workgroups)
-  const int np = static_cast<int>(wb - wa + 1);
-  for (int k = threadIdx.x; k < np; k += blockDim.x) {
-    const int64_t wv = wa + k;
-    const int64_t st = U * wv / NW;
-    const bool empty = st == U * (wv + 1) / NW;
-    slot_s[k] = empty ? -1 : static_cast<int32_t>(wv * 2 + (k == 0 && st < s0 ? 1 : 0));
-  }
-  __syncthreads();
+  const int wa = blockIdx.x;
+  const int4 rec = reinterpret_cast<const int4*>(a.ws_merge)[wa];
+  if (rec.x < 0) return;
+  const int b = rec.x, g = rec.y, wb = rec.z, first = rec.w;
   for (int idx = threadIdx.x; idx < G * D; idx += blockDim.x) {
     const int h = idx / D, d = idx % D;
-    float M = -INFINITY;
-    for (int k = 0; k < np; ++k)
-      if (slot_s[k] >= 0) M = fmaxf(M, a.ws_m[static_cast<int64_t>(slot_s[k]) * G + h]);
-    float num = 0.f, den = 0.f;
-    if (M != -INFINITY) {
-      for (int k = 0; k < np; ++k) {
-        if (slot_s[k] < 0) continue;
-        const int64_t slot = static_cast<int64_t>(slot_s[k]) * G + h;
-        const float f = a.ws_l[slot] * __builtin_amdgcn_exp2f(a.ws_m[slot] - M);
-        den += f;
-        num += f * a.ws_o[slot * D + d];
-      }
+    float M = -INFINITY, num = 0.f, den = 0.f;
+#pragma unroll 4
+    for (int v = wa; v <= wb; ++v) {
+      const int64_t slot = static_cast<int64_t>(2 * v + (v == wa ? first : 0)) * G + h;
+      const float m = a.ws_m[slot], l = a.ws_l[slot], o = a.ws_o[slot * D + d];
+      if (!(l > 0.f)) continue;
+      const float m_new = fmaxf(M, m);
+      const float c = __builtin_amdgcn_exp2f(M - m_new);  // 0 for the first piece
+      const float f = l * __builtin_amdgcn_exp2f(m - m_new);
+      den = den * c + f;
+      num = num * c + f * o;
+      M = m_new;
     }
     const int64_t row = static_cast<int64_t>(b) * a.Hq + static_cast<int64_t>(g) * G + h;
     a.out[row * D + d] = den > 0.f ? num / den : 0.f;
@@ -650,7 +656,7 @@ hipError_t launch_gd(const DecodeArgs& a, hipStream_t stream) {
                      stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((streamk_reduce_kernel<G, D>), dim3(a.B, a.Hkv), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((streamk_reduce_kernel<Gb, D>), dim3(a.nw), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -28,7 +28,7 @@ struct DecodeArgs {
   int32_t partition;          // tokens per partition (multiple of 64)
   int32_t np_max;             // ceil(max_seq_len / partition), >= 1
   int32_t nw;                 // balanced schedule: workgroups (0 = fixed partitions)
-  int32_t* ws_cum;            // balanced schedule: pair-count prefix sums [B + 1]
+  int32_t* ws_merge;          // balanced schedule: per-workgroup merge records [nw][4]
   float scale_log2;           // softmax scale * log2(e)
 };
 
