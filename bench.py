@@ -144,21 +144,21 @@ class StepRunner:
         self.ws = torch.empty(pkv.decode_workspace_size(w.B, w.Hq, w.Hkv, w.D, max_len, partition),
                               dtype=torch.uint8, device=dev)
         self.out = torch.empty((w.B, w.Hq, w.D), dtype=torch.float32, device=dev)
-        # staging for the per-step host arrays, written by pa_step straight into pinned memory:
-        # slots int64[B] | seq_lens int32[B] | table_index int32[B] | cow pairs int32[B][2];
-        # two pinned buffers used in turn, one device copy
+        # the per-step host arrays, written by pa_step straight into pinned memory and read there
+        # by the kernels: slots int64[B] | seq_lens int32[B] | table_index int32[B] | cow pairs
+        # int32[B][2]; two pinned buffers used in turn
         B = w.B
         self.off = [0, 8 * B, 12 * B, 16 * B]
         nbytes = 24 * B
         self.pinned = [torch.empty(nbytes, dtype=torch.uint8, pin_memory=True) for _ in range(2)]
         self.hev = HipEvents()
         # decode timing events, recorded before / after each decode; the one before step s's
-        # decode also marks its staging copy done, which guards pinned buffer s % 2
+        # decode also marks the end of the launches that read pinned buffer s % 2
         self.n_ev = total_steps + 2
         self.ev_before = [self.hev.create() for _ in range(self.n_ev)]
         self.ev_after = [self.hev.create() for _ in range(self.n_ev)]
         self.timed = []
-        self.stage = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        self.lens_step = torch.empty(B, dtype=torch.int32, device=dev)  # written by the append
         self.step_no = 0
         self.max_len = int(self.lens.max())
         # ctypes arguments that do not change from step to step
@@ -170,8 +170,7 @@ class StepRunner:
         self.seqs_p = self.seqs.ctypes.data_as(C.POINTER(C.c_int32))
         self.hp = [[C.cast(pb.data_ptr() + o, C.POINTER(C.c_int64 if j == 0 else C.c_int32))
                     for j, o in enumerate(self.off)] for pb in self.pinned]
-        sd = self.stage.data_ptr()
-        self.d_slots, self.d_lens, self.d_tidx, self.d_pairs = (sd + o for o in self.off)
+        self.raw = [[pb.data_ptr() + o for o in self.off] for pb in self.pinned]
         self.kv_code = {"f32": pkv.PA_F32, "bf16": pkv.PA_BF16, "i8": pkv.PA_I8}[w.kv_dtype]
         self.q_code = {"f32": pkv.PA_F32, "bf16": pkv.PA_BF16}[w.q_dtype]
         self.stream = torch.cuda.current_stream().cuda_stream
@@ -181,8 +180,9 @@ class StepRunner:
             self.lens_dev = torch.from_numpy(self.lens).to(dev)
 
     def step(self, time_decode: bool = False):
-        """One decode step through the C ABI: allocator step into pinned memory, one H2D copy,
-        copy-on-write copies (if any), fused append + table patch, decode."""
+        """One decode step through the C ABI: allocator step into pinned memory, copy-on-write
+        copies (if any), fused append + table patch + length copy reading the pinned arrays,
+        decode."""
         torch, pkv, w, L = self.torch, self.pkv, self.w, self.L
         s = self.step_no
         if w.append:
@@ -194,22 +194,22 @@ class StepRunner:
                            self.C.byref(self.n_cow))
             if st != 0:
                 raise pkv.PagedKVError(st, "pa_step")
-            self.stage.copy_(self.pinned[i], non_blocking=True)
+            h_slots, h_lens, h_tidx, h_pairs = self.raw[i]
             self.max_len += 1
             n_cow = self.n_cow.value
             if n_cow:
                 st = L.pa_copy_blocks(self.k.data_ptr(), self.v.data_ptr(), self.ks_p, self.vs_p,
-                                      self.d_pairs, n_cow, w.Hkv, w.D, w.bs, w.NB, self.kv_code,
+                                      h_pairs, n_cow, w.Hkv, w.D, w.bs, w.NB, self.kv_code,
                                       self.stream)
                 if st != 0:
                     raise pkv.PagedKVError(st, "pa_copy_blocks")
             kn, vn = self.new[s % len(self.new)]
-            st = L.pa_append_step(kn.data_ptr(), vn.data_ptr(), self.d_slots, self.d_tidx,
+            lens_d = self.lens_step.data_ptr()
+            st = L.pa_append_step(kn.data_ptr(), vn.data_ptr(), h_slots, h_tidx, h_lens, lens_d,
                                   self.k.data_ptr(), self.v.data_ptr(), self.tables.data_ptr(),
                                   self.MB, w.B, w.Hkv, w.D, w.bs, w.NB, self.kv_code, self.stream)
             if st != 0:
                 raise pkv.PagedKVError(st, "pa_append_step")
-            lens_d = self.d_lens
             self.lens += 1
         else:
             lens_d = self.lens_dev.data_ptr()

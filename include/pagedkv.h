@@ -29,6 +29,9 @@
  *     stream) and return without synchronising.  A launch error returns PA_ERR_DEVICE.
  *   - The library allocates no device memory.  Scratch space for pa_decode is a caller buffer
  *     of at least pa_decode_workspace_size() bytes.
+ *   - "Device-readable" arrays (the per-step slot mappings, table indices, lengths and copy
+ *     pairs below) may be device memory or pinned host memory (hipHostMalloc): the kernels read
+ *     each entry once, so a step's host-made arrays need no separate upload.
  *   - Not checked on the device, the caller's contract: block ids in tables, slot mappings and
  *     copy pairs lie in [0, NB); seq_lens[b] <= max_seq_len.  Kernels clamp lengths to
  *     max_seq_len and skip table entries outside [0, NB), so a broken contract gives wrong
@@ -141,7 +144,7 @@ int pa_free_list(const pa_allocator* a, int32_t* out, int32_t cap, int32_t* n);
 /* Append one token per sequence ([Serving] "What the KV Cache Is": each decode step appends one
  * more token's K and V; "The Life of a Request").  k_new, v_new: device [B][Hkv][D] in the
  * cache dtype (PA_F32 or PA_BF16; int8 caches are written by their quantiser, not here).
- * slot_mapping: device [B] int64, -1 = skip this sequence.  Writes K into k_cache[slot/bs][g]
+ * slot_mapping: device-readable [B] int64, -1 = skip this sequence.  Writes K into k_cache[slot/bs][g]
  * [slot%bs][:] and V into v_cache[slot/bs][g][:][slot%bs]; nothing else is touched.  Two
  * sequences must not share a slot.  Constraints: B >= 0, Hkv >= 1, D in {64, 128}, bs == 16. */
 int pa_kv_append(const void* k_new, const void* v_new, const int64_t* slot_mapping,
@@ -149,7 +152,7 @@ int pa_kv_append(const void* k_new, const void* v_new, const int64_t* slot_mappi
                  int32_t NB, int32_t kv_dtype, void* stream);
 
 /* Copy-on-write block copies ([Serving] "Sharing comes for free"; [Walkthrough] "Step 8").
- * pairs: device [n][2] int32 (src, dst).  Copies the whole K and V tile of block src over block
+ * pairs: device-readable [n][2] int32 (src, dst).  Copies the whole K and V tile of block src over block
  * dst, and for PA_I8 also both scales (k_scale, v_scale must then be non-NULL).  Destinations
  * must be distinct and no destination may be another pair's source (the allocator never
  * produces either).  n == 0 enqueues nothing. */
@@ -159,17 +162,21 @@ int pa_copy_blocks(void* k_cache, void* v_cache, float* k_scale, float* v_scale,
 
 /* Patch a device block table after pa_step: for every i < B with table_index[i] >= 0,
  * block_tables[i][table_index[i]] = slots[i] / bs.  slots (int64) and table_index (int32) are
- * device [B] arrays; entries outside [0, max_blocks) are skipped. */
+ * device-readable [B] arrays; entries outside [0, max_blocks) are skipped. */
 int pa_update_block_tables(int32_t* block_tables, int32_t max_blocks, const int64_t* slots,
                            const int32_t* table_index, int32_t B, int32_t bs, void* stream);
 
-/* pa_kv_append and pa_update_block_tables in one launch: the cache writes of a decode step once
- * its copy-on-write copies (pa_copy_blocks) are enqueued.  Arguments as for those two calls;
- * table_index may be NULL (no table changes). */
+/* The device side of a decode step's bookkeeping in one launch, once its copy-on-write copies
+ * (pa_copy_blocks) are enqueued: pa_kv_append, pa_update_block_tables, and
+ * seq_lens_out[b] = seq_lens_in[b] (the lengths pa_step produced, for pa_decode).  Arguments as
+ * for those calls; table_index may be NULL (no table changes); seq_lens_in / seq_lens_out are
+ * both NULL (no copy) or both set: a device-readable and a device [B] int32 array.  With pa_step
+ * writing its arrays into pinned host memory, this call reads them there directly. */
 int pa_append_step(const void* k_new, const void* v_new, const int64_t* slot_mapping,
-                   const int32_t* table_index, void* k_cache, void* v_cache,
-                   int32_t* block_tables, int32_t max_blocks, int32_t B, int32_t Hkv, int32_t D,
-                   int32_t bs, int32_t NB, int32_t kv_dtype, void* stream);
+                   const int32_t* table_index, const int32_t* seq_lens_in, int32_t* seq_lens_out,
+                   void* k_cache, void* v_cache, int32_t* block_tables, int32_t max_blocks,
+                   int32_t B, int32_t Hkv, int32_t D, int32_t bs, int32_t NB, int32_t kv_dtype,
+                   void* stream);
 
 /* Bytes of scratch that pa_decode needs for these sizes (same partition_tokens as the decode
  * call).  Returns 0 for invalid sizes.  The size does not depend on the lengths themselves, so a

@@ -55,8 +55,8 @@ _SIGNATURES = {
     "pa_copy_blocks": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                                  _vp]),
     "pa_update_block_tables": (C.c_int, [_vp, _i32, _vp, _vp, _i32, _i32, _vp]),
-    "pa_append_step": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
-                                 _i32, _i32, _vp]),
+    "pa_append_step": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
+                                 _i32, _i32, _i32, _i32, _vp]),
     "pa_decode_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "pa_decode": (C.c_int, [_vp, _vp, _i32, _vp, _vp, _i32, _vp, _vp, _vp, _i32, _vp, _i32,
                             _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz, _vp]),
@@ -276,6 +276,19 @@ def _dev(t, name, dtype=None):
     return t.data_ptr()
 
 
+def _readable(t, name, dtype=None):
+    """A device-readable array: a device tensor or a pinned host tensor."""
+    if t is None:
+        return None
+    if not t.is_cuda and not t.is_pinned():
+        raise ValueError(f"{name} must be a device tensor or pinned host memory")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
 def _stream(stream=None):
     torch = _torch()
     s = torch.cuda.current_stream() if stream is None else stream
@@ -294,7 +307,7 @@ def kv_append(k_new, v_new, slot_mapping, k_cache, v_cache, stream=None) -> None
     if k_new.dtype != k_cache.dtype or v_new.dtype != k_cache.dtype or v_cache.dtype != k_cache.dtype:
         raise TypeError("k_new, v_new, k_cache and v_cache must share one dtype")
     _check(lib().pa_kv_append(_dev(k_new, "k_new"), _dev(v_new, "v_new"),
-                              _dev(slot_mapping, "slot_mapping", torch.int64),
+                              _readable(slot_mapping, "slot_mapping", torch.int64),
                               _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), B, Hkv, D, bs,
                               NB, _dtype_code(k_cache), _stream(stream)), "pa_kv_append")
 
@@ -309,7 +322,7 @@ def copy_blocks(k_cache, v_cache, pairs, k_scale=None, v_scale=None, stream=None
     _check(lib().pa_copy_blocks(_dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
                                 _dev(k_scale, "k_scale", torch.float32),
                                 _dev(v_scale, "v_scale", torch.float32),
-                                _dev(pairs, "pairs", torch.int32) if n else None, n, Hkv, D, bs,
+                                _readable(pairs, "pairs", torch.int32) if n else None, n, Hkv, D, bs,
                                 NB, _dtype_code(k_cache), _stream(stream)), "pa_copy_blocks")
 
 
@@ -320,14 +333,15 @@ def update_block_tables(block_tables, slots, table_index, stream=None) -> None:
     if tuple(slots.shape) != (B,) or tuple(table_index.shape) != (B,):
         raise ValueError("slots and table_index must be [B]")
     _check(lib().pa_update_block_tables(_dev(block_tables, "block_tables", torch.int32), MB,
-                                        _dev(slots, "slots", torch.int64),
-                                        _dev(table_index, "table_index", torch.int32), B,
+                                        _readable(slots, "slots", torch.int64),
+                                        _readable(table_index, "table_index", torch.int32), B,
                                         BLOCK_SIZE, _stream(stream)), "pa_update_block_tables")
 
 
 def append_step(k_new, v_new, slot_mapping, table_index, k_cache, v_cache, block_tables,
-                stream=None) -> None:
-    """kv_append and update_block_tables in one launch."""
+                seq_lens=None, seq_lens_out=None, stream=None) -> None:
+    """kv_append, update_block_tables and (with seq_lens / seq_lens_out) a copy of the new
+    lengths in one launch.  slot_mapping, table_index and seq_lens may be pinned host tensors."""
     torch = _torch()
     NB, Hkv, bs, D = k_cache.shape
     B = k_new.shape[0]
@@ -339,9 +353,14 @@ def append_step(k_new, v_new, slot_mapping, table_index, k_cache, v_cache, block
         raise ValueError("block_tables must be [B][max_blocks]")
     if k_new.dtype != k_cache.dtype or v_new.dtype != k_cache.dtype or v_cache.dtype != k_cache.dtype:
         raise TypeError("k_new, v_new, k_cache and v_cache must share one dtype")
+    for t, n in ((table_index, "table_index"), (seq_lens, "seq_lens"), (seq_lens_out, "seq_lens_out")):
+        if t is not None and tuple(t.shape) != (B,):
+            raise ValueError(f"{n} must be [B]")
     _check(lib().pa_append_step(_dev(k_new, "k_new"), _dev(v_new, "v_new"),
-                                _dev(slot_mapping, "slot_mapping", torch.int64),
-                                _dev(table_index, "table_index", torch.int32),
+                                _readable(slot_mapping, "slot_mapping", torch.int64),
+                                _readable(table_index, "table_index", torch.int32),
+                                _readable(seq_lens, "seq_lens", torch.int32),
+                                _dev(seq_lens_out, "seq_lens_out", torch.int32),
                                 _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
                                 _dev(block_tables, "block_tables", torch.int32),
                                 block_tables.shape[1], B, Hkv, D, bs, NB, _dtype_code(k_cache),

@@ -55,14 +55,15 @@ int pa_kv_append(const void* k_new, const void* v_new, const int64_t* slot_mappi
   if (B == 0) return PA_OK;
   if (!k_new || !v_new || !slot_mapping || !k_cache || !v_cache) return PA_ERR_INVALID;
   return status_of(pa::launch_kv_append(k_new, v_new, slot_mapping, k_cache, v_cache, B, Hkv, D,
-                                        NB, elem_bytes(kv_dtype), nullptr, nullptr, 0,
-                                        static_cast<hipStream_t>(stream)));
+                                        NB, elem_bytes(kv_dtype), nullptr, nullptr, 0, nullptr,
+                                        nullptr, static_cast<hipStream_t>(stream)));
 }
 
 int pa_append_step(const void* k_new, const void* v_new, const int64_t* slot_mapping,
-                   const int32_t* table_index, void* k_cache, void* v_cache,
-                   int32_t* block_tables, int32_t max_blocks, int32_t B, int32_t Hkv, int32_t D,
-                   int32_t bs, int32_t NB, int32_t kv_dtype, void* stream) {
+                   const int32_t* table_index, const int32_t* seq_lens_in, int32_t* seq_lens_out,
+                   void* k_cache, void* v_cache, int32_t* block_tables, int32_t max_blocks,
+                   int32_t B, int32_t Hkv, int32_t D, int32_t bs, int32_t NB, int32_t kv_dtype,
+                   void* stream) {
   if (B < 0 || Hkv < 1 || NB < 1 || max_blocks < 0 || (D != 64 && D != 128))
     return PA_ERR_INVALID;
   if (bs != pa::kBlockSize) return PA_ERR_UNSUPPORTED;
@@ -72,9 +73,11 @@ int pa_append_step(const void* k_new, const void* v_new, const int64_t* slot_map
   if (B == 0) return PA_OK;
   if (!k_new || !v_new || !slot_mapping || !k_cache || !v_cache) return PA_ERR_INVALID;
   if (table_index && !block_tables) return PA_ERR_INVALID;
+  if ((seq_lens_in == nullptr) != (seq_lens_out == nullptr)) return PA_ERR_INVALID;
   return status_of(pa::launch_kv_append(k_new, v_new, slot_mapping, k_cache, v_cache, B, Hkv, D,
                                         NB, elem_bytes(kv_dtype), table_index, block_tables,
-                                        max_blocks, static_cast<hipStream_t>(stream)));
+                                        max_blocks, seq_lens_in, seq_lens_out,
+                                        static_cast<hipStream_t>(stream)));
 }
 
 int pa_copy_blocks(void* k_cache, void* v_cache, float* k_scale, float* v_scale,

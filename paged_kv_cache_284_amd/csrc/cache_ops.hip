@@ -11,37 +11,52 @@
 namespace pa {
 namespace {
 
-// One thread per element of k_new / v_new.  K rows are contiguous in the tile; V is dim-major,
-// so consecutive d land 32 B (bf16) apart -- the write is small enough for that not to matter.
-// With a table (the fused step), the first thread of each sequence also patches its block-table
-// entry when the step gave the sequence a new or copied block.
+// One workgroup per sequence.  Its first thread reads the sequence's slot (and table index and
+// length) once -- those arrays may live in pinned host memory, where every read crosses the bus
+// -- and the workgroup's threads then copy the Hkv x D elements.  K rows are contiguous in the
+// tile; V is dim-major, so consecutive d land 32 B (bf16) apart -- the write is small enough for
+// that not to matter.  With a table (the fused step) the first thread also patches the
+// sequence's block-table entry when the step gave it a new or copied block, and with lens_out it
+// copies the sequence's new length.
 template <typename T>
 __global__ void __launch_bounds__(256) kv_append_kernel(const T* __restrict__ k_new,
                                                         const T* __restrict__ v_new,
                                                         const int64_t* __restrict__ slots,
                                                         T* __restrict__ k_cache,
-                                                        T* __restrict__ v_cache, int32_t B,
-                                                        int32_t Hkv, int32_t D, int32_t NB,
+                                                        T* __restrict__ v_cache, int32_t Hkv,
+                                                        int32_t D, int32_t NB,
                                                         const int32_t* __restrict__ table_index,
                                                         int32_t* __restrict__ tables,
-                                                        int32_t max_blocks) {
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  const int64_t total = static_cast<int64_t>(B) * Hkv * D;
-  if (i >= total) return;
-  const int32_t d = static_cast<int32_t>(i % D);
-  const int32_t g = static_cast<int32_t>((i / D) % Hkv);
-  const int32_t b = static_cast<int32_t>(i / (static_cast<int64_t>(D) * Hkv));
-  const int64_t slot = slots[b];
-  if (slot < 0 || slot >= static_cast<int64_t>(NB) * kBlockSize) return;
+                                                        int32_t max_blocks,
+                                                        const int32_t* __restrict__ lens_in,
+                                                        int32_t* __restrict__ lens_out) {
+  const int32_t b = blockIdx.x;
+  __shared__ int64_t slot_s;
+  __shared__ int32_t index_s;
+  // three threads issue the three reads at once: one bus round trip
+  if (threadIdx.x == 0) {
+    const int64_t slot = slots[b];
+    slot_s = (slot >= 0 && slot < static_cast<int64_t>(NB) * kBlockSize) ? slot : -1;
+  } else if (threadIdx.x == 1) {
+    index_s = tables ? table_index[b] : -1;
+  } else if (threadIdx.x == 2 && lens_out) {
+    lens_out[b] = lens_in[b];
+  }
+  __syncthreads();
+  const int64_t slot = slot_s;
+  if (slot < 0) return;
+  if (threadIdx.x == 0 && index_s >= 0 && index_s < max_blocks)
+    tables[static_cast<int64_t>(b) * max_blocks + index_s] = static_cast<int32_t>(slot / kBlockSize);
   const int64_t blk = slot / kBlockSize;
   const int32_t off = static_cast<int32_t>(slot % kBlockSize);
-  const int64_t tile = (blk * Hkv + g);
-  k_cache[(tile * kBlockSize + off) * D + d] = k_new[i];
-  v_cache[(tile * D + d) * kBlockSize + off] = v_new[i];
-  if (tables && g == 0 && d == 0) {
-    const int32_t j = table_index[b];
-    if (j >= 0 && j < max_blocks)
-      tables[static_cast<int64_t>(b) * max_blocks + j] = static_cast<int32_t>(blk);
+  const int32_t n = Hkv * D;
+  const T* kn = k_new + static_cast<int64_t>(b) * n;
+  const T* vn = v_new + static_cast<int64_t>(b) * n;
+  for (int32_t e = threadIdx.x; e < n; e += blockDim.x) {
+    const int32_t g = e / D, d = e % D;
+    const int64_t tile = blk * Hkv + g;
+    k_cache[(tile * kBlockSize + off) * D + d] = kn[e];
+    v_cache[(tile * D + d) * kBlockSize + off] = vn[e];
   }
 }
 
@@ -53,8 +68,10 @@ __global__ void __launch_bounds__(256) copy_blocks_kernel(uint4* __restrict__ k_
                                                           const int32_t* __restrict__ pairs,
                                                           int32_t chunks, int32_t Hkv,
                                                           int32_t NB) {
-  const int32_t src = pairs[2 * blockIdx.x];
-  const int32_t dst = pairs[2 * blockIdx.x + 1];
+  __shared__ int32_t pair_s[2];  // read once: the pairs may live in pinned host memory
+  if (threadIdx.x < 2) pair_s[threadIdx.x] = pairs[2 * blockIdx.x + threadIdx.x];
+  __syncthreads();
+  const int32_t src = pair_s[0], dst = pair_s[1];
   if (src < 0 || src >= NB || dst < 0 || dst >= NB) return;
   const int64_t s0 = static_cast<int64_t>(src) * chunks;
   const int64_t d0 = static_cast<int64_t>(dst) * chunks;
@@ -88,21 +105,22 @@ __global__ void __launch_bounds__(256) update_tables_kernel(int32_t* __restrict_
 hipError_t launch_kv_append(const void* k_new, const void* v_new, const int64_t* slots,
                             void* k_cache, void* v_cache, int32_t B, int32_t Hkv, int32_t D,
                             int32_t NB, int32_t elem_bytes, const int32_t* table_index,
-                            int32_t* tables, int32_t max_blocks, hipStream_t stream) {
-  const int64_t total = static_cast<int64_t>(B) * Hkv * D;
-  if (total == 0) return hipSuccess;
+                            int32_t* tables, int32_t max_blocks, const int32_t* lens_in,
+                            int32_t* lens_out, hipStream_t stream) {
+  if (B == 0) return hipSuccess;
   if (!table_index) tables = nullptr;
-  const dim3 grid(static_cast<unsigned>((total + 255) / 256));
+  if (!lens_in) lens_out = nullptr;
+  const dim3 grid(static_cast<unsigned>(B));
   if (elem_bytes == 4) {
     hipLaunchKernelGGL(kv_append_kernel<uint32_t>, grid, dim3(256), 0, stream,
                        static_cast<const uint32_t*>(k_new), static_cast<const uint32_t*>(v_new),
                        slots, static_cast<uint32_t*>(k_cache), static_cast<uint32_t*>(v_cache),
-                       B, Hkv, D, NB, table_index, tables, max_blocks);
+                       Hkv, D, NB, table_index, tables, max_blocks, lens_in, lens_out);
   } else if (elem_bytes == 2) {
     hipLaunchKernelGGL(kv_append_kernel<uint16_t>, grid, dim3(256), 0, stream,
                        static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new),
                        slots, static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache),
-                       B, Hkv, D, NB, table_index, tables, max_blocks);
+                       Hkv, D, NB, table_index, tables, max_blocks, lens_in, lens_out);
   } else {
     return hipErrorInvalidValue;
   }

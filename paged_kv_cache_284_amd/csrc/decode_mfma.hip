@@ -42,6 +42,7 @@ namespace pa {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -78,18 +79,21 @@ struct PairRegsI8 {
   float ks_a, ks_b, vs_a, vs_b;
 };
 
-// Eight int8 codes c -> eight bf16 values of u = c + 128 (0..255, exact in bf16).  The +128
-// offset is taken out of the dot products by the caller.
-__device__ __forceinline__ bf16x8 codes_to_bf16(uint32_t x0, uint32_t x1) {
+// Eight int8 codes c -> eight fp16 values 1152 + c (exact).  Flipping the sign bit gives the
+// byte u = c + 128; a byte permute then sets each u under the fp16 exponent of 1024, giving
+// 1024 + u.  Three ALU ops per four codes; the caller takes the 1152 offset out of the sums.
+__device__ __forceinline__ f16x8 codes_to_f16(uint32_t x0, uint32_t x1) {
+  constexpr uint32_t kExp = 0x64646464u;  // high byte of fp16 1024
   const uint32_t u0 = x0 ^ 0x80808080u, u1 = x1 ^ 0x80808080u;
-  f32x8 f;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    f[e] = static_cast<float>((u0 >> (8 * e)) & 0xffu);
-    f[4 + e] = static_cast<float>((u1 >> (8 * e)) & 0xffu);
-  }
-  return __builtin_convertvector(f, bf16x8);
+  u32x4 r;
+  // v_perm_b32 picks result bytes from {src0 = bytes 4..7, src1 = bytes 0..3}
+  r[0] = __builtin_amdgcn_perm(u0, kExp, 0x00050004u);  // {u.b0, 0x64, u.b1, 0x64}
+  r[1] = __builtin_amdgcn_perm(u0, kExp, 0x00070006u);
+  r[2] = __builtin_amdgcn_perm(u1, kExp, 0x00050004u);
+  r[3] = __builtin_amdgcn_perm(u1, kExp, 0x00070006u);
+  return __builtin_bit_cast(f16x8, r);
 }
+constexpr float kCodeOffset = 1152.f;  // codes_to_f16(c) = kCodeOffset + c
 
 template <int G, int D, bool kStream, bool kI8>
 __global__ void __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -149,10 +153,20 @@ decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
       for (int s = 0; s < kSteps; ++s) {
         if constexpr (kI8) {
-          qv[s] = load16(q + 16 * (qg + 4 * (s / 2)) + 8 * (s % 2));
+          // int8 cache: the score MFMA runs in fp16 (bf16 -> fp16 is exact in fp16's normal
+          // range), next to fp16 codes
+          const u32x4 raw = load16(q + 16 * (qg + 4 * (s / 2)) + 8 * (s % 2));
+          f32x8 f;
 #pragma unroll
-          for (int c = 0; c < 4; ++c)
-            qsum += __uint_as_float(qv[s][c] << 16) + __uint_as_float(qv[s][c] & 0xffff0000u);
+          for (int c = 0; c < 4; ++c) {
+            f[2 * c] = __uint_as_float(raw[c] << 16);
+            f[2 * c + 1] = __uint_as_float(raw[c] & 0xffff0000u);
+          }
+          const f16x8 h = __builtin_convertvector(f, f16x8);
+          qv[s] = __builtin_bit_cast(u32x4, h);
+          const f32x8 back = __builtin_convertvector(h, f32x8);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) qsum += back[e];
         } else {
           qv[s] = load16(q + 32 * s + 8 * qg);
         }
@@ -219,14 +233,16 @@ decode_mfma_kernel(DecodeArgs a) {
       if constexpr (kI8) {
 #pragma unroll
         for (int c = 0; c < kSteps / 2; ++c) {
-          s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(codes_to_bf16(R.k1[c][0], R.k1[c][1]),
-                                                        as_bf16x8(qv[2 * c]), s1, 0, 0, 0);
-          s2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(codes_to_bf16(R.k2[c][0], R.k2[c][1]),
-                                                        as_bf16x8(qv[2 * c]), s2, 0, 0, 0);
-          s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(codes_to_bf16(R.k1[c][2], R.k1[c][3]),
-                                                        as_bf16x8(qv[2 * c + 1]), s1, 0, 0, 0);
-          s2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(codes_to_bf16(R.k2[c][2], R.k2[c][3]),
-                                                        as_bf16x8(qv[2 * c + 1]), s2, 0, 0, 0);
+          const f16x8 q0 = __builtin_bit_cast(f16x8, qv[2 * c]);
+          const f16x8 q1 = __builtin_bit_cast(f16x8, qv[2 * c + 1]);
+          s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes_to_f16(R.k1[c][0], R.k1[c][1]), q0,
+                                                       s1, 0, 0, 0);
+          s2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes_to_f16(R.k2[c][0], R.k2[c][1]), q0,
+                                                       s2, 0, 0, 0);
+          s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes_to_f16(R.k1[c][2], R.k1[c][3]), q1,
+                                                       s1, 0, 0, 0);
+          s2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes_to_f16(R.k2[c][2], R.k2[c][3]), q1,
+                                                       s2, 0, 0, 0);
         }
       } else {
 #pragma unroll
@@ -241,9 +257,9 @@ decode_mfma_kernel(DecodeArgs a) {
       const bool tail = (tok0 + kPair > end) || R.blk_b < 0 || R.blk_a < 0;
       float sc[8];
       if constexpr (kI8) {
-        // score = k_scale * sum_d q_d (u_d - 128), u = code + 128
+        // score = k_scale * sum_d q_d c_d = k_scale * (sum_d q_d (1152 + c_d) - 1152 sum_d q_d)
         const float f = (vblk_sel ? R.ks_b : R.ks_a) * a.scale_log2;
-        const float off = 128.f * qsum;
+        const float off = kCodeOffset * qsum;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           sc[e] = (s1[e] - off) * f;
@@ -296,7 +312,7 @@ decode_mfma_kernel(DecodeArgs a) {
       }
       l_run = l_run * alpha + psum;
       if constexpr (kI8) {
-        // fold this block's V scale into P; keep the sum of P to take out the +128 offset
+        // fold this block's V scale into P; keep the sum of P to take out the code offset
         const float vs = vblk_sel ? R.vs_b : R.vs_a;
         float csum = 0.f;
 #pragma unroll
@@ -318,43 +334,71 @@ decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
         for (int n = 0; n < kTiles; ++n) acc[n][j] *= aj;
       }
-      // P as bf16 hi + lo
-      const bf16x8 p_hi = __builtin_convertvector(pv, bf16x8);
-      const u32x4 hi_bits = __builtin_bit_cast(u32x4, p_hi);
-      f32x8 rest;
+      if constexpr (kI8) {
+        // P as fp16 hi + lo next to fp16 codes
+        const f16x8 p_hi = __builtin_convertvector(pv, f16x8);
+        const f16x8 p_lo = __builtin_convertvector(pv - __builtin_convertvector(p_hi, f32x8),
+                                                   f16x8);
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        rest[2 * c] = pv[2 * c] - __uint_as_float(hi_bits[c] << 16);
-        rest[2 * c + 1] = pv[2 * c + 1] - __uint_as_float(hi_bits[c] & 0xffff0000u);
-      }
-      const bf16x8 p_lo = __builtin_convertvector(rest, bf16x8);
-#pragma unroll
-      for (int n = 0; n < kTiles; ++n) {
-        bf16x8 vop;
-        if constexpr (kI8) {
-          vop = codes_to_bf16(R.v[n][0], R.v[n][1]);
-        } else {
-          vop = as_bf16x8(R.v[n]);
+        for (int n = 0; n < kTiles; ++n) {
+          const f16x8 vop = codes_to_f16(R.v[n][0], R.v[n][1]);
+          acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(p_hi, vop, acc[n], 0, 0, 0);
+          acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(p_lo, vop, acc[n], 0, 0, 0);
         }
-        acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(p_hi, vop, acc[n], 0, 0, 0);
-        acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(p_lo, vop, acc[n], 0, 0, 0);
+      } else {
+        // P as bf16 hi + lo
+        const bf16x8 p_hi = __builtin_convertvector(pv, bf16x8);
+        const u32x4 hi_bits = __builtin_bit_cast(u32x4, p_hi);
+        f32x8 rest;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          rest[2 * c] = pv[2 * c] - __uint_as_float(hi_bits[c] << 16);
+          rest[2 * c + 1] = pv[2 * c + 1] - __uint_as_float(hi_bits[c] & 0xffff0000u);
+        }
+        const bf16x8 p_lo = __builtin_convertvector(rest, bf16x8);
+#pragma unroll
+        for (int n = 0; n < kTiles; ++n) {
+          acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(p_hi, as_bf16x8(R.v[n]), acc[n], 0, 0, 0);
+          acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(p_lo, as_bf16x8(R.v[n]), acc[n], 0, 0, 0);
+        }
       }
     };
 
-    // software pipeline: the next pair's loads are in flight while the current one is computed
+    // software pipeline: the next pair's loads (bf16), or the next two pairs' (int8: half the
+    // bytes per pair, so twice the pairs keep as many bytes in flight) are issued before the
+    // current pair is computed
     {
       const int step = solo ? 1 : kWaves;
-      Regs ra, rb;
       int i = solo ? i0 : i0 + w;
-      if (i < i1) load_pair(i, ra);
-      while (i < i1) {
+      if constexpr (kI8) {
+        Regs ra, rb, rc;
+        if (i < i1) load_pair(i, ra);
         if (i + step < i1) load_pair(i + step, rb);
-        compute_pair(i, ra);
-        i += step;
-        if (i >= i1) break;
-        if (i + step < i1) load_pair(i + step, ra);
-        compute_pair(i, rb);
-        i += step;
+        while (i < i1) {
+          if (i + 2 * step < i1) load_pair(i + 2 * step, rc);
+          compute_pair(i, ra);
+          i += step;
+          if (i >= i1) break;
+          if (i + 2 * step < i1) load_pair(i + 2 * step, ra);
+          compute_pair(i, rb);
+          i += step;
+          if (i >= i1) break;
+          if (i + 2 * step < i1) load_pair(i + 2 * step, rb);
+          compute_pair(i, rc);
+          i += step;
+        }
+      } else {
+        Regs ra, rb;
+        if (i < i1) load_pair(i, ra);
+        while (i < i1) {
+          if (i + step < i1) load_pair(i + step, rb);
+          compute_pair(i, ra);
+          i += step;
+          if (i >= i1) break;
+          if (i + step < i1) load_pair(i + step, ra);
+          compute_pair(i, rb);
+          i += step;
+        }
       }
     }
 
@@ -378,7 +422,7 @@ decode_mfma_kernel(DecodeArgs a) {
         const float cj = kI8 ? __shfl(c_tot, h % G, 64) : 0.f;
         if (h < G) {
 #pragma unroll
-          for (int n = 0; n < kTiles; ++n) o_s[w][slot][h][16 * n + r] = acc[n][j] - 128.f * cj;
+          for (int n = 0; n < kTiles; ++n) o_s[w][slot][h][16 * n + r] = acc[n][j] - kCodeOffset * cj;
         }
       }
     };
@@ -398,7 +442,7 @@ decode_mfma_kernel(DecodeArgs a) {
           const int64_t slot = part * G + h;
 #pragma unroll
           for (int n = 0; n < kTiles; ++n) {
-            const float o = lj > 0.f ? (acc[n][j] - 128.f * cj) / lj : 0.f;
+            const float o = lj > 0.f ? (acc[n][j] - kCodeOffset * cj) / lj : 0.f;
             if (dest == 0) {
               a.out[row * D + 16 * n + r] = o;
             } else {

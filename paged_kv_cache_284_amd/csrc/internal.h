@@ -45,10 +45,12 @@ int mfma_workgroups_per_cu();
 int32_t auto_partition(int32_t B, int32_t Hq, int32_t max_seq_len);
 
 // table_index / tables may be NULL; otherwise the launch also patches the block tables.
+// lens_in / lens_out may be NULL; otherwise the launch also copies the sequence lengths.
 hipError_t launch_kv_append(const void* k_new, const void* v_new, const int64_t* slots,
                             void* k_cache, void* v_cache, int32_t B, int32_t Hkv, int32_t D,
                             int32_t NB, int32_t elem_bytes, const int32_t* table_index,
-                            int32_t* tables, int32_t max_blocks, hipStream_t stream);
+                            int32_t* tables, int32_t max_blocks, const int32_t* lens_in,
+                            int32_t* lens_out, hipStream_t stream);
 hipError_t launch_copy_blocks(void* k_cache, void* v_cache, float* k_scale, float* v_scale,
                               const int32_t* pairs, int32_t n, int32_t Hkv, int32_t D,
                               int32_t NB, int32_t elem_bytes, hipStream_t stream);

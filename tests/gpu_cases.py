@@ -109,9 +109,16 @@ class Case:
                 pkv.copy_blocks(self.k, self.v, torch.from_numpy(pairs).cuda(), self.ks, self.vs)
             slots_d = torch.from_numpy(slots).cuda()
             tidx_d = torch.from_numpy(tidx).cuda()
+            self.lens_step = None
             if self.fused:
+                # the step's host arrays straight from pinned memory, lengths copied on the way
+                # (kept referenced until the step has synchronised: the kernel reads them late)
+                self.pinned = [torch.from_numpy(a).pin_memory()
+                               for a in (slots, tidx, lens_after.astype(np.int32))]
+                self.lens_step = torch.empty(w.B, dtype=torch.int32, device="cuda")
                 pkv.append_step(to_device(k_new, w.kv_dtype), to_device(v_new, w.kv_dtype),
-                                slots_d, tidx_d, self.k, self.v, self.tables)
+                                self.pinned[0], self.pinned[1], self.k, self.v, self.tables,
+                                seq_lens=self.pinned[2], seq_lens_out=self.lens_step)
             else:
                 pkv.update_block_tables(self.tables, slots_d, tidx_d)
                 pkv.kv_append(to_device(k_new, w.kv_dtype), to_device(v_new, w.kv_dtype), slots_d,
@@ -131,6 +138,9 @@ class Case:
                                   np.ascontiguousarray(self.host["v"]).view(np.uint8))
         q = inputs.queries(w, s)
         lens_d = torch.from_numpy(lens_p).cuda()
+        if w.append and self.lens_step is not None:
+            assert np.array_equal(self.lens_step.cpu().numpy(), lens_p)
+            lens_d = self.lens_step
         max_len = int(lens_p.max())
         out = pkv.decode(to_device(q, w.q_dtype), self.k, self.v, self.tables, lens_d, max_len,
                          w.scale, self.ks, self.vs, partition_tokens=partition_tokens)

@@ -103,10 +103,12 @@ def test_append_and_copy_reject_on_host():
     assert L.pa_update_block_tables(None, 8, FAKE, FAKE, 2, 16, None) == pkv.PA_ERR_INVALID
     assert L.pa_update_block_tables(FAKE, 8, FAKE, FAKE, 2, 32, None) == pkv.PA_ERR_UNSUPPORTED
     assert L.pa_update_block_tables(None, 8, None, None, 0, 16, None) == pkv.PA_OK
-    assert L.pa_append_step(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 8, 4, 8, 128, 16, 10,
-                            pkv.PA_BF16, None) == pkv.PA_ERR_INVALID   # table_index, no table
-    assert L.pa_append_step(FAKE, FAKE, FAKE, None, FAKE, FAKE, None, 8, 4, 8, 128, 16, 10,
-                            pkv.PA_I8, None) == pkv.PA_ERR_UNSUPPORTED
+    assert L.pa_append_step(FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, None, 8, 4, 8, 128,
+                            16, 10, pkv.PA_BF16, None) == pkv.PA_ERR_INVALID   # index, no table
+    assert L.pa_append_step(FAKE, FAKE, FAKE, None, FAKE, None, FAKE, FAKE, None, 8, 4, 8, 128,
+                            16, 10, pkv.PA_BF16, None) == pkv.PA_ERR_INVALID   # lens in, no out
+    assert L.pa_append_step(FAKE, FAKE, FAKE, None, None, None, FAKE, FAKE, None, 8, 4, 8, 128,
+                            16, 10, pkv.PA_I8, None) == pkv.PA_ERR_UNSUPPORTED
 
 
 def test_workspace_size():
