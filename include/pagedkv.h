@@ -76,7 +76,9 @@ int pa_abi_version(void);
  * unique: a FIFO free list, initialised from `free_order`; allocations pop the head; a block
  * whose count reaches zero is pushed to the tail, in the logical order of the table it leaves;
  * batch calls serve sequences in the order given; sequence ids count up from 0 and are never
- * reused.  Calls that run out of blocks return PA_ERR_OOM and change nothing.
+ * reused.  When the free list is empty an allocation evicts the least recently used cached
+ * block (prefix caching, below).  Calls that run out of blocks return PA_ERR_OOM and change
+ * nothing.
  */
 typedef struct pa_allocator pa_allocator;
 
@@ -122,8 +124,41 @@ int pa_step(pa_allocator* a, const int32_t* seqs, int32_t B, int64_t* slots, int
             int32_t* table_index, int32_t* cow_pairs, int32_t* n_cow);
 
 /* Drop a sequence: each of its blocks loses a reference; blocks left with none go to the tail
- * of the free list in table order ([Serving] "The Life of a Request"). */
+ * of the free list in table order ([Serving] "The Life of a Request"), except published blocks,
+ * which become evictable (see prefix caching below). */
 int pa_seq_free(pa_allocator* a, int32_t seq);
+
+/* ---- automatic prefix caching ([Serving] "Prefix Caching and Chunked Prefill" / "Automatic
+ * prefix caching", "Putting It Together: The Life of a Request") ----
+ * A sequence created by pa_seq_create_prefix knows its token ids.  Each of its blocks that is
+ * full and whose ids are all known is published under a chained hash: FNV-1a (64-bit) over the
+ * little-endian bytes of the parent hash followed by the block's bs token ids (int32), the first
+ * block's parent being FNV-1a of the 8 salt bytes.  The hash covers the whole prefix, so a block
+ * matches only when every token before it matches too; a different salt never matches.  A
+ * published block whose last reference is released is not freed: it joins an LRU list of
+ * evictable blocks (the sequence's blocks last-first, so prefixes outlive their extensions), can
+ * still be matched, and is evicted -- oldest first, its hash dropped -- only when an allocation
+ * finds the free list empty.  When two blocks hold the same content, the first published keeps
+ * the hash.  Matches compare the stored ids too, so a hash collision never reuses a wrong block.
+ * Sequences made by pa_seq_create never publish; with only those, nothing above changes. */
+
+/* New sequence for a prompt of n token ids (copied), reusing the longest run of cached blocks
+ * that match its leading full blocks among the first n - 1 tokens (at least one prompt token is
+ * left to compute: generation needs its query).  *n_cached receives the number of tokens whose
+ * K/V is already in the pool (a multiple of bs; the sequence's length); the caller reserves
+ * slots for tokens n_cached..n-1 (pa_seq_reserve) and writes them.  salt: 0 or a per-tenant
+ * value mixed into the first block's hash. */
+int pa_seq_create_prefix(pa_allocator* a, const int32_t* tokens, int32_t n, uint64_t salt,
+                         int32_t* seq, int32_t* n_cached);
+/* Append n token ids to what a pa_seq_create_prefix sequence knows (generated tokens, before
+ * or after their slots are reserved); newly complete blocks are published.  PA_ERR_INVALID for
+ * a sequence made by pa_seq_create. */
+int pa_seq_add_tokens(pa_allocator* a, int32_t seq, const int32_t* tokens, int32_t n);
+/* Number of evictable cached blocks, and the list in eviction order (up to cap; *n = total). */
+int pa_num_evictable(const pa_allocator* a, int32_t* n);
+int pa_evictable_list(const pa_allocator* a, int32_t* out, int32_t cap, int32_t* n);
+/* Whether a block is published, and its hash (0 when not). */
+int pa_block_hash(const pa_allocator* a, int32_t block, uint64_t* hash, int32_t* cached);
 
 int pa_seq_len(const pa_allocator* a, int32_t seq, int32_t* len);
 /* Copies up to `cap` table entries to out; *n receives the table length. */

@@ -10,7 +10,8 @@ product.  Both sides (oracle and HIP library) consume the exact bytes produced h
 Seeds follow ``numpy.random.default_rng([284, config_id, stream, ...])`` with the streams
 
     0 lengths, 1 free-list permutation, 2 queries, 3 K pool, 4 V pool,
-    5 new-token K/V of a step, 6 peak mask (long-context workload).
+    5 new-token K/V of a step, 6 peak mask (long-context workload),
+    7 prompt token ids, 8 K/V of the tokens a request writes (prompt / prefill).
 
 Physical layouts produced here (the library and the oracle document the same layouts):
 
@@ -320,6 +321,19 @@ def pool(w: Workload) -> dict:
         vq, vs = quantize_int8_pool(v)
         return {"k": kq, "v": vq, "k_scale": ks, "v_scale": vs}
     return {"k": _cast(k, w.kv_dtype), "v": _cast(v, w.kv_dtype)}
+
+
+def prompt_tokens(cid: int, request: int, n: int, vocab: int = 32000) -> np.ndarray:
+    """Token ids of a synthetic prompt, int32 [n] (stream 7)."""
+    return _rng(cid, 7, request).integers(0, vocab, n, dtype=np.int64).astype(np.int32)
+
+
+def token_kv(cid: int, request: int, n: int, Hkv: int, D: int, dtype: str):
+    """K and V [n][Hkv][D] of n tokens written by one request, in the cache dtype (stream 8)."""
+    rng = _rng(cid, 8, request)
+    k = _normal(rng, (n, Hkv, D))
+    v = _normal(rng, (n, Hkv, D))
+    return _cast(k, dtype), _cast(v, dtype)
 
 
 def new_tokens(w: Workload, step: int = 0) -> Tuple[np.ndarray, np.ndarray]:

@@ -51,6 +51,11 @@ _SIGNATURES = {
     "pa_block_refcount": (C.c_int, [_vp, _i32, _pi32]),
     "pa_num_free": (C.c_int, [_vp, _pi32]),
     "pa_free_list": (C.c_int, [_vp, _pi32, _i32, _pi32]),
+    "pa_seq_create_prefix": (C.c_int, [_vp, _pi32, _i32, C.c_uint64, _pi32, _pi32]),
+    "pa_seq_add_tokens": (C.c_int, [_vp, _i32, _pi32, _i32]),
+    "pa_num_evictable": (C.c_int, [_vp, _pi32]),
+    "pa_evictable_list": (C.c_int, [_vp, _pi32, _i32, _pi32]),
+    "pa_block_hash": (C.c_int, [_vp, _i32, C.POINTER(C.c_uint64), _pi32]),
     "pa_kv_append": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
     "pa_copy_blocks": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                                  _vp]),
@@ -228,6 +233,41 @@ class Allocator:
         out = np.zeros(max(n.value, 1), np.int32)
         _check(lib().pa_free_list(self._h, _p32(out), n.value, C.byref(n)), "pa_free_list")
         return out[:n.value].tolist()
+
+    # -- automatic prefix caching --------------------------------------------------------------
+    def create_prefix(self, tokens, salt: int = 0) -> Tuple[int, int]:
+        """A sequence for a prompt of token ids, reusing matching cached blocks: (id, tokens
+        already cached)."""
+        t = _i32_array(tokens)
+        s, n = _i32(), _i32()
+        _check(lib().pa_seq_create_prefix(self._h, _p32(t) if t.size else None, t.size,
+                                          C.c_uint64(salt & (2**64 - 1)), C.byref(s),
+                                          C.byref(n)), "pa_seq_create_prefix")
+        return s.value, n.value
+
+    def add_tokens(self, seq: int, tokens) -> None:
+        t = _i32_array(tokens)
+        _check(lib().pa_seq_add_tokens(self._h, seq, _p32(t) if t.size else None, t.size),
+               "pa_seq_add_tokens")
+
+    def num_evictable(self) -> int:
+        n = _i32()
+        _check(lib().pa_num_evictable(self._h, C.byref(n)), "pa_num_evictable")
+        return n.value
+
+    def evictable_list(self) -> List[int]:
+        n = _i32()
+        _check(lib().pa_evictable_list(self._h, None, 0, C.byref(n)), "pa_evictable_list")
+        out = np.zeros(max(n.value, 1), np.int32)
+        _check(lib().pa_evictable_list(self._h, _p32(out), n.value, C.byref(n)),
+               "pa_evictable_list")
+        return out[:n.value].tolist()
+
+    def block_hash(self, block: int) -> Optional[int]:
+        """The block's published hash, or None when it is not cached."""
+        h, c = C.c_uint64(), _i32()
+        _check(lib().pa_block_hash(self._h, block, C.byref(h), C.byref(c)), "pa_block_hash")
+        return h.value if c.value else None
 
 
 def run_script(alloc: Allocator, ops) -> dict:
