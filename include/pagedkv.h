@@ -244,6 +244,25 @@ int pa_decode(float* out, const void* q, int32_t q_dtype, const void* k_cache,
               int32_t NB, float scale, int32_t partition_tokens, void* workspace,
               size_t workspace_bytes, void* stream);
 
+/* Chunked-prefill attention over the paged cache ([Serving] "Two Phases: Prefill and Decode":
+ * prefill runs a prompt's tokens in parallel, each attending to all earlier ones; "Prefix
+ * Caching and Chunked Prefill" / "Chunked prefill": a long prefill runs as a series of chunks).
+ * Sequence b's chunk is query rows cu_q[b] .. cu_q[b+1]-1 of q, the last n_b = cu_q[b+1]-cu_q[b]
+ * of its seq_lens[b] tokens, whose K/V are already in the cache (pa_kv_append with one batch
+ * entry per token).  Query i of the chunk sits at position p = seq_lens[b] - n_b + i:
+ *     out[row][h] = sum_{t <= p} softmax_t(scale * <q[row][h], K_t>) V_t   (KV head h/(Hq/Hkv)),
+ * and a row with p < 0 gets zeros.
+ *   q: device [T][Hq][D] PA_BF16; k_cache / v_cache PA_BF16 (other dtypes: PA_ERR_UNSUPPORTED);
+ *   out: device [T][Hq][D] fp32; cu_q: device [B + 1] int32, non-decreasing, cu_q[0] = 0,
+ *   cu_q[B] = T; seq_lens: device [B] int32; max_seq_len bounds every seq_lens[b];
+ *   Hq/Hkv in {1, 2, 4, 8, 16}, D in {64, 128}, bs == 16.  Needs no workspace.  Compute-bound:
+ *   each K/V tile is shared by 16 queries of every head of its group. */
+int pa_prefill(float* out, const void* q, int32_t q_dtype, const void* k_cache,
+               const void* v_cache, int32_t kv_dtype, const int32_t* block_tables,
+               int32_t max_blocks, const int32_t* seq_lens, const int32_t* cu_q,
+               int32_t max_seq_len, int32_t B, int32_t T, int32_t Hq, int32_t Hkv, int32_t D,
+               int32_t bs, int32_t NB, float scale, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -11,7 +11,8 @@ Seeds follow ``numpy.random.default_rng([284, config_id, stream, ...])`` with th
 
     0 lengths, 1 free-list permutation, 2 queries, 3 K pool, 4 V pool,
     5 new-token K/V of a step, 6 peak mask (long-context workload),
-    7 prompt token ids, 8 K/V of the tokens a request writes (prompt / prefill).
+    7 prompt token ids, 8 K/V of the tokens a request writes (prompt / prefill),
+    9 chunk sizes of a chunked prefill, 10 the chunk's queries.
 
 Physical layouts produced here (the library and the oracle document the same layouts):
 
@@ -334,6 +335,18 @@ def token_kv(cid: int, request: int, n: int, Hkv: int, D: int, dtype: str):
     k = _normal(rng, (n, Hkv, D))
     v = _normal(rng, (n, Hkv, D))
     return _cast(k, dtype), _cast(v, dtype)
+
+
+def chunk_sizes(w: Workload, lo: int, hi: int) -> np.ndarray:
+    """Chunked prefill: the number of new query tokens of each sequence, U{lo..hi} capped at its
+    context length (stream 9)."""
+    n = _rng(w.cid, 9).integers(lo, hi, size=w.B, endpoint=True).astype(np.int64)
+    return np.minimum(n, w.lengths)
+
+
+def chunk_queries(w: Workload, T: int) -> np.ndarray:
+    """q [T][Hq][D] of a prefill chunk (stream 10): fp32 array or bf16 bits."""
+    return _cast(_normal(_rng(w.cid, 10), (T, w.Hq, w.D)), w.q_dtype)
 
 
 def new_tokens(w: Workload, step: int = 0) -> Tuple[np.ndarray, np.ndarray]:

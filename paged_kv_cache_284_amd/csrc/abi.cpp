@@ -239,4 +239,48 @@ int pa_decode(float* out, const void* q, int32_t q_dtype, const void* k_cache,
   return status_of(pa::launch_splitk_reduce(a, s));
 }
 
+int pa_prefill(float* out, const void* q, int32_t q_dtype, const void* k_cache,
+               const void* v_cache, int32_t kv_dtype, const int32_t* block_tables,
+               int32_t max_blocks, const int32_t* seq_lens, const int32_t* cu_q,
+               int32_t max_seq_len, int32_t B, int32_t T, int32_t Hq, int32_t Hkv, int32_t D,
+               int32_t bs, int32_t NB, float scale, void* stream) {
+  if (B < 0 || T < 0 || Hq < 1 || Hkv < 1 || NB < 1 || max_blocks < 0 || max_seq_len < 0)
+    return PA_ERR_INVALID;
+  if (Hq % Hkv != 0 || (D != 64 && D != 128)) return PA_ERR_INVALID;
+  const int32_t G = Hq / Hkv;
+  if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16) return PA_ERR_UNSUPPORTED;
+  if (bs != pa::kBlockSize) return PA_ERR_UNSUPPORTED;
+  if (q_dtype != PA_BF16 || kv_dtype != PA_BF16) {
+    const bool known = (q_dtype == PA_F32 || q_dtype == PA_BF16) && elem_bytes(kv_dtype) != 0;
+    return known ? PA_ERR_UNSUPPORTED : PA_ERR_INVALID;
+  }
+  if (static_cast<int64_t>(max_seq_len) > static_cast<int64_t>(max_blocks) * bs)
+    return PA_ERR_INVALID;
+  if (!(scale == scale)) return PA_ERR_INVALID;
+  if (B == 0 || T == 0) return PA_OK;
+  if (!out || !q || !k_cache || !v_cache || !seq_lens || !cu_q || (max_blocks > 0 && !block_tables))
+    return PA_ERR_INVALID;
+  pa::PrefillArgs a{};
+  a.out = out;
+  a.q = q;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.tables = block_tables;
+  a.seq_lens = seq_lens;
+  a.cu_q = cu_q;
+  a.max_blocks = max_blocks;
+  a.max_seq_len = max_seq_len;
+  a.B = B;
+  a.T = T;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.D = D;
+  a.NB = NB;
+  const int64_t tiles = (static_cast<int64_t>(T) + 15) / 16 + B;  // sum of ceil(n_b / 16)
+  if (tiles > INT32_MAX) return PA_ERR_INVALID;
+  a.max_tiles = static_cast<int32_t>(tiles);
+  a.scale_log2 = scale * kLog2e;
+  return status_of(pa::launch_prefill_mfma(a, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

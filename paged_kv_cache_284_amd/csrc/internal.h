@@ -32,6 +32,21 @@ struct DecodeArgs {
   float scale_log2;           // softmax scale * log2(e)
 };
 
+// Everything one chunked-prefill launch needs.  Pointers are device pointers.
+struct PrefillArgs {
+  float* out;                 // [T][Hq][D]
+  const void* q;              // [T][Hq][D] bf16
+  const void* k;              // [NB][Hkv][bs][D] bf16
+  const void* v;              // [NB][Hkv][D][bs] bf16
+  const int32_t* tables;      // [B][max_blocks]
+  const int32_t* seq_lens;    // [B] context length, the chunk included
+  const int32_t* cu_q;        // [B + 1] first query row of each sequence's chunk
+  int32_t max_blocks, max_seq_len;
+  int32_t B, T, Hq, Hkv, D, NB;
+  int32_t max_tiles;          // grid bound on the number of 16-query tiles
+  float scale_log2;
+};
+
 // Upper bound on balanced-schedule workgroups; sizes the workspace.
 constexpr int kMaxBalancedWorkgroups = 1024;
 // Largest batch / group size the balanced schedule takes (its prefix sums and per-wave states
@@ -64,5 +79,7 @@ hipError_t launch_decode_generic(const DecodeArgs& a, int q_dtype, int kv_dtype,
 // 8 or 16.
 hipError_t launch_decode_mfma(const DecodeArgs& a, bool int8_cache, hipStream_t stream);
 hipError_t launch_splitk_reduce(const DecodeArgs& a, hipStream_t stream);
+// bf16 query and cache; D 64/128; group size 1, 2, 4, 8 or 16.
+hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t stream);
 
 }  // namespace pa

@@ -1,0 +1,287 @@
+// Chunked-prefill attention over the paged cache on the gfx950 matrix cores.
+//
+// What it computes ("How LLM Inference Serving Works", "Two Phases: Prefill and Decode": prefill
+// runs the prompt's tokens in parallel, each depending on all earlier ones; "Prefix Caching and
+// Chunked Prefill" / "Chunked prefill": a long prefill runs as a series of chunks).  Sequence b
+// brings a chunk of n_b query tokens, the last n_b of its L_b cached tokens; query i sits at
+// position p = L_b - n_b + i and attends to tokens 0..p of the sequence through its block table.
+//
+// Unlike decode this is a dense contraction with reuse: 16 queries share every K and V tile, so
+// the path is bound by the matrix cores, not by HBM.  The layout mirrors the decode kernel with
+// the 16 columns of each MFMA tile holding 16 *queries* of one head instead of the replicated
+// heads of a group:
+//   scores  S^T = K . Q^T: two 16(token) x 16(query) tiles per block pair (32 tokens); with the
+//           decode kernel's token order, lane l ends up with the 8 scores of tokens
+//           8*(l/16)..+7 for query l%16 -- exactly its P operand for P . V;
+//   P . V   O += P . V as 16(query) x 16(dim) tiles, V tiles dim-major in HBM;
+// online softmax per query (exp2 domain), the causal limit p applied per lane.
+// A workgroup holds the waves of (up to four of) one KV head's query heads for one 16-query
+// tile, so they read the same K/V tiles back to back and share them in the caches.
+#include <cmath>
+
+#include "internal.h"
+#include "pagedkv.h"
+
+namespace pa {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kTile = 16;              // queries per wave
+constexpr int kPairTok = 2 * kBlockSize;
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
+__device__ __forceinline__ u32x4 ld16(const uint16_t* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+
+template <int D>
+struct KVRegs {
+  u32x4 k1[D / 32];
+  u32x4 k2[D / 32];
+  u32x4 v[D / 16];
+  int32_t blk_a, blk_b;
+};
+
+// Sequence and tile of global tile index `tile`: tiles are numbered sequence by sequence,
+// ceil(n_b / 16) per sequence.  Every lane of the wave returns the same answer; b = -1 when the
+// index is past the last tile.
+__device__ void locate_tile(const int32_t* __restrict__ cu_q, int B, int tile, int* b_out,
+                            int* j_out) {
+  const int lane = threadIdx.x % 64;
+  int base = 0;  // tiles before the current chunk of 64 sequences
+  for (int b0 = 0; b0 < B; b0 += 64) {
+    const int b = b0 + lane;
+    const int n = b < B ? max(cu_q[b + 1] - cu_q[b], 0) : 0;
+    const int t = (n + kTile - 1) / kTile;
+    int incl = t;  // inclusive prefix over the chunk
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += y;
+    }
+    const int excl = incl - t;
+    // the lane whose range [base + excl, base + incl) holds `tile`
+    const bool mine = b < B && tile >= base + excl && tile < base + incl;
+    const unsigned long long hit = __ballot(mine);
+    if (hit) {
+      const int src = __ffsll(static_cast<long long>(hit)) - 1;
+      *b_out = b0 + src;
+      *j_out = tile - base - __shfl(excl, src, 64);
+      return;
+    }
+    base += __shfl(incl, 63, 64);
+  }
+  *b_out = -1;
+  *j_out = 0;
+}
+
+// Waves per workgroup: the group's query heads, at most 4 (larger groups span blockIdx.z).
+template <int G>
+constexpr int kHeadsPerWG = G < 4 ? G : 4;
+
+template <int G, int D>
+__global__ void __launch_bounds__(64 * kHeadsPerWG<G>) __attribute__((amdgpu_waves_per_eu(2, 2)))
+prefill_mfma_kernel(PrefillArgs a) {
+  constexpr int kSteps = D / 32;
+  constexpr int kTiles = D / 16;
+  const int lane = threadIdx.x % 64;
+  const int w = threadIdx.x / 64;
+  const int r = lane % 16, qg = lane / 16;
+  const int g = blockIdx.y;
+  const int h = g * G + blockIdx.z * kHeadsPerWG<G> + w;  // this wave's query head
+
+  int b, j;
+  locate_tile(a.cu_q, a.B, blockIdx.x, &b, &j);
+  if (b < 0) return;
+  const int row0 = a.cu_q[b];
+  const int n = a.cu_q[b + 1] - row0;
+  const int L = min(max(a.seq_lens[b], 0), a.max_seq_len);
+  const int qi0 = j * kTile;
+  const int q_last = min(qi0 + kTile, n) - 1;    // last query of the tile
+  const int p_max = L - n + q_last;               // its position: the tile's causal reach
+  const int kv_end = min(L, p_max + 1);
+  // this lane's query (column r) and its causal limit
+  const int my_q = qi0 + r;
+  const int my_p = L - n + my_q;
+  const int32_t* __restrict__ table = a.tables + static_cast<int64_t>(b) * a.max_blocks;
+  const uint16_t* __restrict__ kc = static_cast<const uint16_t*>(a.k);
+  const uint16_t* __restrict__ vc = static_cast<const uint16_t*>(a.v);
+  const int NB = a.NB, Hkv = a.Hkv;
+
+  // Q^T operand: query column r, dims 32 s + 8 qg .. +8 (row clamped into the chunk)
+  u32x4 qv[kSteps];
+  {
+    const int qrow = min(max(row0 + min(my_q, n - 1), 0), a.T - 1);
+    const uint16_t* q = static_cast<const uint16_t*>(a.q) +
+                        (static_cast<int64_t>(qrow) * a.Hq + h) * D;
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) qv[s] = ld16(q + 32 * s + 8 * qg);
+  }
+
+  const int tok1 = (r / 8) * 16 + ((r / 4) % 2) * 8 + (r % 4);
+  const int tok2 = tok1 + 4;
+  const int vsel = qg / 2, vtok = 8 * (qg % 2);
+
+  auto load_pair = [&](int i, KVRegs<D>& R) {
+    const int tok0 = i * kPairTok;
+    const int jb = tok0 / kBlockSize;
+    int32_t ba = table[jb];
+    int32_t bb = (tok0 + kBlockSize < kv_end) ? table[jb + 1] : -1;
+    ba = (ba >= 0 && ba < NB) ? ba : -1;
+    bb = (bb >= 0 && bb < NB) ? bb : -1;
+    R.blk_a = ba;
+    R.blk_b = bb;
+    const int64_t ta = (static_cast<int64_t>(ba < 0 ? 0 : ba) * Hkv + g) * (kBlockSize * D);
+    const int64_t tb = (static_cast<int64_t>(bb < 0 ? 0 : bb) * Hkv + g) * (kBlockSize * D);
+    const uint16_t* k1 = kc + (tok1 < 16 ? ta : tb) + (tok1 % 16) * D + 8 * qg;
+    const uint16_t* k2 = kc + (tok2 < 16 ? ta : tb) + (tok2 % 16) * D + 8 * qg;
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) {
+      R.k1[s] = ld16(k1 + 32 * s);
+      R.k2[s] = ld16(k2 + 32 * s);
+    }
+    const uint16_t* v = vc + (vsel ? tb : ta) + r * kBlockSize + vtok;
+#pragma unroll
+    for (int t = 0; t < kTiles; ++t) R.v[t] = ld16(v + 16 * t * kBlockSize);
+  };
+
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x4 acc[kTiles];
+#pragma unroll
+  for (int t = 0; t < kTiles; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto compute_pair = [&](int i, KVRegs<D>& R) {
+    const int tok0 = i * kPairTok;
+    f32x4 s1 = {0.f, 0.f, 0.f, 0.f}, s2 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) {
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(R.k1[s]), as_bf16x8(qv[s]), s1, 0, 0, 0);
+      s2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(R.k2[s]), as_bf16x8(qv[s]), s2, 0, 0, 0);
+    }
+    const int t_first = tok0 + 8 * qg;
+    const int32_t my_blk = vsel ? R.blk_b : R.blk_a;
+    // causal and context limits: token t is kept for this lane's query when t <= my_p, t < L
+    const int limit = min(my_p, L - 1);
+    float sc[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      sc[e] = s1[e] * a.scale_log2;
+      sc[4 + e] = s2[e] * a.scale_log2;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (t_first + e > limit || my_blk < 0) sc[e] = -INFINITY;
+    if (tok0 + kPairTok > L || R.blk_a < 0 || R.blk_b < 0) {
+      // tokens past the context (or of a missing block) must not reach P.V even with p = 0
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const bool k0 = my_blk >= 0 && t_first + 2 * c < L;
+        const bool k1 = my_blk >= 0 && t_first + 2 * c + 1 < L;
+        const uint32_t keep = (k0 ? 0x0000ffffu : 0u) | (k1 ? 0xffff0000u : 0u);
+#pragma unroll
+        for (int t = 0; t < kTiles; ++t) R.v[t][c] &= keep;
+      }
+    }
+    float bmax = sc[0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) bmax = fmaxf(bmax, sc[e]);
+    bmax = fmaxf(bmax, __shfl_xor(bmax, 16, 64));
+    bmax = fmaxf(bmax, __shfl_xor(bmax, 32, 64));
+    const float m_new = fmaxf(m_run, bmax);
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    m_run = m_new;
+    f32x8 pv;
+    float psum = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      pv[e] = __builtin_amdgcn_exp2f(sc[e] - m_use);
+      psum += pv[e];
+    }
+    l_run = l_run * alpha + psum;
+    // accumulator rows 4 qg + jj hold query 4 qg + jj, whose alpha lives in lane 4 qg + jj
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const float aj = __shfl(alpha, 4 * qg + jj, 64);
+#pragma unroll
+      for (int t = 0; t < kTiles; ++t) acc[t][jj] *= aj;
+    }
+    const bf16x8 p_hi = __builtin_convertvector(pv, bf16x8);
+    const u32x4 hb = __builtin_bit_cast(u32x4, p_hi);
+    f32x8 rest;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      rest[2 * c] = pv[2 * c] - __uint_as_float(hb[c] << 16);
+      rest[2 * c + 1] = pv[2 * c + 1] - __uint_as_float(hb[c] & 0xffff0000u);
+    }
+    const bf16x8 p_lo = __builtin_convertvector(rest, bf16x8);
+#pragma unroll
+    for (int t = 0; t < kTiles; ++t) {
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(p_hi, as_bf16x8(R.v[t]), acc[t], 0, 0, 0);
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(p_lo, as_bf16x8(R.v[t]), acc[t], 0, 0, 0);
+    }
+  };
+
+  const int n_pairs = kv_end > 0 ? (kv_end + kPairTok - 1) / kPairTok : 0;
+  {
+    KVRegs<D> ra, rb;
+    int i = 0;
+    if (i < n_pairs) load_pair(i, ra);
+    while (i < n_pairs) {
+      if (i + 1 < n_pairs) load_pair(i + 1, rb);
+      compute_pair(i, ra);
+      if (++i >= n_pairs) break;
+      if (i + 1 < n_pairs) load_pair(i + 1, ra);
+      compute_pair(i, rb);
+      ++i;
+    }
+  }
+
+  // l summed over the four lane groups belongs to query r; rows 4 qg + jj take it from there
+  float l_tot = l_run + __shfl_xor(l_run, 16, 64);
+  l_tot += __shfl_xor(l_tot, 32, 64);
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) {
+    const int qq = qi0 + 4 * qg + jj;
+    const float lq = __shfl(l_tot, 4 * qg + jj, 64);
+    if (qq < n && row0 + qq < a.T && row0 + qq >= 0) {
+      float* o = a.out + (static_cast<int64_t>(row0 + qq) * a.Hq + h) * D;
+#pragma unroll
+      for (int t = 0; t < kTiles; ++t) o[16 * t + r] = lq > 0.f ? acc[t][jj] / lq : 0.f;
+    }
+  }
+}
+
+template <int G, int D>
+hipError_t launch_gd(const PrefillArgs& a, hipStream_t stream) {
+  const dim3 grid(static_cast<unsigned>(a.max_tiles), static_cast<unsigned>(a.Hkv),
+                  static_cast<unsigned>(G / kHeadsPerWG<G>));
+  hipLaunchKernelGGL((prefill_mfma_kernel<G, D>), grid, dim3(64 * kHeadsPerWG<G>), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <int G>
+hipError_t launch_g(const PrefillArgs& a, hipStream_t stream) {
+  if (a.D == 128) return launch_gd<G, 128>(a, stream);
+  if (a.D == 64) return launch_gd<G, 64>(a, stream);
+  return hipErrorNotSupported;
+}
+
+}  // namespace
+
+hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t stream) {
+  switch (a.Hq / a.Hkv) {
+    case 1: return launch_g<1>(a, stream);
+    case 2: return launch_g<2>(a, stream);
+    case 4: return launch_g<4>(a, stream);
+    case 8: return launch_g<8>(a, stream);
+    case 16: return launch_g<16>(a, stream);
+    default: return hipErrorNotSupported;
+  }
+}
+
+}  // namespace pa

@@ -1,0 +1,67 @@
+"""Chunked-prefill parity: pa_prefill (HIP, through the C-ABI) against the oracle's
+prefill_paged on the same pools and tables, within the bf16 tolerance.  Chunks cover fresh
+prompts (chunk = whole context), chunks after a cached prefix, single-token chunks, chunk sizes
+off the 16-query tile, empty sequences, and every group size; the pools are poisoned outside the
+live tokens so that an unmasked read shows up."""
+import numpy as np
+import pytest
+import torch
+
+import inputs
+import paged_kv_cache_284_amd as pkv
+from oracle.prefill import prefill_paged
+from tests.gpu_cases import TOL, Case, say, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def _workload(G, D, lens, cid):
+    w = inputs.llama8b_decode(B=len(lens), lo=1, hi=2, cid=cid, name="prefill")
+    w.lengths = np.array(lens, np.int64)
+    w.Hkv, w.Hq, w.D = 2, 2 * G, D
+    w.NB = int(sum((L + 15) // 16 for L in lens)) + 8
+    w.append = False
+    return w
+
+
+def _run(w, chunks, rows=None):
+    case = Case(w)
+    tables, lens = case.py.export(case.seqs, case.MB)
+    tables, lens = np.array(tables, np.int32), np.array(lens, np.int32)
+    cu = np.concatenate([[0], np.cumsum(chunks)]).astype(np.int32)
+    T = int(cu[-1])
+    q = inputs.chunk_queries(w, T)
+    say(f"prefill G={w.G} D={w.D} lens={list(lens)[:8]} chunks={list(chunks)[:8]} T={T}")
+    out = pkv.prefill(to_device(q, "bf16"), case.k, case.v, case.tables,
+                      torch.from_numpy(lens).cuda(), torch.from_numpy(cu).cuda(),
+                      int(lens.max()), w.scale).cpu().numpy()
+    ref = prefill_paged(q, "bf16", case.host["k"], case.host["v"], "bf16", tables, lens, cu,
+                        w.bs, w.scale, rows=rows)
+    if rows is None:
+        err = float(np.max(np.abs(out.astype(np.float64) - ref)))
+        assert np.all(np.isfinite(out))
+    else:
+        err = max(float(np.max(np.abs(out[r, h].astype(np.float64) - ref[r, h])))
+                  for r, h in rows)
+    say(f"max-abs error {err:.2e}")
+    assert err <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("G,D", [(4, 128), (1, 64), (2, 128), (8, 64), (16, 128)])
+def test_mixed_chunks(G, D):
+    lens = [37, 100, 16, 1, 0, 257, 64, 33]
+    chunks = [37, 20, 16, 1, 0, 100, 1, 17]     # whole, after a prefix, exact tile, single, empty
+    _run(_workload(G, D, lens, cid=60 + G + D), chunks)
+
+
+def test_llama_shaped_chunk_sampled():
+    """Llama-3.1-8B heads: 4 sequences of 1.5-3K cached tokens taking 512-token chunks; the
+    oracle checks sampled (row, head) pairs."""
+    w = inputs.llama8b_decode(B=4, lo=1536, hi=3072, cid=71, name="prefill_llama")
+    w.append = False
+    chunks = inputs.chunk_sizes(w, 512, 512)
+    rng = np.random.default_rng([284, 71, 99])
+    T = int(chunks.sum())
+    rows = sorted({(int(r), int(h)) for r, h in zip(rng.integers(0, T, 40), rng.integers(0, 32, 40))})
+    rows += [(T - 1, 0), (0, 31)]
+    _run(w, chunks, rows=rows)
