@@ -3,9 +3,9 @@
 
 One step is one pass of the whole hot path over the batch:
   host allocator step (slot of each new token, lengths, table changes, copy-on-write pairs)
-  written straight into pinned memory -> one H2D copy of those arrays
-  -> copy_blocks (only when a copy-on-write arose) -> fused append + block-table patch
-  -> decode (+ merge of split segments).
+  written straight into pinned memory, where the kernels read them
+  -> copy_blocks (only when a copy-on-write arose) -> fused append + block-table patch + length
+  copy -> decode (+ merge of split segments).
 Inputs (pools, queries, new tokens) are resident in HBM before the timed region starts.
 
 Prints one JSON line: whole-job tokens/s (B decode tokens per step), the decode kernel's achieved
@@ -13,6 +13,10 @@ HBM GB/s against the MI355X peak (algorithmic bytes / mean launch time from HIP 
 launch stream), and the CPU oracle timed on the host cores.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload llama8b_decode]
+
+--workload prefill_llama8b measures the chunked-prefill path instead: one step appends a
+512-token chunk per sequence (one pa_kv_append entry per token) and runs pa_prefill over it;
+the roofline is then the matrix cores' bf16 peak.
 """
 from __future__ import annotations
 
@@ -30,6 +34,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0   # dense MFMA bf16
 METRIC = "paged decode attn: tokens/s + achieved HBM GB/s (% of MI355X peak)"
 KV_BYTES = {"f32": 4, "bf16": 2, "i8": 1}
 
@@ -232,6 +237,180 @@ class StepRunner:
                 for s, lens in self.timed]
 
 
+def prefill_flops(w, lens, chunks) -> int:
+    """Algorithmic flops of a chunked prefill: for every query (position p) and query head,
+    2 D per key for the scores and 2 D per key for P.V over keys 0..p."""
+    total_keys = 0
+    for L, n in zip(lens, chunks):
+        L, n = int(L), int(n)
+        first = L - n + 1                      # keys seen by the chunk's first query
+        total_keys += n * first + n * (n - 1) // 2
+    return 4 * w.D * w.Hq * total_keys
+
+
+class PrefillRunner:
+    """Device state of a chunked-prefill workload: the cache holds each sequence's context, the
+    step rewrites the chunk's K/V (one pa_kv_append entry per token) and runs pa_prefill."""
+
+    def __init__(self, w, chunks):
+        import torch
+        import inputs
+        import paged_kv_cache_284_amd as pkv
+        self.torch, self.pkv, self.w = torch, pkv, w
+        alloc = pkv.Allocator(w.NB, w.bs, inputs.free_order(w))
+        ids = pkv.run_script(alloc, inputs.setup_script(w))
+        seqs = [ids[b] for b in range(w.B)]
+        self.MB = (int(w.lengths.max()) + w.bs - 1) // w.bs + 1
+        tables, lens = alloc.export(seqs, self.MB)
+        self.lens_h = lens.astype(np.int32)
+        self.chunks = np.asarray(chunks, np.int64)
+        cu = np.concatenate([[0], np.cumsum(self.chunks)]).astype(np.int32)
+        self.T = int(cu[-1])
+        # slots of the chunk tokens: the last n_b positions of each sequence
+        slots = []
+        ks, vs = [], []
+        for b in range(w.B):
+            L, n = int(lens[b]), int(self.chunks[b])
+            for p in range(L - n, L):
+                slots.append(int(tables[b][p // w.bs]) * w.bs + p % w.bs)
+            kn, vn = inputs.token_kv(w.cid, b, n, w.Hkv, w.D, w.kv_dtype)
+            ks.append(kn)
+            vs.append(vn)
+        pool = inputs.pool(w)
+
+        def up(a):
+            a = np.ascontiguousarray(a)
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        self.k, self.v = up(pool["k"]), up(pool["v"])
+        del pool
+        self.k_new, self.v_new = up(np.concatenate(ks)), up(np.concatenate(vs))
+        self.slots = torch.tensor(slots, dtype=torch.int64, device="cuda")
+        self.tables = torch.from_numpy(tables).cuda()
+        self.lens = torch.from_numpy(self.lens_h).cuda()
+        self.cu = torch.from_numpy(cu).cuda()
+        self.q = up(inputs.chunk_queries(w, self.T))
+        self.out = torch.empty((self.T, w.Hq, w.D), dtype=torch.float32, device="cuda")
+        self.hev = HipEvents()
+        self.stream = torch.cuda.current_stream().cuda_stream
+        self.events = []
+
+    def step(self, time_it: bool = False):
+        pkv, w = self.pkv, self.w
+        pkv.kv_append(self.k_new, self.v_new, self.slots, self.k, self.v)
+        e0 = e1 = None
+        if time_it:
+            e0, e1 = self.hev.create(), self.hev.create()
+            self.hev.record(e0, self.stream)
+        pkv.prefill(self.q, self.k, self.v, self.tables, self.lens, self.cu,
+                    int(self.lens_h.max()), w.scale, out=self.out)
+        if time_it:
+            self.hev.record(e1, self.stream)
+            self.events.append((e0, e1))
+
+    def prefill_ms(self):
+        return [self.hev.elapsed_ms(a, b) for a, b in self.events]
+
+
+def prefill_workload():
+    import inputs
+    w = inputs.llama8b_decode(B=8, lo=2048, hi=4096, cid=72, name="prefill_llama8b")
+    w.append = False
+    return w, inputs.chunk_sizes(w, 512, 512)
+
+
+def cpu_baseline_prefill(min_seconds: float = 10.0) -> dict:
+    """The fp64 oracle on sampled (query row, head) pairs of the prefill workload, one thread,
+    scaled to query tokens/s (a token is Hq row-heads)."""
+    env = dict(os.environ, OMP_NUM_THREADS="1", OPENBLAS_NUM_THREADS="1", MKL_NUM_THREADS="1")
+    code = f"""
+import sys, time, json, numpy as np
+sys.path.insert(0, {ROOT!r})
+import inputs
+from oracle.allocator import PyAllocator, run_script
+from oracle.prefill import prefill_paged
+from bench import prefill_workload
+w, chunks = prefill_workload()
+a = PyAllocator(w.NB, w.bs, inputs.free_order(w))
+ids = run_script(a, inputs.setup_script(w))
+seqs = [ids[b] for b in range(w.B)]
+tables, lens = a.export(seqs, max(len(a.table(s)) for s in seqs))
+pool = inputs.pool(w)
+cu = np.concatenate([[0], np.cumsum(chunks)])
+T = int(cu[-1])
+q = inputs.chunk_queries(w, T)
+rng = np.random.default_rng(0)
+done, t0 = 0, time.perf_counter()
+while True:
+    b = int(rng.integers(0, w.B))
+    g = int(rng.integers(0, w.Hkv))
+    rows = [(int(cu[b]) + int(i), h) for i in rng.integers(0, int(chunks[b]), 32)
+            for h in range(g * w.G, (g + 1) * w.G)]
+    prefill_paged(q[cu[b]:cu[b + 1]], w.q_dtype, pool["k"], pool["v"], w.kv_dtype, [tables[b]],
+                  [lens[b]], [0, int(chunks[b])], w.bs, w.scale,
+                  rows=[(r - int(cu[b]), h) for r, h in rows])
+    done += len(rows)
+    el = time.perf_counter() - t0
+    if el >= {min_seconds}:
+        break
+print(json.dumps({{"rowheads": done, "seconds": el}}))
+"""
+    r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True,
+                       cwd=ROOT)
+    if r.returncode != 0:
+        raise RuntimeError(r.stderr[-2000:])
+    d = json.loads(r.stdout.strip().splitlines()[-1])
+    w, _ = prefill_workload()
+    return {"value": round(d["rowheads"] / w.Hq / d["seconds"], 2), "unit": "tokens/s",
+            "cores": 1, "kind": "oracle",
+            "sample": f"{d['rowheads']} sampled (query row, head) outputs of the workload "
+                      f"(32 rows x the G heads of one KV head per draw, fp64 numpy, 1 thread) "
+                      f"in {d['seconds']:.1f} s"}
+
+
+def run_prefill(args):
+    import torch
+    w, chunks = prefill_workload()
+    runner = PrefillRunner(w, chunks)
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        runner.step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        runner.step(time_it=True)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms = runner.prefill_ms()
+    mean_ms = float(np.mean(ms))
+    flops = prefill_flops(w, runner.lens_h, chunks)
+    tflops = flops / (mean_ms * 1e-3) / 1e12
+    rec = {
+        "metric": "paged chunked-prefill attn: query tokens/s + achieved MFMA TFLOP/s",
+        "value": round(runner.T * args.steps / elapsed, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) K/V/q, shapes of the workload; no weights)",
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "head_dim": w.D,
+                   "block_size": w.bs, "chunk_tokens": [int(c) for c in chunks],
+                   "context_tokens": [int(x) for x in runner.lens_h]},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None},
+        "prefill_ms_mean": round(mean_ms, 5),
+        "prefill_algorithmic_flops": flops,
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline_prefill(args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+
+
 def cpu_baseline(name: str, min_seconds: float = 10.0) -> dict:
     """Time the fp64 oracle on one decode step of the same workload, one thread, in a child
     process (input generation excluded)."""
@@ -332,6 +511,9 @@ def main():
 
     import paged_kv_cache_284_amd as pkv
     pkv.lib()
+    if args.workload.startswith("prefill"):
+        run_prefill(args)
+        return
 
     total = args.warmup + args.steps
     w = build_workload(args.workload, total)
