@@ -178,13 +178,29 @@ int pa_free_list(const pa_allocator* a, int32_t* out, int32_t cap, int32_t* n);
 
 /* Append one token per sequence ([Serving] "What the KV Cache Is": each decode step appends one
  * more token's K and V; "The Life of a Request").  k_new, v_new: device [B][Hkv][D] in the
- * cache dtype (PA_F32 or PA_BF16; int8 caches are written by their quantiser, not here).
+ * cache dtype (PA_F32 or PA_BF16; int8 caches are written by pa_kv_append_int8).
  * slot_mapping: device-readable [B] int64, -1 = skip this sequence.  Writes K into k_cache[slot/bs][g]
  * [slot%bs][:] and V into v_cache[slot/bs][g][:][slot%bs]; nothing else is touched.  Two
  * sequences must not share a slot.  Constraints: B >= 0, Hkv >= 1, D in {64, 128}, bs == 16. */
 int pa_kv_append(const void* k_new, const void* v_new, const int64_t* slot_mapping,
                  void* k_cache, void* v_cache, int32_t B, int32_t Hkv, int32_t D, int32_t bs,
                  int32_t NB, int32_t kv_dtype, void* stream);
+
+/* Append into an int8 cache, quantising on the way (the write side of a quantised cache:
+ * [Walkthrough] keeps KV as int8 with a scale per block and head).  k_new, v_new: device
+ * [B][Hkv][D] in new_dtype (PA_F32 or PA_BF16); slot_mapping as for pa_kv_append; k_cache,
+ * v_cache int8 in the usual layouts; k_scale, v_scale device [NB][Hkv] fp32.  Entries apply in
+ * batch order; entries writing into the same block must be consecutive in the batch (one
+ * token per sequence, or a sequence's chunk in order, both are).  Per (block, KV head), K and V
+ * alike, all in fp32 with IEEE division and round-half-to-even: c = max|x| / 127 for the new
+ * vector x; at offset 0 the block's scale becomes c; otherwise a c above the scale s grows the
+ * scale to c and re-rounds the block's earlier codes, code = clamp(rint(code * (s / c)), -127,
+ * 127); the new slot gets clamp(rint(x / scale), -127, 127), or 0 while the scale is 0.  So a
+ * block's scale is always max|x| / 127 over its tokens; a block of zeros has scale 0. */
+int pa_kv_append_int8(const void* k_new, const void* v_new, int32_t new_dtype,
+                      const int64_t* slot_mapping, int8_t* k_cache, int8_t* v_cache,
+                      float* k_scale, float* v_scale, int32_t B, int32_t Hkv, int32_t D,
+                      int32_t bs, int32_t NB, void* stream);
 
 /* Copy-on-write block copies ([Serving] "Sharing comes for free"; [Walkthrough] "Step 8").
  * pairs: device-readable [n][2] int32 (src, dst).  Copies the whole K and V tile of block src over block

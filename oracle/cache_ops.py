@@ -44,3 +44,63 @@ def copy_blocks(k_pool, v_pool, pairs, k_scale=None, v_scale=None):
             ks[dst] = ks[src]
             vs[dst] = vs[src]
     return k_out, v_out, ks, vs
+
+
+def append_int8(k_codes, v_codes, k_scale, v_scale, k_new, v_new, slots, bs):
+    """Quantising append into an int8 cache (the write side of a quantised cache, "LLM serving
+    (vLLM, quantized inference): Visual walkthrough": KV kept as int8 with a scale per block).
+    Returns copies of (k_codes, v_codes, k_scale, v_scale).
+
+    k_new / v_new: [B][Hkv][D] float32 (bf16 inputs widen exactly).  Entries are applied in
+    batch order; for entry b with slot s >= 0 (block blk, offset off) and every KV head g, for K
+    and V alike, with x the new vector and all arithmetic in float32 (IEEE division,
+    round-half-to-even):
+      * c = max|x| / 127 is the scale the token alone would need;
+      * off == 0 (a fresh block): scale := c;
+      * otherwise, with the block's scale s: if c > s, the scale grows to c and the codes of
+        the block's first off slots are re-rounded to it, code := clamp(rint(code * (s / c)),
+        -127, 127); else the scale stays;
+      * the new slot gets clamp(rint(x / scale), -127, 127), or 0 when the scale is 0.
+    The scale of a block thus stays max over its tokens of max|x| / 127 (the absmax scale of the
+    whole block's valid slots); a block with only zeros so far has scale 0 (it dequantises to
+    zeros).  Earlier tokens' codes are re-rounded from their codes: the originals are gone.
+    """
+    kc, vc = k_codes.copy(), v_codes.copy()
+    ks, vs = k_scale.copy(), v_scale.copy()
+    f32 = np.float32
+    k_new = np.asarray(k_new, f32)
+    v_new = np.asarray(v_new, f32)
+    Hkv = kc.shape[1]
+    for b, s in enumerate(np.asarray(slots).tolist()):
+        if s < 0:
+            continue
+        blk, off = divmod(int(s), bs)
+        for g in range(Hkv):
+            for x, codes, scales, token_major in ((k_new[b, g], kc, ks, True),
+                                                  (v_new[b, g], vc, vs, False)):
+                cand = f32(np.max(np.abs(x))) / f32(127.0)
+                if off == 0:
+                    scale = cand
+                else:
+                    old = scales[blk, g]
+                    scale = old
+                    if cand > old:
+                        r = f32(old) / f32(cand)
+                        tile = codes[blk, g]
+                        prev = tile[:off, :] if token_major else tile[:, :off]
+                        new_prev = np.clip(np.rint(prev.astype(f32) * r), -127, 127)
+                        if token_major:
+                            tile[:off, :] = new_prev.astype(np.int8)
+                        else:
+                            tile[:, :off] = new_prev.astype(np.int8)
+                        scale = cand
+                if scale > 0:
+                    q = np.clip(np.rint(x / f32(scale)), -127, 127).astype(np.int8)
+                else:
+                    q = np.zeros_like(x, dtype=np.int8)
+                if token_major:
+                    codes[blk, g, off, :] = q
+                else:
+                    codes[blk, g, :, off] = q
+                scales[blk, g] = scale
+    return kc, vc, ks, vs

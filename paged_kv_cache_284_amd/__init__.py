@@ -57,6 +57,8 @@ _SIGNATURES = {
     "pa_evictable_list": (C.c_int, [_vp, _pi32, _i32, _pi32]),
     "pa_block_hash": (C.c_int, [_vp, _i32, C.POINTER(C.c_uint64), _pi32]),
     "pa_kv_append": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
+    "pa_kv_append_int8": (C.c_int, [_vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
+                                    _i32, _i32, _vp]),
     "pa_copy_blocks": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                                  _vp]),
     "pa_update_block_tables": (C.c_int, [_vp, _i32, _vp, _vp, _i32, _i32, _vp]),
@@ -352,6 +354,29 @@ def kv_append(k_new, v_new, slot_mapping, k_cache, v_cache, stream=None) -> None
                               _readable(slot_mapping, "slot_mapping", torch.int64),
                               _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), B, Hkv, D, bs,
                               NB, _dtype_code(k_cache), _stream(stream)), "pa_kv_append")
+
+
+def kv_append_int8(k_new, v_new, slot_mapping, k_cache, v_cache, k_scale, v_scale,
+                   stream=None) -> None:
+    """Quantising append into an int8 cache: k_new/v_new [B][Hkv][D] bf16 or fp32."""
+    torch = _torch()
+    NB, Hkv, bs, D = k_cache.shape
+    B = k_new.shape[0]
+    if tuple(k_new.shape) != (B, Hkv, D) or tuple(v_new.shape) != (B, Hkv, D):
+        raise ValueError("k_new/v_new must be [B][Hkv][D]")
+    if k_cache.dtype != torch.int8 or v_cache.dtype != torch.int8:
+        raise TypeError("caches must be int8")
+    if tuple(v_cache.shape) != (NB, Hkv, D, bs) or tuple(k_scale.shape) != (NB, Hkv):
+        raise ValueError("v_cache must be [NB][Hkv][D][bs], scales [NB][Hkv]")
+    if k_new.dtype != v_new.dtype:
+        raise TypeError("k_new and v_new must share a dtype")
+    _check(lib().pa_kv_append_int8(_dev(k_new, "k_new"), _dev(v_new, "v_new"),
+                                   _dtype_code(k_new),
+                                   _readable(slot_mapping, "slot_mapping", torch.int64),
+                                   _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+                                   _dev(k_scale, "k_scale", torch.float32),
+                                   _dev(v_scale, "v_scale", torch.float32), B, Hkv, D, bs, NB,
+                                   _stream(stream)), "pa_kv_append_int8")
 
 
 def copy_blocks(k_cache, v_cache, pairs, k_scale=None, v_scale=None, stream=None) -> None:

@@ -59,6 +59,21 @@ int pa_kv_append(const void* k_new, const void* v_new, const int64_t* slot_mappi
                                         nullptr, static_cast<hipStream_t>(stream)));
 }
 
+int pa_kv_append_int8(const void* k_new, const void* v_new, int32_t new_dtype,
+                      const int64_t* slot_mapping, int8_t* k_cache, int8_t* v_cache,
+                      float* k_scale, float* v_scale, int32_t B, int32_t Hkv, int32_t D,
+                      int32_t bs, int32_t NB, void* stream) {
+  if (B < 0 || Hkv < 1 || NB < 1 || (D != 64 && D != 128)) return PA_ERR_INVALID;
+  if (bs != pa::kBlockSize) return PA_ERR_UNSUPPORTED;
+  if (new_dtype != PA_F32 && new_dtype != PA_BF16) return PA_ERR_INVALID;
+  if (B == 0) return PA_OK;
+  if (!k_new || !v_new || !slot_mapping || !k_cache || !v_cache || !k_scale || !v_scale)
+    return PA_ERR_INVALID;
+  return status_of(pa::launch_kv_append_i8(k_new, v_new, new_dtype == PA_BF16, slot_mapping,
+                                           k_cache, v_cache, k_scale, v_scale, B, Hkv, D, NB,
+                                           static_cast<hipStream_t>(stream)));
+}
+
 int pa_append_step(const void* k_new, const void* v_new, const int64_t* slot_mapping,
                    const int32_t* table_index, const int32_t* seq_lens_in, int32_t* seq_lens_out,
                    void* k_cache, void* v_cache, int32_t* block_tables, int32_t max_blocks,

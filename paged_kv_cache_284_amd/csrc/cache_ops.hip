@@ -60,6 +60,88 @@ __global__ void __launch_bounds__(256) kv_append_kernel(const T* __restrict__ k_
   }
 }
 
+// Quantising append into an int8 cache.  One wave per (batch entry, KV head); the wave of the
+// first entry of a run of consecutive entries that write into the same block takes the whole
+// run in order (a block's scale and codes evolve token by token), the others exit.  Per token
+// and for K and V alike (all fp32, IEEE division, round-half-to-even): c = max|x| / 127; a fresh
+// block (offset 0) takes scale c; otherwise a larger c grows the scale to c and re-rounds the
+// block's earlier codes by old/c; the new slot gets clamp(rint(x / scale), -127, 127) (0 for a
+// zero scale).  Lane l only ever touches dims d = l (mod 64) of the tile, so the re-rounding
+// reads back only what the same lane wrote.
+template <typename TIn>
+__device__ __forceinline__ float widen(TIn x);
+template <>
+__device__ __forceinline__ float widen<float>(float x) { return x; }
+template <>
+__device__ __forceinline__ float widen<uint16_t>(uint16_t x) {
+  return __uint_as_float(static_cast<uint32_t>(x) << 16);
+}
+
+template <typename TIn>
+__device__ void quantise_token(const TIn* __restrict__ x, int8_t* tile, float* scale_slot,
+                               float* scale_reg, bool fresh, int off, int D, bool token_major) {
+  const int lane = threadIdx.x;
+  float amax = 0.f;
+  for (int d = lane; d < D; d += 64) amax = fmaxf(amax, fabsf(widen<TIn>(x[d])));
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+  const float cand = amax / 127.f;
+  float scale;
+  if (fresh) {
+    scale = cand;
+  } else {
+    const float old = *scale_reg;
+    scale = old;
+    if (cand > old) {
+      const float r = old / cand;
+      for (int d = lane; d < D; d += 64) {
+        for (int row = 0; row < off; ++row) {
+          int8_t* c = token_major ? tile + row * D + d : tile + d * kBlockSize + row;
+          const float q = __builtin_rintf(static_cast<float>(*c) * r);
+          *c = static_cast<int8_t>(fminf(fmaxf(q, -127.f), 127.f));
+        }
+      }
+      scale = cand;
+    }
+  }
+  for (int d = lane; d < D; d += 64) {
+    float q = 0.f;
+    if (scale > 0.f) q = fminf(fmaxf(__builtin_rintf(widen<TIn>(x[d]) / scale), -127.f), 127.f);
+    int8_t* c = token_major ? tile + off * D + d : tile + d * kBlockSize + off;
+    *c = static_cast<int8_t>(q);
+  }
+  *scale_reg = scale;
+  if (lane == 0) *scale_slot = scale;
+}
+
+template <typename TIn>
+__global__ void __launch_bounds__(64) kv_append_i8_kernel(const TIn* __restrict__ k_new,
+                                                           const TIn* __restrict__ v_new,
+                                                           const int64_t* __restrict__ slots,
+                                                           int8_t* k_cache, int8_t* v_cache,
+                                                           float* k_scale, float* v_scale,
+                                                           int32_t B, int32_t Hkv, int32_t D,
+                                                           int32_t NB) {
+  const int i = blockIdx.x, g = blockIdx.y;
+  const int64_t cap = static_cast<int64_t>(NB) * kBlockSize;
+  auto block_of = [&](int64_t s) -> int64_t { return (s >= 0 && s < cap) ? s / kBlockSize : -1; };
+  const int64_t blk = block_of(slots[i]);
+  if (blk < 0) return;
+  if (i > 0 && block_of(slots[i - 1]) == blk) return;  // not the first entry of its run
+  const int64_t tile = blk * Hkv + g;
+  int8_t* kt = k_cache + tile * kBlockSize * D;
+  int8_t* vt = v_cache + tile * kBlockSize * D;
+  float ks_reg = k_scale[tile], vs_reg = v_scale[tile];  // the block's scales so far
+  for (int j = i; j < B; ++j) {
+    const int64_t sj = slots[j];
+    if (block_of(sj) != blk) break;
+    const int off = static_cast<int>(sj % kBlockSize);
+    const int64_t src = (static_cast<int64_t>(j) * Hkv + g) * D;
+    quantise_token<TIn>(k_new + src, kt, k_scale + tile, &ks_reg, off == 0, off, D, true);
+    quantise_token<TIn>(v_new + src, vt, v_scale + tile, &vs_reg, off == 0, off, D, false);
+  }
+}
+
 // One workgroup per pair; its threads stride over the 16-byte chunks of the K and V tiles.
 __global__ void __launch_bounds__(256) copy_blocks_kernel(uint4* __restrict__ k_cache,
                                                           uint4* __restrict__ v_cache,
@@ -123,6 +205,24 @@ hipError_t launch_kv_append(const void* k_new, const void* v_new, const int64_t*
                        Hkv, D, NB, table_index, tables, max_blocks, lens_in, lens_out);
   } else {
     return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_append_i8(const void* k_new, const void* v_new, bool bf16_new,
+                               const int64_t* slots, int8_t* k_cache, int8_t* v_cache,
+                               float* k_scale, float* v_scale, int32_t B, int32_t Hkv, int32_t D,
+                               int32_t NB, hipStream_t stream) {
+  if (B == 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>(B), static_cast<unsigned>(Hkv));
+  if (bf16_new) {
+    hipLaunchKernelGGL(kv_append_i8_kernel<uint16_t>, grid, dim3(64), 0, stream,
+                       static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new),
+                       slots, k_cache, v_cache, k_scale, v_scale, B, Hkv, D, NB);
+  } else {
+    hipLaunchKernelGGL(kv_append_i8_kernel<float>, grid, dim3(64), 0, stream,
+                       static_cast<const float*>(k_new), static_cast<const float*>(v_new), slots,
+                       k_cache, v_cache, k_scale, v_scale, B, Hkv, D, NB);
   }
   return hipGetLastError();
 }

@@ -66,6 +66,11 @@ hipError_t launch_kv_append(const void* k_new, const void* v_new, const int64_t*
                             int32_t NB, int32_t elem_bytes, const int32_t* table_index,
                             int32_t* tables, int32_t max_blocks, const int32_t* lens_in,
                             int32_t* lens_out, hipStream_t stream);
+// Quantising append into an int8 cache; new tokens in bf16 (bf16_new) or fp32.
+hipError_t launch_kv_append_i8(const void* k_new, const void* v_new, bool bf16_new,
+                               const int64_t* slots, int8_t* k_cache, int8_t* v_cache,
+                               float* k_scale, float* v_scale, int32_t B, int32_t Hkv, int32_t D,
+                               int32_t NB, hipStream_t stream);
 hipError_t launch_copy_blocks(void* k_cache, void* v_cache, float* k_scale, float* v_scale,
                               const int32_t* pairs, int32_t n, int32_t Hkv, int32_t D,
                               int32_t NB, int32_t elem_bytes, hipStream_t stream);

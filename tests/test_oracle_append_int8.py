@@ -1,0 +1,111 @@
+"""Pins for the quantising int8 append: a fresh one-token block equals the harness's absmax
+quantiser on that token; the block scale always equals the absmax rule over the block's valid
+tokens; rounding bounds; blocks whose scale did not grow keep their codes; brute force."""
+import math
+
+import numpy as np
+
+import inputs
+from oracle.cache_ops import append_int8
+
+
+def _empty(NB, Hkv, D, bs=16):
+    return (np.zeros((NB, Hkv, bs, D), np.int8), np.zeros((NB, Hkv, D, bs), np.int8),
+            np.zeros((NB, Hkv), np.float32), np.zeros((NB, Hkv), np.float32))
+
+
+def test_fresh_block_equals_the_absmax_quantiser():
+    rng = np.random.default_rng(0)
+    x = rng.standard_normal((1, 2, 64)).astype(np.float32)
+    kc, vc, ks, vs = append_int8(*_empty(4, 2, 64), x, x * 2, [3 * 16], 16)
+    ref_codes, ref_scale = inputs.quantize_int8_pool(x[0][:, None, :], tile_axes=(1, 2))
+    assert np.array_equal(kc[3, :, 0, :], ref_codes[:, 0, :])
+    assert np.array_equal(ks[3], ref_scale)
+    ref_v, ref_vs = inputs.quantize_int8_pool((2 * x[0])[:, None, :], tile_axes=(1, 2))
+    assert np.array_equal(vc[3, :, :, 0], ref_v[:, 0, :]) and np.array_equal(vs[3], ref_vs)
+
+
+def test_scale_is_the_block_absmax_rule_and_codes_are_bounded():
+    rng = np.random.default_rng(1)
+    Hkv, D, bs = 2, 32, 16
+    state = _empty(2, Hkv, D)
+    toks = []
+    growths = np.zeros((bs, Hkv))        # scale growths each token has been re-rounded through
+    for off in range(bs):
+        x = (rng.standard_normal((1, Hkv, D)) * rng.uniform(0.1, 3)).astype(np.float32)
+        toks.append(x[0])
+        before = state[2][1].copy()
+        state = append_int8(*state, x, x, [16 + off], bs)
+        kc, vc, ks, vs = state
+        if off:
+            growths[:off] += (ks[1] > before)[None, :]
+        allx = np.stack(toks)                                   # [off+1][Hkv][D]
+        amax = np.max(np.abs(allx), axis=(0, 2)).astype(np.float32)
+        assert np.array_equal(ks[1], amax / np.float32(127))    # the absmax rule, exactly
+        assert np.array_equal(vs[1], ks[1])
+        # the newest token is within half a step; each re-rounding adds at most half a step
+        # of a scale no larger than the current one
+        deq = kc[1, :, :off + 1, :].astype(np.float64) * ks[1][:, None, None]
+        err = np.abs(deq - np.transpose(allx, (1, 0, 2)))          # [Hkv][off+1][D]
+        assert np.all(err[:, off, :] <= ks[1][:, None] / 2 + 1e-12)
+        bound = (growths[:off + 1].T + 1) * ks[1][:, None] / 2    # [Hkv][off+1]
+        assert np.all(err <= bound[:, :, None] + 1e-12)
+        assert np.all(np.abs(kc) <= 127)
+
+
+def test_no_growth_leaves_codes_alone_and_growth_rerounds():
+    Hkv, D = 1, 8
+    big = np.full((1, Hkv, D), 4.0, np.float32)
+    small = np.full((1, Hkv, D), 1.0, np.float32)
+    s = append_int8(*_empty(1, Hkv, D), big, big, [0], 16)
+    s2 = append_int8(*s, small, small, [1], 16)
+    assert np.array_equal(s2[0][0, 0, 0], s[0][0, 0, 0]) and s2[2][0, 0] == s[2][0, 0]
+    assert np.all(s2[0][0, 0, 1] == np.rint(np.float32(1.0) / s[2][0, 0]))
+    # growth: 1.0 first, then 4.0 -> the first row is re-rounded by 1/4
+    t = append_int8(*_empty(1, Hkv, D), small, small, [0], 16)
+    t2 = append_int8(*t, big, big, [1], 16)
+    assert np.all(t[0][0, 0, 0] == 127) and np.all(t2[0][0, 0, 1] == 127)
+    r = np.float32(t[2][0, 0]) / np.float32(t2[2][0, 0])
+    assert np.all(t2[0][0, 0, 0] == np.rint(np.float32(127) * r))     # 31.75 -> 32
+
+
+def test_zero_tokens_keep_scale_zero_until_data_arrives():
+    z = np.zeros((1, 1, 8), np.float32)
+    s = append_int8(*_empty(1, 1, 8), z, z, [0], 16)
+    assert s[2][0, 0] == 0 and np.all(s[0][0, 0, 0] == 0)
+    x = np.linspace(-1, 1, 8, dtype=np.float32).reshape(1, 1, 8)
+    s2 = append_int8(*s, x, x, [1], 16)
+    assert s2[2][0, 0] == np.float32(1) / np.float32(127)
+    assert np.all(s2[0][0, 0, 0] == 0) and s2[0][0, 0, 1, -1] == 127
+
+
+def test_batch_order_and_skips():
+    rng = np.random.default_rng(2)
+    x = rng.standard_normal((3, 1, 8)).astype(np.float32)
+    both = append_int8(*_empty(2, 1, 8), x, x, [0, -1, 1], 16)
+    one = append_int8(*_empty(2, 1, 8), x[:1], x[:1], [0], 16)
+    two = append_int8(*one, x[2:], x[2:], [1], 16)
+    for a, b in zip(both, two):
+        assert np.array_equal(a, b)
+
+
+def test_brute_force_scalar():
+    rng = np.random.default_rng(3)
+    vals = [rng.standard_normal((1, 1, 4)).astype(np.float32) * k for k in (0.5, 2.0, 1.0)]
+    state = _empty(1, 1, 4)
+    for i, x in enumerate(vals):
+        state = append_int8(*state, x, x, [i], 16)
+    # scalar re-derivation with Python floats rounded through float32 at every step
+    f = lambda v: float(np.float32(v))  # noqa: E731
+    codes, scale = [], 0.0
+    for i, x in enumerate(vals):
+        c = f(f(max(abs(float(t)) for t in x.ravel())) / 127.0)
+        if i == 0:
+            scale = c
+        elif c > scale:
+            r = f(scale / c)
+            codes = [[max(-127, min(127, round(f(q * r)))) for q in row] for row in codes]
+            scale = c
+        codes.append([max(-127, min(127, round(f(float(t) / scale)))) for t in x.ravel()])
+    assert state[2][0, 0] == np.float32(scale)
+    assert np.array_equal(state[0][0, 0, :3, :], np.array(codes, np.int8))
