@@ -160,6 +160,30 @@ int pa_evictable_list(const pa_allocator* a, int32_t* out, int32_t cap, int32_t*
 /* Whether a block is published, and its hash (0 when not). */
 int pa_block_hash(const pa_allocator* a, int32_t block, uint64_t* hash, int32_t* cached);
 
+/* ---- preemption by swapping ([Serving] "When memory runs out anyway": a preempted request's
+ * blocks are freed; its KV is either dropped and recomputed later, or swapped out to CPU memory
+ * and brought back) ----
+ * The allocator also hands out blocks of a host swap pool (num_cpu_blocks blocks in the same
+ * layout, e.g. pinned host memory) from a FIFO free list of its own.  A swapped-out sequence
+ * keeps its length and token ids but holds no device blocks; calls that need its blocks return
+ * PA_ERR_STATE until it is swapped in; pa_seq_len and pa_seq_free still work. */
+
+/* Sets the swap pool size, once. */
+int pa_alloc_set_swap(pa_allocator* a, int32_t num_cpu_blocks);
+/* Swap a resident sequence out: each of its table's blocks gets a swap block (FIFO) and
+ * pairs[j] = (device block, swap block) in table order, *n = count (cap must be >= the table
+ * length, else PA_ERR_INVALID with *n set).  The device blocks are then released as by
+ * pa_seq_free.  The caller copies the pairs device -> host (pa_swap_blocks) on the stream
+ * before anything can write the released blocks.  PA_ERR_OOM (nothing changed) when the swap
+ * pool is short. */
+int pa_seq_swap_out(pa_allocator* a, int32_t seq, int32_t* pairs, int32_t cap, int32_t* n);
+/* Swap a swapped-out sequence back in: fresh device blocks (allocated like any other, possibly
+ * evicting cached ones), pairs[j] = (swap block, device block) in table order; the swap blocks
+ * return to the tail of the swap free list.  The caller copies the pairs host -> device before
+ * anything can reuse the swap blocks.  PA_ERR_OOM (nothing changed) when the device is short. */
+int pa_seq_swap_in(pa_allocator* a, int32_t seq, int32_t* pairs, int32_t cap, int32_t* n);
+int pa_num_free_swap(const pa_allocator* a, int32_t* n);
+
 int pa_seq_len(const pa_allocator* a, int32_t seq, int32_t* len);
 /* Copies up to `cap` table entries to out; *n receives the table length. */
 int pa_seq_table(const pa_allocator* a, int32_t seq, int32_t* out, int32_t cap, int32_t* n);
@@ -210,6 +234,18 @@ int pa_kv_append_int8(const void* k_new, const void* v_new, int32_t new_dtype,
 int pa_copy_blocks(void* k_cache, void* v_cache, float* k_scale, float* v_scale,
                    const int32_t* pairs, int32_t n, int32_t Hkv, int32_t D, int32_t bs,
                    int32_t NB, int32_t kv_dtype, void* stream);
+
+/* Copy whole blocks between two pools of the same layout -- the device pool and a host swap
+ * pool (pinned host memory, device-readable and -writable) for preemption by swapping, or any
+ * two device pools: for i < n, block pairs[i][1] of the destination := block pairs[i][0] of the
+ * source (K, V, and for PA_I8 both scales, which must then all be non-NULL).  One launch for
+ * the whole batch.  Pairs are device-readable int32 [n][2]; destination blocks must be
+ * distinct; entries outside [0, src_blocks) or [0, dst_blocks) are skipped. */
+int pa_swap_blocks(const void* src_k, const void* src_v, const float* src_k_scale,
+                   const float* src_v_scale, int32_t src_blocks, void* dst_k, void* dst_v,
+                   float* dst_k_scale, float* dst_v_scale, int32_t dst_blocks,
+                   const int32_t* pairs, int32_t n, int32_t Hkv, int32_t D, int32_t bs,
+                   int32_t kv_dtype, void* stream);
 
 /* Patch a device block table after pa_step: for every i < B with table_index[i] >= 0,
  * block_tables[i][table_index[i]] = slots[i] / bs.  slots (int64) and table_index (int32) are

@@ -54,6 +54,12 @@ _SIGNATURES = {
     "pa_seq_create_prefix": (C.c_int, [_vp, _pi32, _i32, C.c_uint64, _pi32, _pi32]),
     "pa_seq_add_tokens": (C.c_int, [_vp, _i32, _pi32, _i32]),
     "pa_num_evictable": (C.c_int, [_vp, _pi32]),
+    "pa_alloc_set_swap": (C.c_int, [_vp, _i32]),
+    "pa_seq_swap_out": (C.c_int, [_vp, _i32, _pi32, _i32, _pi32]),
+    "pa_seq_swap_in": (C.c_int, [_vp, _i32, _pi32, _i32, _pi32]),
+    "pa_num_free_swap": (C.c_int, [_vp, _pi32]),
+    "pa_swap_blocks": (C.c_int, [_vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _i32, _vp, _i32,
+                                 _i32, _i32, _i32, _i32, _vp]),
     "pa_evictable_list": (C.c_int, [_vp, _pi32, _i32, _pi32]),
     "pa_block_hash": (C.c_int, [_vp, _i32, C.POINTER(C.c_uint64), _pi32]),
     "pa_kv_append": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
@@ -238,6 +244,30 @@ class Allocator:
         _check(lib().pa_free_list(self._h, _p32(out), n.value, C.byref(n)), "pa_free_list")
         return out[:n.value].tolist()
 
+    # -- preemption by swapping -----------------------------------------------------------------
+    def set_swap(self, num_cpu_blocks: int) -> None:
+        _check(lib().pa_alloc_set_swap(self._h, num_cpu_blocks), "pa_alloc_set_swap")
+
+    def _swap(self, fn, name, seq):
+        m = -(-self.length(seq) // self.block_size)    # the table's length
+        n = _i32()
+        out = np.zeros((max(m, 1), 2), np.int32)
+        _check(fn(self._h, seq, _p32(out), m, C.byref(n)), name)
+        return [tuple(p) for p in out[:n.value].tolist()]
+
+    def swap_out(self, seq: int) -> List[Tuple[int, int]]:
+        """(device block, swap block) pairs in table order; the device blocks are released."""
+        return self._swap(lib().pa_seq_swap_out, "pa_seq_swap_out", seq)
+
+    def swap_in(self, seq: int) -> List[Tuple[int, int]]:
+        """(swap block, device block) pairs in table order."""
+        return self._swap(lib().pa_seq_swap_in, "pa_seq_swap_in", seq)
+
+    def num_free_swap(self) -> int:
+        n = _i32()
+        _check(lib().pa_num_free_swap(self._h, C.byref(n)), "pa_num_free_swap")
+        return n.value
+
     # -- automatic prefix caching --------------------------------------------------------------
     def create_prefix(self, tokens, salt: int = 0) -> Tuple[int, int]:
         """A sequence for a prompt of token ids, reusing matching cached blocks: (id, tokens
@@ -377,6 +407,26 @@ def kv_append_int8(k_new, v_new, slot_mapping, k_cache, v_cache, k_scale, v_scal
                                    _dev(k_scale, "k_scale", torch.float32),
                                    _dev(v_scale, "v_scale", torch.float32), B, Hkv, D, bs, NB,
                                    _stream(stream)), "pa_kv_append_int8")
+
+
+def swap_blocks(src_k, src_v, dst_k, dst_v, pairs, src_scales=(None, None),
+                dst_scales=(None, None), stream=None) -> None:
+    """Copy whole blocks between two pools of one layout (device and pinned host swap pool):
+    dst block pairs[i][1] := src block pairs[i][0]."""
+    torch = _torch()
+    NBs, Hkv, bs, D = src_k.shape
+    NBd = dst_k.shape[0]
+    n = pairs.shape[0]
+    if tuple(dst_k.shape[1:]) != (Hkv, bs, D) or src_k.dtype != dst_k.dtype:
+        raise ValueError("pools must share a layout and dtype")
+    for t, nm in ((src_k, "src_k"), (src_v, "src_v"), (dst_k, "dst_k"), (dst_v, "dst_v")):
+        _readable(t, nm)
+    sp = [_readable(x, "scale", torch.float32) for x in src_scales]
+    dp = [_readable(x, "scale", torch.float32) for x in dst_scales]
+    _check(lib().pa_swap_blocks(src_k.data_ptr(), src_v.data_ptr(), sp[0], sp[1], NBs,
+                                dst_k.data_ptr(), dst_v.data_ptr(), dp[0], dp[1], NBd,
+                                _readable(pairs, "pairs", torch.int32) if n else None, n, Hkv, D,
+                                bs, _dtype_code(src_k), _stream(stream)), "pa_swap_blocks")
 
 
 def copy_blocks(k_cache, v_cache, pairs, k_scale=None, v_scale=None, stream=None) -> None:

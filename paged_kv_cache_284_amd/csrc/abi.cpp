@@ -110,6 +110,30 @@ int pa_copy_blocks(void* k_cache, void* v_cache, float* k_scale, float* v_scale,
                                           NB, eb, static_cast<hipStream_t>(stream)));
 }
 
+int pa_swap_blocks(const void* src_k, const void* src_v, const float* src_k_scale,
+                   const float* src_v_scale, int32_t src_blocks, void* dst_k, void* dst_v,
+                   float* dst_k_scale, float* dst_v_scale, int32_t dst_blocks,
+                   const int32_t* pairs, int32_t n, int32_t Hkv, int32_t D, int32_t bs,
+                   int32_t kv_dtype, void* stream) {
+  if (n < 0 || Hkv < 1 || src_blocks < 1 || dst_blocks < 1 || (D != 64 && D != 128))
+    return PA_ERR_INVALID;
+  if (bs != pa::kBlockSize) return PA_ERR_UNSUPPORTED;
+  const int eb = elem_bytes(kv_dtype);
+  if (eb == 0) return PA_ERR_INVALID;
+  if (n == 0) return PA_OK;
+  if (!src_k || !src_v || !dst_k || !dst_v || !pairs) return PA_ERR_INVALID;
+  if (kv_dtype == PA_I8) {
+    if (!src_k_scale || !src_v_scale || !dst_k_scale || !dst_v_scale) return PA_ERR_INVALID;
+  } else {
+    src_k_scale = src_v_scale = nullptr;
+    dst_k_scale = dst_v_scale = nullptr;
+  }
+  return status_of(pa::launch_copy_tiles(src_k, src_v, src_k_scale, src_v_scale, src_blocks,
+                                         dst_k, dst_v, dst_k_scale, dst_v_scale, dst_blocks,
+                                         pairs, n, Hkv, D, eb,
+                                         static_cast<hipStream_t>(stream)));
+}
+
 int pa_update_block_tables(int32_t* block_tables, int32_t max_blocks, const int64_t* slots,
                            const int32_t* table_index, int32_t B, int32_t bs, void* stream) {
   if (B < 0 || max_blocks < 0) return PA_ERR_INVALID;

@@ -41,6 +41,9 @@ struct Sequence {
   uint64_t salt = 0;
   std::vector<int32_t> tokens;  // token ids known so far
   std::vector<uint64_t> chain;  // chained hash of each full block handled so far
+  // swap preemption: while swapped out, the K/V sit in these host swap blocks, in table order
+  bool swapped = false;
+  std::vector<int32_t> cpu_table;
 };
 
 enum class Change : uint8_t { kInPlace, kNewBlock, kCopy };
@@ -105,8 +108,29 @@ struct pa_allocator {
   std::vector<int32_t> lru_prev, lru_next;
   int32_t lru_head = -1, lru_tail = -1, lru_size = 0;
 
+  // host swap space (preemption by swapping): FIFO free list of swap block ids
+  int32_t num_cpu_blocks = 0;
+  std::deque<int32_t> cpu_free;
+
+  // a live sequence whose blocks are on the device
   bool valid_seq(int32_t s) const {
+    return s >= 0 && s < static_cast<int32_t>(seqs.size()) && seqs[s].live && !seqs[s].swapped;
+  }
+  // a live sequence, resident or swapped out
+  bool known_seq(int32_t s) const {
     return s >= 0 && s < static_cast<int32_t>(seqs.size()) && seqs[s].live;
+  }
+
+  // Drop one reference from each of a table's blocks: private blocks left without references
+  // go to the free list in table order; cached ones join the LRU list last block first, so a
+  // prefix outlives the blocks that extend it.
+  void release_table(const std::vector<int32_t>& table) {
+    for (int32_t b : table) {
+      refcount[b] -= 1;
+      if (refcount[b] == 0 && !cached[b]) free_list.push_back(b);
+    }
+    for (auto it = table.rbegin(); it != table.rend(); ++it)
+      if (refcount[*it] == 0 && cached[*it]) lru_push_back(*it);
   }
 
   void lru_unlink(int32_t b) {
@@ -391,16 +415,12 @@ int pa_step(pa_allocator* a, const int32_t* seqs, int32_t B, int64_t* slots, int
 
 int pa_seq_free(pa_allocator* a, int32_t seq) {
   if (!a) return PA_ERR_INVALID;
-  if (!a->valid_seq(seq)) return PA_ERR_STATE;
+  if (!a->known_seq(seq)) return PA_ERR_STATE;
   Sequence& q = a->seqs[seq];
-  // Blocks left without references: private ones go to the free list in table order; cached
-  // ones join the LRU list last block first, so a prefix outlives the blocks that extend it.
-  for (int32_t b : q.table) {
-    a->refcount[b] -= 1;
-    if (a->refcount[b] == 0 && !a->cached[b]) a->free_list.push_back(b);
-  }
-  for (auto it = q.table.rbegin(); it != q.table.rend(); ++it)
-    if (a->refcount[*it] == 0 && a->cached[*it]) a->lru_push_back(*it);
+  a->release_table(q.table);
+  for (int32_t c : q.cpu_table) a->cpu_free.push_back(c);
+  q.cpu_table.clear();
+  q.swapped = false;
   q.table.clear();
   q.table.shrink_to_fit();
   q.tokens.clear();
@@ -454,6 +474,75 @@ int pa_seq_add_tokens(pa_allocator* a, int32_t seq, const int32_t* tokens, int32
   return PA_OK;
 }
 
+int pa_alloc_set_swap(pa_allocator* a, int32_t num_cpu_blocks) {
+  if (!a || num_cpu_blocks < 0) return PA_ERR_INVALID;
+  if (a->num_cpu_blocks != 0) return PA_ERR_STATE;  // set once
+  a->num_cpu_blocks = num_cpu_blocks;
+  for (int32_t i = 0; i < num_cpu_blocks; ++i) a->cpu_free.push_back(i);
+  return PA_OK;
+}
+
+int pa_seq_swap_out(pa_allocator* a, int32_t seq, int32_t* pairs, int32_t cap, int32_t* n) {
+  if (!a || !n || cap < 0 || (cap > 0 && !pairs)) return PA_ERR_INVALID;
+  if (!a->valid_seq(seq)) return PA_ERR_STATE;
+  Sequence& q = a->seqs[seq];
+  const int32_t m = static_cast<int32_t>(q.table.size());
+  *n = m;
+  if (cap < m) return PA_ERR_INVALID;
+  if (static_cast<int32_t>(a->cpu_free.size()) < m) return PA_ERR_OOM;
+  q.cpu_table.resize(m);
+  for (int32_t j = 0; j < m; ++j) {
+    q.cpu_table[j] = a->cpu_free.front();
+    a->cpu_free.pop_front();
+    pairs[2 * j] = q.table[j];
+    pairs[2 * j + 1] = q.cpu_table[j];
+  }
+  a->release_table(q.table);
+  q.table.clear();
+  q.chain.clear();  // the blocks it published stay cached (or evictable) on their own
+  q.swapped = true;
+  return PA_OK;
+}
+
+int pa_seq_swap_in(pa_allocator* a, int32_t seq, int32_t* pairs, int32_t cap, int32_t* n) {
+  if (!a || !n || cap < 0 || (cap > 0 && !pairs)) return PA_ERR_INVALID;
+  if (!a->known_seq(seq) || !a->seqs[seq].swapped) return PA_ERR_STATE;
+  Sequence& q = a->seqs[seq];
+  const int32_t m = static_cast<int32_t>(q.cpu_table.size());
+  *n = m;
+  if (cap < m) return PA_ERR_INVALID;
+  std::vector<int32_t> got;
+  std::vector<uint8_t> evicted;
+  got.reserve(m);
+  for (int32_t j = 0; j < m; ++j) {
+    bool ev = false;
+    const int32_t b = a->take_block(&ev);
+    if (b < 0) {  // undo, newest first
+      for (int32_t k = static_cast<int32_t>(got.size()) - 1; k >= 0; --k)
+        a->give_back(got[k], evicted[k]);
+      return PA_ERR_OOM;
+    }
+    got.push_back(b);
+    evicted.push_back(ev);
+  }
+  q.table = got;
+  for (int32_t j = 0; j < m; ++j) {
+    pairs[2 * j] = q.cpu_table[j];
+    pairs[2 * j + 1] = got[j];
+    a->cpu_free.push_back(q.cpu_table[j]);
+  }
+  q.cpu_table.clear();
+  q.swapped = false;
+  a->publish(seq);
+  return PA_OK;
+}
+
+int pa_num_free_swap(const pa_allocator* a, int32_t* n) {
+  if (!a || !n) return PA_ERR_INVALID;
+  *n = static_cast<int32_t>(a->cpu_free.size());
+  return PA_OK;
+}
+
 int pa_num_evictable(const pa_allocator* a, int32_t* n) {
   if (!a || !n) return PA_ERR_INVALID;
   *n = a->lru_size;
@@ -477,7 +566,7 @@ int pa_block_hash(const pa_allocator* a, int32_t block, uint64_t* hash, int32_t*
 
 int pa_seq_len(const pa_allocator* a, int32_t seq, int32_t* len) {
   if (!a || !len) return PA_ERR_INVALID;
-  if (!a->valid_seq(seq)) return PA_ERR_STATE;
+  if (!a->known_seq(seq)) return PA_ERR_STATE;
   *len = a->seqs[seq].len;
   return PA_OK;
 }
@@ -541,6 +630,6 @@ const char* pa_status_string(int status) {
   }
 }
 
-int pa_abi_version(void) { return 2; }
+int pa_abi_version(void) { return 3; }
 
 }  // extern "C"

@@ -143,28 +143,30 @@ __global__ void __launch_bounds__(64) kv_append_i8_kernel(const TIn* __restrict_
 }
 
 // One workgroup per pair; its threads stride over the 16-byte chunks of the K and V tiles.
-__global__ void __launch_bounds__(256) copy_blocks_kernel(uint4* __restrict__ k_cache,
-                                                          uint4* __restrict__ v_cache,
-                                                          float* __restrict__ k_scale,
-                                                          float* __restrict__ v_scale,
-                                                          const int32_t* __restrict__ pairs,
-                                                          int32_t chunks, int32_t Hkv,
-                                                          int32_t NB) {
+// Source and destination pools may be the same (copy-on-write) or different (swapping to and
+// from a host pool in pinned memory, which the kernel reads or writes over the bus).
+__global__ void __launch_bounds__(256) copy_tiles_kernel(const uint4* src_k, const uint4* src_v,
+                                                         const float* src_ks, const float* src_vs,
+                                                         int32_t src_blocks, uint4* dst_k,
+                                                         uint4* dst_v, float* dst_ks,
+                                                         float* dst_vs, int32_t dst_blocks,
+                                                         const int32_t* __restrict__ pairs,
+                                                         int32_t chunks, int32_t Hkv) {
   __shared__ int32_t pair_s[2];  // read once: the pairs may live in pinned host memory
   if (threadIdx.x < 2) pair_s[threadIdx.x] = pairs[2 * blockIdx.x + threadIdx.x];
   __syncthreads();
   const int32_t src = pair_s[0], dst = pair_s[1];
-  if (src < 0 || src >= NB || dst < 0 || dst >= NB) return;
+  if (src < 0 || src >= src_blocks || dst < 0 || dst >= dst_blocks) return;
   const int64_t s0 = static_cast<int64_t>(src) * chunks;
   const int64_t d0 = static_cast<int64_t>(dst) * chunks;
   for (int32_t c = threadIdx.x; c < chunks; c += blockDim.x) {
-    k_cache[d0 + c] = k_cache[s0 + c];
-    v_cache[d0 + c] = v_cache[s0 + c];
+    dst_k[d0 + c] = src_k[s0 + c];
+    dst_v[d0 + c] = src_v[s0 + c];
   }
-  if (k_scale) {
+  if (src_ks) {
     for (int32_t g = threadIdx.x; g < Hkv; g += blockDim.x) {
-      k_scale[static_cast<int64_t>(dst) * Hkv + g] = k_scale[static_cast<int64_t>(src) * Hkv + g];
-      v_scale[static_cast<int64_t>(dst) * Hkv + g] = v_scale[static_cast<int64_t>(src) * Hkv + g];
+      dst_ks[static_cast<int64_t>(dst) * Hkv + g] = src_ks[static_cast<int64_t>(src) * Hkv + g];
+      dst_vs[static_cast<int64_t>(dst) * Hkv + g] = src_vs[static_cast<int64_t>(src) * Hkv + g];
     }
   }
 }
@@ -230,12 +232,22 @@ hipError_t launch_kv_append_i8(const void* k_new, const void* v_new, bool bf16_n
 hipError_t launch_copy_blocks(void* k_cache, void* v_cache, float* k_scale, float* v_scale,
                               const int32_t* pairs, int32_t n, int32_t Hkv, int32_t D,
                               int32_t NB, int32_t elem_bytes, hipStream_t stream) {
+  return launch_copy_tiles(k_cache, v_cache, k_scale, v_scale, NB, k_cache, v_cache, k_scale,
+                           v_scale, NB, pairs, n, Hkv, D, elem_bytes, stream);
+}
+
+hipError_t launch_copy_tiles(const void* src_k, const void* src_v, const float* src_ks,
+                             const float* src_vs, int32_t src_blocks, void* dst_k, void* dst_v,
+                             float* dst_ks, float* dst_vs, int32_t dst_blocks,
+                             const int32_t* pairs, int32_t n, int32_t Hkv, int32_t D,
+                             int32_t elem_bytes, hipStream_t stream) {
   if (n == 0) return hipSuccess;
   const int64_t tile_bytes = static_cast<int64_t>(Hkv) * kBlockSize * D * elem_bytes;
   const int32_t chunks = static_cast<int32_t>(tile_bytes / 16);
-  hipLaunchKernelGGL(copy_blocks_kernel, dim3(n), dim3(256), 0, stream,
-                     static_cast<uint4*>(k_cache), static_cast<uint4*>(v_cache), k_scale, v_scale,
-                     pairs, chunks, Hkv, NB);
+  hipLaunchKernelGGL(copy_tiles_kernel, dim3(n), dim3(256), 0, stream,
+                     static_cast<const uint4*>(src_k), static_cast<const uint4*>(src_v), src_ks,
+                     src_vs, src_blocks, static_cast<uint4*>(dst_k), static_cast<uint4*>(dst_v),
+                     dst_ks, dst_vs, dst_blocks, pairs, chunks, Hkv);
   return hipGetLastError();
 }
 

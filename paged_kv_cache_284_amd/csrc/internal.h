@@ -71,6 +71,12 @@ hipError_t launch_kv_append_i8(const void* k_new, const void* v_new, bool bf16_n
                                const int64_t* slots, int8_t* k_cache, int8_t* v_cache,
                                float* k_scale, float* v_scale, int32_t B, int32_t Hkv, int32_t D,
                                int32_t NB, hipStream_t stream);
+// Whole-tile copies from one pool to another of the same layout (scales optional).
+hipError_t launch_copy_tiles(const void* src_k, const void* src_v, const float* src_ks,
+                             const float* src_vs, int32_t src_blocks, void* dst_k, void* dst_v,
+                             float* dst_ks, float* dst_vs, int32_t dst_blocks,
+                             const int32_t* pairs, int32_t n, int32_t Hkv, int32_t D,
+                             int32_t elem_bytes, hipStream_t stream);
 hipError_t launch_copy_blocks(void* k_cache, void* v_cache, float* k_scale, float* v_scale,
                               const int32_t* pairs, int32_t n, int32_t Hkv, int32_t D,
                               int32_t NB, int32_t elem_bytes, hipStream_t stream);
