@@ -518,15 +518,15 @@ def summarize_counters(d: str, copy_mib: int = 512) -> dict:
         "hbm_bytes_per_launch": int((mean(dec_f) * fs + mean(dec_w) * ws) * 1024),
         "kernel_sources_sha256": kernel_sources_hash(),
         "commands": [
-            "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_FETCH_SIZE -o dec -- "
+            "rocprofv3 --pmc FETCH_SIZE --output-format csv -d prof_out/pmc_FETCH_SIZE -o dec -- "
             "python3 -u bench.py --steps 3 --warmup 1 --no-cpu-baseline",
-            "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_WRITE_SIZE -o dec -- "
+            "rocprofv3 --pmc WRITE_SIZE --output-format csv -d prof_out/pmc_WRITE_SIZE -o dec -- "
             "python3 -u bench.py --steps 3 --warmup 1 --no-cpu-baseline",
-            "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_copy_FETCH_SIZE -o cp "
+            "rocprofv3 --pmc FETCH_SIZE --output-format csv -d prof_out/pmc_copy_FETCH_SIZE -o cp "
             f"-- python3 -u bench.py --copy-reference {copy_mib}",
-            "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_copy_WRITE_SIZE -o cp "
+            "rocprofv3 --pmc WRITE_SIZE --output-format csv -d prof_out/pmc_copy_WRITE_SIZE -o cp "
             f"-- python3 -u bench.py --copy-reference {copy_mib}",
-            "python3 bench.py --summarize-counters gpurun_out",
+            "python3 bench.py --summarize-counters prof_out",
         ],
     }
     return out
@@ -556,7 +556,7 @@ def main():
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the decode path shards by sequence or KV head with no "
-              "exchange, and this build runs and reports a single MI355X only.", file=sys.stderr)
+              "exchange, and it runs and reports a single MI355X only.", file=sys.stderr)
         sys.exit(2)
 
     import torch
