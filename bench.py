@@ -36,7 +36,7 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBPS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0   # dense MFMA bf16
 METRIC = "paged decode attn: tokens/s + achieved HBM GB/s (% of MI355X peak)"
-KV_BYTES = {"f32": 4, "bf16": 2, "i8": 1}
+KV_BYTES = {"f32": 4, "bf16": 2, "i8": 1, "i4": 0.5}
 
 
 def algorithmic_bytes(w, lens) -> int:
@@ -44,8 +44,8 @@ def algorithmic_bytes(w, lens) -> int:
     every touched (block, KV head) tile, q, out, the table entries in use and the lengths."""
     lens = np.asarray(lens, np.int64)
     blocks = (lens + w.bs - 1) // w.bs
-    kv = int(lens.sum()) * w.Hkv * w.D * 2 * KV_BYTES[w.kv_dtype]
-    scales = int(blocks.sum()) * w.Hkv * 2 * 4 if w.kv_dtype == "i8" else 0
+    kv = int(int(lens.sum()) * w.Hkv * w.D * 2 * KV_BYTES[w.kv_dtype])
+    scales = int(blocks.sum()) * w.Hkv * 2 * 4 if w.kv_dtype in ("i8", "i4") else 0
     q = w.B * w.Hq * w.D * KV_BYTES[w.q_dtype]
     out = w.B * w.Hq * w.D * 4
     return kv + scales + q + out + int(blocks.sum()) * 4 + w.B * 4
@@ -99,6 +99,8 @@ def build_workload(name: str, total_steps: int):
         return inputs.long_context()
     if name == "int8_mha":
         return inputs.int8_mha()
+    if name == "int4_mha":
+        return inputs.int4_mha()
     if name == "tiny_fp32":
         return inputs.tiny_fp32()
     raise SystemExit(f"unknown workload {name}")
@@ -132,7 +134,7 @@ class StepRunner:
         self.k = up(pool["k"], w.kv_dtype)
         self.v = up(pool["v"], w.kv_dtype)
         self.ks = self.vs = None
-        if w.kv_dtype == "i8":
+        if w.kv_dtype in ("i8", "i4"):
             self.ks = up(pool["k_scale"], "f32")
             self.vs = up(pool["v_scale"], "f32")
         del pool
@@ -176,7 +178,8 @@ class StepRunner:
         self.hp = [[C.cast(pb.data_ptr() + o, C.POINTER(C.c_int64 if j == 0 else C.c_int32))
                     for j, o in enumerate(self.off)] for pb in self.pinned]
         self.raw = [[pb.data_ptr() + o for o in self.off] for pb in self.pinned]
-        self.kv_code = {"f32": pkv.PA_F32, "bf16": pkv.PA_BF16, "i8": pkv.PA_I8}[w.kv_dtype]
+        self.kv_code = {"f32": pkv.PA_F32, "bf16": pkv.PA_BF16, "i8": pkv.PA_I8,
+                        "i4": pkv.PA_I4}[w.kv_dtype]
         self.q_code = {"f32": pkv.PA_F32, "bf16": pkv.PA_BF16}[w.q_dtype]
         self.stream = torch.cuda.current_stream().cuda_stream
         self.ks_p = self.ks.data_ptr() if self.ks is not None else None
@@ -611,7 +614,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {"bf16": "bf16", "f32": "f32", "i8": "i8"}[w.kv_dtype],
+        "dtype": w.kv_dtype,
         "data": "synthetic (seeded N(0,1) K/V/q, shapes of the workload; no weights)",
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "head_dim": w.D,
                    "block_size": w.bs, "kv_dtype": w.kv_dtype, "q_dtype": w.q_dtype,

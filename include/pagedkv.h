@@ -14,7 +14,12 @@
  * Device layouts (row-major, all owned by the caller):
  *   k_cache   [NB][Hkv][bs][D]   token-major inside each (block, KV head) tile
  *   v_cache   [NB][Hkv][D][bs]   dim-major inside each (block, KV head) tile
- *   k_scale, v_scale [NB][Hkv] fp32, int8 caches only (value = code * scale)
+ *   k_scale, v_scale [NB][Hkv] fp32, quantised caches only (value = code * scale)
+ *   PA_I4 caches pack two codes per byte: K [NB][Hkv][bs][D/2], V [NB][Hkv][D][bs/2] bytes;
+ *     every 4-byte group holds 8 consecutive elements of its row (dims for K, tokens for V):
+ *     elements 0..3 in the low nibbles of bytes 0..3, elements 4..7 in the high nibbles, each
+ *     nibble code + 8, codes in [-7, 7] ([Walkthrough] "Step 1": bytes per element set the
+ *     cache size; INT4 halves INT8 again)
  *   q, out    [B][Hq][D]; out is always fp32
  *   block_tables [B][max_blocks] int32, unused entries may hold anything (e.g. -1)
  *   seq_lens  [B] int32
@@ -57,7 +62,7 @@ enum pa_status {
   PA_ERR_STATE = -5        /* allocator: unknown or released sequence id */
 };
 
-enum pa_dtype { PA_F32 = 0, PA_BF16 = 1, PA_I8 = 2 };
+enum pa_dtype { PA_F32 = 0, PA_BF16 = 1, PA_I8 = 2, PA_I4 = 3 };
 
 /* Static text for a status code. */
 const char* pa_status_string(int status);
@@ -226,9 +231,17 @@ int pa_kv_append_int8(const void* k_new, const void* v_new, int32_t new_dtype,
                       float* k_scale, float* v_scale, int32_t B, int32_t Hkv, int32_t D,
                       int32_t bs, int32_t NB, void* stream);
 
+/* pa_kv_append_int8 for a packed int4 cache (layout above): the same rule with 7 in place of
+ * 127 -- scale = max|x| / 7 grown token by token, codes clamp(rint(x / scale), -7, 7), earlier
+ * codes re-rounded by old/new when the scale grows.  k_cache, v_cache: the packed bytes. */
+int pa_kv_append_int4(const void* k_new, const void* v_new, int32_t new_dtype,
+                      const int64_t* slot_mapping, uint8_t* k_cache, uint8_t* v_cache,
+                      float* k_scale, float* v_scale, int32_t B, int32_t Hkv, int32_t D,
+                      int32_t bs, int32_t NB, void* stream);
+
 /* Copy-on-write block copies ([Serving] "Sharing comes for free"; [Walkthrough] "Step 8").
  * pairs: device-readable [n][2] int32 (src, dst).  Copies the whole K and V tile of block src over block
- * dst, and for PA_I8 also both scales (k_scale, v_scale must then be non-NULL).  Destinations
+ * dst, and for PA_I8 / PA_I4 also both scales (k_scale, v_scale must then be non-NULL).  Destinations
  * must be distinct and no destination may be another pair's source (the allocator never
  * produces either).  n == 0 enqueues nothing. */
 int pa_copy_blocks(void* k_cache, void* v_cache, float* k_scale, float* v_scale,
@@ -238,7 +251,7 @@ int pa_copy_blocks(void* k_cache, void* v_cache, float* k_scale, float* v_scale,
 /* Copy whole blocks between two pools of the same layout -- the device pool and a host swap
  * pool (pinned host memory, device-readable and -writable) for preemption by swapping, or any
  * two device pools: for i < n, block pairs[i][1] of the destination := block pairs[i][0] of the
- * source (K, V, and for PA_I8 both scales, which must then all be non-NULL).  One launch for
+ * source (K, V, and for PA_I8 / PA_I4 both scales, which must then all be non-NULL).  One launch for
  * the whole batch.  Pairs are device-readable int32 [n][2]; destination blocks must be
  * distinct; entries outside [0, src_blocks) or [0, dst_blocks) are skipped. */
 int pa_swap_blocks(const void* src_k, const void* src_v, const float* src_k_scale,
@@ -278,7 +291,9 @@ size_t pa_decode_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
  *     out[b][h] = sum_t softmax_t(scale * <q[b][h], K_t>) V_t,  t < seq_lens[b],
  * token t at block_tables[b][t/bs], offset t%bs; int8 elements are code * scale of their
  * (block, KV head).  seq_lens[b] == 0 gives out[b] = 0.
- *   q_dtype:  PA_F32 or PA_BF16.  kv_dtype: PA_F32, PA_BF16 or PA_I8 (then k_scale/v_scale).
+ *   q_dtype:  PA_F32 or PA_BF16.  kv_dtype: PA_F32, PA_BF16, PA_I8 or PA_I4 (then
+ *   k_scale/v_scale; PA_I4 needs a PA_BF16 q and Hq/Hkv in {1, 2, 4, 8, 16}, else
+ *   PA_ERR_UNSUPPORTED).
  *   Hq % Hkv == 0, Hq/Hkv <= 16, D in {64, 128}, bs == 16.
  *   max_seq_len: host bound on every seq_lens[b], 0 <= max_seq_len <= max_blocks*bs.
  *   partition_tokens: 0 = balanced schedule: the block pairs of all (sequence, KV head)

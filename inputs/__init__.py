@@ -35,7 +35,7 @@ import numpy as np
 
 SEED_ROOT = 284
 
-KV_F32, KV_BF16, KV_I8 = "f32", "bf16", "i8"
+KV_F32, KV_BF16, KV_I8, KV_I4 = "f32", "bf16", "i8", "i4"
 
 
 # --------------------------------------------------------------------------------------------
@@ -159,6 +159,14 @@ def shared_prefix_batch(B: int = 256, group: int = 8, prefix_tokens: int = 1024,
                     append=True, steps=steps, group=group, prefix_tokens=prefix_tokens)
 
 
+def int4_mha(B: int = 32, lo: int = 1, hi: int = 2048, Hq: int = 40, cid: int = 6,
+             name: str = "int4_mha") -> Workload:
+    """The int8_mha layer shape with a packed int4 cache (half a byte per element)."""
+    w = int8_mha(B=B, lo=lo, hi=hi, Hq=Hq, cid=cid, name=name)
+    w.kv_dtype = KV_I4
+    return w
+
+
 def int8_mha(B: int = 32, lo: int = 1, hi: int = 2048, Hq: int = 40, cid: int = 5,
              name: str = "int8_mha") -> Workload:
     """LLaMA-13B-like MHA layer (40/40 heads, D=128) with an int8 cache and fp32 scales."""
@@ -174,6 +182,7 @@ FULL = {
     "long_context": long_context,
     "shared_prefix_batch": shared_prefix_batch,
     "int8_mha": int8_mha,
+    "int4_mha": int4_mha,
 }
 
 
@@ -191,6 +200,8 @@ def small(name: str) -> Workload:
                                    lo=1, hi=400, steps=4, cid=14, name="shared_prefix_small")
     if name == "int8_mha":
         return int8_mha(B=6, lo=1, hi=700, cid=15, name="int8_mha_small")
+    if name == "int4_mha":
+        return int4_mha(B=6, lo=1, hi=700, cid=16, name="int4_mha_small")
     raise KeyError(name)
 
 
@@ -299,19 +310,35 @@ def pool_f32(w: Workload) -> Tuple[np.ndarray, np.ndarray]:
     return k, v
 
 
-def quantize_int8_pool(x: np.ndarray, tile_axes=(2, 3)) -> Tuple[np.ndarray, np.ndarray]:
-    """Symmetric absmax int8 codes with one fp32 scale per (block, head) tile.
+def quantize_int8_pool(x: np.ndarray, tile_axes=(2, 3), qmax: int = 127
+                       ) -> Tuple[np.ndarray, np.ndarray]:
+    """Symmetric absmax codes with one fp32 scale per (block, head) tile.
 
-    scale = absmax / 127 in fp32 (1.0 for an all-zero tile); code = clamp(rint(x / scale),
-    -127, 127) with fp32 division and round-half-to-even.  The absmax runs over every slot of
-    the physical tile.  Returns (codes int8 same shape as x, scales fp32 [NB][Hkv]).
+    scale = absmax / qmax in fp32 (1.0 for an all-zero tile); code = clamp(rint(x / scale),
+    -qmax, qmax) with fp32 division and round-half-to-even.  The absmax runs over every slot of
+    the physical tile.  qmax = 127 gives int8 codes, 7 the int4 codes.  Returns (codes int8 same
+    shape as x, scales fp32 [NB][Hkv]).
     """
     x = np.asarray(x, np.float32)
     amax = np.max(np.abs(x), axis=tile_axes).astype(np.float32)
-    scale = np.where(amax > 0, amax / np.float32(127.0), np.float32(1.0)).astype(np.float32)
+    scale = np.where(amax > 0, amax / np.float32(qmax), np.float32(1.0)).astype(np.float32)
     s = np.expand_dims(scale, tile_axes)
-    codes = np.clip(np.rint(x / s), -127, 127).astype(np.int8)
+    codes = np.clip(np.rint(x / s), -qmax, qmax).astype(np.int8)
     return codes, scale
+
+
+def pack_int4(codes: np.ndarray) -> np.ndarray:
+    """Device bytes of int4 codes in [-7, 7] along the last axis (n elements -> n/2 bytes):
+    byte 4m + j holds element 8m + j in its low nibble and element 8m + j + 4 in its high
+    nibble, each nibble being code + 8.  Applied to a K pool [NB][Hkv][bs][D] (rows of dims) or
+    a V pool [NB][Hkv][D][bs] (rows of tokens)."""
+    c = np.asarray(codes, np.int16) + 8
+    n = c.shape[-1]
+    out = np.zeros(c.shape[:-1] + (n // 2,), np.uint8)
+    for m in range(n // 8):
+        for j in range(4):
+            out[..., 4 * m + j] = (c[..., 8 * m + j] | (c[..., 8 * m + j + 4] << 4)).astype(np.uint8)
+    return out
 
 
 def pool(w: Workload) -> dict:
@@ -321,6 +348,10 @@ def pool(w: Workload) -> dict:
         kq, ks = quantize_int8_pool(k)
         vq, vs = quantize_int8_pool(v)
         return {"k": kq, "v": vq, "k_scale": ks, "v_scale": vs}
+    if w.kv_dtype == KV_I4:
+        kq, ks = quantize_int8_pool(k, qmax=7)
+        vq, vs = quantize_int8_pool(v, qmax=7)
+        return {"k": pack_int4(kq), "v": pack_int4(vq), "k_scale": ks, "v_scale": vs}
     return {"k": _cast(k, w.kv_dtype), "v": _cast(v, w.kv_dtype)}
 
 

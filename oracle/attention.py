@@ -19,7 +19,8 @@ which query heads share a KV head, contiguous groups are the plain reading).
 Physical layout (the pages fix none; this is the layout both sides use):
     K pool [NB][Hkv][bs][D], V pool [NB][Hkv][D][bs], int8 scales [NB][Hkv] (K and V apart).
 An int8 element dequantises to float64(code) * float64(scale of its (block, KV head)); the
-product of an 8-bit integer and a 24-bit significand is exact in float64.
+product of an 8-bit integer and a 24-bit significand is exact in float64.  int4 caches hold
+packed nibbles (layout in oracle.int4) and dequantise the same way.
 
 An empty context (L = 0) has no keys; its output is defined as zero.
 """
@@ -51,6 +52,13 @@ def gather_sequence(k_pool, v_pool, kv_dtype, k_scale, v_scale, table, L, g, bs)
     t = np.arange(L)
     blk = np.asarray(table)[t // bs].astype(np.int64)   # physical block of each token
     off = t % bs                                        # slot inside that block
+    if kv_dtype == "i4":                                # packed nibbles (oracle.int4)
+        from oracle import int4
+        K = int4.k_codes(k_pool, blk, g, off).astype(np.float64)
+        V = int4.v_codes(v_pool, blk, g, off).astype(np.float64)
+        K = K * np.asarray(k_scale, np.float32)[blk, g].astype(np.float64)[:, None]
+        V = V * np.asarray(v_scale, np.float32)[blk, g].astype(np.float64)[:, None]
+        return K, V
     K = to_f64(k_pool[blk, g, off, :], kv_dtype)        # [L][D]
     V = to_f64(v_pool[blk, g, :, off], kv_dtype)        # [L][D]
     if kv_dtype == "i8":

@@ -46,6 +46,17 @@ def copy_blocks(k_pool, v_pool, pairs, k_scale=None, v_scale=None):
     return k_out, v_out, ks, vs
 
 
+def append_int4(k_pool, v_pool, k_scale, v_scale, k_new, v_new, slots, bs):
+    """The quantising append of append_int8 with 4-bit codes: 7 in place of 127 (scale =
+    max|x| / 7, codes in [-7, 7]), on packed pools (layout in oracle.int4).  Returns copies of
+    (k_pool, v_pool, k_scale, v_scale)."""
+    from oracle import int4
+    kc, vc = int4.unpack_pool(k_pool, v_pool)
+    kc, vc, ks, vs = _append_quant(kc, vc, k_scale, v_scale, k_new, v_new, slots, bs, 7)
+    kp, vp = int4.pack_pool(kc, vc)
+    return kp, vp, ks, vs
+
+
 def append_int8(k_codes, v_codes, k_scale, v_scale, k_new, v_new, slots, bs):
     """Quantising append into an int8 cache (the write side of a quantised cache, "LLM serving
     (vLLM, quantized inference): Visual walkthrough": KV kept as int8 with a scale per block).
@@ -65,9 +76,15 @@ def append_int8(k_codes, v_codes, k_scale, v_scale, k_new, v_new, slots, bs):
     whole block's valid slots); a block with only zeros so far has scale 0 (it dequantises to
     zeros).  Earlier tokens' codes are re-rounded from their codes: the originals are gone.
     """
+    return _append_quant(k_codes, v_codes, k_scale, v_scale, k_new, v_new, slots, bs, 127)
+
+
+def _append_quant(k_codes, v_codes, k_scale, v_scale, k_new, v_new, slots, bs, qmax):
+    """append_int8's rule with codes in [-qmax, qmax] (scale = max|x| / qmax)."""
     kc, vc = k_codes.copy(), v_codes.copy()
     ks, vs = k_scale.copy(), v_scale.copy()
     f32 = np.float32
+    qm = f32(qmax)
     k_new = np.asarray(k_new, f32)
     v_new = np.asarray(v_new, f32)
     Hkv = kc.shape[1]
@@ -78,7 +95,7 @@ def append_int8(k_codes, v_codes, k_scale, v_scale, k_new, v_new, slots, bs):
         for g in range(Hkv):
             for x, codes, scales, token_major in ((k_new[b, g], kc, ks, True),
                                                   (v_new[b, g], vc, vs, False)):
-                cand = f32(np.max(np.abs(x))) / f32(127.0)
+                cand = f32(np.max(np.abs(x))) / qm
                 if off == 0:
                     scale = cand
                 else:
@@ -88,14 +105,14 @@ def append_int8(k_codes, v_codes, k_scale, v_scale, k_new, v_new, slots, bs):
                         r = f32(old) / f32(cand)
                         tile = codes[blk, g]
                         prev = tile[:off, :] if token_major else tile[:, :off]
-                        new_prev = np.clip(np.rint(prev.astype(f32) * r), -127, 127)
+                        new_prev = np.clip(np.rint(prev.astype(f32) * r), -qm, qm)
                         if token_major:
                             tile[:off, :] = new_prev.astype(np.int8)
                         else:
                             tile[:, :off] = new_prev.astype(np.int8)
                         scale = cand
                 if scale > 0:
-                    q = np.clip(np.rint(x / f32(scale)), -127, 127).astype(np.int8)
+                    q = np.clip(np.rint(x / f32(scale)), -qm, qm).astype(np.int8)
                 else:
                     q = np.zeros_like(x, dtype=np.int8)
                 if token_major:

@@ -27,7 +27,7 @@ LIB_PATH = os.path.join(_HERE, "libpagedkv.so")
 
 PA_OK, PA_ERR_INVALID, PA_ERR_OOM, PA_ERR_DEVICE, PA_ERR_UNSUPPORTED, PA_ERR_STATE = \
     0, -1, -2, -3, -4, -5
-PA_F32, PA_BF16, PA_I8 = 0, 1, 2
+PA_F32, PA_BF16, PA_I8, PA_I4 = 0, 1, 2, 3
 BLOCK_SIZE = 16
 
 _i32, _i64, _sz, _vp, _f32 = C.c_int32, C.c_int64, C.c_size_t, C.c_void_p, C.c_float
@@ -64,6 +64,8 @@ _SIGNATURES = {
     "pa_block_hash": (C.c_int, [_vp, _i32, C.POINTER(C.c_uint64), _pi32]),
     "pa_kv_append": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
     "pa_kv_append_int8": (C.c_int, [_vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
+                                    _i32, _i32, _vp]),
+    "pa_kv_append_int4": (C.c_int, [_vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
                                     _i32, _i32, _vp]),
     "pa_copy_blocks": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                                  _vp]),
@@ -331,8 +333,9 @@ def _torch():
 
 
 def _dtype_code(t) -> int:
+    """Element type code of a tensor: uint8 caches hold packed int4 codes (two per byte)."""
     torch = _torch()
-    m = {torch.float32: PA_F32, torch.bfloat16: PA_BF16, torch.int8: PA_I8}
+    m = {torch.float32: PA_F32, torch.bfloat16: PA_BF16, torch.int8: PA_I8, torch.uint8: PA_I4}
     if t.dtype not in m:
         raise TypeError(f"unsupported dtype {t.dtype}")
     return m[t.dtype]
@@ -409,15 +412,49 @@ def kv_append_int8(k_new, v_new, slot_mapping, k_cache, v_cache, k_scale, v_scal
                                    _stream(stream)), "pa_kv_append_int8")
 
 
+def cache_geometry(k_cache, v_cache):
+    """(NB, Hkv, bs, D) of a K/V pool pair, checking that the layouts agree; packed int4 pools
+    (uint8) hold K [NB][Hkv][bs][D/2] and V [NB][Hkv][D][bs/2]."""
+    NB, Hkv, bs, last = k_cache.shape
+    packed = k_cache.dtype == _torch().uint8
+    D = 2 * last if packed else last
+    want_v = (NB, Hkv, D, bs // 2 if packed else bs)
+    if tuple(v_cache.shape) != want_v or v_cache.dtype != k_cache.dtype:
+        raise ValueError(f"v_cache must be {want_v} of {k_cache.dtype}")
+    return NB, Hkv, bs, D
+
+
+def kv_append_int4(k_new, v_new, slot_mapping, k_cache, v_cache, k_scale, v_scale,
+                   stream=None) -> None:
+    """Quantising append into a packed int4 cache (uint8 pools): k_new/v_new [B][Hkv][D] bf16
+    or fp32."""
+    torch = _torch()
+    if k_cache.dtype != torch.uint8:
+        raise TypeError("int4 caches are uint8 (two codes per byte)")
+    NB, Hkv, bs, D = cache_geometry(k_cache, v_cache)
+    B = k_new.shape[0]
+    if tuple(k_new.shape) != (B, Hkv, D) or tuple(v_new.shape) != (B, Hkv, D):
+        raise ValueError("k_new/v_new must be [B][Hkv][D]")
+    if tuple(k_scale.shape) != (NB, Hkv) or k_new.dtype != v_new.dtype:
+        raise ValueError("scales must be [NB][Hkv]; k_new and v_new share a dtype")
+    _check(lib().pa_kv_append_int4(_dev(k_new, "k_new"), _dev(v_new, "v_new"),
+                                   _dtype_code(k_new),
+                                   _readable(slot_mapping, "slot_mapping", torch.int64),
+                                   _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+                                   _dev(k_scale, "k_scale", torch.float32),
+                                   _dev(v_scale, "v_scale", torch.float32), B, Hkv, D, bs, NB,
+                                   _stream(stream)), "pa_kv_append_int4")
+
+
 def swap_blocks(src_k, src_v, dst_k, dst_v, pairs, src_scales=(None, None),
                 dst_scales=(None, None), stream=None) -> None:
     """Copy whole blocks between two pools of one layout (device and pinned host swap pool):
     dst block pairs[i][1] := src block pairs[i][0]."""
     torch = _torch()
-    NBs, Hkv, bs, D = src_k.shape
+    NBs, Hkv, bs, D = cache_geometry(src_k, src_v)
     NBd = dst_k.shape[0]
     n = pairs.shape[0]
-    if tuple(dst_k.shape[1:]) != (Hkv, bs, D) or src_k.dtype != dst_k.dtype:
+    if tuple(dst_k.shape[1:]) != tuple(src_k.shape[1:]) or src_k.dtype != dst_k.dtype:
         raise ValueError("pools must share a layout and dtype")
     for t, nm in ((src_k, "src_k"), (src_v, "src_v"), (dst_k, "dst_k"), (dst_v, "dst_v")):
         _readable(t, nm)
@@ -432,7 +469,7 @@ def swap_blocks(src_k, src_v, dst_k, dst_v, pairs, src_scales=(None, None),
 def copy_blocks(k_cache, v_cache, pairs, k_scale=None, v_scale=None, stream=None) -> None:
     """Copy whole blocks (K, V and int8 scales) for each (src, dst) row of pairs int32 [n][2]."""
     torch = _torch()
-    NB, Hkv, bs, D = k_cache.shape
+    NB, Hkv, bs, D = cache_geometry(k_cache, v_cache)
     n = pairs.shape[0]
     if n and tuple(pairs.shape) != (n, 2):
         raise ValueError("pairs must be [n][2]")
@@ -495,8 +532,8 @@ def decode(q, k_cache, v_cache, block_tables, seq_lens, max_seq_len: int, scale:
     """Paged decode attention; returns out [B][Hq][D] float32."""
     torch = _torch()
     B, Hq, D = q.shape
-    NB, Hkv, bs, Dk = k_cache.shape
-    if Dk != D or tuple(v_cache.shape) != (NB, Hkv, D, bs):
+    NB, Hkv, bs, Dk = cache_geometry(k_cache, v_cache)
+    if Dk != D:
         raise ValueError("cache shapes do not match q")
     if block_tables.dim() != 2 or block_tables.shape[0] != B or tuple(seq_lens.shape) != (B,):
         raise ValueError("block_tables must be [B][max_blocks] and seq_lens [B]")

@@ -9,13 +9,22 @@
 
 namespace {
 
-int elem_bytes(int32_t dtype) {
+int elem_bytes(int32_t dtype) {  // whole bytes per element (0: none, or not a byte type)
   switch (dtype) {
     case PA_F32: return 4;
     case PA_BF16: return 2;
     case PA_I8: return 1;
     default: return 0;
   }
+}
+
+bool known_kv(int32_t dtype) { return elem_bytes(dtype) != 0 || dtype == PA_I4; }
+bool quantised(int32_t dtype) { return dtype == PA_I8 || dtype == PA_I4; }
+
+// Bytes of one block of K (or of V): Hkv tiles of bs x D elements.
+int64_t block_bytes(int32_t dtype, int32_t Hkv, int32_t D) {
+  const int64_t elems = static_cast<int64_t>(Hkv) * pa::kBlockSize * D;
+  return dtype == PA_I4 ? elems / 2 : elems * elem_bytes(dtype);
 }
 
 int status_of(hipError_t e) {
@@ -50,7 +59,7 @@ int pa_kv_append(const void* k_new, const void* v_new, const int64_t* slot_mappi
   if (B < 0 || Hkv < 1 || NB < 1 || (D != 64 && D != 128)) return PA_ERR_INVALID;
   if (bs != pa::kBlockSize) return PA_ERR_UNSUPPORTED;
   if (kv_dtype != PA_F32 && kv_dtype != PA_BF16) {
-    return kv_dtype == PA_I8 ? PA_ERR_UNSUPPORTED : PA_ERR_INVALID;
+    return quantised(kv_dtype) ? PA_ERR_UNSUPPORTED : PA_ERR_INVALID;
   }
   if (B == 0) return PA_OK;
   if (!k_new || !v_new || !slot_mapping || !k_cache || !v_cache) return PA_ERR_INVALID;
@@ -74,6 +83,21 @@ int pa_kv_append_int8(const void* k_new, const void* v_new, int32_t new_dtype,
                                            static_cast<hipStream_t>(stream)));
 }
 
+int pa_kv_append_int4(const void* k_new, const void* v_new, int32_t new_dtype,
+                      const int64_t* slot_mapping, uint8_t* k_cache, uint8_t* v_cache,
+                      float* k_scale, float* v_scale, int32_t B, int32_t Hkv, int32_t D,
+                      int32_t bs, int32_t NB, void* stream) {
+  if (B < 0 || Hkv < 1 || NB < 1 || (D != 64 && D != 128)) return PA_ERR_INVALID;
+  if (bs != pa::kBlockSize) return PA_ERR_UNSUPPORTED;
+  if (new_dtype != PA_F32 && new_dtype != PA_BF16) return PA_ERR_INVALID;
+  if (B == 0) return PA_OK;
+  if (!k_new || !v_new || !slot_mapping || !k_cache || !v_cache || !k_scale || !v_scale)
+    return PA_ERR_INVALID;
+  return status_of(pa::launch_kv_append_i4(k_new, v_new, new_dtype == PA_BF16, slot_mapping,
+                                           k_cache, v_cache, k_scale, v_scale, B, Hkv, D, NB,
+                                           static_cast<hipStream_t>(stream)));
+}
+
 int pa_append_step(const void* k_new, const void* v_new, const int64_t* slot_mapping,
                    const int32_t* table_index, const int32_t* seq_lens_in, int32_t* seq_lens_out,
                    void* k_cache, void* v_cache, int32_t* block_tables, int32_t max_blocks,
@@ -83,7 +107,7 @@ int pa_append_step(const void* k_new, const void* v_new, const int64_t* slot_map
     return PA_ERR_INVALID;
   if (bs != pa::kBlockSize) return PA_ERR_UNSUPPORTED;
   if (kv_dtype != PA_F32 && kv_dtype != PA_BF16) {
-    return kv_dtype == PA_I8 ? PA_ERR_UNSUPPORTED : PA_ERR_INVALID;
+    return quantised(kv_dtype) ? PA_ERR_UNSUPPORTED : PA_ERR_INVALID;
   }
   if (B == 0) return PA_OK;
   if (!k_new || !v_new || !slot_mapping || !k_cache || !v_cache) return PA_ERR_INVALID;
@@ -100,14 +124,14 @@ int pa_copy_blocks(void* k_cache, void* v_cache, float* k_scale, float* v_scale,
                    int32_t NB, int32_t kv_dtype, void* stream) {
   if (n < 0 || Hkv < 1 || NB < 1 || (D != 64 && D != 128)) return PA_ERR_INVALID;
   if (bs != pa::kBlockSize) return PA_ERR_UNSUPPORTED;
-  const int eb = elem_bytes(kv_dtype);
-  if (eb == 0) return PA_ERR_INVALID;
+  if (!known_kv(kv_dtype)) return PA_ERR_INVALID;
   if (n == 0) return PA_OK;
   if (!k_cache || !v_cache || !pairs) return PA_ERR_INVALID;
-  if (kv_dtype == PA_I8 && (!k_scale || !v_scale)) return PA_ERR_INVALID;
-  if (kv_dtype != PA_I8) k_scale = v_scale = nullptr;
-  return status_of(pa::launch_copy_blocks(k_cache, v_cache, k_scale, v_scale, pairs, n, Hkv, D,
-                                          NB, eb, static_cast<hipStream_t>(stream)));
+  if (quantised(kv_dtype) && (!k_scale || !v_scale)) return PA_ERR_INVALID;
+  if (!quantised(kv_dtype)) k_scale = v_scale = nullptr;
+  return status_of(pa::launch_copy_blocks(k_cache, v_cache, k_scale, v_scale, pairs, n, Hkv,
+                                          NB, block_bytes(kv_dtype, Hkv, D),
+                                          static_cast<hipStream_t>(stream)));
 }
 
 int pa_swap_blocks(const void* src_k, const void* src_v, const float* src_k_scale,
@@ -118,11 +142,10 @@ int pa_swap_blocks(const void* src_k, const void* src_v, const float* src_k_scal
   if (n < 0 || Hkv < 1 || src_blocks < 1 || dst_blocks < 1 || (D != 64 && D != 128))
     return PA_ERR_INVALID;
   if (bs != pa::kBlockSize) return PA_ERR_UNSUPPORTED;
-  const int eb = elem_bytes(kv_dtype);
-  if (eb == 0) return PA_ERR_INVALID;
+  if (!known_kv(kv_dtype)) return PA_ERR_INVALID;
   if (n == 0) return PA_OK;
   if (!src_k || !src_v || !dst_k || !dst_v || !pairs) return PA_ERR_INVALID;
-  if (kv_dtype == PA_I8) {
+  if (quantised(kv_dtype)) {
     if (!src_k_scale || !src_v_scale || !dst_k_scale || !dst_v_scale) return PA_ERR_INVALID;
   } else {
     src_k_scale = src_v_scale = nullptr;
@@ -130,7 +153,7 @@ int pa_swap_blocks(const void* src_k, const void* src_v, const float* src_k_scal
   }
   return status_of(pa::launch_copy_tiles(src_k, src_v, src_k_scale, src_v_scale, src_blocks,
                                          dst_k, dst_v, dst_k_scale, dst_v_scale, dst_blocks,
-                                         pairs, n, Hkv, D, eb,
+                                         pairs, n, Hkv, block_bytes(kv_dtype, Hkv, D),
                                          static_cast<hipStream_t>(stream)));
 }
 
@@ -206,7 +229,7 @@ int pa_decode(float* out, const void* q, int32_t q_dtype, const void* k_cache,
   if (Hq / Hkv > 16) return PA_ERR_UNSUPPORTED;
   if (bs != pa::kBlockSize) return PA_ERR_UNSUPPORTED;
   if (q_dtype != PA_F32 && q_dtype != PA_BF16) return PA_ERR_INVALID;
-  if (elem_bytes(kv_dtype) == 0) return PA_ERR_INVALID;
+  if (!known_kv(kv_dtype)) return PA_ERR_INVALID;
   if (static_cast<int64_t>(max_seq_len) > static_cast<int64_t>(max_blocks) * bs)
     return PA_ERR_INVALID;
   if (partition_tokens != 0 &&
@@ -216,7 +239,7 @@ int pa_decode(float* out, const void* q, int32_t q_dtype, const void* k_cache,
   if (B == 0) return PA_OK;
   if (!out || !q || !k_cache || !v_cache || !seq_lens || (max_blocks > 0 && !block_tables))
     return PA_ERR_INVALID;
-  if (kv_dtype == PA_I8 && (!k_scale || !v_scale)) return PA_ERR_INVALID;
+  if (quantised(kv_dtype) && (!k_scale || !v_scale)) return PA_ERR_INVALID;
 
   pa::DecodeArgs a{};
   a.out = out;
@@ -243,7 +266,8 @@ int pa_decode(float* out, const void* q, int32_t q_dtype, const void* k_cache,
     return PA_ERR_INVALID;
 
   const int G = Hq / Hkv;
-  const bool mfma = q_dtype == PA_BF16 && (kv_dtype == PA_BF16 || kv_dtype == PA_I8) &&
+  const bool mfma = q_dtype == PA_BF16 &&
+                    (kv_dtype == PA_BF16 || kv_dtype == PA_I8 || kv_dtype == PA_I4) &&
                     (G == 1 || G == 2 || G == 4 || G == 8 || G == 16);
   const bool balanced = mfma && partition_tokens == 0 && B <= pa::kMaxBalancedBatch &&
                         G <= pa::kMaxBalancedGroup;
@@ -271,7 +295,8 @@ int pa_decode(float* out, const void* q, int32_t q_dtype, const void* k_cache,
     a.ws_o = reinterpret_cast<float*>(base + 2 * align256(rows * 4));
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = mfma ? pa::launch_decode_mfma(a, kv_dtype == PA_I8, s)
+  if (!mfma && kv_dtype == PA_I4) return PA_ERR_UNSUPPORTED;  // int4: matrix-core kernel only
+  hipError_t e = mfma ? pa::launch_decode_mfma(a, kv_dtype, s)
                       : pa::launch_decode_generic(a, q_dtype, kv_dtype, s);
   if (e != hipSuccess) return status_of(e);
   if (balanced) return PA_OK;
@@ -290,7 +315,7 @@ int pa_prefill(float* out, const void* q, int32_t q_dtype, const void* k_cache,
   if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16) return PA_ERR_UNSUPPORTED;
   if (bs != pa::kBlockSize) return PA_ERR_UNSUPPORTED;
   if (q_dtype != PA_BF16 || kv_dtype != PA_BF16) {
-    const bool known = (q_dtype == PA_F32 || q_dtype == PA_BF16) && elem_bytes(kv_dtype) != 0;
+    const bool known = (q_dtype == PA_F32 || q_dtype == PA_BF16) && known_kv(kv_dtype);
     return known ? PA_ERR_UNSUPPORTED : PA_ERR_INVALID;
   }
   if (static_cast<int64_t>(max_seq_len) > static_cast<int64_t>(max_blocks) * bs)

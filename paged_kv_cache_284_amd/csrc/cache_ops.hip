@@ -142,6 +142,121 @@ __global__ void __launch_bounds__(64) kv_append_i8_kernel(const TIn* __restrict_
   }
 }
 
+// Quantising append into a packed int4 cache: the int8 rule with 7 in place of 127, codes
+// stored as nibbles c + 8 (a 4-byte group holds 8 consecutive elements of a row: 0..3 in the
+// low nibbles, 4..7 in the high ones).  K rows are dims of one token: lane l owns byte l of the
+// row (two dims), so a token's row is written whole.  V rows are tokens of one dim: lane l owns
+// dims l, l + 64, and a token is one nibble, read-modified-written by its dim's lane.
+__device__ __forceinline__ int nibble_code(uint8_t byte, int hi) {
+  return static_cast<int>((byte >> (4 * hi)) & 0xf) - 8;
+}
+__device__ __forceinline__ uint8_t with_nibble(uint8_t byte, int hi, int code) {
+  const uint8_t u = static_cast<uint8_t>(code + 8) & 0xf;
+  return hi ? static_cast<uint8_t>((byte & 0x0f) | (u << 4)) : static_cast<uint8_t>((byte & 0xf0) | u);
+}
+__device__ __forceinline__ int quant7(float x, float scale) {
+  if (!(scale > 0.f)) return 0;
+  return static_cast<int>(fminf(fmaxf(__builtin_rintf(x / scale), -7.f), 7.f));
+}
+__device__ __forceinline__ int requant7(int code, float r) {
+  return static_cast<int>(fminf(fmaxf(__builtin_rintf(static_cast<float>(code) * r), -7.f), 7.f));
+}
+__device__ __forceinline__ float wave_absmax(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// New scale of a block for a token whose own scale would be `cand` (see the int8 kernel).
+__device__ __forceinline__ float next_scale(bool fresh, float old, float cand, bool* grew) {
+  *grew = !fresh && cand > old;
+  return (fresh || cand > old) ? cand : old;
+}
+
+template <typename TIn>
+__device__ void append_i4_k(const TIn* __restrict__ x, uint8_t* tile, float* scale_slot,
+                            float* scale_reg, bool fresh, int off, int D) {
+  const int lane = threadIdx.x;
+  const int row_bytes = D / 2;
+  const bool mine = lane < row_bytes;
+  const int e_lo = 8 * (lane / 4) + lane % 4, e_hi = e_lo + 4;  // the dims of byte `lane`
+  const float x_lo = mine ? widen<TIn>(x[e_lo]) : 0.f;
+  const float x_hi = mine ? widen<TIn>(x[e_hi]) : 0.f;
+  const float cand = wave_absmax(fmaxf(fabsf(x_lo), fabsf(x_hi))) / 7.f;
+  bool grew;
+  const float scale = next_scale(fresh, *scale_reg, cand, &grew);
+  if (grew && mine) {
+    const float r = *scale_reg / cand;
+    for (int row = 0; row < off; ++row) {
+      uint8_t* p = tile + row * row_bytes + lane;
+      const uint8_t b = *p;
+      *p = with_nibble(with_nibble(b, 0, requant7(nibble_code(b, 0), r)), 1,
+                       requant7(nibble_code(b, 1), r));
+    }
+  }
+  if (mine) {
+    tile[off * row_bytes + lane] =
+        with_nibble(with_nibble(0, 0, quant7(x_lo, scale)), 1, quant7(x_hi, scale));
+  }
+  *scale_reg = scale;
+  if (lane == 0) *scale_slot = scale;
+}
+
+template <typename TIn>
+__device__ void append_i4_v(const TIn* __restrict__ x, uint8_t* tile, float* scale_slot,
+                            float* scale_reg, bool fresh, int off, int D) {
+  const int lane = threadIdx.x;
+  constexpr int kRowBytes = kBlockSize / 2;
+  float amax = 0.f;
+  for (int d = lane; d < D; d += 64) amax = fmaxf(amax, fabsf(widen<TIn>(x[d])));
+  const float cand = wave_absmax(amax) / 7.f;
+  bool grew;
+  const float scale = next_scale(fresh, *scale_reg, cand, &grew);
+  auto at = [](int t) { return 4 * (t / 8) + t % 4; };  // byte of token t in a dim row
+  for (int d = lane; d < D; d += 64) {
+    uint8_t* row = tile + d * kRowBytes;
+    if (grew) {
+      const float r = *scale_reg / cand;
+      for (int t = 0; t < off; ++t) {
+        const int hi = (t % 8) / 4;
+        row[at(t)] = with_nibble(row[at(t)], hi, requant7(nibble_code(row[at(t)], hi), r));
+      }
+    }
+    const int hi = (off % 8) / 4;
+    row[at(off)] = with_nibble(row[at(off)], hi, quant7(widen<TIn>(x[d]), scale));
+  }
+  *scale_reg = scale;
+  if (lane == 0) *scale_slot = scale;
+}
+
+template <typename TIn>
+__global__ void __launch_bounds__(64) kv_append_i4_kernel(const TIn* __restrict__ k_new,
+                                                           const TIn* __restrict__ v_new,
+                                                           const int64_t* __restrict__ slots,
+                                                           uint8_t* k_cache, uint8_t* v_cache,
+                                                           float* k_scale, float* v_scale,
+                                                           int32_t B, int32_t Hkv, int32_t D,
+                                                           int32_t NB) {
+  const int i = blockIdx.x, g = blockIdx.y;
+  const int64_t cap = static_cast<int64_t>(NB) * kBlockSize;
+  auto block_of = [&](int64_t s) -> int64_t { return (s >= 0 && s < cap) ? s / kBlockSize : -1; };
+  const int64_t blk = block_of(slots[i]);
+  if (blk < 0) return;
+  if (i > 0 && block_of(slots[i - 1]) == blk) return;  // not the first entry of its run
+  const int64_t tile = blk * Hkv + g;
+  uint8_t* kt = k_cache + tile * kBlockSize * (D / 2);
+  uint8_t* vt = v_cache + tile * kBlockSize * (D / 2);
+  float ks_reg = k_scale[tile], vs_reg = v_scale[tile];
+  for (int j = i; j < B; ++j) {
+    const int64_t sj = slots[j];
+    if (block_of(sj) != blk) break;
+    const int off = static_cast<int>(sj % kBlockSize);
+    const int64_t src = (static_cast<int64_t>(j) * Hkv + g) * D;
+    append_i4_k<TIn>(k_new + src, kt, k_scale + tile, &ks_reg, off == 0, off, D);
+    append_i4_v<TIn>(v_new + src, vt, v_scale + tile, &vs_reg, off == 0, off, D);
+  }
+}
+
 // One workgroup per pair; its threads stride over the 16-byte chunks of the K and V tiles.
 // Source and destination pools may be the same (copy-on-write) or different (swapping to and
 // from a host pool in pinned memory, which the kernel reads or writes over the bus).
@@ -229,21 +344,38 @@ hipError_t launch_kv_append_i8(const void* k_new, const void* v_new, bool bf16_n
   return hipGetLastError();
 }
 
+hipError_t launch_kv_append_i4(const void* k_new, const void* v_new, bool bf16_new,
+                               const int64_t* slots, uint8_t* k_cache, uint8_t* v_cache,
+                               float* k_scale, float* v_scale, int32_t B, int32_t Hkv, int32_t D,
+                               int32_t NB, hipStream_t stream) {
+  if (B == 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>(B), static_cast<unsigned>(Hkv));
+  if (bf16_new) {
+    hipLaunchKernelGGL(kv_append_i4_kernel<uint16_t>, grid, dim3(64), 0, stream,
+                       static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new),
+                       slots, k_cache, v_cache, k_scale, v_scale, B, Hkv, D, NB);
+  } else {
+    hipLaunchKernelGGL(kv_append_i4_kernel<float>, grid, dim3(64), 0, stream,
+                       static_cast<const float*>(k_new), static_cast<const float*>(v_new), slots,
+                       k_cache, v_cache, k_scale, v_scale, B, Hkv, D, NB);
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_copy_blocks(void* k_cache, void* v_cache, float* k_scale, float* v_scale,
-                              const int32_t* pairs, int32_t n, int32_t Hkv, int32_t D,
-                              int32_t NB, int32_t elem_bytes, hipStream_t stream) {
+                              const int32_t* pairs, int32_t n, int32_t Hkv, int32_t NB,
+                              int64_t block_bytes, hipStream_t stream) {
   return launch_copy_tiles(k_cache, v_cache, k_scale, v_scale, NB, k_cache, v_cache, k_scale,
-                           v_scale, NB, pairs, n, Hkv, D, elem_bytes, stream);
+                           v_scale, NB, pairs, n, Hkv, block_bytes, stream);
 }
 
 hipError_t launch_copy_tiles(const void* src_k, const void* src_v, const float* src_ks,
                              const float* src_vs, int32_t src_blocks, void* dst_k, void* dst_v,
                              float* dst_ks, float* dst_vs, int32_t dst_blocks,
-                             const int32_t* pairs, int32_t n, int32_t Hkv, int32_t D,
-                             int32_t elem_bytes, hipStream_t stream) {
+                             const int32_t* pairs, int32_t n, int32_t Hkv, int64_t block_bytes,
+                             hipStream_t stream) {
   if (n == 0) return hipSuccess;
-  const int64_t tile_bytes = static_cast<int64_t>(Hkv) * kBlockSize * D * elem_bytes;
-  const int32_t chunks = static_cast<int32_t>(tile_bytes / 16);
+  const int32_t chunks = static_cast<int32_t>(block_bytes / 16);
   hipLaunchKernelGGL(copy_tiles_kernel, dim3(n), dim3(256), 0, stream,
                      static_cast<const uint4*>(src_k), static_cast<const uint4*>(src_v), src_ks,
                      src_vs, src_blocks, static_cast<uint4*>(dst_k), static_cast<uint4*>(dst_v),

@@ -95,10 +95,46 @@ __device__ __forceinline__ f16x8 codes_to_f16(uint32_t x0, uint32_t x1) {
 }
 constexpr float kCodeOffset = 1152.f;  // codes_to_f16(c) = kCodeOffset + c
 
-template <int G, int D, bool kStream, bool kI8>
+// int4 cache: eight packed codes (elements 0..3 in the low nibbles of the four bytes, 4..7 in
+// the high nibbles, each nibble c + 8) -> eight fp16 values 1032 + c, in element order.  The
+// nibbles are split into bytes by a mask and a shift; the same byte permute as for int8 then
+// sets each under the exponent of 1024.
+__device__ __forceinline__ f16x8 nibbles_to_f16(uint32_t x) {
+  constexpr uint32_t kExp = 0x64646464u;
+  const uint32_t lo = x & 0x0f0f0f0fu, hi = (x >> 4) & 0x0f0f0f0fu;
+  u32x4 r;
+  r[0] = __builtin_amdgcn_perm(lo, kExp, 0x00050004u);  // elements 0, 1
+  r[1] = __builtin_amdgcn_perm(lo, kExp, 0x00070006u);  // 2, 3
+  r[2] = __builtin_amdgcn_perm(hi, kExp, 0x00050004u);  // 4, 5
+  r[3] = __builtin_amdgcn_perm(hi, kExp, 0x00070006u);  // 6, 7
+  return __builtin_bit_cast(f16x8, r);
+}
+constexpr float kNibbleOffset = 1032.f;  // nibbles_to_f16(c) = kNibbleOffset + c
+
+// int4 cache tiles: K [bs][D/2] bytes, V [D][bs/2] bytes; one 4-byte group holds the 8 dims a
+// lane feeds one k-step (K) or its 8 tokens of one dim (V).
+template <int D>
+struct PairRegsI4 {
+  static constexpr int kSteps = D / 32;
+  static constexpr int kTiles = D / 16;
+  uint32_t k1[kSteps];
+  uint32_t k2[kSteps];
+  uint32_t v[kTiles];
+  int32_t blk_a, blk_b;
+  float ks_a, ks_b, vs_a, vs_b;
+};
+
+// Cache element kinds of the kernel template.
+constexpr int kKvBf16 = 0, kKvI8 = 1, kKvI4 = 2;
+
+template <int G, int D, bool kStream, int kKV>
 __global__ void __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
 decode_mfma_kernel(DecodeArgs a) {
-  using Regs = std::conditional_t<kI8, PairRegsI8<D>, PairRegs<D>>;
+  constexpr bool kI4 = kKV == kKvI4;
+  constexpr bool kI8 = kKV == kKvI8 || kI4;  // a quantised cache (scales, offset codes)
+  constexpr float kOffset = kI4 ? kNibbleOffset : kCodeOffset;
+  using Regs = std::conditional_t<kI4, PairRegsI4<D>,
+                                  std::conditional_t<kI8, PairRegsI8<D>, PairRegs<D>>>;
   constexpr int kSteps = D / 32;
   constexpr int kTiles = D / 16;
 
@@ -153,9 +189,11 @@ decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
       for (int s = 0; s < kSteps; ++s) {
         if constexpr (kI8) {
-          // int8 cache: the score MFMA runs in fp16 (bf16 -> fp16 is exact in fp16's normal
-          // range), next to fp16 codes
-          const u32x4 raw = load16(q + 16 * (qg + 4 * (s / 2)) + 8 * (s % 2));
+          // quantised cache: the score MFMA runs in fp16 (bf16 -> fp16 is exact in fp16's
+          // normal range), next to fp16 codes.  int4: step s covers dims
+          // 8 kSteps qg + 8 s .. +8, the 4-byte group a lane loads for that step.
+          const u32x4 raw = kI4 ? load16(q + 8 * kSteps * qg + 8 * s)
+                                : load16(q + 16 * (qg + 4 * (s / 2)) + 8 * (s % 2));
           f32x8 f;
 #pragma unroll
           for (int c = 0; c < 4; ++c) {
@@ -190,7 +228,36 @@ decode_mfma_kernel(DecodeArgs a) {
       const int64_t tb = static_cast<int64_t>(bb < 0 ? 0 : bb) * Hkv + g;
       const int64_t tile_a = ta * (kBlockSize * D);
       const int64_t tile_b = tb * (kBlockSize * D);
-      if constexpr (kI8) {
+      if constexpr (kI4) {
+        R.ks_a = a.k_scale[ta];
+        R.ks_b = a.k_scale[tb];
+        R.vs_a = a.v_scale[ta];
+        R.vs_b = a.v_scale[tb];
+        const int64_t h_a = tile_a / 2, h_b = tile_b / 2;  // tiles of bs * D / 2 bytes
+        const uint8_t* k1 = kc8 + (tok1 < 16 ? h_a : h_b) + (tok1 % 16) * (D / 2) + 4 * kSteps * qg;
+        const uint8_t* k2 = kc8 + (tok2 < 16 ? h_a : h_b) + (tok2 % 16) * (D / 2) + 4 * kSteps * qg;
+        if constexpr (kSteps == 4) {
+          const u32x4 x1 = *reinterpret_cast<const u32x4*>(k1);
+          const u32x4 x2 = *reinterpret_cast<const u32x4*>(k2);
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            R.k1[c] = x1[c];
+            R.k2[c] = x2[c];
+          }
+        } else {
+          const u32x2 x1 = *reinterpret_cast<const u32x2*>(k1);
+          const u32x2 x2 = *reinterpret_cast<const u32x2*>(k2);
+#pragma unroll
+          for (int c = 0; c < 2; ++c) {
+            R.k1[c] = x1[c];
+            R.k2[c] = x2[c];
+          }
+        }
+        const uint8_t* v = vc8 + (vblk_sel ? h_b : h_a) + r * (kBlockSize / 2) + 4 * (qg % 2);
+#pragma unroll
+        for (int n = 0; n < kTiles; ++n)
+          R.v[n] = *reinterpret_cast<const uint32_t*>(v + 16 * n * (kBlockSize / 2));
+      } else if constexpr (kI8) {
         R.ks_a = a.k_scale[ta];
         R.ks_b = a.k_scale[tb];
         R.vs_a = a.v_scale[ta];
@@ -230,7 +297,14 @@ decode_mfma_kernel(DecodeArgs a) {
     auto compute_pair = [&](int i, Regs& R) {
       const int tok0 = i * kPair;
       f32x4 s1 = {0.f, 0.f, 0.f, 0.f}, s2 = {0.f, 0.f, 0.f, 0.f};
-      if constexpr (kI8) {
+      if constexpr (kI4) {
+#pragma unroll
+        for (int c = 0; c < kSteps; ++c) {
+          const f16x8 qc = __builtin_bit_cast(f16x8, qv[c]);
+          s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(nibbles_to_f16(R.k1[c]), qc, s1, 0, 0, 0);
+          s2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(nibbles_to_f16(R.k2[c]), qc, s2, 0, 0, 0);
+        }
+      } else if constexpr (kI8) {
 #pragma unroll
         for (int c = 0; c < kSteps / 2; ++c) {
           const f16x8 q0 = __builtin_bit_cast(f16x8, qv[2 * c]);
@@ -259,7 +333,7 @@ decode_mfma_kernel(DecodeArgs a) {
       if constexpr (kI8) {
         // score = k_scale * sum_d q_d c_d = k_scale * (sum_d q_d (1152 + c_d) - 1152 sum_d q_d)
         const float f = (vblk_sel ? R.ks_b : R.ks_a) * a.scale_log2;
-        const float off = kCodeOffset * qsum;
+        const float off = kOffset * qsum;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           sc[e] = (s1[e] - off) * f;
@@ -341,7 +415,12 @@ decode_mfma_kernel(DecodeArgs a) {
                                                    f16x8);
 #pragma unroll
         for (int n = 0; n < kTiles; ++n) {
-          const f16x8 vop = codes_to_f16(R.v[n][0], R.v[n][1]);
+          f16x8 vop;
+          if constexpr (kI4) {
+            vop = nibbles_to_f16(R.v[n]);
+          } else {
+            vop = codes_to_f16(R.v[n][0], R.v[n][1]);
+          }
           acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(p_hi, vop, acc[n], 0, 0, 0);
           acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(p_lo, vop, acc[n], 0, 0, 0);
         }
@@ -422,7 +501,7 @@ decode_mfma_kernel(DecodeArgs a) {
         const float cj = kI8 ? __shfl(c_tot, h % G, 64) : 0.f;
         if (h < G) {
 #pragma unroll
-          for (int n = 0; n < kTiles; ++n) o_s[w][slot][h][16 * n + r] = acc[n][j] - kCodeOffset * cj;
+          for (int n = 0; n < kTiles; ++n) o_s[w][slot][h][16 * n + r] = acc[n][j] - kOffset * cj;
         }
       }
     };
@@ -442,7 +521,7 @@ decode_mfma_kernel(DecodeArgs a) {
           const int64_t slot = part * G + h;
 #pragma unroll
           for (int n = 0; n < kTiles; ++n) {
-            const float o = lj > 0.f ? (acc[n][j] - kCodeOffset * cj) / lj : 0.f;
+            const float o = lj > 0.f ? (acc[n][j] - kOffset * cj) / lj : 0.f;
             if (dest == 0) {
               a.out[row * D + 16 * n + r] = o;
             } else {
@@ -686,17 +765,17 @@ __global__ void __launch_bounds__(256) streamk_reduce_kernel(DecodeArgs a) {
   }
 }
 
-template <int G, int D, bool kI8>
+template <int G, int D, int kKV>
 hipError_t launch_gd(const DecodeArgs& a, hipStream_t stream) {
   if (a.nw == 0 || G > kMaxBalancedGroup) {
     const dim3 grid(a.np_max, a.Hkv, a.B);
-    hipLaunchKernelGGL((decode_mfma_kernel<G, D, false, kI8>), grid, dim3(64 * kWaves), 0, stream,
+    hipLaunchKernelGGL((decode_mfma_kernel<G, D, false, kKV>), grid, dim3(64 * kWaves), 0, stream,
                        a);
     return hipGetLastError();
   }
   constexpr int Gb = G <= kMaxBalancedGroup ? G : kMaxBalancedGroup;  // never launched for G > 8
   const size_t lds = static_cast<size_t>(a.B + 1) * sizeof(int32_t);
-  hipLaunchKernelGGL((decode_mfma_kernel<Gb, D, true, kI8>), dim3(a.nw), dim3(64 * kWaves), lds,
+  hipLaunchKernelGGL((decode_mfma_kernel<Gb, D, true, kKV>), dim3(a.nw), dim3(64 * kWaves), lds,
                      stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -704,21 +783,21 @@ hipError_t launch_gd(const DecodeArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int G, bool kI8>
+template <int G, int kKV>
 hipError_t launch_g(const DecodeArgs& a, hipStream_t stream) {
-  if (a.D == 128) return launch_gd<G, 128, kI8>(a, stream);
-  if (a.D == 64) return launch_gd<G, 64, kI8>(a, stream);
+  if (a.D == 128) return launch_gd<G, 128, kKV>(a, stream);
+  if (a.D == 64) return launch_gd<G, 64, kKV>(a, stream);
   return hipErrorNotSupported;
 }
 
-template <bool kI8>
+template <int kKV>
 hipError_t launch_kv(const DecodeArgs& a, hipStream_t stream) {
   switch (a.Hq / a.Hkv) {
-    case 1: return launch_g<1, kI8>(a, stream);
-    case 2: return launch_g<2, kI8>(a, stream);
-    case 4: return launch_g<4, kI8>(a, stream);
-    case 8: return launch_g<8, kI8>(a, stream);
-    case 16: return launch_g<16, kI8>(a, stream);
+    case 1: return launch_g<1, kKV>(a, stream);
+    case 2: return launch_g<2, kKV>(a, stream);
+    case 4: return launch_g<4, kKV>(a, stream);
+    case 8: return launch_g<8, kKV>(a, stream);
+    case 16: return launch_g<16, kKV>(a, stream);
     default: return hipErrorNotSupported;
   }
 }
@@ -729,7 +808,7 @@ int mfma_workgroups_per_cu() {
   static int cached = 0;
   if (cached == 0) {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_mfma_kernel<4, 128, true, false>,
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_mfma_kernel<4, 128, true, kKvBf16>,
                                                      64 * kWaves, 1024) != hipSuccess ||
         n < 1)
       n = 1;
@@ -738,8 +817,10 @@ int mfma_workgroups_per_cu() {
   return cached;
 }
 
-hipError_t launch_decode_mfma(const DecodeArgs& a, bool int8_cache, hipStream_t stream) {
-  return int8_cache ? launch_kv<true>(a, stream) : launch_kv<false>(a, stream);
+hipError_t launch_decode_mfma(const DecodeArgs& a, int kv_dtype, hipStream_t stream) {
+  if (kv_dtype == PA_I8) return launch_kv<kKvI8>(a, stream);
+  if (kv_dtype == PA_I4) return launch_kv<kKvI4>(a, stream);
+  return launch_kv<kKvBf16>(a, stream);
 }
 
 }  // namespace pa

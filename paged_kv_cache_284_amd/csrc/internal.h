@@ -71,24 +71,30 @@ hipError_t launch_kv_append_i8(const void* k_new, const void* v_new, bool bf16_n
                                const int64_t* slots, int8_t* k_cache, int8_t* v_cache,
                                float* k_scale, float* v_scale, int32_t B, int32_t Hkv, int32_t D,
                                int32_t NB, hipStream_t stream);
-// Whole-tile copies from one pool to another of the same layout (scales optional).
+// Quantising append into a packed int4 cache; new tokens in bf16 (bf16_new) or fp32.
+hipError_t launch_kv_append_i4(const void* k_new, const void* v_new, bool bf16_new,
+                               const int64_t* slots, uint8_t* k_cache, uint8_t* v_cache,
+                               float* k_scale, float* v_scale, int32_t B, int32_t Hkv, int32_t D,
+                               int32_t NB, hipStream_t stream);
+// Whole-block copies from one pool to another of the same layout (scales optional);
+// block_bytes = bytes of one block of K (= of V), a multiple of 16.
 hipError_t launch_copy_tiles(const void* src_k, const void* src_v, const float* src_ks,
                              const float* src_vs, int32_t src_blocks, void* dst_k, void* dst_v,
                              float* dst_ks, float* dst_vs, int32_t dst_blocks,
-                             const int32_t* pairs, int32_t n, int32_t Hkv, int32_t D,
-                             int32_t elem_bytes, hipStream_t stream);
+                             const int32_t* pairs, int32_t n, int32_t Hkv, int64_t block_bytes,
+                             hipStream_t stream);
 hipError_t launch_copy_blocks(void* k_cache, void* v_cache, float* k_scale, float* v_scale,
-                              const int32_t* pairs, int32_t n, int32_t Hkv, int32_t D,
-                              int32_t NB, int32_t elem_bytes, hipStream_t stream);
+                              const int32_t* pairs, int32_t n, int32_t Hkv, int32_t NB,
+                              int64_t block_bytes, hipStream_t stream);
 hipError_t launch_update_tables(int32_t* tables, int32_t max_blocks, const int64_t* slots,
                                 const int32_t* table_index, int32_t B, hipStream_t stream);
 
 // Returns hipErrorNotSupported when no kernel of this family takes the combination.
 hipError_t launch_decode_generic(const DecodeArgs& a, int q_dtype, int kv_dtype,
                                  hipStream_t stream);
-// bf16 query; bf16 or int8 cache (int8: k_scale / v_scale set); D 64/128; group size 1, 2, 4,
-// 8 or 16.
-hipError_t launch_decode_mfma(const DecodeArgs& a, bool int8_cache, hipStream_t stream);
+// bf16 query; bf16, int8 or int4 cache (PA_BF16 / PA_I8 / PA_I4; the quantised ones with
+// k_scale / v_scale set); D 64/128; group size 1, 2, 4, 8 or 16.
+hipError_t launch_decode_mfma(const DecodeArgs& a, int kv_dtype, hipStream_t stream);
 hipError_t launch_splitk_reduce(const DecodeArgs& a, hipStream_t stream);
 // bf16 query and cache; D 64/128; group size 1, 2, 4, 8 or 16.
 hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t stream);

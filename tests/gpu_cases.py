@@ -19,8 +19,8 @@ import paged_kv_cache_284_amd as pkv
 from oracle import attention, cache_ops
 from oracle.allocator import PyAllocator, run_script
 
-TOL = {"f32": 1e-5, "bf16": 8e-3, "i8": 2e-2}
-TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16, "i8": torch.int8}
+TOL = {"f32": 1e-5, "bf16": 8e-3, "i8": 2e-2, "i4": 2e-2}
+TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16, "i8": torch.int8, "i4": torch.uint8}
 
 
 def say(msg: str) -> None:
@@ -50,6 +50,13 @@ def poison_unused(pool: dict, w, tables, lens) -> None:
             n = min(w.bs, int(L) - j * w.bs)
             used[row[j], :n] = True
     blk, slot = np.nonzero(~used)
+    if w.kv_dtype == "i4":
+        # packed nibbles: code -8 (nibble 0) is outside [-7, 7], so a read of it shows up
+        pool["k"][blk, :, slot, :] = 0
+        for b_, t in zip(blk.tolist(), slot.tolist()):   # slots t and t + 4 share a byte
+            keep = np.uint8(0x0F if (t % 8) // 4 == 1 else 0xF0)
+            pool["v"][b_, :, :, 4 * (t // 8) + t % 4] &= keep
+        return
     if w.kv_dtype == "i8":
         pv = inputs.POISON_I8
     elif w.kv_dtype == "bf16":
@@ -83,7 +90,7 @@ class Case:
         self.k = to_device(self.host["k"], dt)
         self.v = to_device(self.host["v"], dt)
         self.ks = self.vs = None
-        if dt == "i8":
+        if dt in ("i8", "i4"):
             self.ks = torch.from_numpy(self.host["k_scale"]).cuda()
             self.vs = torch.from_numpy(self.host["v_scale"]).cuda()
         t_l, _ = self.lib.export(self.seqs, self.MB)

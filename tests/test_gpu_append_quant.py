@@ -1,5 +1,5 @@
-"""The quantising int8 append (pa_kv_append_int8) against the oracle's append_int8: codes and
-scales bit-exact after every call, for prompt chunks (runs of consecutive slots in one block),
+"""The quantising appends (pa_kv_append_int8, pa_kv_append_int4 into packed nibbles) against the
+oracle's append_int8 / append_int4: codes (bytes) and scales bit-exact after every call, for prompt chunks (runs of consecutive slots in one block),
 decode steps (one token per sequence) with blocks whose scale grows, stays, or starts from
 zero, and both input dtypes.  Then decode reads the cache it wrote, within the int8 tolerance."""
 import numpy as np
@@ -10,22 +10,29 @@ import inputs
 import paged_kv_cache_284_amd as pkv
 from oracle import attention
 from oracle.allocator import PyAllocator
-from oracle.cache_ops import append_int8
+from oracle.cache_ops import append_int4, append_int8
 from tests.gpu_cases import TOL, say, to_device
 
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("new_dtype,D", [("bf16", 128), ("f32", 64)])
-def test_quantising_append_matches_oracle(new_dtype, D):
+@pytest.mark.parametrize("kind,new_dtype,D", [("i8", "bf16", 128), ("i8", "f32", 64),
+                                               ("i4", "bf16", 128), ("i4", "f32", 64)])
+def test_quantising_append_matches_oracle(kind, new_dtype, D):
     NB, bs, Hkv, G, B = 96, 16, 4, 2, 6
-    rng = np.random.default_rng([284, 80, D])
+    rng = np.random.default_rng([284, 80, D, len(kind)])
     order = rng.permutation(NB).astype(np.int32)
     lib = pkv.Allocator(NB, bs, order)
     py = PyAllocator(NB, bs, order)
     # stale bytes everywhere: fresh blocks must not read them
-    kc = rng.integers(-128, 128, (NB, Hkv, bs, D)).astype(np.int8)
-    vc = rng.integers(-128, 128, (NB, Hkv, D, bs)).astype(np.int8)
+    if kind == "i8":
+        kc = rng.integers(-128, 128, (NB, Hkv, bs, D)).astype(np.int8)
+        vc = rng.integers(-128, 128, (NB, Hkv, D, bs)).astype(np.int8)
+        device_append, oracle_append = pkv.kv_append_int8, append_int8
+    else:
+        kc = rng.integers(0, 256, (NB, Hkv, bs, D // 2)).astype(np.uint8)
+        vc = rng.integers(0, 256, (NB, Hkv, D, bs // 2)).astype(np.uint8)
+        device_append, oracle_append = pkv.kv_append_int4, append_int4
     ks = rng.random((NB, Hkv)).astype(np.float32)
     vs = rng.random((NB, Hkv)).astype(np.float32)
     dk, dv = torch.from_numpy(kc).cuda(), torch.from_numpy(vc).cuda()
@@ -44,9 +51,9 @@ def test_quantising_append_matches_oracle(new_dtype, D):
 
     def apply(slots, kn, vn, kf, vf):
         nonlocal host
-        pkv.kv_append_int8(to_device(kn, new_dtype), to_device(vn, new_dtype),
-                           torch.tensor(slots, dtype=torch.int64, device="cuda"), dk, dv, dks, dvs)
-        host = append_int8(*host, kf, vf, slots, bs)
+        device_append(to_device(kn, new_dtype), to_device(vn, new_dtype),
+                      torch.tensor(slots, dtype=torch.int64, device="cuda"), dk, dv, dks, dvs)
+        host = oracle_append(*host, kf, vf, slots, bs)
         torch.cuda.synchronize()
         assert np.array_equal(dk.cpu().numpy(), host[0])
         assert np.array_equal(dv.cpu().numpy(), host[1])
@@ -63,7 +70,7 @@ def test_quantising_append_matches_oracle(new_dtype, D):
         growth = np.linspace(0.2, 3.0, n, dtype=np.float32)[None, :].repeat(2, 0)
         apply(slots_p, *draw(n, b, growth))
         seqs.append(s_p)
-    say(f"prompts written, D={D}, inputs {new_dtype}")
+    say(f"{kind}: prompts written, D={D}, inputs {new_dtype}")
     for step in range(20):                               # decode steps
         slots_l, _ = lib.step(seqs)
         slots_p, _ = py.step(seqs)
@@ -78,8 +85,8 @@ def test_quantising_append_matches_oracle(new_dtype, D):
     out = pkv.decode(to_device(q, "bf16"), dk, dv, torch.from_numpy(tables).cuda(),
                      torch.from_numpy(lens).cuda(), int(lens.max()), 1 / np.sqrt(D), dks,
                      dvs).cpu().numpy()
-    ref = attention.decode_paged(q, "bf16", host[0], host[1], "i8", tables, lens, bs,
+    ref = attention.decode_paged(q, "bf16", host[0], host[1], kind, tables, lens, bs,
                                  1 / np.sqrt(D), host[2], host[3])
     err = float(np.max(np.abs(out.astype(np.float64) - ref)))
     say(f"decode over the appended cache: max-abs error {err:.2e}")
-    assert err <= TOL["i8"]
+    assert err <= TOL[kind]

@@ -16,7 +16,8 @@ from tests.gpu_cases import TOL, Case, max_err, sample_heads, say, to_device
 
 pytestmark = pytest.mark.gpu
 
-SMALL = ["tiny_fp32", "llama8b_decode", "long_context", "shared_prefix_batch", "int8_mha"]
+SMALL = ["tiny_fp32", "llama8b_decode", "long_context", "shared_prefix_batch", "int8_mha",
+         "int4_mha"]
 
 
 @pytest.mark.parametrize("name", SMALL)
@@ -34,7 +35,7 @@ def test_small_workload_all_steps(name, partition, fused):
 
 
 @pytest.mark.parametrize("name", ["llama8b_decode", "long_context", "shared_prefix_batch",
-                                  "int8_mha", "tiny_fp32"])
+                                  "int8_mha", "int4_mha", "tiny_fp32"])
 def test_full_workload_sampled(name):
     """The full-size workloads in the default launch configuration; the oracle computes sampled
     (sequence, head) rows one by one."""
@@ -66,7 +67,8 @@ def _ragged_case(kv="bf16", G=4, D=128, lens=(0, 1, 15, 16, 17, 63, 64, 65, 200,
 
 @pytest.mark.parametrize("kv,G,D", [("bf16", 4, 128), ("bf16", 1, 64), ("f32", 2, 64),
                                     ("f32", 16, 128), ("bf16", 8, 128), ("i8", 1, 128),
-                                    ("i8", 4, 64), ("bf16", 16, 128)])
+                                    ("i8", 4, 64), ("bf16", 16, 128), ("i4", 1, 128),
+                                    ("i4", 4, 64), ("i4", 16, 128)])
 @pytest.mark.parametrize("partition", [0, 64])
 def test_edge_lengths(kv, G, D, partition):
     """Empty, single-token, block-boundary and partition-boundary lengths, several group sizes."""

@@ -16,7 +16,7 @@ from tests.gpu_cases import TOL, from_device_bits, say, to_device
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("kv", ["bf16", "i8"])
+@pytest.mark.parametrize("kv", ["bf16", "i8", "i4"])
 def test_swap_out_reuse_swap_in(kv):
     w = inputs.llama8b_decode(B=6, lo=20, hi=120, cid=85, name="swap")
     w.Hkv, w.Hq, w.D, w.append = 2, 8, 64, False
@@ -38,12 +38,12 @@ def test_swap_out_reuse_swap_in(kv):
     shape_v = (NCPU,) + host["v"].shape[1:]
     npdt = host["k"].dtype
     swap = {"k": np.zeros(shape_k, npdt), "v": np.zeros(shape_v, npdt)}
-    tdt = {"bf16": torch.int16, "i8": torch.int8}[kv]
+    tdt = {"bf16": torch.int16, "i8": torch.int8, "i4": torch.uint8}[kv]
     pin = {"k": torch.zeros(shape_k, dtype=tdt).pin_memory(),
            "v": torch.zeros(shape_v, dtype=tdt).pin_memory()}
     if kv == "bf16":
         pin = {k: t.view(torch.bfloat16) for k, t in pin.items()}
-    if kv == "i8":
+    if kv in ("i8", "i4"):
         for s in ("k_scale", "v_scale"):
             swap[s] = np.zeros((NCPU, w.Hkv), np.float32)
             pin[s] = torch.zeros((NCPU, w.Hkv), dtype=torch.float32).pin_memory()
