@@ -124,8 +124,9 @@ struct PairRegsI4 {
   float ks_a, ks_b, vs_a, vs_b;
 };
 
-// Cache element kinds of the kernel template.
+// Cache element kinds of the kernel template, and the pairs each keeps in flight per wave.
 constexpr int kKvBf16 = 0, kKvI8 = 1, kKvI4 = 2;
+constexpr int kDepthBf16 = 2, kDepthI8 = 3, kDepthI4 = 4;
 
 template <int G, int D, bool kStream, int kKV>
 __global__ void __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -135,6 +136,7 @@ decode_mfma_kernel(DecodeArgs a) {
   constexpr float kOffset = kI4 ? kNibbleOffset : kCodeOffset;
   using Regs = std::conditional_t<kI4, PairRegsI4<D>,
                                   std::conditional_t<kI8, PairRegsI8<D>, PairRegs<D>>>;
+  constexpr int kDepth = kI4 ? kDepthI4 : (kI8 ? kDepthI8 : kDepthBf16);  // pairs in flight
   constexpr int kSteps = D / 32;
   constexpr int kTiles = D / 16;
 
@@ -333,11 +335,11 @@ decode_mfma_kernel(DecodeArgs a) {
       if constexpr (kI8) {
         // score = k_scale * sum_d q_d c_d = k_scale * (sum_d q_d (1152 + c_d) - 1152 sum_d q_d)
         const float f = (vblk_sel ? R.ks_b : R.ks_a) * a.scale_log2;
-        const float off = kOffset * qsum;
+        const float c0 = -kOffset * qsum * f;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          sc[e] = (s1[e] - off) * f;
-          sc[4 + e] = (s2[e] - off) * f;
+          sc[e] = fmaf(s1[e], f, c0);
+          sc[4 + e] = fmaf(s2[e], f, c0);
         }
       } else {
 #pragma unroll
@@ -385,18 +387,23 @@ decode_mfma_kernel(DecodeArgs a) {
         psum += pv[e];
       }
       l_run = l_run * alpha + psum;
+      f16x8 p16;
       if constexpr (kI8) {
-        // fold this block's V scale into P; keep the sum of P to take out the code offset
+        // fold this block's V scale into P and round it to the fp16 operand once; the code
+        // offset is taken out with the sum of exactly those operands, so it cancels exactly
+        // (a sum of unrounded P would leave the rounding error times the offset)
         const float vs = vblk_sel ? R.vs_b : R.vs_a;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pv[e] *= vs;
+        p16 = __builtin_convertvector(pv, f16x8);
+        const f32x8 pr = __builtin_convertvector(p16, f32x8);
         float csum = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          pv[e] *= vs;
-          csum += pv[e];
-        }
+        for (int e = 0; e < 8; ++e) csum += pr[e];
         c_run = c_run * alpha + csum;
       }
-      // rescale the accumulators: rows 4 qg + j hold head (4 qg + j) % G
+      // rescale the accumulators: rows 4 qg + j hold head (4 qg + j) % G (unconditionally: a
+      // wave-wide test for alpha == 1 costs more than the multiplies it saves)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         float aj;
@@ -409,10 +416,8 @@ decode_mfma_kernel(DecodeArgs a) {
         for (int n = 0; n < kTiles; ++n) acc[n][j] *= aj;
       }
       if constexpr (kI8) {
-        // P as fp16 hi + lo next to fp16 codes
-        const f16x8 p_hi = __builtin_convertvector(pv, f16x8);
-        const f16x8 p_lo = __builtin_convertvector(pv - __builtin_convertvector(p_hi, f32x8),
-                                                   f16x8);
+        // P as one fp16 operand (11-bit significand: its rounding stays far inside the int8 /
+        // int4 tolerance) next to fp16 codes
 #pragma unroll
         for (int n = 0; n < kTiles; ++n) {
           f16x8 vop;
@@ -421,8 +426,7 @@ decode_mfma_kernel(DecodeArgs a) {
           } else {
             vop = codes_to_f16(R.v[n][0], R.v[n][1]);
           }
-          acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(p_hi, vop, acc[n], 0, 0, 0);
-          acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(p_lo, vop, acc[n], 0, 0, 0);
+          acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(p16, vop, acc[n], 0, 0, 0);
         }
       } else {
         // P as bf16 hi + lo
@@ -443,40 +447,24 @@ decode_mfma_kernel(DecodeArgs a) {
       }
     };
 
-    // software pipeline: the next pair's loads (bf16), or the next two pairs' (int8: half the
-    // bytes per pair, so twice the pairs keep as many bytes in flight) are issued before the
-    // current pair is computed
+    // software pipeline: the loads of the next kDepth - 1 pairs are in flight while the
+    // current pair is computed (narrower codes carry fewer bytes per pair, so they keep more
+    // pairs in flight).  The loop is unrolled kDepth times so every buffer index is static.
     {
       const int step = solo ? 1 : kWaves;
       int i = solo ? i0 : i0 + w;
-      if constexpr (kI8) {
-        Regs ra, rb, rc;
-        if (i < i1) load_pair(i, ra);
-        if (i + step < i1) load_pair(i + step, rb);
-        while (i < i1) {
-          if (i + 2 * step < i1) load_pair(i + 2 * step, rc);
-          compute_pair(i, ra);
+      Regs R[kDepth];
+#pragma unroll
+      for (int j = 0; j + 1 < kDepth; ++j)
+        if (i + j * step < i1) load_pair(i + j * step, R[j]);
+      while (i < i1) {
+#pragma unroll
+        for (int j = 0; j < kDepth; ++j) {
+          const int ahead = i + (kDepth - 1) * step;
+          if (ahead < i1) load_pair(ahead, R[(j + kDepth - 1) % kDepth]);
+          compute_pair(i, R[j]);
           i += step;
           if (i >= i1) break;
-          if (i + 2 * step < i1) load_pair(i + 2 * step, ra);
-          compute_pair(i, rb);
-          i += step;
-          if (i >= i1) break;
-          if (i + 2 * step < i1) load_pair(i + 2 * step, rb);
-          compute_pair(i, rc);
-          i += step;
-        }
-      } else {
-        Regs ra, rb;
-        if (i < i1) load_pair(i, ra);
-        while (i < i1) {
-          if (i + step < i1) load_pair(i + step, rb);
-          compute_pair(i, ra);
-          i += step;
-          if (i >= i1) break;
-          if (i + step < i1) load_pair(i + step, ra);
-          compute_pair(i, rb);
-          i += step;
         }
       }
     }
