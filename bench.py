@@ -471,6 +471,8 @@ def traffic_from_profiles(kernel_src_hash: str):
 
 
 DECODE_SOURCES = ("decode_mfma.hip", "internal.h")
+# the balanced bf16 decode kernel of the Llama-3.1-8B-shaped batch (G = 4, D = 128)
+DECODE_KERNEL = "decode_mfma_kernel<4, 128, true, 0>"
 
 
 def kernel_sources_hash() -> str:
@@ -498,9 +500,11 @@ def summarize_counters(d: str, copy_mib: int = 512) -> dict:
         return sum(vals) / len(vals)
 
     dec_f = [float(r["Counter_Value"]) for r in rows("pmc_FETCH_SIZE", "dec")
-             if "decode_mfma_kernel<4, 128, true, false>" in r["Kernel_Name"]]
+             if DECODE_KERNEL in r["Kernel_Name"]]
     dec_w = [float(r["Counter_Value"]) for r in rows("pmc_WRITE_SIZE", "dec")
-             if "decode_mfma_kernel<4, 128, true, false>" in r["Kernel_Name"]]
+             if DECODE_KERNEL in r["Kernel_Name"]]
+    if not dec_f or not dec_w:
+        raise SystemExit(f"no {DECODE_KERNEL} dispatch in the counter runs under {d}")
     # the device-to-device copy torch issues for Tensor.copy_ (the fill before it is skipped)
     big = lambda rs: [float(r["Counter_Value"]) for r in rs  # noqa: E731
                       if "copyBuffer" in r["Kernel_Name"]]

@@ -340,7 +340,7 @@ int pa_prefill(float* out, const void* q, int32_t q_dtype, const void* k_cache,
   a.Hkv = Hkv;
   a.D = D;
   a.NB = NB;
-  const int64_t tiles = (static_cast<int64_t>(T) + 15) / 16 + B;  // sum of ceil(n_b / 16)
+  const int64_t tiles = (static_cast<int64_t>(T) + 63) / 64 + B;  // sum of ceil(n_b / 64)
   if (tiles > INT32_MAX) return PA_ERR_INVALID;
   a.max_tiles = static_cast<int32_t>(tiles);
   a.scale_log2 = scale * kLog2e;

@@ -43,7 +43,7 @@ struct PrefillArgs {
   const int32_t* cu_q;        // [B + 1] first query row of each sequence's chunk
   int32_t max_blocks, max_seq_len;
   int32_t B, T, Hq, Hkv, D, NB;
-  int32_t max_tiles;          // grid bound on the number of 16-query tiles
+  int32_t max_tiles;          // grid bound on the number of 64-query workgroups
   float scale_log2;
 };
 
