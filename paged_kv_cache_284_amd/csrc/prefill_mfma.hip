@@ -15,8 +15,8 @@
 //           8*(l/16)..+7 for query l%16 -- exactly its P operand for P . V;
 //   P . V   O^T += V^T . P^T as 16(dim) x 16(query) tiles, V tiles dim-major in HBM, so a
 //           lane's accumulator column is its own query;
-// online softmax per query (exp2 domain) with a lazily moved maximum, the causal limit p applied
-// per lane on the pairs that reach it.
+// softmax per query (exp2 domain) against a fixed reference, the causal limit p applied per lane
+// on the pairs that reach it.
 // A wave takes 16 queries of up to four query heads of one KV head: each K/V operand it loads
 // feeds the MFMAs of all its heads.  A workgroup holds four such waves on consecutive 16-query
 // tiles of one sequence, which read the same K/V tiles back to back and share them in cache.
@@ -60,14 +60,11 @@ __device__ __forceinline__ float sum_across_groups(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-constexpr float kLazyLog2 = 8.f;  // slack of the running maximum, in log2 units
+constexpr float kOverP = 2.305843e18f;    // 2^61: a pair's P sum above this asks for a rerun
+constexpr float kUnderL = 8.6736174e-19f;  // 2^-60: a final l below this asks for a rerun
 
-template <int D>
-struct KVRegs {
-  u32x4 k1[D / 32];
-  u32x4 k2[D / 32];
-  u32x4 v[D / 16];
-  int32_t blk_a, blk_b;
+struct Pair {
+  int32_t a, b;  // the blocks of tokens 0..15 and 16..31 of a 32-token pair
 };
 
 // Sequence and group of global group index `group`: groups of kGroup queries are numbered
@@ -163,142 +160,187 @@ prefill_mfma_kernel(PrefillArgs a) {
   const int tok2 = tok1 + 4;
   const int vsel = qg / 2, vtok = 8 * (qg % 2);
 
-  auto load_pair = [&](int i, KVRegs<D>& R) {
+  // Blocks of pair i (two consecutive table entries; -1 marks a missing or unused block).
+  auto blocks_of = [&](int i) -> Pair {
     const int tok0 = i * kPairTok;
     const int jb = tok0 / kBlockSize;
     int32_t ba = table[jb];
     int32_t bb = (tok0 + kBlockSize < kv_end) ? table[jb + 1] : -1;
-    ba = (ba >= 0 && ba < NB) ? ba : -1;
-    bb = (bb >= 0 && bb < NB) ? bb : -1;
-    R.blk_a = ba;
-    R.blk_b = bb;
-    const int64_t ta = (static_cast<int64_t>(ba < 0 ? 0 : ba) * Hkv + g) * (kBlockSize * D);
-    const int64_t tb = (static_cast<int64_t>(bb < 0 ? 0 : bb) * Hkv + g) * (kBlockSize * D);
-    const uint16_t* k1 = kc + (tok1 < 16 ? ta : tb) + (tok1 % 16) * D + 8 * qg;
-    const uint16_t* k2 = kc + (tok2 < 16 ? ta : tb) + (tok2 % 16) * D + 8 * qg;
+    return Pair{(ba >= 0 && ba < NB) ? ba : -1, (bb >= 0 && bb < NB) ? bb : -1};
+  };
+  auto tile_of = [&](int32_t blk) {
+    return (static_cast<int64_t>(blk < 0 ? 0 : blk) * Hkv + g) * (kBlockSize * D);
+  };
+  u32x4 k1[kSteps], k2[kSteps], vr[kTiles];
+  auto load_k = [&](Pair bl) {
+    const int64_t ta = tile_of(bl.a), tb = tile_of(bl.b);
+    const uint16_t* p1 = kc + (tok1 < 16 ? ta : tb) + (tok1 % 16) * D + 8 * qg;
+    const uint16_t* p2 = kc + (tok2 < 16 ? ta : tb) + (tok2 % 16) * D + 8 * qg;
 #pragma unroll
     for (int s = 0; s < kSteps; ++s) {
-      R.k1[s] = ld16(k1 + 32 * s);
-      R.k2[s] = ld16(k2 + 32 * s);
+      k1[s] = ld16(p1 + 32 * s);
+      k2[s] = ld16(p2 + 32 * s);
     }
-    const uint16_t* v = vc + (vsel ? tb : ta) + r * kBlockSize + vtok;
+  };
+  auto load_v = [&](Pair bl) {
+    const uint16_t* pv = vc + tile_of(vsel ? bl.b : bl.a) + r * kBlockSize + vtok;
 #pragma unroll
-    for (int t = 0; t < kTiles; ++t) R.v[t] = ld16(v + 16 * t * kBlockSize);
+    for (int t = 0; t < kTiles; ++t) vr[t] = ld16(pv + 16 * t * kBlockSize);
   };
 
-  float m_run[kH], l_run[kH];
+  // Softmax against a fixed reference per query instead of a running maximum: P = 2^(s c - ref)
+  // and the accumulators are never rescaled; the quotient acc / l is the same for any ref.  The
+  // reference is the scaled maximum of the first pair (tokens 0..31), a score the sum contains,
+  // so the largest P is at least 1 and nothing that matters underflows.  Should a later pair's
+  // P sum pass 2^61 (a score more than about 2^61 above the reference), or the final l stay
+  // below 2^-60 (the first pair had no key for this query), the wave sweeps its keys once for
+  // the exact maximum and runs the tile again with that as the reference, which no score can
+  // exceed.
+  float ref[kH], l_run[kH];
   f32x4 acc[kH][kTiles];
-#pragma unroll
-  for (int hh = 0; hh < kH; ++hh) {
-    m_run[hh] = -INFINITY;
-    l_run[hh] = 0.f;
-#pragma unroll
-    for (int t = 0; t < kTiles; ++t) acc[hh][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
+  const int p_first = L - n + qi0;     // position of the tile's first query
+  const int limit = min(my_p, L - 1);  // keys t <= limit count for this lane's query
+  const int n_pairs = kv_end > 0 ? (kv_end + kPairTok - 1) / kPairTok : 0;
 
-  const int p_first = L - n + qi0;  // position of the tile's first query
-  auto compute_pair = [&](int i, KVRegs<D>& R) {
-    const int tok0 = i * kPairTok;
-    const int t_first = tok0 + 8 * qg;
-    const int32_t my_blk = vsel ? R.blk_b : R.blk_a;
-    // Only pairs that reach past the tile's first query, past the context or into a missing
-    // block need masks (wave-uniform test).
-    const bool edge =
-        tok0 + kPairTok - 1 > p_first || tok0 + kPairTok > L || R.blk_a < 0 || R.blk_b < 0;
-    // causal and context limits: token t is kept for this lane's query when t <= my_p, t < L
-    const int limit = min(my_p, L - 1);
-    if (tok0 + kPairTok > L || R.blk_a < 0 || R.blk_b < 0) {
-      // tokens past the context (or of a missing block) must not reach P.V even with p = 0
-#pragma unroll
-      for (int cc = 0; cc < 4; ++cc) {
-        const bool k0 = my_blk >= 0 && t_first + 2 * cc < L;
-        const bool k1 = my_blk >= 0 && t_first + 2 * cc + 1 < L;
-        const uint32_t keep = (k0 ? 0x0000ffffu : 0u) | (k1 ? 0xffff0000u : 0u);
-#pragma unroll
-        for (int t = 0; t < kTiles; ++t) R.v[t][cc] &= keep;
-      }
-    }
+  f32x4 s1[kH], s2[kH];
+  auto scores = [&]() {
 #pragma unroll
     for (int hh = 0; hh < kH; ++hh) {
-      f32x4 s1 = {0.f, 0.f, 0.f, 0.f}, s2 = {0.f, 0.f, 0.f, 0.f};
+      s1[hh] = f32x4{0.f, 0.f, 0.f, 0.f};
+      s2[hh] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < kSteps; ++s) {
-        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(R.k1[s]), as_bf16x8(qv[hh][s]), s1,
-                                                      0, 0, 0);
-        s2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(R.k2[s]), as_bf16x8(qv[hh][s]), s2,
-                                                      0, 0, 0);
-      }
-      float sr[8];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        sr[e] = s1[e];
-        sr[4 + e] = s2[e];
-      }
-      if (edge) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (t_first + e > limit || my_blk < 0) sr[e] = -INFINITY;
-      }
-      float bmax = sr[0];
-#pragma unroll
-      for (int e = 1; e < 8; ++e) bmax = fmaxf(bmax, sr[e]);
-      bmax = max_across_groups(bmax);
-      const float bm = bmax * c;  // the pair's largest scaled score of this lane's query
-      // Lazy rescaling: the running maximum moves only when a score exceeds it by more than
-      // kLazyLog2, so P stays below 2^kLazyLog2 and most pairs skip the accumulator rescale.
-      const bool grow = bm > m_run[hh] + kLazyLog2;
-      if (__ballot(grow)) {
-        const float m_new = grow ? bm : m_run[hh];
-        const float alpha = __builtin_amdgcn_exp2f(m_run[hh] - m_new);
-        m_run[hh] = m_new;
-        l_run[hh] *= alpha;
-#pragma unroll
-        for (int t = 0; t < kTiles; ++t) acc[hh][t] *= alpha;
-      }
-      const float m_use = m_run[hh] == -INFINITY ? 0.f : m_run[hh];
-      f32x8 pv;
-      float psum = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        pv[e] = __builtin_amdgcn_exp2f(fmaf(sr[e], c, -m_use));
-        psum += pv[e];
-      }
-      l_run[hh] += psum;
-      // O^T += V^T . P^T: V rows are dims, P^T columns are this lane's query, so the
-      // accumulator column of a lane is its own query and the rescale above needs no shuffle.
-      // P enters as a bf16 pair hi + lo, which carries it to about 16 bits.
-      const bf16x8 p_hi = __builtin_convertvector(pv, bf16x8);
-      const u32x4 hb = __builtin_bit_cast(u32x4, p_hi);
-      f32x8 rest;
-#pragma unroll
-      for (int cc = 0; cc < 4; ++cc) {
-        rest[2 * cc] = pv[2 * cc] - __uint_as_float(hb[cc] << 16);
-        rest[2 * cc + 1] = pv[2 * cc + 1] - __uint_as_float(hb[cc] & 0xffff0000u);
-      }
-      const bf16x8 p_lo = __builtin_convertvector(rest, bf16x8);
-#pragma unroll
-      for (int t = 0; t < kTiles; ++t) {
-        acc[hh][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(R.v[t]), p_hi, acc[hh][t],
-                                                              0, 0, 0);
-        acc[hh][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(R.v[t]), p_lo, acc[hh][t],
-                                                              0, 0, 0);
+        s1[hh] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(k1[s]), as_bf16x8(qv[hh][s]),
+                                                          s1[hh], 0, 0, 0);
+        s2[hh] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(k2[s]), as_bf16x8(qv[hh][s]),
+                                                          s2[hh], 0, 0, 0);
       }
     }
   };
-
-  const int n_pairs = kv_end > 0 ? (kv_end + kPairTok - 1) / kPairTok : 0;
-  {
-    KVRegs<D> ra, rb;
-    int i = 0;
-    if (i < n_pairs) load_pair(i, ra);
-    while (i < n_pairs) {
-      if (i + 1 < n_pairs) load_pair(i + 1, rb);
-      compute_pair(i, ra);
-      if (++i >= n_pairs) break;
-      if (i + 1 < n_pairs) load_pair(i + 1, ra);
-      compute_pair(i, rb);
-      ++i;
+  // -inf for keys past this lane's query, past the context or in a missing block
+  auto mask_scores = [&](int tok0, int32_t my_blk) {
+    const int t_first = tok0 + 8 * qg;
+#pragma unroll
+    for (int hh = 0; hh < kH; ++hh) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (t_first + e > limit || my_blk < 0) s1[hh][e] = -INFINITY;
+        if (t_first + 4 + e > limit || my_blk < 0) s2[hh][e] = -INFINITY;
+      }
     }
+  };
+  auto is_edge = [&](int tok0, Pair bl) {  // pairs that need masks (wave-uniform)
+    return tok0 + kPairTok > L || bl.a < 0 || bl.b < 0 || tok0 + kPairTok - 1 > p_first;
+  };
+  // scaled maximum over the scores in s1, s2 of this lane's query (all four lane groups)
+  auto pair_max = [&](int hh) {
+    float m = fmaxf(fmaxf(fmaxf(s1[hh][0], s1[hh][1]), fmaxf(s1[hh][2], s1[hh][3])),
+                    fmaxf(fmaxf(s2[hh][0], s2[hh][1]), fmaxf(s2[hh][2], s2[hh][3])));
+    return max_across_groups(m) * c;
+  };
+  // exact maximum over all keys of the tile (the rare second pass)
+  auto sweep_max = [&]() {
+#pragma unroll
+    for (int hh = 0; hh < kH; ++hh) ref[hh] = -INFINITY;
+    Pair cur = blocks_of(0);
+    load_k(cur);
+    for (int i = 0; i < n_pairs; ++i) {
+      const bool more = i + 1 < n_pairs;
+      const Pair nxt = more ? blocks_of(i + 1) : Pair{-1, -1};
+      scores();
+      if (more) load_k(nxt);
+      if (is_edge(i * kPairTok, cur)) mask_scores(i * kPairTok, vsel ? cur.b : cur.a);
+#pragma unroll
+      for (int hh = 0; hh < kH; ++hh) ref[hh] = fmaxf(ref[hh], pair_max(hh));
+      cur = nxt;
+    }
+  };
+
+  if (n_pairs > 0) {
+    const Pair b0 = blocks_of(0);
+    load_k(b0);
+    scores();
+    if (is_edge(0, b0)) mask_scores(0, vsel ? b0.b : b0.a);
+#pragma unroll
+    for (int hh = 0; hh < kH; ++hh) ref[hh] = pair_max(hh);
+  }
+  for (int pass = 0; pass < 2; ++pass) {
+    float r0[kH];
+#pragma unroll
+    for (int hh = 0; hh < kH; ++hh) {
+      r0[hh] = ref[hh] == -INFINITY ? 0.f : ref[hh];
+      l_run[hh] = 0.f;
+#pragma unroll
+      for (int t = 0; t < kTiles; ++t) acc[hh][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    bool over = false;
+    Pair cur = n_pairs > 0 ? blocks_of(0) : Pair{-1, -1};
+    if (n_pairs > 0) {
+      load_k(cur);
+      load_v(cur);
+    }
+    // One pair of blocks per step, single-buffered: the next pair's K is requested once every
+    // head's scores have consumed this pair's K, and its V once P . V has consumed this V.
+    for (int i = 0; i < n_pairs; ++i) {
+      const int tok0 = i * kPairTok;
+      const int t_first = tok0 + 8 * qg;
+      const bool more = i + 1 < n_pairs;
+      const Pair nxt = more ? blocks_of(i + 1) : Pair{-1, -1};
+      const int32_t my_blk = vsel ? cur.b : cur.a;
+      scores();
+      if (more) load_k(nxt);
+      if (tok0 + kPairTok > L || cur.a < 0 || cur.b < 0) {
+        // tokens past the context (or of a missing block) must not reach P.V even with p = 0
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) {
+          const bool k0 = my_blk >= 0 && t_first + 2 * cc < L;
+          const bool k1b = my_blk >= 0 && t_first + 2 * cc + 1 < L;
+          const uint32_t keep = (k0 ? 0x0000ffffu : 0u) | (k1b ? 0xffff0000u : 0u);
+#pragma unroll
+          for (int t = 0; t < kTiles; ++t) vr[t][cc] &= keep;
+        }
+      }
+      if (is_edge(tok0, cur)) mask_scores(tok0, my_blk);
+#pragma unroll
+      for (int hh = 0; hh < kH; ++hh) {
+        f32x8 pv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          pv[e] = __builtin_amdgcn_exp2f(fmaf(s1[hh][e], c, -r0[hh]));
+          pv[4 + e] = __builtin_amdgcn_exp2f(fmaf(s2[hh][e], c, -r0[hh]));
+        }
+        const float psum = ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
+        l_run[hh] += psum;
+        over = over || !(psum <= kOverP);
+        // O^T += V^T . P^T: V rows are dims, P^T columns are this lane's query, so the
+        // accumulator column of a lane is its own query.  P enters as a bf16 pair hi + lo,
+        // which carries it to about 16 bits.
+        const bf16x8 p_hi = __builtin_convertvector(pv, bf16x8);
+        const u32x4 hb = __builtin_bit_cast(u32x4, p_hi);
+        f32x8 rest;
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) {
+          rest[2 * cc] = pv[2 * cc] - __uint_as_float(hb[cc] << 16);
+          rest[2 * cc + 1] = pv[2 * cc + 1] - __uint_as_float(hb[cc] & 0xffff0000u);
+        }
+        const bf16x8 p_lo = __builtin_convertvector(rest, bf16x8);
+#pragma unroll
+        for (int t = 0; t < kTiles; ++t) {
+          acc[hh][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vr[t]), p_hi,
+                                                                acc[hh][t], 0, 0, 0);
+          acc[hh][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vr[t]), p_lo,
+                                                                acc[hh][t], 0, 0, 0);
+        }
+      }
+      if (more) load_v(nxt);
+      cur = nxt;
+    }
+    if (pass == 1) break;
+    // queries of this lane's column whose keys were all masked keep l = 0 in both passes
+#pragma unroll
+    for (int hh = 0; hh < kH; ++hh) over = over || l_run[hh] < kUnderL;
+    if (!__ballot(over)) break;
+    sweep_max();
   }
 
   // l summed over the four lane groups is query r's; a lane holds dims 16 t + 4 qg .. +3 of it

@@ -24,19 +24,21 @@ def _workload(G, D, lens, cid):
     return w
 
 
-def _run(w, chunks, rows=None):
+def _run(w, chunks, rows=None, scale=None):
+    scale = w.scale if scale is None else scale
     case = Case(w)
     tables, lens = case.py.export(case.seqs, case.MB)
     tables, lens = np.array(tables, np.int32), np.array(lens, np.int32)
     cu = np.concatenate([[0], np.cumsum(chunks)]).astype(np.int32)
     T = int(cu[-1])
     q = inputs.chunk_queries(w, T)
-    say(f"prefill G={w.G} D={w.D} lens={list(lens)[:8]} chunks={list(chunks)[:8]} T={T}")
+    say(f"prefill G={w.G} D={w.D} lens={list(lens)[:8]} chunks={list(chunks)[:8]} T={T} "
+        f"scale={scale}")
     out = pkv.prefill(to_device(q, "bf16"), case.k, case.v, case.tables,
                       torch.from_numpy(lens).cuda(), torch.from_numpy(cu).cuda(),
-                      int(lens.max()), w.scale).cpu().numpy()
+                      int(lens.max()), scale).cpu().numpy()
     ref = prefill_paged(q, "bf16", case.host["k"], case.host["v"], "bf16", tables, lens, cu,
-                        w.bs, w.scale, rows=rows)
+                        w.bs, scale, rows=rows)
     if rows is None:
         err = float(np.max(np.abs(out.astype(np.float64) - ref)))
         assert np.all(np.isfinite(out))
@@ -65,3 +67,18 @@ def test_llama_shaped_chunk_sampled():
     rows = sorted({(int(r), int(h)) for r, h in zip(rng.integers(0, T, 40), rng.integers(0, 32, 40))})
     rows += [(T - 1, 0), (0, 31)]
     _run(w, chunks, rows=rows)
+
+
+@pytest.mark.parametrize("scale", [1.0, 25.0, -0.125])
+def test_score_range(scale):
+    """Large scales put later scores far above the first key pair's maximum (the kernel then
+    sweeps for the exact maximum and runs the tile again); a negative scale flips the sign of
+    every score."""
+    w = _workload(4, 128, [300, 64, 700, 17], cid=80)
+    _run(w, [300, 33, 129, 17], scale=scale)
+
+
+def test_chunk_longer_than_context():
+    """Rows whose position L - n + i is negative have no keys and come out zero."""
+    w = _workload(4, 128, [5, 40, 0, 70], cid=81)
+    _run(w, [8, 40, 3, 70])
