@@ -1,4 +1,5 @@
-// bf16 paged decode attention on the gfx950 matrix cores.
+// Paged decode attention on the gfx950 matrix cores: bf16 q over a bf16, int8 or packed int4
+// cache.
 //
 // What it computes ("How LLM Inference Serving Works", "What the KV Cache Is, and How Big It
 // Gets": the new token's query is scored against every cached key and the values are mixed by
@@ -32,6 +33,11 @@
 // exactly the 8 tokens it must supply as its P operand (tokens 8*(l/16)..+7 of the pair for head
 // (l%16)%G): softmax and P.V need no cross-lane transposition.  P is fed as a bf16 hi/lo pair
 // (p = hi + lo to ~16 bits) so the rounding of P stays far below the bf16 tolerance.
+// Quantised caches run v_mfma_f32_16x16x32_f16 instead: codes expand to fp16 values offset + c
+// (a byte permute for int8, a nibble mask and permute for int4), q enters once as fp16, P as one
+// fp16 operand, and the offset is taken out of both sums using the same rounded q and P values
+// the matrix cores saw, so it cancels exactly.  Loads of kDepth pairs are in flight per wave
+// (more for the narrower caches, whose pairs are fewer bytes).
 #include <cmath>
 #include <type_traits>
 
