@@ -477,12 +477,14 @@ TRAFFIC_WORKLOAD = "llama8b_decode"
 
 
 def kernel_sources_hash() -> str:
-    """sha256 over the sources the decode kernel is built from."""
+    """sha256 over the code of the sources the decode kernel is built from: each line with its
+    // comment and surrounding blanks removed, empty lines dropped (comment edits keep it)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "paged_kv_cache_284_amd", "csrc")
     for f in DECODE_SOURCES:
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(f.encode() + fh.read())
+        with open(os.path.join(csrc, f), encoding="utf-8") as fh:
+            code = [ln.split("//", 1)[0].strip() for ln in fh]
+        h.update(f.encode() + "\n".join(ln for ln in code if ln).encode())
     return h.hexdigest()
 
 
