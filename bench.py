@@ -10,7 +10,11 @@ Inputs (pools, queries, new tokens) are resident in HBM before the timed region 
 
 Prints one JSON line: whole-job tokens/s (B decode tokens per step), the decode kernel's achieved
 HBM GB/s against the MI355X peak (algorithmic bytes / mean launch time from HIP events on the
-launch stream), and the CPU oracle timed on the host cores.
+launch stream), and the CPU oracle timed on the host cores.  Algorithmic bytes count a block
+that several sequences share once (unique bytes); the per-sequence sum is reported beside them.
+Also reported: the append's time per step (copy-on-write copies included), the decode timed
+alone after reading 1 GiB of other memory (cold caches), a plain device copy's rate for context,
+and the oracle on all host threads.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload llama8b_decode]
 
@@ -39,13 +43,25 @@ METRIC = "paged decode attn: tokens/s + achieved HBM GB/s (% of MI355X peak)"
 KV_BYTES = {"f32": 4, "bf16": 2, "i8": 1, "i4": 0.5}
 
 
-def algorithmic_bytes(w, lens) -> int:
-    """Bytes a decode launch must move at minimum: K/V of every cached token, the int8 scales of
-    every touched (block, KV head) tile, q, out, the table entries in use and the lengths."""
+def algorithmic_bytes(w, lens, tables=None) -> int:
+    """Bytes a decode launch must move at minimum: K/V of every cached token, the int8 / int4
+    scales of every touched (block, KV head) tile, q, out, the table entries in use and the
+    lengths.  With the block tables given, a physical block that several sequences share counts
+    once, with as many tokens as its longest user reads (the unique bytes)."""
     lens = np.asarray(lens, np.int64)
     blocks = (lens + w.bs - 1) // w.bs
-    kv = int(int(lens.sum()) * w.Hkv * w.D * 2 * KV_BYTES[w.kv_dtype])
-    scales = int(blocks.sum()) * w.Hkv * 2 * 4 if w.kv_dtype in ("i8", "i4") else 0
+    per_token = w.Hkv * w.D * 2 * KV_BYTES[w.kv_dtype]
+    if tables is None:
+        tokens, touched = int(lens.sum()), int(blocks.sum())
+    else:
+        used = {}
+        for b in range(w.B):
+            for j in range(int(blocks[b])):
+                blk = int(tables[b][j])
+                used[blk] = max(used.get(blk, 0), int(min(w.bs, lens[b] - j * w.bs)))
+        tokens, touched = sum(used.values()), len(used)
+    kv = int(tokens * per_token)
+    scales = touched * w.Hkv * 2 * 4 if w.kv_dtype in ("i8", "i4") else 0
     q = w.B * w.Hq * w.D * KV_BYTES[w.q_dtype]
     out = w.B * w.Hq * w.D * 4
     return kv + scales + q + out + int(blocks.sum()) * 4 + w.B * 4
@@ -164,6 +180,7 @@ class StepRunner:
         self.n_ev = total_steps + 2
         self.ev_before = [self.hev.create() for _ in range(self.n_ev)]
         self.ev_after = [self.hev.create() for _ in range(self.n_ev)]
+        self.ev_append = [self.hev.create() for _ in range(self.n_ev)]  # before copies + append
         self.timed = []
         self.lens_step = torch.empty(B, dtype=torch.int32, device=dev)  # written by the append
         self.step_no = 0
@@ -205,6 +222,7 @@ class StepRunner:
             h_slots, h_lens, h_tidx, h_pairs = self.raw[i]
             self.max_len += 1
             n_cow = self.n_cow.value
+            self.hev.record(self.ev_append[s], self.stream)
             if n_cow:
                 st = L.pa_copy_blocks(self.k.data_ptr(), self.v.data_ptr(), self.ks_p, self.vs_p,
                                       h_pairs, n_cow, w.Hkv, w.D, w.bs, w.NB, self.kv_code,
@@ -222,22 +240,54 @@ class StepRunner:
         else:
             lens_d = self.lens_dev.data_ptr()
         self.hev.record(self.ev_before[s], self.stream)
-        st = L.pa_decode(self.out.data_ptr(), self.q[s % len(self.q)].data_ptr(), self.q_code,
-                         self.k.data_ptr(), self.v.data_ptr(), self.kv_code, self.ks_p, self.vs_p,
-                         self.tables.data_ptr(), self.MB, lens_d, self.max_len, w.B, w.Hq, w.Hkv,
-                         w.D, w.bs, w.NB, w.scale, self.partition, self.ws.data_ptr(),
-                         self.ws.numel(), self.stream)
-        if st != 0:
-            raise pkv.PagedKVError(st, "pa_decode")
+        self.lens_d = lens_d
+        self.decode(self.q[s % len(self.q)])
         self.hev.record(self.ev_after[s], self.stream)
         if time_decode:
-            self.timed.append((s, self.lens.copy()))
+            self.timed.append((s, self.lens.copy(), n_cow if w.append else 0))
         self.step_no += 1
+
+    def decode(self, q):
+        """pa_decode over the current cache state (no allocator or cache change)."""
+        w = self.w
+        st = self.L.pa_decode(self.out.data_ptr(), q.data_ptr(), self.q_code, self.k.data_ptr(),
+                              self.v.data_ptr(), self.kv_code, self.ks_p, self.vs_p,
+                              self.tables.data_ptr(), self.MB, self.lens_d, self.max_len, w.B,
+                              w.Hq, w.Hkv, w.D, w.bs, w.NB, w.scale, self.partition,
+                              self.ws.data_ptr(), self.ws.numel(), self.stream)
+        if st != 0:
+            raise self.pkv.PagedKVError(st, "pa_decode")
 
     def decode_ms(self):
         """(ms, lengths) of every timed decode launch (after the stream has drained)."""
         return [(self.hev.elapsed_ms(self.ev_before[s], self.ev_after[s]), lens)
-                for s, lens in self.timed]
+                for s, lens, _ in self.timed]
+
+    def append_ms(self):
+        """(ms, copy-on-write pairs) of the copies + append of every timed step."""
+        if not self.w.append:
+            return []
+        return [(self.hev.elapsed_ms(self.ev_append[s], self.ev_before[s]), n_cow)
+                for s, _, n_cow in self.timed]
+
+    def cold_decode_ms(self, reps: int, scrub_bytes: int = 1 << 30):
+        """Decode launches timed alone, each after a read of scrub_bytes of other memory (4x the
+        256 MB last-level cache), as the previous layer's attention would leave the caches: no
+        K/V line or translation cached, and no dirty line left to write back.  Events bracket
+        the decode only."""
+        torch = self.torch
+        scrub = torch.ones(scrub_bytes // 4, dtype=torch.float32, device="cuda")
+        total = torch.empty((), dtype=torch.float32, device="cuda")
+        ev = [(self.hev.create(), self.hev.create()) for _ in range(reps)]
+        q = self.q[(self.step_no - 1) % len(self.q)]
+        for a, b in ev:
+            torch.sum(scrub, dim=0, out=total)
+            self.hev.record(a, self.stream)
+            self.decode(q)
+            self.hev.record(b, self.stream)
+        torch.cuda.synchronize()
+        del scrub, total
+        return [self.hev.elapsed_ms(a, b) for a, b in ev]
 
 
 def prefill_flops(w, lens, chunks) -> int:
@@ -414,10 +464,18 @@ def run_prefill(args):
     print(json.dumps(rec), flush=True)
 
 
-def cpu_baseline(name: str, min_seconds: float = 10.0) -> dict:
-    """Time the fp64 oracle on one decode step of the same workload, one thread, in a child
-    process (input generation excluded)."""
-    env = dict(os.environ, OMP_NUM_THREADS="1", OPENBLAS_NUM_THREADS="1", MKL_NUM_THREADS="1")
+def host_threads() -> int:
+    """Threads this process may use: the CPU affinity, capped by OMP_NUM_THREADS when set."""
+    n = len(os.sched_getaffinity(0))
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    return min(n, int(env)) if env.isdigit() and int(env) > 0 else n
+
+
+def cpu_baseline(name: str, min_seconds: float = 10.0, threads: int = 1) -> dict:
+    """Time the fp64 oracle on one decode step of the same workload with `threads` BLAS threads,
+    in a child process (input generation excluded)."""
+    t = str(threads)
+    env = dict(os.environ, OMP_NUM_THREADS=t, OPENBLAS_NUM_THREADS=t, MKL_NUM_THREADS=t)
     code = f"""
 import sys, time, json, numpy as np
 sys.path.insert(0, {ROOT!r})
@@ -447,13 +505,34 @@ print(json.dumps({{"reps": reps, "seconds": el, "B": w.B}}))
     r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True,
                        cwd=ROOT)
     if r.returncode != 0:
-        return {"value": None, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+        return {"value": None, "unit": "tokens/s", "cores": threads, "kind": "oracle",
                 "sample": f"failed: {r.stderr[-300:]}"}
     d = json.loads(r.stdout.strip().splitlines()[-1])
     tps = d["B"] * d["reps"] / d["seconds"]
-    return {"value": round(tps, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+    return {"value": round(tps, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"{d['reps']} full decode step(s) of the workload (B={d['B']}, all heads, "
-                      f"fp64 numpy, 1 thread) in {d['seconds']:.1f} s"}
+                      f"fp64 numpy, {threads} thread{'s' if threads > 1 else ''}) in "
+                      f"{d['seconds']:.1f} s"}
+
+
+def stream_copy_gbps(nbytes: int = 1 << 30, reps: int = 5) -> float:
+    """Device-to-device copy rate (bytes read + written per second) of the runtime's copy, for
+    context beside the decode rate."""
+    import torch
+    src = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    hev = HipEvents()
+    stream = torch.cuda.current_stream().cuda_stream
+    a, b = hev.create(), hev.create()
+    hev.record(a, stream)
+    for _ in range(reps):
+        dst.copy_(src)
+    hev.record(b, stream)
+    torch.cuda.synchronize()
+    ms = hev.elapsed_ms(a, b)
+    del src, dst
+    return round(2 * nbytes * reps / (ms * 1e-3) / 1e9, 1)
 
 
 def traffic_from_profiles(kernel_src_hash: str):
@@ -551,6 +630,9 @@ def main():
     ap.add_argument("--partition", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--cold-reps", type=int, default=10,
+                    help="decode launches timed alone after a 1 GiB read of other memory "
+                         "(0: skip)")
     ap.add_argument("--copy-reference", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB five times (calibrates the "
                          "FETCH_SIZE / WRITE_SIZE counters against known bytes) and exit")
@@ -604,10 +686,16 @@ def main():
 
     timed = runner.decode_ms()
     ms = [t for t, _ in timed]
-    byts = [algorithmic_bytes(w, lens) for _, lens in timed]
+    # the tables after the last step serve every timed step: warm-up has made every
+    # copy-on-write, and blocks a later step adds hold no token of an earlier one
+    tables_now, _ = runner.alloc.export(runner.seqs, runner.MB)
+    logical = [algorithmic_bytes(w, lens) for _, lens in timed]
+    byts = [algorithmic_bytes(w, lens, tables_now) for _, lens in timed]
     mean_ms = float(np.mean(ms))
     achieved = float(np.mean(byts)) / (mean_ms * 1e-3) / 1e9
     tokens_per_s = w.B * args.steps / elapsed
+    app = runner.append_ms()
+    cold = runner.cold_decode_ms(args.cold_reps) if args.cold_reps else []
     # the committed counters cover the headline batch only
     traffic = (traffic_from_profiles(kernel_sources_hash())
                if args.workload == TRAFFIC_WORKLOAD else None)
@@ -633,13 +721,26 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
                      "traffic": traffic},
         "decode_ms_mean": round(mean_ms, 5),
+        "decode_ms_median": round(float(np.median(ms)), 5),
         "decode_ms_p10_p90": [round(float(np.percentile(ms, 10)), 5),
                               round(float(np.percentile(ms, 90)), 5)],
         "decode_algorithmic_bytes_mean": int(np.mean(byts)),
+        "decode_logical_bytes_mean": int(np.mean(logical)),
         "decode_tokens_per_s": round(w.B / (mean_ms * 1e-3), 1),
     }
+    if app:
+        rec["append_ms_mean"] = round(float(np.mean([t for t, _ in app])), 5)
+        rec["append_cow_pairs_timed"] = int(sum(n for _, n in app))
+    if cold:
+        cmed = float(np.median(cold))
+        rec["decode_cold_ms_median"] = round(cmed, 5)
+        rec["decode_cold_gbps"] = round(float(np.mean(byts)) / (cmed * 1e-3) / 1e9, 1)
+    rec["stream_copy_gbps"] = stream_copy_gbps()
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_seconds)
+        n = host_threads()
+        if n > 1:
+            rec["cpu_baseline_all_cores"] = cpu_baseline(args.workload, args.cpu_seconds / 2, n)
     print(json.dumps(rec), flush=True)
 
 

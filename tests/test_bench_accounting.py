@@ -1,0 +1,41 @@
+"""bench.py's byte and flop accounting, checked by hand on tiny cases (CPU only)."""
+import numpy as np
+
+import bench
+import inputs
+
+
+def _w(kv="bf16", B=2, Hq=4, Hkv=2, D=64):
+    w = inputs.tiny_fp32()
+    w.kv_dtype, w.q_dtype, w.B, w.Hq, w.Hkv, w.D = kv, "bf16", B, Hq, Hkv, D
+    return w
+
+
+def test_shared_block_counts_once():
+    w = _w()
+    lens = np.array([20, 18])
+    tables = np.array([[5, 7], [5, 9]])     # block 5 shared in full, 7 and 9 private
+    per_token = w.Hkv * w.D * 2 * 2         # K and V, bf16
+    fixed = w.B * w.Hq * w.D * 2 + w.B * w.Hq * w.D * 4 + 4 * 4 + w.B * 4  # q, out, 4 table entries, lens
+    assert bench.algorithmic_bytes(w, lens) == 38 * per_token + fixed
+    assert bench.algorithmic_bytes(w, lens, tables) == (16 + 4 + 2) * per_token + fixed
+
+
+def test_partially_shared_block_takes_its_longest_reader():
+    w = _w(kv="i8")
+    lens = np.array([10, 13])
+    tables = np.array([[3], [3]])           # one block read to 10 and to 13 tokens
+    per_token = w.Hkv * w.D * 2 * 1
+    fixed = w.B * w.Hq * w.D * 2 + w.B * w.Hq * w.D * 4 + 2 * 4 + w.B * 4
+    scales = 1 * w.Hkv * 2 * 4               # one touched tile per KV head, K and V scales
+    assert bench.algorithmic_bytes(w, lens, tables) == 13 * per_token + scales + fixed
+
+
+def test_prefill_flops_brute_force():
+    w = _w(Hq=4, D=64)
+    lens, chunks = [7, 5, 3], [3, 5, 1]
+    keys = 0
+    for L, n in zip(lens, chunks):
+        for i in range(n):
+            keys += (L - n + i) + 1          # keys 0..p of the query at position p
+    assert bench.prefill_flops(w, lens, chunks) == 4 * w.D * w.Hq * keys
