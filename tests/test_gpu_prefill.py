@@ -82,3 +82,15 @@ def test_chunk_longer_than_context():
     """Rows whose position L - n + i is negative have no keys and come out zero."""
     w = _workload(4, 128, [5, 40, 0, 70], cid=81)
     _run(w, [8, 40, 3, 70])
+
+
+def test_bench_prefill_workload_sampled():
+    """The chunked-prefill batch bench.py times (B 8, 512-query chunks after 1.5-3.6 K cached
+    tokens), through the same launch configuration, checked on sampled (row, head) pairs."""
+    import bench
+    w, chunks = bench.prefill_workload()
+    rng = np.random.default_rng([284, 72, 99])
+    T = int(chunks.sum())
+    rows = sorted({(int(r), int(h)) for r, h in zip(rng.integers(0, T, 48), rng.integers(0, 32, 48))})
+    rows += [(0, 0), (511, 31), (T - 1, 5)]
+    _run(w, chunks, rows=rows)
