@@ -319,16 +319,20 @@ int pa_decode(float* out, const void* q, int32_t q_dtype, const void* k_cache,
  * entry per token).  Query i of the chunk sits at position p = seq_lens[b] - n_b + i:
  *     out[row][h] = sum_{t <= p} softmax_t(scale * <q[row][h], K_t>) V_t   (KV head h/(Hq/Hkv)),
  * and a row with p < 0 gets zeros.
- *   q: device [T][Hq][D] PA_BF16; k_cache / v_cache PA_BF16 (other dtypes: PA_ERR_UNSUPPORTED);
+ *   q: device [T][Hq][D] PA_BF16 (PA_F32: PA_ERR_UNSUPPORTED).
+ *   k_cache / v_cache: PA_BF16, PA_I8 or PA_I4 in the layouts above (PA_F32:
+ *   PA_ERR_UNSUPPORTED); for PA_I8 / PA_I4 also k_scale / v_scale, device [NB][Hkv] fp32
+ *   (element = code * scale), else ignored.  Quantised caches run the products in fp16: q and
+ *   P * v_scale are rounded to fp16, and v_scale must stay below 2^14 (|V| below 2^21 for int8).
  *   out: device [T][Hq][D] fp32; cu_q: device [B + 1] int32, non-decreasing, cu_q[0] = 0,
  *   cu_q[B] = T; seq_lens: device [B] int32; max_seq_len bounds every seq_lens[b];
  *   Hq/Hkv in {1, 2, 4, 8, 16}, D in {64, 128}, bs == 16.  Needs no workspace.  Compute-bound:
  *   each K/V tile is shared by 16 queries of every head of its group. */
 int pa_prefill(float* out, const void* q, int32_t q_dtype, const void* k_cache,
-               const void* v_cache, int32_t kv_dtype, const int32_t* block_tables,
-               int32_t max_blocks, const int32_t* seq_lens, const int32_t* cu_q,
-               int32_t max_seq_len, int32_t B, int32_t T, int32_t Hq, int32_t Hkv, int32_t D,
-               int32_t bs, int32_t NB, float scale, void* stream);
+               const void* v_cache, int32_t kv_dtype, const float* k_scale, const float* v_scale,
+               const int32_t* block_tables, int32_t max_blocks, const int32_t* seq_lens,
+               const int32_t* cu_q, int32_t max_seq_len, int32_t B, int32_t T, int32_t Hq,
+               int32_t Hkv, int32_t D, int32_t bs, int32_t NB, float scale, void* stream);
 
 #ifdef __cplusplus
 }

@@ -73,8 +73,8 @@ _SIGNATURES = {
     "pa_append_step": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
                                  _i32, _i32, _i32, _i32, _vp]),
     "pa_decode_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
-    "pa_prefill": (C.c_int, [_vp, _vp, _i32, _vp, _vp, _i32, _vp, _i32, _vp, _vp, _i32, _i32,
-                             _i32, _i32, _i32, _i32, _i32, _i32, _f32, _vp]),
+    "pa_prefill": (C.c_int, [_vp, _vp, _i32, _vp, _vp, _i32, _vp, _vp, _vp, _i32, _vp, _vp,
+                             _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _vp]),
     "pa_decode": (C.c_int, [_vp, _vp, _i32, _vp, _vp, _i32, _vp, _vp, _vp, _i32, _vp, _i32,
                             _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz, _vp]),
 }
@@ -557,15 +557,16 @@ def decode(q, k_cache, v_cache, block_tables, seq_lens, max_seq_len: int, scale:
 
 
 def prefill(q, k_cache, v_cache, block_tables, seq_lens, cu_q, max_seq_len: int, scale: float,
-            out=None, stream=None):
+            k_scale=None, v_scale=None, out=None, stream=None):
     """Chunked-prefill attention: q [T][Hq][D] bf16 packed by cu_q [B+1]; each sequence's chunk
-    is the last cu_q[b+1]-cu_q[b] of its seq_lens[b] cached tokens.  Returns out [T][Hq][D]
+    is the last cu_q[b+1]-cu_q[b] of its seq_lens[b] cached tokens.  The cache is bf16, int8 or
+    packed int4 (uint8 bytes; then k_scale / v_scale [NB][Hkv] float32).  Returns out [T][Hq][D]
     float32."""
     torch = _torch()
     T, Hq, D = q.shape
-    NB, Hkv, bs, Dk = k_cache.shape
+    NB, Hkv, bs, Dk = cache_geometry(k_cache, v_cache)
     B = seq_lens.shape[0]
-    if Dk != D or tuple(v_cache.shape) != (NB, Hkv, D, bs):
+    if Dk != D:
         raise ValueError("cache shapes do not match q")
     if block_tables.dim() != 2 or block_tables.shape[0] != B or tuple(cu_q.shape) != (B + 1,):
         raise ValueError("block_tables must be [B][max_blocks] and cu_q [B+1]")
@@ -575,7 +576,9 @@ def prefill(q, k_cache, v_cache, block_tables, seq_lens, cu_q, max_seq_len: int,
         raise ValueError("out must be [T][Hq][D]")
     _check(lib().pa_prefill(_dev(out, "out", torch.float32), _dev(q, "q"), _dtype_code(q),
                             _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
-                            _dtype_code(k_cache), _dev(block_tables, "block_tables", torch.int32),
+                            _dtype_code(k_cache), _dev(k_scale, "k_scale", torch.float32),
+                            _dev(v_scale, "v_scale", torch.float32),
+                            _dev(block_tables, "block_tables", torch.int32),
                             block_tables.shape[1], _dev(seq_lens, "seq_lens", torch.int32),
                             _dev(cu_q, "cu_q", torch.int32), max_seq_len, B, T, Hq, Hkv, D, bs,
                             NB, float(scale), _stream(stream)), "pa_prefill")

@@ -304,27 +304,32 @@ int pa_decode(float* out, const void* q, int32_t q_dtype, const void* k_cache,
 }
 
 int pa_prefill(float* out, const void* q, int32_t q_dtype, const void* k_cache,
-               const void* v_cache, int32_t kv_dtype, const int32_t* block_tables,
-               int32_t max_blocks, const int32_t* seq_lens, const int32_t* cu_q,
-               int32_t max_seq_len, int32_t B, int32_t T, int32_t Hq, int32_t Hkv, int32_t D,
-               int32_t bs, int32_t NB, float scale, void* stream) {
+               const void* v_cache, int32_t kv_dtype, const float* k_scale, const float* v_scale,
+               const int32_t* block_tables, int32_t max_blocks, const int32_t* seq_lens,
+               const int32_t* cu_q, int32_t max_seq_len, int32_t B, int32_t T, int32_t Hq,
+               int32_t Hkv, int32_t D, int32_t bs, int32_t NB, float scale, void* stream) {
   if (B < 0 || T < 0 || Hq < 1 || Hkv < 1 || NB < 1 || max_blocks < 0 || max_seq_len < 0)
     return PA_ERR_INVALID;
   if (Hq % Hkv != 0 || (D != 64 && D != 128)) return PA_ERR_INVALID;
   const int32_t G = Hq / Hkv;
   if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16) return PA_ERR_UNSUPPORTED;
   if (bs != pa::kBlockSize) return PA_ERR_UNSUPPORTED;
-  if (q_dtype != PA_BF16 || kv_dtype != PA_BF16) {
+  if (q_dtype != PA_BF16 || kv_dtype == PA_F32) {
     const bool known = (q_dtype == PA_F32 || q_dtype == PA_BF16) && known_kv(kv_dtype);
     return known ? PA_ERR_UNSUPPORTED : PA_ERR_INVALID;
   }
+  if (!known_kv(kv_dtype)) return PA_ERR_INVALID;
   if (static_cast<int64_t>(max_seq_len) > static_cast<int64_t>(max_blocks) * bs)
     return PA_ERR_INVALID;
   if (!(scale == scale)) return PA_ERR_INVALID;
   if (B == 0 || T == 0) return PA_OK;
   if (!out || !q || !k_cache || !v_cache || !seq_lens || !cu_q || (max_blocks > 0 && !block_tables))
     return PA_ERR_INVALID;
+  if (quantised(kv_dtype) && (!k_scale || !v_scale)) return PA_ERR_INVALID;
   pa::PrefillArgs a{};
+  a.kv_kind = kv_dtype == PA_I8 ? pa::kKvI8 : (kv_dtype == PA_I4 ? pa::kKvI4 : pa::kKvBf16);
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
   a.out = out;
   a.q = q;
   a.k = k_cache;

@@ -630,6 +630,6 @@ const char* pa_status_string(int status) {
   }
 }
 
-int pa_abi_version(void) { return 3; }
+int pa_abi_version(void) { return 4; }
 
 }  // extern "C"

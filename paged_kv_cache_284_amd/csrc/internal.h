@@ -33,11 +33,14 @@ struct DecodeArgs {
 };
 
 // Everything one chunked-prefill launch needs.  Pointers are device pointers.
+// Cache element kinds the matrix-core kernels are templated on.
+constexpr int kKvBf16 = 0, kKvI8 = 1, kKvI4 = 2;
+
 struct PrefillArgs {
   float* out;                 // [T][Hq][D]
   const void* q;              // [T][Hq][D] bf16
-  const void* k;              // [NB][Hkv][bs][D] bf16
-  const void* v;              // [NB][Hkv][D][bs] bf16
+  const void* k;              // [NB][Hkv][bs][D] bf16 / int8, [NB][Hkv][bs][D/2] packed int4
+  const void* v;              // [NB][Hkv][D][bs] bf16 / int8, [NB][Hkv][D][bs/2] packed int4
   const int32_t* tables;      // [B][max_blocks]
   const int32_t* seq_lens;    // [B] context length, the chunk included
   const int32_t* cu_q;        // [B + 1] first query row of each sequence's chunk
@@ -45,6 +48,9 @@ struct PrefillArgs {
   int32_t B, T, Hq, Hkv, D, NB;
   int32_t max_tiles;          // grid bound on the number of 64-query workgroups
   float scale_log2;
+  int32_t kv_kind;            // 0 bf16, 1 int8, 2 packed int4 cache
+  const float* k_scale;       // [NB][Hkv], quantised caches
+  const float* v_scale;
 };
 
 // Upper bound on balanced-schedule workgroups; sizes the workspace.

@@ -24,6 +24,7 @@
 
 #include "internal.h"
 #include "pagedkv.h"
+#include "quant_f16.h"
 
 namespace pa {
 namespace {
@@ -32,6 +33,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kTile = 16;              // queries per wave
 constexpr int kPairTok = 2 * kBlockSize;
@@ -61,6 +64,7 @@ __device__ __forceinline__ float sum_across_groups(float x) {
 }
 
 constexpr float kOverP = 2.305843e18f;    // 2^61: a pair's P sum above this asks for a rerun
+constexpr float kOverPQ = 16384.f;         // 2^14: the same bound on P x V scale (fp16 operand)
 constexpr float kUnderL = 8.6736174e-19f;  // 2^-60: a final l below this asks for a rerun
 
 struct Pair {
@@ -107,12 +111,53 @@ constexpr int kHeadsPerWave = G < 4 ? G : 4;
 constexpr int kWavesPerWG = 4;                       // consecutive 16-query tiles
 constexpr int kGroupQueries = kTile * kWavesPerWG;   // queries per workgroup
 
-template <int G, int D>
+// Operand registers of one block pair for each cache kind.  bf16: K rows (two 16-token halves
+// of the score tile) and V rows as 16-byte loads.  int8: 16 dims of a K row per load (two
+// k-steps), 8 tokens of a V row per 8-byte load.  int4: the 4-byte groups of packed nibbles a
+// lane feeds one k-step (K) or its 8 tokens of one dim (V).
+template <int kKV, int D>
+struct KOps;
+template <int D>
+struct KOps<kKvBf16, D> {
+  u32x4 k1[D / 32], k2[D / 32];
+  float ks_a, ks_b;
+};
+template <int D>
+struct KOps<kKvI8, D> {
+  u32x4 k1[D / 64], k2[D / 64];
+  float ks_a, ks_b;
+};
+template <int D>
+struct KOps<kKvI4, D> {
+  uint32_t k1[D / 32], k2[D / 32];
+  float ks_a, ks_b;
+};
+template <int kKV, int D>
+struct VOps;
+template <int D>
+struct VOps<kKvBf16, D> {
+  u32x4 v[D / 16];
+  float vs_a, vs_b;
+};
+template <int D>
+struct VOps<kKvI8, D> {
+  u32x2 v[D / 16];
+  float vs_a, vs_b;
+};
+template <int D>
+struct VOps<kKvI4, D> {
+  uint32_t v[D / 16];
+  float vs_a, vs_b;
+};
+
+template <int G, int D, int kKV>
 __global__ void __launch_bounds__(64 * kWavesPerWG) __attribute__((amdgpu_waves_per_eu(1, 1)))
 prefill_mfma_kernel(PrefillArgs a) {
   constexpr int kSteps = D / 32;
   constexpr int kTiles = D / 16;
   constexpr int kH = kHeadsPerWave<G>;
+  constexpr bool kQ = kKV != kKvBf16;  // quantised cache: fp16 matrix-core operands
+  constexpr float kOffset = kKV == kKvI4 ? kNibbleOffset : kCodeOffset;
   const int lane = threadIdx.x % 64;
   const int w = threadIdx.x / 64;
   const int r = lane % 16, qg = lane / 16;
@@ -134,25 +179,50 @@ prefill_mfma_kernel(PrefillArgs a) {
   const int my_q = qi0 + r;
   const int my_p = L - n + my_q;
   const int32_t* __restrict__ table = a.tables + static_cast<int64_t>(b) * a.max_blocks;
-  const uint16_t* __restrict__ kc = static_cast<const uint16_t*>(a.k);
-  const uint16_t* __restrict__ vc = static_cast<const uint16_t*>(a.v);
   const int NB = a.NB, Hkv = a.Hkv;
 
-  // Scores enter the exponent as fma(s, c, -m) with c = |scale log2 e| > 0; a negative scale
-  // flips the sign of q instead (exact in bf16), and c = 0 is raised to the least normal float,
-  // which leaves every score's product with it a zero of the exponent's rounding.
+  // bf16: scores enter the exponent as fma(s, c, -m) with c = |scale log2 e| > 0; a negative
+  // scale flips the sign of q instead (exact), and c = 0 is raised to the least normal float,
+  // which leaves every score's product with it a zero of the exponent's rounding.  Quantised
+  // caches fold c with the block's K scale into the score itself (cx = 1 below).
   const float c = fmaxf(fabsf(a.scale_log2), 1.17549435e-38f);
-  const uint32_t q_sign = a.scale_log2 < 0.f ? 0x80008000u : 0u;
-  // Q^T operands: query column r of head h0 + hh, dims 32 s + 8 qg .. +8 (row clamped)
+  const float cx = kQ ? 1.f : c;
+  const bool q_neg = a.scale_log2 < 0.f;
+  // Q^T operands: query column r of head h0 + hh (row clamped).  bf16: step s covers dims
+  // 32 s + 8 qg .. +8.  Quantised: fp16 (bf16 -> fp16 is exact in fp16's normal range); int8
+  // step s covers dims 16 (qg + 4 (s / 2)) + 8 (s % 2) .. +8 (the 16-dim K loads), int4 step s
+  // dims 8 kSteps qg + 8 s .. +8 (the packed 4-byte groups).  qsum: the sum of the rounded fp16
+  // q over the head's dims, which takes the code offset out of the scores.
   u32x4 qv[kH][kSteps];
+  float qsum[kH];
   {
     const int qrow = min(max(row0 + min(my_q, n - 1), 0), a.T - 1);
 #pragma unroll
     for (int hh = 0; hh < kH; ++hh) {
       const uint16_t* q = static_cast<const uint16_t*>(a.q) +
                           (static_cast<int64_t>(qrow) * a.Hq + h0 + hh) * D;
+      float part = 0.f;
 #pragma unroll
-      for (int s = 0; s < kSteps; ++s) qv[hh][s] = ld16(q + 32 * s + 8 * qg) ^ q_sign;
+      for (int s = 0; s < kSteps; ++s) {
+        if constexpr (kQ) {
+          const u32x4 raw = kKV == kKvI4 ? ld16(q + 8 * kSteps * qg + 8 * s)
+                                         : ld16(q + 16 * (qg + 4 * (s / 2)) + 8 * (s % 2));
+          f32x8 f;
+#pragma unroll
+          for (int cc = 0; cc < 4; ++cc) {
+            f[2 * cc] = __uint_as_float((raw[cc] << 16) ^ (q_neg ? 0x80000000u : 0u));
+            f[2 * cc + 1] = __uint_as_float((raw[cc] & 0xffff0000u) ^ (q_neg ? 0x80000000u : 0u));
+          }
+          const f16x8 h = __builtin_convertvector(f, f16x8);
+          qv[hh][s] = __builtin_bit_cast(u32x4, h);
+          const f32x8 back = __builtin_convertvector(h, f32x8);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) part += back[e];
+        } else {
+          qv[hh][s] = ld16(q + 32 * s + 8 * qg) ^ (q_neg ? 0x80008000u : 0u);
+        }
+      }
+      qsum[hh] = kQ ? sum_across_groups(part) : 0.f;
     }
   }
 
@@ -168,41 +238,90 @@ prefill_mfma_kernel(PrefillArgs a) {
     int32_t bb = (tok0 + kBlockSize < kv_end) ? table[jb + 1] : -1;
     return Pair{(ba >= 0 && ba < NB) ? ba : -1, (bb >= 0 && bb < NB) ? bb : -1};
   };
-  auto tile_of = [&](int32_t blk) {
-    return (static_cast<int64_t>(blk < 0 ? 0 : blk) * Hkv + g) * (kBlockSize * D);
+  auto tile_idx = [&](int32_t blk) {  // (block, KV head) tile number
+    return static_cast<int64_t>(blk < 0 ? 0 : blk) * Hkv + g;
   };
-  u32x4 k1[kSteps], k2[kSteps], vr[kTiles];
+  KOps<kKV, D> ko;
+  VOps<kKV, D> vo;
   auto load_k = [&](Pair bl) {
-    const int64_t ta = tile_of(bl.a), tb = tile_of(bl.b);
-    const uint16_t* p1 = kc + (tok1 < 16 ? ta : tb) + (tok1 % 16) * D + 8 * qg;
-    const uint16_t* p2 = kc + (tok2 < 16 ? ta : tb) + (tok2 % 16) * D + 8 * qg;
+    const int64_t ia = tile_idx(bl.a), ib = tile_idx(bl.b);
+    if constexpr (kKV == kKvBf16) {
+      const uint16_t* kc = static_cast<const uint16_t*>(a.k);
+      const uint16_t* p1 = kc + (tok1 < 16 ? ia : ib) * (kBlockSize * D) + (tok1 % 16) * D + 8 * qg;
+      const uint16_t* p2 = kc + (tok2 < 16 ? ia : ib) * (kBlockSize * D) + (tok2 % 16) * D + 8 * qg;
 #pragma unroll
-    for (int s = 0; s < kSteps; ++s) {
-      k1[s] = ld16(p1 + 32 * s);
-      k2[s] = ld16(p2 + 32 * s);
+      for (int s = 0; s < kSteps; ++s) {
+        ko.k1[s] = ld16(p1 + 32 * s);
+        ko.k2[s] = ld16(p2 + 32 * s);
+      }
+    } else {
+      ko.ks_a = a.k_scale[ia];
+      ko.ks_b = a.k_scale[ib];
+      const uint8_t* kc = static_cast<const uint8_t*>(a.k);
+      if constexpr (kKV == kKvI8) {
+        const uint8_t* p1 = kc + (tok1 < 16 ? ia : ib) * (kBlockSize * D) + (tok1 % 16) * D + 16 * qg;
+        const uint8_t* p2 = kc + (tok2 < 16 ? ia : ib) * (kBlockSize * D) + (tok2 % 16) * D + 16 * qg;
+#pragma unroll
+        for (int cc = 0; cc < kSteps / 2; ++cc) {
+          ko.k1[cc] = *reinterpret_cast<const u32x4*>(p1 + 64 * cc);
+          ko.k2[cc] = *reinterpret_cast<const u32x4*>(p2 + 64 * cc);
+        }
+      } else {  // int4: tiles of bs * D / 2 bytes
+        const uint8_t* p1 = kc + (tok1 < 16 ? ia : ib) * (kBlockSize * D / 2) +
+                            (tok1 % 16) * (D / 2) + 4 * kSteps * qg;
+        const uint8_t* p2 = kc + (tok2 < 16 ? ia : ib) * (kBlockSize * D / 2) +
+                            (tok2 % 16) * (D / 2) + 4 * kSteps * qg;
+#pragma unroll
+        for (int cc = 0; cc < kSteps; ++cc) {
+          ko.k1[cc] = *reinterpret_cast<const uint32_t*>(p1 + 4 * cc);
+          ko.k2[cc] = *reinterpret_cast<const uint32_t*>(p2 + 4 * cc);
+        }
+      }
     }
   };
   auto load_v = [&](Pair bl) {
-    const uint16_t* pv = vc + tile_of(vsel ? bl.b : bl.a) + r * kBlockSize + vtok;
+    const int64_t it = tile_idx(vsel ? bl.b : bl.a);
+    if constexpr (kKV == kKvBf16) {
+      const uint16_t* pv = static_cast<const uint16_t*>(a.v) + it * (kBlockSize * D) +
+                           r * kBlockSize + vtok;
 #pragma unroll
-    for (int t = 0; t < kTiles; ++t) vr[t] = ld16(pv + 16 * t * kBlockSize);
+      for (int t = 0; t < kTiles; ++t) vo.v[t] = ld16(pv + 16 * t * kBlockSize);
+    } else {
+      vo.vs_a = a.v_scale[tile_idx(bl.a)];
+      vo.vs_b = a.v_scale[tile_idx(bl.b)];
+      const uint8_t* vc = static_cast<const uint8_t*>(a.v);
+      if constexpr (kKV == kKvI8) {
+        const uint8_t* pv = vc + it * (kBlockSize * D) + r * kBlockSize + vtok;
+#pragma unroll
+        for (int t = 0; t < kTiles; ++t)
+          vo.v[t] = *reinterpret_cast<const u32x2*>(pv + 16 * t * kBlockSize);
+      } else {
+        const uint8_t* pv = vc + it * (kBlockSize * D / 2) + r * (kBlockSize / 2) + 4 * (qg % 2);
+#pragma unroll
+        for (int t = 0; t < kTiles; ++t)
+          vo.v[t] = *reinterpret_cast<const uint32_t*>(pv + 16 * t * (kBlockSize / 2));
+      }
+    }
   };
 
   // Softmax against a fixed reference per query instead of a running maximum: P = 2^(s c - ref)
   // and the accumulators are never rescaled; the quotient acc / l is the same for any ref.  The
   // reference is the scaled maximum of the first pair (tokens 0..31), a score the sum contains,
   // so the largest P is at least 1 and nothing that matters underflows.  Should a later pair's
-  // P sum pass 2^61 (a score more than about 2^61 above the reference), or the final l stay
-  // below 2^-60 (the first pair had no key for this query), the wave sweeps its keys once for
-  // the exact maximum and runs the tile again with that as the reference, which no score can
-  // exceed.
-  float ref[kH], l_run[kH];
+  // P sum leave range (past 2^61 for bf16; for quantised caches, P times the V scale past 2^14,
+  // so that the fp16 P operand stays finite), or the final l stay below 2^-60 (the first pair
+  // had no key for this query), the wave sweeps its keys once for the exact maximum and runs the
+  // tile again with that as the reference, which no score can exceed.
+  float ref[kH], l_run[kH], c_run[kH];
   f32x4 acc[kH][kTiles];
   const int p_first = L - n + qi0;     // position of the tile's first query
   const int limit = min(my_p, L - 1);  // keys t <= limit count for this lane's query
   const int n_pairs = kv_end > 0 ? (kv_end + kPairTok - 1) / kPairTok : 0;
 
   f32x4 s1[kH], s2[kH];
+  // Scores of the pair in ko: bf16 leaves the raw products (scaled in the exponent); quantised
+  // caches turn them into log2-domain scores, ks (sum q (offset + c) - offset qsum) |scale log2 e|,
+  // with the K scale of the block this lane's tokens come from.
   auto scores = [&]() {
 #pragma unroll
     for (int hh = 0; hh < kH; ++hh) {
@@ -210,10 +329,33 @@ prefill_mfma_kernel(PrefillArgs a) {
       s2[hh] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < kSteps; ++s) {
-        s1[hh] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(k1[s]), as_bf16x8(qv[hh][s]),
-                                                          s1[hh], 0, 0, 0);
-        s2[hh] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(k2[s]), as_bf16x8(qv[hh][s]),
-                                                          s2[hh], 0, 0, 0);
+        if constexpr (kKV == kKvBf16) {
+          s1[hh] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ko.k1[s]),
+                                                            as_bf16x8(qv[hh][s]), s1[hh], 0, 0, 0);
+          s2[hh] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ko.k2[s]),
+                                                            as_bf16x8(qv[hh][s]), s2[hh], 0, 0, 0);
+        } else {
+          f16x8 a1, a2;
+          if constexpr (kKV == kKvI8) {
+            a1 = codes_to_f16(ko.k1[s / 2][2 * (s % 2)], ko.k1[s / 2][2 * (s % 2) + 1]);
+            a2 = codes_to_f16(ko.k2[s / 2][2 * (s % 2)], ko.k2[s / 2][2 * (s % 2) + 1]);
+          } else {
+            a1 = nibbles_to_f16(ko.k1[s]);
+            a2 = nibbles_to_f16(ko.k2[s]);
+          }
+          const f16x8 qh = __builtin_bit_cast(f16x8, qv[hh][s]);
+          s1[hh] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, qh, s1[hh], 0, 0, 0);
+          s2[hh] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a2, qh, s2[hh], 0, 0, 0);
+        }
+      }
+      if constexpr (kQ) {
+        const float f = (vsel ? ko.ks_b : ko.ks_a) * c;
+        const float c0 = -kOffset * qsum[hh] * f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          s1[hh][e] = fmaf(s1[hh][e], f, c0);
+          s2[hh][e] = fmaf(s2[hh][e], f, c0);
+        }
       }
     }
   };
@@ -236,7 +378,7 @@ prefill_mfma_kernel(PrefillArgs a) {
   auto pair_max = [&](int hh) {
     float m = fmaxf(fmaxf(fmaxf(s1[hh][0], s1[hh][1]), fmaxf(s1[hh][2], s1[hh][3])),
                     fmaxf(fmaxf(s2[hh][0], s2[hh][1]), fmaxf(s2[hh][2], s2[hh][3])));
-    return max_across_groups(m) * c;
+    return max_across_groups(m) * cx;
   };
   // exact maximum over all keys of the tile (the rare second pass)
   auto sweep_max = [&]() {
@@ -270,6 +412,7 @@ prefill_mfma_kernel(PrefillArgs a) {
     for (int hh = 0; hh < kH; ++hh) {
       r0[hh] = ref[hh] == -INFINITY ? 0.f : ref[hh];
       l_run[hh] = 0.f;
+      c_run[hh] = 0.f;
 #pragma unroll
       for (int t = 0; t < kTiles; ++t) acc[hh][t] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
@@ -289,47 +432,73 @@ prefill_mfma_kernel(PrefillArgs a) {
       const int32_t my_blk = vsel ? cur.b : cur.a;
       scores();
       if (more) load_k(nxt);
-      if (tok0 + kPairTok > L || cur.a < 0 || cur.b < 0) {
-        // tokens past the context (or of a missing block) must not reach P.V even with p = 0
+      if constexpr (kKV == kKvBf16) {
+        if (tok0 + kPairTok > L || cur.a < 0 || cur.b < 0) {
+          // tokens past the context (or of a missing block) must not reach P.V even with
+          // p = 0 (their V may be anything); quantised codes are always finite, so there
+          // p = 0 is enough
 #pragma unroll
-        for (int cc = 0; cc < 4; ++cc) {
-          const bool k0 = my_blk >= 0 && t_first + 2 * cc < L;
-          const bool k1b = my_blk >= 0 && t_first + 2 * cc + 1 < L;
-          const uint32_t keep = (k0 ? 0x0000ffffu : 0u) | (k1b ? 0xffff0000u : 0u);
+          for (int cc = 0; cc < 4; ++cc) {
+            const bool k0 = my_blk >= 0 && t_first + 2 * cc < L;
+            const bool k1b = my_blk >= 0 && t_first + 2 * cc + 1 < L;
+            const uint32_t keep = (k0 ? 0x0000ffffu : 0u) | (k1b ? 0xffff0000u : 0u);
 #pragma unroll
-          for (int t = 0; t < kTiles; ++t) vr[t][cc] &= keep;
+            for (int t = 0; t < kTiles; ++t) vo.v[t][cc] &= keep;
+          }
         }
       }
       if (is_edge(tok0, cur)) mask_scores(tok0, my_blk);
+      const float vsc = kQ ? (vsel ? vo.vs_b : vo.vs_a) : 1.f;
 #pragma unroll
       for (int hh = 0; hh < kH; ++hh) {
         f32x8 pv;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          pv[e] = __builtin_amdgcn_exp2f(fmaf(s1[hh][e], c, -r0[hh]));
-          pv[4 + e] = __builtin_amdgcn_exp2f(fmaf(s2[hh][e], c, -r0[hh]));
+          pv[e] = __builtin_amdgcn_exp2f(fmaf(s1[hh][e], cx, -r0[hh]));
+          pv[4 + e] = __builtin_amdgcn_exp2f(fmaf(s2[hh][e], cx, -r0[hh]));
         }
         const float psum = ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
         l_run[hh] += psum;
-        over = over || !(psum <= kOverP);
         // O^T += V^T . P^T: V rows are dims, P^T columns are this lane's query, so the
-        // accumulator column of a lane is its own query.  P enters as a bf16 pair hi + lo,
-        // which carries it to about 16 bits.
-        const bf16x8 p_hi = __builtin_convertvector(pv, bf16x8);
-        const u32x4 hb = __builtin_bit_cast(u32x4, p_hi);
-        f32x8 rest;
+        // accumulator column of a lane is its own query
+        if constexpr (kKV == kKvBf16) {
+          over = over || !(psum <= kOverP);
+          // P enters as a bf16 pair hi + lo, which carries it to about 16 bits
+          const bf16x8 p_hi = __builtin_convertvector(pv, bf16x8);
+          const u32x4 hb = __builtin_bit_cast(u32x4, p_hi);
+          f32x8 rest;
 #pragma unroll
-        for (int cc = 0; cc < 4; ++cc) {
-          rest[2 * cc] = pv[2 * cc] - __uint_as_float(hb[cc] << 16);
-          rest[2 * cc + 1] = pv[2 * cc + 1] - __uint_as_float(hb[cc] & 0xffff0000u);
-        }
-        const bf16x8 p_lo = __builtin_convertvector(rest, bf16x8);
+          for (int cc = 0; cc < 4; ++cc) {
+            rest[2 * cc] = pv[2 * cc] - __uint_as_float(hb[cc] << 16);
+            rest[2 * cc + 1] = pv[2 * cc + 1] - __uint_as_float(hb[cc] & 0xffff0000u);
+          }
+          const bf16x8 p_lo = __builtin_convertvector(rest, bf16x8);
 #pragma unroll
-        for (int t = 0; t < kTiles; ++t) {
-          acc[hh][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vr[t]), p_hi,
-                                                                acc[hh][t], 0, 0, 0);
-          acc[hh][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vr[t]), p_lo,
-                                                                acc[hh][t], 0, 0, 0);
+          for (int t = 0; t < kTiles; ++t) {
+            acc[hh][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vo.v[t]), p_hi,
+                                                                  acc[hh][t], 0, 0, 0);
+            acc[hh][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vo.v[t]), p_lo,
+                                                                  acc[hh][t], 0, 0, 0);
+          }
+        } else {
+          over = over || !(psum * vsc <= kOverPQ);
+          // P times the block's V scale as one fp16 operand next to the fp16 codes; the code
+          // offset comes out with the sum of exactly these rounded operands, so it cancels
+#pragma unroll
+          for (int e = 0; e < 8; ++e) pv[e] *= vsc;
+          const f16x8 p16 = __builtin_convertvector(pv, f16x8);
+          const f32x8 pr = __builtin_convertvector(p16, f32x8);
+          c_run[hh] += ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
+#pragma unroll
+          for (int t = 0; t < kTiles; ++t) {
+            f16x8 vop;
+            if constexpr (kKV == kKvI8) {
+              vop = codes_to_f16(vo.v[t][0], vo.v[t][1]);
+            } else {
+              vop = nibbles_to_f16(vo.v[t]);
+            }
+            acc[hh][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop, p16, acc[hh][t], 0, 0, 0);
+          }
         }
       }
       if (more) load_v(nxt);
@@ -349,23 +518,35 @@ prefill_mfma_kernel(PrefillArgs a) {
 #pragma unroll
   for (int hh = 0; hh < kH; ++hh) {
     const float lq = sum_across_groups(l_run[hh]);
+    const float off = kQ ? kOffset * sum_across_groups(c_run[hh]) : 0.f;
     if (store) {
       float* o = a.out + (static_cast<int64_t>(out_row) * a.Hq + h0 + hh) * D + 4 * qg;
 #pragma unroll
       for (int t = 0; t < kTiles; ++t) {
-        const f32x4 y = lq > 0.f ? acc[hh][t] / lq : f32x4{0.f, 0.f, 0.f, 0.f};
+        const f32x4 y = lq > 0.f ? (acc[hh][t] - off) / lq : f32x4{0.f, 0.f, 0.f, 0.f};
         *reinterpret_cast<f32x4*>(o + 16 * t) = y;
       }
     }
   }
 }
 
-template <int G, int D>
-hipError_t launch_gd(const PrefillArgs& a, hipStream_t stream) {
+template <int G, int D, int kKV>
+hipError_t launch_gdk(const PrefillArgs& a, hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>(a.max_tiles), static_cast<unsigned>(a.Hkv),
                   static_cast<unsigned>(G / kHeadsPerWave<G>));
-  hipLaunchKernelGGL((prefill_mfma_kernel<G, D>), grid, dim3(64 * kWavesPerWG), 0, stream, a);
+  hipLaunchKernelGGL((prefill_mfma_kernel<G, D, kKV>), grid, dim3(64 * kWavesPerWG), 0, stream,
+                     a);
   return hipGetLastError();
+}
+
+template <int G, int D>
+hipError_t launch_gd(const PrefillArgs& a, hipStream_t stream) {
+  switch (a.kv_kind) {
+    case kKvBf16: return launch_gdk<G, D, kKvBf16>(a, stream);
+    case kKvI8: return launch_gdk<G, D, kKvI8>(a, stream);
+    case kKvI4: return launch_gdk<G, D, kKvI4>(a, stream);
+    default: return hipErrorNotSupported;
+  }
 }
 
 template <int G>

@@ -15,10 +15,11 @@ from tests.gpu_cases import TOL, Case, say, to_device
 pytestmark = pytest.mark.gpu
 
 
-def _workload(G, D, lens, cid):
+def _workload(G, D, lens, cid, kv="bf16"):
     w = inputs.llama8b_decode(B=len(lens), lo=1, hi=2, cid=cid, name="prefill")
     w.lengths = np.array(lens, np.int64)
     w.Hkv, w.Hq, w.D = 2, 2 * G, D
+    w.kv_dtype = kv
     w.NB = int(sum((L + 15) // 16 for L in lens)) + 8
     w.append = False
     return w
@@ -32,13 +33,14 @@ def _run(w, chunks, rows=None, scale=None):
     cu = np.concatenate([[0], np.cumsum(chunks)]).astype(np.int32)
     T = int(cu[-1])
     q = inputs.chunk_queries(w, T)
-    say(f"prefill G={w.G} D={w.D} lens={list(lens)[:8]} chunks={list(chunks)[:8]} T={T} "
-        f"scale={scale}")
+    say(f"prefill G={w.G} D={w.D} kv={w.kv_dtype} lens={list(lens)[:8]} "
+        f"chunks={list(chunks)[:8]} T={T} scale={scale}")
     out = pkv.prefill(to_device(q, "bf16"), case.k, case.v, case.tables,
                       torch.from_numpy(lens).cuda(), torch.from_numpy(cu).cuda(),
-                      int(lens.max()), scale).cpu().numpy()
-    ref = prefill_paged(q, "bf16", case.host["k"], case.host["v"], "bf16", tables, lens, cu,
-                        w.bs, scale, rows=rows)
+                      int(lens.max()), scale, k_scale=case.ks, v_scale=case.vs).cpu().numpy()
+    ref = prefill_paged(q, "bf16", case.host["k"], case.host["v"], w.kv_dtype, tables, lens, cu,
+                        w.bs, scale, case.host.get("k_scale"), case.host.get("v_scale"),
+                        rows=rows)
     if rows is None:
         err = float(np.max(np.abs(out.astype(np.float64) - ref)))
         assert np.all(np.isfinite(out))
@@ -46,7 +48,7 @@ def _run(w, chunks, rows=None, scale=None):
         err = max(float(np.max(np.abs(out[r, h].astype(np.float64) - ref[r, h])))
                   for r, h in rows)
     say(f"max-abs error {err:.2e}")
-    assert err <= TOL["bf16"]
+    assert err <= TOL[w.kv_dtype]
 
 
 @pytest.mark.parametrize("G,D", [(4, 128), (1, 64), (2, 128), (8, 64), (16, 128)])
@@ -94,3 +96,23 @@ def test_bench_prefill_workload_sampled():
     rows = sorted({(int(r), int(h)) for r, h in zip(rng.integers(0, T, 48), rng.integers(0, 32, 48))})
     rows += [(0, 0), (511, 31), (T - 1, 5)]
     _run(w, chunks, rows=rows)
+
+
+@pytest.mark.parametrize("kv", ["i8", "i4"])
+@pytest.mark.parametrize("G,D", [(4, 128), (1, 64), (2, 128), (16, 64)])
+def test_quantised_cache_mixed_chunks(kv, G, D):
+    """Chunked prefill over int8 and packed int4 caches (codes and per-block scales), the same
+    chunk mix as the bf16 case, within the quantised tolerance of the oracle on the dequantised
+    values."""
+    lens = [37, 100, 16, 1, 0, 257, 64, 33]
+    chunks = [37, 20, 16, 1, 0, 100, 1, 17]
+    _run(_workload(G, D, lens, cid=90 + G + D, kv=kv), chunks)
+
+
+@pytest.mark.parametrize("kv", ["i8", "i4"])
+@pytest.mark.parametrize("scale", [1.0, -0.125])
+def test_quantised_score_range(kv, scale):
+    """A large scale drives P times the V scale past the fp16 bound of the first reference (the
+    exact-maximum rerun); a negative scale flips every score."""
+    w = _workload(4, 128, [300, 64, 700, 17], cid=95, kv=kv)
+    _run(w, [300, 33, 129, 17], scale=scale)

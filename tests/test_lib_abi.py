@@ -39,7 +39,7 @@ def test_binding_covers_every_declared_symbol():
 def test_status_strings():
     assert pkv.status_string(0) == "ok"
     assert pkv.status_string(-2) == "out of free blocks"
-    assert pkv.lib().pa_abi_version() == 3
+    assert pkv.lib().pa_abi_version() == 4
 
 
 FAKE = C.c_void_p(0x1000)  # never dereferenced: every call below must fail its host checks
@@ -82,6 +82,39 @@ def test_decode_rejects_on_host(kw, code):
 
 def test_decode_empty_batch_is_a_no_op():
     assert _decode(B=0, out=None, q=None) == pkv.PA_OK
+
+
+def _prefill(**kw):
+    args = dict(out=FAKE, q=FAKE, q_dtype=pkv.PA_BF16, k=FAKE, v=FAKE, kv_dtype=pkv.PA_BF16,
+                ks=None, vs=None, tables=FAKE, max_blocks=8, lens=FAKE, cu=FAKE, max_seq_len=128,
+                B=2, T=64, Hq=32, Hkv=8, D=128, bs=16, NB=100, scale=0.1, stream=None)
+    args.update(kw)
+    return pkv.lib().pa_prefill(*args.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(out=None), pkv.PA_ERR_INVALID),
+    (dict(cu=None), pkv.PA_ERR_INVALID),
+    (dict(Hq=30), pkv.PA_ERR_INVALID),                 # Hq % Hkv != 0
+    (dict(D=96), pkv.PA_ERR_INVALID),
+    (dict(bs=32), pkv.PA_ERR_UNSUPPORTED),
+    (dict(Hq=136, Hkv=8), pkv.PA_ERR_UNSUPPORTED),     # group of 17
+    (dict(q_dtype=pkv.PA_F32), pkv.PA_ERR_UNSUPPORTED),
+    (dict(kv_dtype=pkv.PA_F32), pkv.PA_ERR_UNSUPPORTED),
+    (dict(kv_dtype=7), pkv.PA_ERR_INVALID),
+    (dict(kv_dtype=pkv.PA_I8), pkv.PA_ERR_INVALID),    # int8 without scales
+    (dict(kv_dtype=pkv.PA_I4, ks=FAKE), pkv.PA_ERR_INVALID),   # int4 without v_scale
+    (dict(max_seq_len=129), pkv.PA_ERR_INVALID),       # beyond max_blocks * bs
+    (dict(T=-1), pkv.PA_ERR_INVALID),
+    (dict(scale=float("nan")), pkv.PA_ERR_INVALID),
+])
+def test_prefill_rejects_on_host(kw, code):
+    assert _prefill(**kw) == code
+
+
+def test_prefill_empty_is_a_no_op():
+    assert _prefill(T=0, out=None, q=None) == pkv.PA_OK
+    assert _prefill(B=0, out=None, kv_dtype=pkv.PA_I8) == pkv.PA_OK
 
 
 def test_append_and_copy_reject_on_host():
