@@ -20,7 +20,8 @@ and the oracle on all host threads.
 
 --workload prefill_llama8b measures the chunked-prefill path instead: one step appends a
 512-token chunk per sequence (one pa_kv_append entry per token) and runs pa_prefill over it;
-the roofline is then the matrix cores' bf16 peak.
+the roofline is then the matrix cores' bf16 peak (fp16 for the int8 / int4 caches of
+prefill_llama8b_i8 / prefill_llama8b_i4, the same 2.5 PFLOP/s).
 """
 from __future__ import annotations
 
@@ -303,7 +304,8 @@ def prefill_flops(w, lens, chunks) -> int:
 
 class PrefillRunner:
     """Device state of a chunked-prefill workload: the cache holds each sequence's context, the
-    step rewrites the chunk's K/V (one pa_kv_append entry per token) and runs pa_prefill."""
+    step rewrites the chunk's K/V (one append entry per token: pa_kv_append, or the quantising
+    append for int8 / int4 caches) and runs pa_prefill."""
 
     def __init__(self, w, chunks):
         import torch
@@ -326,7 +328,9 @@ class PrefillRunner:
             L, n = int(lens[b]), int(self.chunks[b])
             for p in range(L - n, L):
                 slots.append(int(tables[b][p // w.bs]) * w.bs + p % w.bs)
-            kn, vn = inputs.token_kv(w.cid, b, n, w.Hkv, w.D, w.kv_dtype)
+            # quantised caches take bf16 tokens through the quantising append
+            kn, vn = inputs.token_kv(w.cid, b, n, w.Hkv, w.D,
+                                     "bf16" if w.kv_dtype in ("i8", "i4") else w.kv_dtype)
             ks.append(kn)
             vs.append(vn)
         pool = inputs.pool(w)
@@ -334,7 +338,14 @@ class PrefillRunner:
         def up(a):
             a = np.ascontiguousarray(a)
             return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
-        self.k, self.v = up(pool["k"]), up(pool["v"])
+        self.ks = self.vs = None
+        if w.kv_dtype in ("i8", "i4"):
+            self.k = torch.from_numpy(np.ascontiguousarray(pool["k"])).cuda()
+            self.v = torch.from_numpy(np.ascontiguousarray(pool["v"])).cuda()
+            self.ks = torch.from_numpy(pool["k_scale"]).cuda()
+            self.vs = torch.from_numpy(pool["v_scale"]).cuda()
+        else:
+            self.k, self.v = up(pool["k"]), up(pool["v"])
         del pool
         self.k_new, self.v_new = up(np.concatenate(ks)), up(np.concatenate(vs))
         self.slots = torch.tensor(slots, dtype=torch.int64, device="cuda")
@@ -349,13 +360,19 @@ class PrefillRunner:
 
     def step(self, time_it: bool = False):
         pkv, w = self.pkv, self.w
-        pkv.kv_append(self.k_new, self.v_new, self.slots, self.k, self.v)
+        if w.kv_dtype == "i8":
+            pkv.kv_append_int8(self.k_new, self.v_new, self.slots, self.k, self.v, self.ks, self.vs)
+        elif w.kv_dtype == "i4":
+            pkv.kv_append_int4(self.k_new, self.v_new, self.slots, self.k, self.v, self.ks, self.vs)
+        else:
+            pkv.kv_append(self.k_new, self.v_new, self.slots, self.k, self.v)
         e0 = e1 = None
         if time_it:
             e0, e1 = self.hev.create(), self.hev.create()
             self.hev.record(e0, self.stream)
         pkv.prefill(self.q, self.k, self.v, self.tables, self.lens, self.cu,
-                    int(self.lens_h.max()), w.scale, out=self.out)
+                    int(self.lens_h.max()), w.scale, k_scale=self.ks, v_scale=self.vs,
+                    out=self.out)
         if time_it:
             self.hev.record(e1, self.stream)
             self.events.append((e0, e1))
@@ -364,14 +381,20 @@ class PrefillRunner:
         return [self.hev.elapsed_ms(a, b) for a, b in self.events]
 
 
-def prefill_workload():
+PREFILL_KV = {"prefill_llama8b": "bf16", "prefill_llama8b_i8": "i8", "prefill_llama8b_i4": "i4"}
+
+
+def prefill_workload(name: str = "prefill_llama8b"):
+    """Llama-3.1-8B heads, B 8, contexts U[2048, 4096] ending in a 512-token chunk each; the
+    _i8 / _i4 variants keep the cache as int8 or packed int4 codes with per-block scales."""
     import inputs
-    w = inputs.llama8b_decode(B=8, lo=2048, hi=4096, cid=72, name="prefill_llama8b")
+    w = inputs.llama8b_decode(B=8, lo=2048, hi=4096, cid=72, name=name)
     w.append = False
+    w.kv_dtype = PREFILL_KV[name]
     return w, inputs.chunk_sizes(w, 512, 512)
 
 
-def cpu_baseline_prefill(min_seconds: float = 10.0) -> dict:
+def cpu_baseline_prefill(name: str, min_seconds: float = 10.0) -> dict:
     """The fp64 oracle on sampled (query row, head) pairs of the prefill workload, one thread,
     scaled to query tokens/s (a token is Hq row-heads)."""
     env = dict(os.environ, OMP_NUM_THREADS="1", OPENBLAS_NUM_THREADS="1", MKL_NUM_THREADS="1")
@@ -382,7 +405,7 @@ import inputs
 from oracle.allocator import PyAllocator, run_script
 from oracle.prefill import prefill_paged
 from bench import prefill_workload
-w, chunks = prefill_workload()
+w, chunks = prefill_workload({name!r})
 a = PyAllocator(w.NB, w.bs, inputs.free_order(w))
 ids = run_script(a, inputs.setup_script(w))
 seqs = [ids[b] for b in range(w.B)]
@@ -399,8 +422,8 @@ while True:
     rows = [(int(cu[b]) + int(i), h) for i in rng.integers(0, int(chunks[b]), 32)
             for h in range(g * w.G, (g + 1) * w.G)]
     prefill_paged(q[cu[b]:cu[b + 1]], w.q_dtype, pool["k"], pool["v"], w.kv_dtype, [tables[b]],
-                  [lens[b]], [0, int(chunks[b])], w.bs, w.scale,
-                  rows=[(r - int(cu[b]), h) for r, h in rows])
+                  [lens[b]], [0, int(chunks[b])], w.bs, w.scale, pool.get("k_scale"),
+                  pool.get("v_scale"), rows=[(r - int(cu[b]), h) for r, h in rows])
     done += len(rows)
     el = time.perf_counter() - t0
     if el >= {min_seconds}:
@@ -412,7 +435,7 @@ print(json.dumps({{"rowheads": done, "seconds": el}}))
     if r.returncode != 0:
         raise RuntimeError(r.stderr[-2000:])
     d = json.loads(r.stdout.strip().splitlines()[-1])
-    w, _ = prefill_workload()
+    w, _ = prefill_workload(name)
     return {"value": round(d["rowheads"] / w.Hq / d["seconds"], 2), "unit": "tokens/s",
             "cores": 1, "kind": "oracle",
             "sample": f"{d['rowheads']} sampled (query row, head) outputs of the workload "
@@ -422,7 +445,7 @@ print(json.dumps({{"rowheads": done, "seconds": el}}))
 
 def run_prefill(args):
     import torch
-    w, chunks = prefill_workload()
+    w, chunks = prefill_workload(args.workload)
     runner = PrefillRunner(w, chunks)
     torch.cuda.synchronize()
     for _ in range(args.warmup):
@@ -448,10 +471,11 @@ def run_prefill(args):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": w.kv_dtype,
         "data": "synthetic (seeded N(0,1) K/V/q, shapes of the workload; no weights)",
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "head_dim": w.D,
-                   "block_size": w.bs, "chunk_tokens": [int(c) for c in chunks],
+                   "block_size": w.bs, "kv_dtype": w.kv_dtype,
+                   "chunk_tokens": [int(c) for c in chunks],
                    "context_tokens": [int(x) for x in runner.lens_h]},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
@@ -460,7 +484,7 @@ def run_prefill(args):
         "prefill_algorithmic_flops": flops,
     }
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline_prefill(args.cpu_seconds)
+        rec["cpu_baseline"] = cpu_baseline_prefill(args.workload, args.cpu_seconds)
     print(json.dumps(rec), flush=True)
 
 
