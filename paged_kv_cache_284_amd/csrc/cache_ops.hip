@@ -6,6 +6,8 @@
 // writes to it).  All three are bit copies; they move a few KiB to a few MiB per step and are
 // bound by launch latency, so they favour simple, fully coalesced addressing over occupancy
 // tuning.
+#include <type_traits>
+
 #include "internal.h"
 
 namespace pa {
@@ -60,14 +62,21 @@ __global__ void __launch_bounds__(256) kv_append_kernel(const T* __restrict__ k_
   }
 }
 
-// Quantising append into an int8 cache.  One wave per (batch entry, KV head); the wave of the
-// first entry of a run of consecutive entries that write into the same block takes the whole
-// run in order (a block's scale and codes evolve token by token), the others exit.  Per token
-// and for K and V alike (all fp32, IEEE division, round-half-to-even): c = max|x| / 127; a fresh
-// block (offset 0) takes scale c; otherwise a larger c grows the scale to c and re-rounds the
-// block's earlier codes by old/c; the new slot gets clamp(rint(x / scale), -127, 127) (0 for a
-// zero scale).  Lane l only ever touches dims d = l (mod 64) of the tile, so the re-rounding
-// reads back only what the same lane wrote.
+// Quantising appends into int8 and packed int4 caches.  One wave per (batch entry, KV head), four
+// entries to a workgroup; the wave of the first entry of a run of consecutive entries that write
+// into the same block takes the whole run in order (a block's scale and codes evolve token by
+// token), the others exit.
+// Per token and for K and V alike (all fp32, IEEE division, round-half-to-even): c = max|x| /
+// qmax (qmax 127 for int8, 7 for int4); a fresh block (offset 0) takes scale c; otherwise a
+// larger c grows the scale to c and re-rounds the block's earlier rows by old/c; the new row gets
+// clamp(rint(x / scale), -qmax, qmax) (0 for a zero scale).  The wave holds the whole (block,
+// head) tile's codes in registers for the run -- each lane a fixed share of the elements of
+// every row -- and writes the tile and its scales back once at the end.
+//
+// Element ownership.  K rows are the dims of one token: int8 lane l owns dims l + 64 j; int4 lane
+// l owns byte l of a row (dims 8 (l / 4) + l % 4 and that + 4: a 4-byte group holds 8
+// consecutive elements, 0..3 in the low nibbles, 4..7 in the high ones).  V rows are the 16
+// tokens of one dim: lane l owns dims l + 64 j for both widths.
 template <typename TIn>
 __device__ __forceinline__ float widen(TIn x);
 template <>
@@ -77,183 +86,202 @@ __device__ __forceinline__ float widen<uint16_t>(uint16_t x) {
   return __uint_as_float(static_cast<uint32_t>(x) << 16);
 }
 
-template <typename TIn>
-__device__ void quantise_token(const TIn* __restrict__ x, int8_t* tile, float* scale_slot,
-                               float* scale_reg, bool fresh, int off, int D, bool token_major) {
-  const int lane = threadIdx.x;
-  float amax = 0.f;
-  for (int d = lane; d < D; d += 64) amax = fmaxf(amax, fabsf(widen<TIn>(x[d])));
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
-  const float cand = amax / 127.f;
-  float scale;
-  if (fresh) {
-    scale = cand;
-  } else {
-    const float old = *scale_reg;
-    scale = old;
-    if (cand > old) {
-      const float r = old / cand;
-      for (int d = lane; d < D; d += 64) {
-        for (int row = 0; row < off; ++row) {
-          int8_t* c = token_major ? tile + row * D + d : tile + d * kBlockSize + row;
-          const float q = __builtin_rintf(static_cast<float>(*c) * r);
-          *c = static_cast<int8_t>(fminf(fmaxf(q, -127.f), 127.f));
-        }
-      }
-      scale = cand;
-    }
-  }
-  for (int d = lane; d < D; d += 64) {
-    float q = 0.f;
-    if (scale > 0.f) q = fminf(fmaxf(__builtin_rintf(widen<TIn>(x[d]) / scale), -127.f), 127.f);
-    int8_t* c = token_major ? tile + off * D + d : tile + d * kBlockSize + off;
-    *c = static_cast<int8_t>(q);
-  }
-  *scale_reg = scale;
-  if (lane == 0) *scale_slot = scale;
-}
-
-template <typename TIn>
-__global__ void __launch_bounds__(64) kv_append_i8_kernel(const TIn* __restrict__ k_new,
-                                                           const TIn* __restrict__ v_new,
-                                                           const int64_t* __restrict__ slots,
-                                                           int8_t* k_cache, int8_t* v_cache,
-                                                           float* k_scale, float* v_scale,
-                                                           int32_t B, int32_t Hkv, int32_t D,
-                                                           int32_t NB) {
-  const int i = blockIdx.x, g = blockIdx.y;
-  const int64_t cap = static_cast<int64_t>(NB) * kBlockSize;
-  auto block_of = [&](int64_t s) -> int64_t { return (s >= 0 && s < cap) ? s / kBlockSize : -1; };
-  const int64_t blk = block_of(slots[i]);
-  if (blk < 0) return;
-  if (i > 0 && block_of(slots[i - 1]) == blk) return;  // not the first entry of its run
-  const int64_t tile = blk * Hkv + g;
-  int8_t* kt = k_cache + tile * kBlockSize * D;
-  int8_t* vt = v_cache + tile * kBlockSize * D;
-  float ks_reg = k_scale[tile], vs_reg = v_scale[tile];  // the block's scales so far
-  for (int j = i; j < B; ++j) {
-    const int64_t sj = slots[j];
-    if (block_of(sj) != blk) break;
-    const int off = static_cast<int>(sj % kBlockSize);
-    const int64_t src = (static_cast<int64_t>(j) * Hkv + g) * D;
-    quantise_token<TIn>(k_new + src, kt, k_scale + tile, &ks_reg, off == 0, off, D, true);
-    quantise_token<TIn>(v_new + src, vt, v_scale + tile, &vs_reg, off == 0, off, D, false);
-  }
-}
-
-// Quantising append into a packed int4 cache: the int8 rule with 7 in place of 127, codes
-// stored as nibbles c + 8 (a 4-byte group holds 8 consecutive elements of a row: 0..3 in the
-// low nibbles, 4..7 in the high ones).  K rows are dims of one token: lane l owns byte l of the
-// row (two dims), so a token's row is written whole.  V rows are tokens of one dim: lane l owns
-// dims l, l + 64, and a token is one nibble, read-modified-written by its dim's lane.
-__device__ __forceinline__ int nibble_code(uint8_t byte, int hi) {
-  return static_cast<int>((byte >> (4 * hi)) & 0xf) - 8;
-}
-__device__ __forceinline__ uint8_t with_nibble(uint8_t byte, int hi, int code) {
-  const uint8_t u = static_cast<uint8_t>(code + 8) & 0xf;
-  return hi ? static_cast<uint8_t>((byte & 0x0f) | (u << 4)) : static_cast<uint8_t>((byte & 0xf0) | u);
-}
-__device__ __forceinline__ int quant7(float x, float scale) {
+template <int kQMax>
+__device__ __forceinline__ int quant_code(float x, float scale) {
   if (!(scale > 0.f)) return 0;
-  return static_cast<int>(fminf(fmaxf(__builtin_rintf(x / scale), -7.f), 7.f));
+  return static_cast<int>(fminf(fmaxf(__builtin_rintf(x / scale), -float(kQMax)), float(kQMax)));
 }
-__device__ __forceinline__ int requant7(int code, float r) {
-  return static_cast<int>(fminf(fmaxf(__builtin_rintf(static_cast<float>(code) * r), -7.f), 7.f));
+template <int kQMax>
+__device__ __forceinline__ int requant_code(int code, float r) {
+  return static_cast<int>(
+      fminf(fmaxf(__builtin_rintf(static_cast<float>(code) * r), -float(kQMax)), float(kQMax)));
+}
+// Maximum over the wave of non-negative values, by register moves only: DPP rotations and quad
+// permutes inside each 16-lane row, then the gfx950 row and half swaps.  (Exact: max does not
+// depend on the order.)
+template <int kCtrl>
+__device__ __forceinline__ float max_dpp(float v) {
+  const int o = __builtin_amdgcn_mov_dpp(__float_as_int(v), kCtrl, 0xf, 0xf, false);
+  return fmaxf(v, __int_as_float(o));
 }
 __device__ __forceinline__ float wave_absmax(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
+  v = max_dpp<0x128>(v);  // row_ror:8
+  v = max_dpp<0x124>(v);  // row_ror:4
+  v = max_dpp<0x4e>(v);   // quad_perm [2, 3, 0, 1]
+  v = max_dpp<0xb1>(v);   // quad_perm [1, 0, 3, 2]
+  auto h = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(h[0]), __uint_as_float(h[1]));
+  h = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(h[0]), __uint_as_float(h[1]));
 }
+// byte and nibble of element t (0..15) in a packed 8-byte row
+__device__ __forceinline__ int nib_byte(int t) { return 4 * (t / 8) + t % 4; }
+__device__ __forceinline__ int nib_shift(int t) { return 4 * ((t % 8) / 4); }
 
-// New scale of a block for a token whose own scale would be `cand` (see the int8 kernel).
-__device__ __forceinline__ float next_scale(bool fresh, float old, float cand, bool* grew) {
-  *grew = !fresh && cand > old;
-  return (fresh || cand > old) ? cand : old;
-}
-
-template <typename TIn>
-__device__ void append_i4_k(const TIn* __restrict__ x, uint8_t* tile, float* scale_slot,
-                            float* scale_reg, bool fresh, int off, int D) {
-  const int lane = threadIdx.x;
-  const int row_bytes = D / 2;
-  const bool mine = lane < row_bytes;
-  const int e_lo = 8 * (lane / 4) + lane % 4, e_hi = e_lo + 4;  // the dims of byte `lane`
-  const float x_lo = mine ? widen<TIn>(x[e_lo]) : 0.f;
-  const float x_hi = mine ? widen<TIn>(x[e_hi]) : 0.f;
-  const float cand = wave_absmax(fmaxf(fabsf(x_lo), fabsf(x_hi))) / 7.f;
-  bool grew;
-  const float scale = next_scale(fresh, *scale_reg, cand, &grew);
-  if (grew && mine) {
-    const float r = *scale_reg / cand;
-    for (int row = 0; row < off; ++row) {
-      uint8_t* p = tile + row * row_bytes + lane;
-      const uint8_t b = *p;
-      *p = with_nibble(with_nibble(b, 0, requant7(nibble_code(b, 0), r)), 1,
-                       requant7(nibble_code(b, 1), r));
-    }
-  }
-  if (mine) {
-    tile[off * row_bytes + lane] =
-        with_nibble(with_nibble(0, 0, quant7(x_lo, scale)), 1, quant7(x_hi, scale));
-  }
-  *scale_reg = scale;
-  if (lane == 0) *scale_slot = scale;
-}
-
-template <typename TIn>
-__device__ void append_i4_v(const TIn* __restrict__ x, uint8_t* tile, float* scale_slot,
-                            float* scale_reg, bool fresh, int off, int D) {
-  const int lane = threadIdx.x;
-  constexpr int kRowBytes = kBlockSize / 2;
+// One token's rule on the codes of one tile held as code[row][k] (k < kK: the elements this
+// lane owns in each row), with the token's values x[k] and the tile's scale so far.
+template <int kQMax, int kK>
+__device__ __forceinline__ void quantise_row(int (&code)[kBlockSize][kK], const float (&x)[kK],
+                                             float* scale, int off) {
   float amax = 0.f;
-  for (int d = lane; d < D; d += 64) amax = fmaxf(amax, fabsf(widen<TIn>(x[d])));
-  const float cand = wave_absmax(amax) / 7.f;
-  bool grew;
-  const float scale = next_scale(fresh, *scale_reg, cand, &grew);
-  auto at = [](int t) { return 4 * (t / 8) + t % 4; };  // byte of token t in a dim row
-  for (int d = lane; d < D; d += 64) {
-    uint8_t* row = tile + d * kRowBytes;
-    if (grew) {
-      const float r = *scale_reg / cand;
-      for (int t = 0; t < off; ++t) {
-        const int hi = (t % 8) / 4;
-        row[at(t)] = with_nibble(row[at(t)], hi, requant7(nibble_code(row[at(t)], hi), r));
-      }
-    }
-    const int hi = (off % 8) / 4;
-    row[at(off)] = with_nibble(row[at(off)], hi, quant7(widen<TIn>(x[d]), scale));
+#pragma unroll
+  for (int k = 0; k < kK; ++k) amax = fmaxf(amax, fabsf(x[k]));
+  const float cand = wave_absmax(amax) / static_cast<float>(kQMax);
+  const float old = *scale;
+  // every row is visited with a select, so that each code stays in its own register
+  if (off != 0 && cand > old) {
+    const float r = old / cand;
+#pragma unroll
+    for (int row = 0; row < kBlockSize; ++row)
+#pragma unroll
+      for (int k = 0; k < kK; ++k)
+        code[row][k] = row < off ? requant_code<kQMax>(code[row][k], r) : code[row][k];
   }
-  *scale_reg = scale;
-  if (lane == 0) *scale_slot = scale;
+  const float sc = (off == 0 || cand > old) ? cand : old;
+#pragma unroll
+  for (int k = 0; k < kK; ++k) {
+    const int q = quant_code<kQMax>(x[k], sc);
+#pragma unroll
+    for (int row = 0; row < kBlockSize; ++row) code[row][k] = row == off ? q : code[row][k];
+  }
+  *scale = sc;
 }
 
-template <typename TIn>
-__global__ void __launch_bounds__(64) kv_append_i4_kernel(const TIn* __restrict__ k_new,
-                                                           const TIn* __restrict__ v_new,
-                                                           const int64_t* __restrict__ slots,
-                                                           uint8_t* k_cache, uint8_t* v_cache,
-                                                           float* k_scale, float* v_scale,
-                                                           int32_t B, int32_t Hkv, int32_t D,
-                                                           int32_t NB) {
-  const int i = blockIdx.x, g = blockIdx.y;
+constexpr int kAppendWaves = 4;  // entries (one wave each) per workgroup of the quantising append
+
+// blockIdx.z = 0 quantises K, 1 quantises V: the two evolve independently, so each wave carries
+// only one token-by-token chain.
+template <typename TIn, int D, int kQMax>
+__global__ void __launch_bounds__(64 * kAppendWaves) kv_append_quant_kernel(
+    const TIn* __restrict__ k_new, const TIn* __restrict__ v_new,
+    const int64_t* __restrict__ slots, uint8_t* k_cache, uint8_t* v_cache, float* k_scale,
+    float* v_scale, int32_t B, int32_t Hkv, int32_t NB) {
+  constexpr bool kI4 = kQMax == 7;
+  constexpr int kJ = D / 64;                       // dims per lane (int8 K, and V)
+  constexpr int kKE = kI4 ? 2 : kJ;                // K elements per lane and row
+  constexpr int kRowK = kI4 ? D / 2 : D;           // bytes per K row
+  constexpr int kRowV = kI4 ? kBlockSize / 2 : kBlockSize;  // bytes per V row
+  const int lane = threadIdx.x % 64;
+  const int i = blockIdx.x * kAppendWaves + static_cast<int>(threadIdx.x) / 64;  // wave's entry
+  const int g = blockIdx.y;
+  const bool is_v = blockIdx.z == 1;
+  if (i >= B) return;  // the waves of a workgroup are independent: no barrier follows
   const int64_t cap = static_cast<int64_t>(NB) * kBlockSize;
   auto block_of = [&](int64_t s) -> int64_t { return (s >= 0 && s < cap) ? s / kBlockSize : -1; };
   const int64_t blk = block_of(slots[i]);
   if (blk < 0) return;
   if (i > 0 && block_of(slots[i - 1]) == blk) return;  // not the first entry of its run
   const int64_t tile = blk * Hkv + g;
-  uint8_t* kt = k_cache + tile * kBlockSize * (D / 2);
-  uint8_t* vt = v_cache + tile * kBlockSize * (D / 2);
-  float ks_reg = k_scale[tile], vs_reg = v_scale[tile];
-  for (int j = i; j < B; ++j) {
-    const int64_t sj = slots[j];
-    if (block_of(sj) != blk) break;
-    const int off = static_cast<int>(sj % kBlockSize);
-    const int64_t src = (static_cast<int64_t>(j) * Hkv + g) * D;
-    append_i4_k<TIn>(k_new + src, kt, k_scale + tile, &ks_reg, off == 0, off, D);
-    append_i4_v<TIn>(v_new + src, vt, v_scale + tile, &vs_reg, off == 0, off, D);
+  const bool kmine = !kI4 || lane < D / 2;        // int4 K: lanes past the row's bytes own none
+  const int e_lo = 8 * (lane / 4) + lane % 4;      // int4 K: the dims of byte `lane`
+  const TIn* x_new = is_v ? v_new : k_new;
+  float* scale_slot = (is_v ? v_scale : k_scale) + tile;
+
+  // the run's entries, 16 at a time: lane t reads entry j0 + t's slot, a ballot gives the run's
+  // length; each entry's values are requested while the previous entry is quantised
+  auto run = [&](auto& code, auto kk_tag, auto fetch) {
+    constexpr int kK = decltype(kk_tag)::value;
+    float sc = *scale_slot;  // the block's scale so far
+    for (int j0 = i;;) {
+      const bool in_batch = lane < kBlockSize && j0 + lane < B;
+      const int64_t my_slot = in_batch ? slots[j0 + lane] : -1;
+      const uint64_t same = __ballot(in_batch && block_of(my_slot) == blk);
+      const int n = __builtin_ctzll(~same);  // leading entries in the block (at most 16)
+      const int my_off = static_cast<int>(my_slot % kBlockSize);
+      float x[kK];
+      fetch(j0, x);  // n >= 1: entry j0 is in the block
+      for (int t = 0; t < n; ++t) {
+        float nx[kK];
+        if (t + 1 < n) fetch(j0 + t + 1, nx);
+        quantise_row<kQMax, kK>(code, x, &sc, __builtin_amdgcn_readlane(my_off, t));
+        if (t + 1 < n) {
+#pragma unroll
+          for (int k = 0; k < kK; ++k) x[k] = nx[k];
+        }
+      }
+      if (n < kBlockSize) break;  // the run ended inside this group of 16
+      j0 += kBlockSize;           // 16 entries all in the block (repeated slots): go on
+    }
+    if (lane == 0) *scale_slot = sc;
+  };
+
+  if (!is_v) {
+    uint8_t* kt = k_cache + tile * kBlockSize * kRowK;
+    int kc[kBlockSize][kKE] = {};
+#pragma unroll
+    for (int row = 0; row < kBlockSize; ++row) {
+      if constexpr (kI4) {
+        if (kmine) {
+          const uint8_t byte = kt[row * kRowK + lane];
+          kc[row][0] = static_cast<int>(byte & 0xf) - 8;
+          kc[row][1] = static_cast<int>(byte >> 4) - 8;
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < kJ; ++j)
+          kc[row][j] =
+              static_cast<int>(reinterpret_cast<const int8_t*>(kt)[row * kRowK + lane + 64 * j]);
+      }
+    }
+    run(kc, std::integral_constant<int, kKE>{}, [&](int j, float (&x)[kKE]) {
+      const TIn* src = x_new + (static_cast<int64_t>(j) * Hkv + g) * D;
+      if constexpr (kI4) {
+        x[0] = kmine ? widen<TIn>(src[e_lo]) : 0.f;
+        x[1] = kmine ? widen<TIn>(src[e_lo + 4]) : 0.f;
+      } else {
+#pragma unroll
+        for (int k = 0; k < kJ; ++k) x[k] = widen<TIn>(src[lane + 64 * k]);
+      }
+    });
+#pragma unroll
+    for (int row = 0; row < kBlockSize; ++row) {
+      if constexpr (kI4) {
+        if (kmine)
+          kt[row * kRowK + lane] = static_cast<uint8_t>(((kc[row][0] + 8) & 0xf) |
+                                                        (((kc[row][1] + 8) & 0xf) << 4));
+      } else {
+#pragma unroll
+        for (int j = 0; j < kJ; ++j)
+          reinterpret_cast<int8_t*>(kt)[row * kRowK + lane + 64 * j] =
+              static_cast<int8_t>(kc[row][j]);
+      }
+    }
+  } else {
+    uint8_t* vt = v_cache + tile * D * kRowV;
+    int vc[kBlockSize][kJ] = {};
+#pragma unroll
+    for (int j = 0; j < kJ; ++j) {
+      const uint8_t* vrow = vt + (lane + 64 * j) * kRowV;
+#pragma unroll
+      for (int t = 0; t < kBlockSize; ++t) {
+        if constexpr (kI4) {
+          vc[t][j] = static_cast<int>((vrow[nib_byte(t)] >> nib_shift(t)) & 0xf) - 8;
+        } else {
+          vc[t][j] = static_cast<int>(reinterpret_cast<const int8_t*>(vrow)[t]);
+        }
+      }
+    }
+    run(vc, std::integral_constant<int, kJ>{}, [&](int j, float (&x)[kJ]) {
+      const TIn* src = x_new + (static_cast<int64_t>(j) * Hkv + g) * D;
+#pragma unroll
+      for (int k = 0; k < kJ; ++k) x[k] = widen<TIn>(src[lane + 64 * k]);
+    });
+#pragma unroll
+    for (int j = 0; j < kJ; ++j) {
+      uint8_t* vrow = vt + (lane + 64 * j) * kRowV;
+      if constexpr (kI4) {
+        uint8_t bytes[kRowV] = {};
+#pragma unroll
+        for (int t = 0; t < kBlockSize; ++t)
+          bytes[nib_byte(t)] |= static_cast<uint8_t>(((vc[t][j] + 8) & 0xf) << nib_shift(t));
+#pragma unroll
+        for (int e = 0; e < kRowV; ++e) vrow[e] = bytes[e];
+      } else {
+#pragma unroll
+        for (int t = 0; t < kBlockSize; ++t)
+          reinterpret_cast<int8_t*>(vrow)[t] = static_cast<int8_t>(vc[t][j]);
+      }
+    }
   }
 }
 
@@ -326,40 +354,47 @@ hipError_t launch_kv_append(const void* k_new, const void* v_new, const int64_t*
   return hipGetLastError();
 }
 
+template <int kQMax>
+hipError_t launch_kv_append_quant(const void* k_new, const void* v_new, bool bf16_new,
+                                  const int64_t* slots, uint8_t* k_cache, uint8_t* v_cache,
+                                  float* k_scale, float* v_scale, int32_t B, int32_t Hkv,
+                                  int32_t D, int32_t NB, hipStream_t stream) {
+  if (B == 0) return hipSuccess;
+  if (D != 64 && D != 128) return hipErrorInvalidValue;
+  const dim3 grid(static_cast<unsigned>((B + kAppendWaves - 1) / kAppendWaves),
+                  static_cast<unsigned>(Hkv), 2);
+  auto go = [&](auto kernel, auto tin) {
+    using T = decltype(tin);
+    hipLaunchKernelGGL(kernel, grid, dim3(64 * kAppendWaves), 0, stream,
+                       static_cast<const T*>(k_new), static_cast<const T*>(v_new), slots, k_cache,
+                       v_cache, k_scale, v_scale, B, Hkv, NB);
+  };
+  if (bf16_new) {
+    if (D == 128) go(kv_append_quant_kernel<uint16_t, 128, kQMax>, uint16_t{});
+    else go(kv_append_quant_kernel<uint16_t, 64, kQMax>, uint16_t{});
+  } else {
+    if (D == 128) go(kv_append_quant_kernel<float, 128, kQMax>, float{});
+    else go(kv_append_quant_kernel<float, 64, kQMax>, float{});
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_kv_append_i8(const void* k_new, const void* v_new, bool bf16_new,
                                const int64_t* slots, int8_t* k_cache, int8_t* v_cache,
                                float* k_scale, float* v_scale, int32_t B, int32_t Hkv, int32_t D,
                                int32_t NB, hipStream_t stream) {
-  if (B == 0) return hipSuccess;
-  const dim3 grid(static_cast<unsigned>(B), static_cast<unsigned>(Hkv));
-  if (bf16_new) {
-    hipLaunchKernelGGL(kv_append_i8_kernel<uint16_t>, grid, dim3(64), 0, stream,
-                       static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new),
-                       slots, k_cache, v_cache, k_scale, v_scale, B, Hkv, D, NB);
-  } else {
-    hipLaunchKernelGGL(kv_append_i8_kernel<float>, grid, dim3(64), 0, stream,
-                       static_cast<const float*>(k_new), static_cast<const float*>(v_new), slots,
-                       k_cache, v_cache, k_scale, v_scale, B, Hkv, D, NB);
-  }
-  return hipGetLastError();
+  return launch_kv_append_quant<127>(k_new, v_new, bf16_new, slots,
+                                     reinterpret_cast<uint8_t*>(k_cache),
+                                     reinterpret_cast<uint8_t*>(v_cache), k_scale, v_scale, B,
+                                     Hkv, D, NB, stream);
 }
 
 hipError_t launch_kv_append_i4(const void* k_new, const void* v_new, bool bf16_new,
                                const int64_t* slots, uint8_t* k_cache, uint8_t* v_cache,
                                float* k_scale, float* v_scale, int32_t B, int32_t Hkv, int32_t D,
                                int32_t NB, hipStream_t stream) {
-  if (B == 0) return hipSuccess;
-  const dim3 grid(static_cast<unsigned>(B), static_cast<unsigned>(Hkv));
-  if (bf16_new) {
-    hipLaunchKernelGGL(kv_append_i4_kernel<uint16_t>, grid, dim3(64), 0, stream,
-                       static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new),
-                       slots, k_cache, v_cache, k_scale, v_scale, B, Hkv, D, NB);
-  } else {
-    hipLaunchKernelGGL(kv_append_i4_kernel<float>, grid, dim3(64), 0, stream,
-                       static_cast<const float*>(k_new), static_cast<const float*>(v_new), slots,
-                       k_cache, v_cache, k_scale, v_scale, B, Hkv, D, NB);
-  }
-  return hipGetLastError();
+  return launch_kv_append_quant<7>(k_new, v_new, bf16_new, slots, k_cache, v_cache, k_scale,
+                                   v_scale, B, Hkv, D, NB, stream);
 }
 
 hipError_t launch_copy_blocks(void* k_cache, void* v_cache, float* k_scale, float* v_scale,
