@@ -29,6 +29,14 @@ COMMON = [
 ]
 
 
+# Per-source flags.  The prefill kernel keeps its score tiles in VGPRs: with the default
+# heuristics at one wave per SIMD the compiler places them in accumulator registers that
+# overlap the P.V accumulators and copies both sides through VGPRs every key pair.
+EXTRA = {
+    "prefill_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def hipcc() -> str:
     env = os.environ.get("HIPCC")
     if env:
@@ -47,7 +55,7 @@ def sources():
 def _compile(src: str) -> str:
     obj = os.path.join(OBJ, os.path.basename(src) + ".o")
     lang = ["-x", "hip"] if src.endswith(".hip") else []
-    cmd = [hipcc(), *COMMON, *lang, "-c", src, "-o", obj]
+    cmd = [hipcc(), *COMMON, *EXTRA.get(os.path.basename(src), []), *lang, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     # the host pass does not know the device-only feature flag; that warning is expected
     err = "\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l)

@@ -346,7 +346,10 @@ int pa_prefill(float* out, const void* q, int32_t q_dtype, const void* k_cache,
   a.D = D;
   a.NB = NB;
   const int64_t tiles = (static_cast<int64_t>(T) + 63) / 64 + B;  // sum of ceil(n_b / 64)
-  if (tiles > INT32_MAX) return PA_ERR_INVALID;
+  // one workgroup per (query group, KV head, block of up to 4 heads) in a 1-D grid; query
+  // positions and key reaches stay within +-(T + max_seq_len)
+  if (tiles * Hq > INT32_MAX || static_cast<int64_t>(T) + max_seq_len > INT32_MAX / 2)
+    return PA_ERR_INVALID;
   a.max_tiles = static_cast<int32_t>(tiles);
   a.scale_log2 = scale * kLog2e;
   return status_of(pa::launch_prefill_mfma(a, static_cast<hipStream_t>(stream)));

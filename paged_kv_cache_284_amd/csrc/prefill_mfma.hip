@@ -20,6 +20,7 @@
 // A wave takes 16 queries of up to four query heads of one KV head: each K/V operand it loads
 // feeds the MFMAs of all its heads.  A workgroup holds four such waves on consecutive 16-query
 // tiles of one sequence, which read the same K/V tiles back to back and share them in cache.
+#include <climits>
 #include <cmath>
 
 #include "internal.h"
@@ -71,40 +72,109 @@ struct Pair {
   int32_t a, b;  // the blocks of tokens 0..15 and 16..31 of a 32-token pair
 };
 
-// Sequence and group of global group index `group`: groups of kGroup queries are numbered
-// sequence by sequence, ceil(n_b / kGroup) per sequence.  Every lane of the wave returns the
-// same answer; b = -1 when the index is past the last group.
-template <int kGroup>
-__device__ void locate_group(const int32_t* __restrict__ cu_q, int B, int group, int* b_out,
-                             int* j_out) {
-  const int lane = threadIdx.x % 64;
-  int base = 0;  // groups before the current chunk of 64 sequences
-  for (int b0 = 0; b0 < B; b0 += 64) {
-    const int b = b0 + lane;
-    const int n = b < B ? max(cu_q[b + 1] - cu_q[b], 0) : 0;
-    const int t = (n + kGroup - 1) / kGroup;
-    int incl = t;  // inclusive prefix over the chunk
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int y = __shfl_up(incl, o, 64);
-      if (lane >= o) incl += y;
-    }
-    const int excl = incl - t;
-    const bool mine = b < B && group >= base + excl && group < base + incl;
-    const unsigned long long hit = __ballot(mine);
-    if (hit) {
-      const int src = __ffsll(static_cast<long long>(hit)) - 1;
-      *b_out = b0 + src;
-      *j_out = group - base - __shfl(excl, src, 64);
-      return;
-    }
-    base += __shfl(incl, 63, 64);
-  }
-  *b_out = -1;
-  *j_out = 0;
+// Integer reduction over the wave (rows of 16 with DPP rotations and quad permutations, then
+// the row swaps), returned as a wave-uniform value.
+template <class Op>
+__device__ __forceinline__ int wave_reduce(int v, Op op) {
+  v = op(v, __builtin_amdgcn_mov_dpp(v, 0x128, 0xf, 0xf, false));  // row_ror:8
+  v = op(v, __builtin_amdgcn_mov_dpp(v, 0x124, 0xf, 0xf, false));  // row_ror:4
+  v = op(v, __builtin_amdgcn_mov_dpp(v, 0x4e, 0xf, 0xf, false));   // quad_perm [2, 3, 0, 1]
+  v = op(v, __builtin_amdgcn_mov_dpp(v, 0xb1, 0xf, 0xf, false));   // quad_perm [1, 0, 3, 2]
+  auto h = __builtin_amdgcn_permlane16_swap(static_cast<uint32_t>(v), static_cast<uint32_t>(v),
+                                            false, false);
+  v = op(static_cast<int>(h[0]), static_cast<int>(h[1]));
+  h = __builtin_amdgcn_permlane32_swap(static_cast<uint32_t>(v), static_cast<uint32_t>(v), false,
+                                       false);
+  v = op(static_cast<int>(h[0]), static_cast<int>(h[1]));
+  return __builtin_amdgcn_readfirstlane(v);
 }
 
-// Query heads per wave: the group's heads, at most 4 (larger groups span blockIdx.z).  Every
+// Work order.  A sequence with L cached tokens and an n-query chunk splits into ceil(n / kGroup)
+// groups of kGroup queries; group j's last query reaches key L - n + min(kGroup (j + 1), n),
+// and a workgroup's time grows with that reach.  Groups are handed out longest reach first
+// (ties in sequence order), so the long workgroups start first and the short ones fill the
+// compute units behind them instead of leaving a tail.  The reach grows strictly with j, so a
+// sequence holds at most one group of any given reach.
+struct SeqGroups {
+  int n, J, base;  // chunk size, number of groups, L - n
+};
+template <int kGroup>
+__device__ __forceinline__ SeqGroups seq_groups(const PrefillArgs& a, int b) {
+  if (b >= a.B) return SeqGroups{0, 0, 0};
+  const int n = min(max(a.cu_q[b + 1] - a.cu_q[b], 0), a.T);
+  const int L = min(max(a.seq_lens[b], 0), a.max_seq_len);
+  return SeqGroups{n, (n + kGroup - 1) / kGroup, L - n};
+}
+// groups of the sequence whose reach is at least v
+template <int kGroup>
+__device__ __forceinline__ int groups_reaching(SeqGroups s, int v) {
+  const int d = v - s.base;  // reach >= v  <=>  min(kGroup (j + 1), n) >= d
+  if (s.J == 0 || d > s.n) return 0;
+  return s.J - (d <= kGroup ? 0 : (d + kGroup - 1) / kGroup - 1);
+}
+// Sequence b and group j of the group ranked `rank` in that order, by bisection on the reach:
+// the largest reach v with more than `rank` groups reaching v is the group's own; the groups
+// reaching further come first, then those of reach v in sequence order.  Every lane returns
+// the same answer; b = -1 past the last group.
+template <int kGroup>
+__device__ void group_of_rank(const PrefillArgs& a, int rank, int* b_out, int* j_out) {
+  const int lane = threadIdx.x % 64;
+  const SeqGroups s0 = seq_groups<kGroup>(a, lane);  // the first 64 sequences stay in registers
+  auto chunk = [&](int b0) { return b0 == 0 ? s0 : seq_groups<kGroup>(a, b0 + lane); };
+  auto add = [](int x, int y) { return x + y; };
+  int n_groups = 0, lo = INT_MAX, hi = INT_MIN;
+  for (int b0 = 0; b0 < a.B; b0 += 64) {
+    const SeqGroups s = chunk(b0);
+    n_groups += s.J;
+    if (s.J > 0) {
+      lo = min(lo, s.base + min(kGroup, s.n));
+      hi = max(hi, s.base + s.n);
+    }
+  }
+  n_groups = wave_reduce(n_groups, add);
+  *b_out = -1;
+  *j_out = 0;
+  if (rank >= n_groups) return;
+  lo = wave_reduce(lo, [](int x, int y) { return min(x, y); });      // every group reaches lo
+  hi = wave_reduce(hi, [](int x, int y) { return max(x, y); }) + 1;  // none reaches hi
+  auto reaching = [&](int v) {
+    int c = 0;
+    for (int b0 = 0; b0 < a.B; b0 += 64) c += groups_reaching<kGroup>(chunk(b0), v);
+    return wave_reduce(c, add);
+  };
+  int above = 0;  // groups reaching hi
+  while (hi - lo > 1) {
+    const int mid = lo + (hi - lo) / 2;
+    const int c = reaching(mid);
+    if (c > rank) {
+      lo = mid;
+    } else {
+      hi = mid;
+      above = c;
+    }
+  }
+  int want = rank - above;  // among the groups of reach exactly lo, in sequence order
+  for (int b0 = 0; b0 < a.B; b0 += 64) {
+    const SeqGroups s = chunk(b0);
+    const int ge = groups_reaching<kGroup>(s, lo);
+    const bool has = ge > groups_reaching<kGroup>(s, lo + 1);
+    const uint64_t m = __ballot(has);
+    const int cnt = __popcll(m);
+    if (want < cnt) {
+      const int before = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
+                                                   __builtin_amdgcn_mbcnt_lo(
+                                                       static_cast<uint32_t>(m), 0u));
+      const uint64_t pick = __ballot(has && before == want);
+      const int src = __ffsll(static_cast<long long>(pick)) - 1;
+      *b_out = b0 + src;
+      *j_out = __shfl(s.J - ge, src, 64);
+      return;
+    }
+    want -= cnt;
+  }
+}
+
+// Query heads per wave: the group's heads, at most 4 (larger groups take several blocks of heads).  Every
 // K/V operand a wave loads feeds the MFMAs of all its heads.
 template <int G>
 constexpr int kHeadsPerWave = G < 4 ? G : 4;
@@ -161,11 +231,15 @@ prefill_mfma_kernel(PrefillArgs a) {
   const int lane = threadIdx.x % 64;
   const int w = threadIdx.x / 64;
   const int r = lane % 16, qg = lane / 16;
-  const int g = blockIdx.y;
-  const int h0 = g * G + blockIdx.z * kH;  // this wave's first query head
+  // blockIdx.x = (rank of the query group) x (KV head, block of kH heads) with the KV heads
+  // innermost: with 8 | Hkv, the workgroups of one KV head share an XCD and its L2
+  const int per_group = a.Hkv * (G / kH);
+  const int hz = blockIdx.x % per_group;
+  const int g = hz % a.Hkv;
+  const int h0 = g * G + (hz / a.Hkv) * kH;  // this wave's first query head
 
   int b, jg;
-  locate_group<kGroupQueries>(a.cu_q, a.B, blockIdx.x, &b, &jg);
+  group_of_rank<kGroupQueries>(a, blockIdx.x / per_group, &b, &jg);
   if (b < 0) return;
   const int row0 = a.cu_q[b];
   const int n = a.cu_q[b + 1] - row0;
@@ -532,10 +606,10 @@ prefill_mfma_kernel(PrefillArgs a) {
 
 template <int G, int D, int kKV>
 hipError_t launch_gdk(const PrefillArgs& a, hipStream_t stream) {
-  const dim3 grid(static_cast<unsigned>(a.max_tiles), static_cast<unsigned>(a.Hkv),
-                  static_cast<unsigned>(G / kHeadsPerWave<G>));
-  hipLaunchKernelGGL((prefill_mfma_kernel<G, D, kKV>), grid, dim3(64 * kWavesPerWG), 0, stream,
-                     a);
+  const int64_t blocks = static_cast<int64_t>(a.max_tiles) * a.Hkv * (G / kHeadsPerWave<G>);
+  if (blocks > INT32_MAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((prefill_mfma_kernel<G, D, kKV>), dim3(static_cast<unsigned>(blocks)),
+                     dim3(64 * kWavesPerWG), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -35,9 +35,12 @@ def _run(w, chunks, rows=None, scale=None):
     q = inputs.chunk_queries(w, T)
     say(f"prefill G={w.G} D={w.D} kv={w.kv_dtype} lens={list(lens)[:8]} "
         f"chunks={list(chunks)[:8]} T={T} scale={scale}")
-    out = pkv.prefill(to_device(q, "bf16"), case.k, case.v, case.tables,
-                      torch.from_numpy(lens).cuda(), torch.from_numpy(cu).cuda(),
-                      int(lens.max()), scale, k_scale=case.ks, v_scale=case.vs).cpu().numpy()
+    # NaN in every output row first: a query group the kernel never schedules stays NaN
+    out = torch.full((T, w.Hq, w.D), float("nan"), dtype=torch.float32, device="cuda")
+    pkv.prefill(to_device(q, "bf16"), case.k, case.v, case.tables,
+                torch.from_numpy(lens).cuda(), torch.from_numpy(cu).cuda(),
+                int(lens.max()), scale, k_scale=case.ks, v_scale=case.vs, out=out)
+    out = out.cpu().numpy()
     ref = prefill_paged(q, "bf16", case.host["k"], case.host["v"], w.kv_dtype, tables, lens, cu,
                         w.bs, scale, case.host.get("k_scale"), case.host.get("v_scale"),
                         rows=rows)
@@ -56,6 +59,19 @@ def test_mixed_chunks(G, D):
     lens = [37, 100, 16, 1, 0, 257, 64, 33]
     chunks = [37, 20, 16, 1, 0, 100, 1, 17]     # whole, after a prefix, exact tile, single, empty
     _run(_workload(G, D, lens, cid=60 + G + D), chunks)
+
+
+@pytest.mark.parametrize("kv", ["bf16", "i8"])
+def test_many_sequences(kv):
+    """130 sequences (more than one wave's worth, so the kernel's longest-first ordering of the
+    query groups walks several chunks of sequences), with empty, single-token, whole-context and
+    partial chunks and many groups of equal reach."""
+    rng = np.random.default_rng([284, 130])
+    lens = [int(x) for x in rng.integers(0, 160, 130)]
+    lens[:6] = [0, 1, 64, 64, 128, 159]
+    chunks = [int(min(L, c)) for L, c in zip(lens, rng.integers(0, 100, 130))]
+    chunks[:6] = [0, 1, 64, 64, 65, 159]
+    _run(_workload(2, 64, lens, cid=131, kv=kv), chunks)
 
 
 def test_llama_shaped_chunk_sampled():

@@ -106,6 +106,7 @@ def _prefill(**kw):
     (dict(kv_dtype=pkv.PA_I4, ks=FAKE), pkv.PA_ERR_INVALID),   # int4 without v_scale
     (dict(max_seq_len=129), pkv.PA_ERR_INVALID),       # beyond max_blocks * bs
     (dict(T=-1), pkv.PA_ERR_INVALID),
+    (dict(T=2**31 - 1), pkv.PA_ERR_INVALID),           # grid of query groups x heads too large
     (dict(scale=float("nan")), pkv.PA_ERR_INVALID),
 ])
 def test_prefill_rejects_on_host(kw, code):
