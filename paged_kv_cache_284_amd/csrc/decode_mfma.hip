@@ -60,6 +60,16 @@ constexpr int kPair = 2 * kBlockSize;  // tokens per wave iteration
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
 
+// Wave-uniform read of memory that no launch of this kernel writes (block tables, int8/int4
+// scales), through the scalar cache.  Going through the constant address space keeps these reads
+// off the vector-memory counter, so waiting for a table entry never waits for the K/V tiles
+// requested before it (vector loads complete in order).
+template <typename T>
+__device__ __forceinline__ T uniform_load(const T* base, int64_t idx) {
+  const __attribute__((address_space(4))) T* p = (const __attribute__((address_space(4))) T*)base;
+  return p[idx];
+}
+
 __device__ __forceinline__ u32x4 load16(const uint16_t* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
@@ -192,10 +202,10 @@ decode_mfma_kernel(DecodeArgs a) {
     }
 
     auto load_pair = [&](int i, Regs& R) {
-      const int tok0 = i * kPair;
+      const int tok0 = __builtin_amdgcn_readfirstlane(i * kPair);
       const int j = tok0 / kBlockSize;
-      int32_t ba = table[j];
-      int32_t bb = (tok0 + kBlockSize < end) ? table[j + 1] : -1;
+      int32_t ba = uniform_load(table, j);
+      int32_t bb = (tok0 + kBlockSize < end) ? uniform_load(table, j + 1) : -1;
       ba = (ba >= 0 && ba < NB) ? ba : -1;
       bb = (bb >= 0 && bb < NB) ? bb : -1;
       R.blk_a = ba;
@@ -205,10 +215,10 @@ decode_mfma_kernel(DecodeArgs a) {
       const int64_t tile_a = ta * (kBlockSize * D);
       const int64_t tile_b = tb * (kBlockSize * D);
       if constexpr (kI4) {
-        R.ks_a = a.k_scale[ta];
-        R.ks_b = a.k_scale[tb];
-        R.vs_a = a.v_scale[ta];
-        R.vs_b = a.v_scale[tb];
+        R.ks_a = uniform_load(a.k_scale, ta);
+        R.ks_b = uniform_load(a.k_scale, tb);
+        R.vs_a = uniform_load(a.v_scale, ta);
+        R.vs_b = uniform_load(a.v_scale, tb);
         const int64_t h_a = tile_a / 2, h_b = tile_b / 2;  // tiles of bs * D / 2 bytes
         const uint8_t* k1 = kc8 + (tok1 < 16 ? h_a : h_b) + (tok1 % 16) * (D / 2) + 4 * kSteps * qg;
         const uint8_t* k2 = kc8 + (tok2 < 16 ? h_a : h_b) + (tok2 % 16) * (D / 2) + 4 * kSteps * qg;
@@ -234,10 +244,10 @@ decode_mfma_kernel(DecodeArgs a) {
         for (int n = 0; n < kTiles; ++n)
           R.v[n] = *reinterpret_cast<const uint32_t*>(v + 16 * n * (kBlockSize / 2));
       } else if constexpr (kI8) {
-        R.ks_a = a.k_scale[ta];
-        R.ks_b = a.k_scale[tb];
-        R.vs_a = a.v_scale[ta];
-        R.vs_b = a.v_scale[tb];
+        R.ks_a = uniform_load(a.k_scale, ta);
+        R.ks_b = uniform_load(a.k_scale, tb);
+        R.vs_a = uniform_load(a.v_scale, ta);
+        R.vs_b = uniform_load(a.v_scale, tb);
         const uint8_t* k1 = kc8 + (tok1 < 16 ? tile_a : tile_b) + (tok1 % 16) * D + 16 * qg;
         const uint8_t* k2 = kc8 + (tok2 < 16 ? tile_a : tile_b) + (tok2 % 16) * D + 16 * qg;
 #pragma unroll
@@ -424,21 +434,29 @@ decode_mfma_kernel(DecodeArgs a) {
     // software pipeline: the loads of the next kDepth - 1 pairs are in flight while the
     // current pair is computed (narrower codes carry fewer bytes per pair, so they keep more
     // pairs in flight).  The loop is unrolled kDepth times so every buffer index is static.
+    // Every iteration issues the same loads: near the end of the piece the look-ahead reloads
+    // the wave's last pair (a cache hit) instead of skipping, because a path without loads
+    // would make the wait before each compute cover the look-ahead loads as well (vector
+    // loads complete in order, and the wait at the join must hold on both paths).
     {
       const int step = solo ? 1 : kWaves;
       int i = solo ? i0 : i0 + w;
-      Regs R[kDepth];
+      if (i < i1) {
+        const int last = i + (i1 - 1 - i) / step * step;  // the wave's last pair of the piece
+        Regs R[kDepth];
 #pragma unroll
-      for (int j = 0; j + 1 < kDepth; ++j)
-        if (i + j * step < i1) load_pair(i + j * step, R[j]);
-      while (i < i1) {
+        for (int j = 0; j + 1 < kDepth; ++j) load_pair(min(i + j * step, last), R[j]);
+        while (i < i1) {
 #pragma unroll
-        for (int j = 0; j < kDepth; ++j) {
-          const int ahead = i + (kDepth - 1) * step;
-          if (ahead < i1) load_pair(ahead, R[(j + kDepth - 1) % kDepth]);
-          compute_pair(i, R[j]);
-          i += step;
-          if (i >= i1) break;
+          for (int j = 0; j < kDepth; ++j) {
+            load_pair(min(i + (kDepth - 1) * step, last), R[(j + kDepth - 1) % kDepth]);
+            // keep the look-ahead loads ahead of this pair's first use of its data: hoisting
+            // an MFMA above them would wait for the look-ahead's predecessors before issuing it
+            __builtin_amdgcn_sched_barrier(0);
+            compute_pair(i, R[j]);
+            i += step;
+            if (i >= i1) break;
+          }
         }
       }
     }
