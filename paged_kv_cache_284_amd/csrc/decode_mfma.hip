@@ -718,27 +718,57 @@ decode_mfma_kernel(DecodeArgs a) {
 // Merge the partial pieces of the segments the balanced schedule cut: one workgroup per decode
 // workgroup wa, reading the record wa left.  The pieces sit in slot `first` of wa and in slot 0
 // of wa + 1 .. wb (an empty span's slot 0 holds l = 0 and is skipped).  Pieces are combined in
-// workgroup order, so the result does not depend on timing.
+// workgroup order, so the result does not depend on timing.  The states of both slots of wa and
+// slot 0 of wa + 1 (every cut segment has those) are requested together with the record, so
+// the common two-piece merge costs one round trip to memory instead of two.
 template <int G, int D>
 __global__ void __launch_bounds__(256) streamk_reduce_kernel(DecodeArgs a) {
   const int wa = blockIdx.x;
+  const bool has_next = wa + 1 < a.nw;
   const int4 rec = reinterpret_cast<const int4*>(a.ws_merge)[wa];
+  constexpr int kPer = (G * D + 255) / 256;
+  float pm[3][kPer], pl[3][kPer], po[3][kPer];
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const int idx = threadIdx.x + 256 * k;
+    if (idx >= G * D) break;
+    const int h = idx / D, d = idx % D;
+#pragma unroll
+    for (int c = 0; c < 3; ++c) {
+      if (c == 2 && !has_next) break;
+      const int64_t slot = static_cast<int64_t>(2 * wa + c) * G + h;  // c = 2: slot 0 of wa + 1
+      pm[c][k] = a.ws_m[slot];
+      pl[c][k] = a.ws_l[slot];
+      po[c][k] = a.ws_o[slot * D + d];
+    }
+  }
   if (rec.x < 0) return;
   const int b = rec.x, g = rec.y, wb = rec.z, first = rec.w;
-  for (int idx = threadIdx.x; idx < G * D; idx += blockDim.x) {
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const int idx = threadIdx.x + 256 * k;
+    if (idx >= G * D) break;
     const int h = idx / D, d = idx % D;
     float M = -INFINITY, num = 0.f, den = 0.f;
-#pragma unroll 4
-    for (int v = wa; v <= wb; ++v) {
-      const int64_t slot = static_cast<int64_t>(2 * v + (v == wa ? first : 0)) * G + h;
-      const float m = a.ws_m[slot], l = a.ws_l[slot], o = a.ws_o[slot * D + d];
-      if (!(l > 0.f)) continue;
+    auto add = [&](float m, float l, float o) {
+      if (!(l > 0.f)) return;
       const float m_new = fmaxf(M, m);
       const float c = __builtin_amdgcn_exp2f(M - m_new);  // 0 for the first piece
       const float f = l * __builtin_amdgcn_exp2f(m - m_new);
       den = den * c + f;
       num = num * c + f * o;
       M = m_new;
+    };
+    if (first == 0) {
+      add(pm[0][k], pl[0][k], po[0][k]);
+    } else {
+      add(pm[1][k], pl[1][k], po[1][k]);
+    }
+    // a record always has wb > wa, so wa + 1 exists
+    add(pm[2][k], pl[2][k], po[2][k]);
+    for (int v = wa + 2; v <= wb; ++v) {
+      const int64_t slot = static_cast<int64_t>(2 * v) * G + h;
+      add(a.ws_m[slot], a.ws_l[slot], a.ws_o[slot * D + d]);
     }
     const int64_t row = static_cast<int64_t>(b) * a.Hq + static_cast<int64_t>(g) * G + h;
     a.out[row * D + d] = den > 0.f ? num / den : 0.f;
