@@ -661,53 +661,88 @@ decode_mfma_kernel(DecodeArgs a) {
       u += take;
     }
     __syncthreads();
-    // merge the pieces that waves share: entries (wave, slot) in order; equal tags form a group
-    __shared__ int32_t grp_s[2 * kWaves + 1][2];
-    __shared__ int32_t ngrp_s;
-    if (threadIdx.x == 0) {
-      int n = 0;
-      int64_t cur = -2;
-      for (int e = 0; e < 2 * kWaves; ++e) {
-        const int64_t t = tag_s[e / 2][e % 2];
-        if (t < 0) continue;
-        if (t != cur) {
-          grp_s[n][0] = e;
-          ++n;
-          cur = t;
-        }
-        grp_s[n - 1][1] = e;
+    // Merge the pieces that waves share.  The 2 kWaves LDS entries e = 2 w + slot are in unit
+    // order, and the entries of one segment (equal tags) are consecutive among the used ones.
+    // First the entries' (m, l) become per-entry weights 2^(m - M) and per-group sums (one
+    // thread per entry and head); then every thread reads its element of all entries at once
+    // and sums each group in entry order, so the result does not depend on timing.
+    constexpr int kE = 2 * kWaves;
+    __shared__ float wt_s[kE][G];   // entry weight 2^(m - M_group) (0 for unused entries)
+    __shared__ float gm_s[kE][G];   // at a group's last entry: the group's M and l
+    __shared__ float gl_s[kE][G];
+    __shared__ uint32_t mask_s[2];  // used entries, last entries of groups
+    const float* mf = &m_s[0][0][0];
+    const float* lf = &l_s[0][0][0];
+    const float* of = &o_s[0][0][0][0];
+    // one thread per (entry, head): the group of an entry is every used entry with its tag
+    for (int t = threadIdx.x; t < kE * G; t += 64 * kWaves) {
+      const int e = t / G, h = t % G;
+      int64_t tg[kE];
+      float mm[kE], ll[kE];
+#pragma unroll
+      for (int o = 0; o < kE; ++o) {
+        tg[o] = tag_s[o / 2][o % 2];
+        mm[o] = mf[o * G + h];
+        ll[o] = lf[o * G + h];
       }
-      ngrp_s = n;
+      const int64_t mine = tag_s[e / 2][e % 2];
+      const float me = mf[e * G + h];
+      const bool used = mine >= 0;
+      float M = -INFINITY;
+#pragma unroll
+      for (int o = 0; o < kE; ++o)
+        if (used && tg[o] == mine) M = fmaxf(M, mm[o]);
+      const bool live = used && M != -INFINITY;
+      float den = 0.f;
+#pragma unroll
+      for (int o = 0; o < kE; ++o)
+        if (live && tg[o] == mine) den += __builtin_amdgcn_exp2f(mm[o] - M) * ll[o];
+      wt_s[e][h] = live ? __builtin_amdgcn_exp2f(me - M) : 0.f;
+      gm_s[e][h] = M;
+      gl_s[e][h] = den;
+    }
+    if (w == 0) {
+      // used entries, and the last entry of each group
+      const int64_t mine = lane < kE ? tag_s[lane / 2][lane % 2] : -1;
+      bool last = mine >= 0;
+#pragma unroll
+      for (int o = 0; o < kE; ++o)
+        if (o > lane && tag_s[o / 2][o % 2] == mine) last = false;
+      const uint64_t um = __ballot(mine >= 0), em = __ballot(last);
+      if (lane == 0) {
+        mask_s[0] = static_cast<uint32_t>(um);
+        mask_s[1] = static_cast<uint32_t>(em);
+      }
     }
     __syncthreads();
-    for (int q = 0; q < ngrp_s; ++q) {
-      const int e0 = grp_s[q][0], e1 = grp_s[q][1];
-      const int* inf = info_s[e0 / 2][e0 % 2];
-      const int b = inf[0], g = inf[1], dest = inf[2], part = inf[3];
+    const uint32_t um = mask_s[0], em = mask_s[1];
+    if (um != 0) {
       for (int idx = threadIdx.x; idx < G * D; idx += 64 * kWaves) {
         const int h = idx / D, d = idx % D;
-        float M = -INFINITY;
-        for (int e = e0; e <= e1; ++e)
-          if (tag_s[e / 2][e % 2] >= 0) M = fmaxf(M, m_s[e / 2][e % 2][h]);
-        float num = 0.f, den = 0.f;
-        if (M != -INFINITY) {
-          for (int e = e0; e <= e1; ++e) {
-            if (tag_s[e / 2][e % 2] < 0) continue;
-            const float f = __builtin_amdgcn_exp2f(m_s[e / 2][e % 2][h] - M);
-            num += f * o_s[e / 2][e % 2][h][d];
-            den += f * l_s[e / 2][e % 2][h];
-          }
-        }
-        const float o = den > 0.f ? num / den : 0.f;
-        const int64_t row = static_cast<int64_t>(b) * a.Hq + static_cast<int64_t>(g) * G + h;
-        if (dest == 0) {
-          a.out[row * D + d] = o;
-        } else {
-          const int64_t slot = static_cast<int64_t>(part) * G + h;
-          a.ws_o[slot * D + d] = o;
-          if (d == 0) {
-            a.ws_m[slot] = M;
-            a.ws_l[slot] = den;
+        float ov[kE];
+#pragma unroll
+        for (int e = 0; e < kE; ++e) ov[e] = of[e * G * D + idx];  // all reads in flight at once
+        float num = 0.f;
+#pragma unroll
+        for (int e = 0; e < kE; ++e) {
+          if ((um >> e) & 1u) num += wt_s[e][h] * ov[e];
+          if ((em >> e) & 1u) {
+            const int* inf = info_s[e / 2][e % 2];
+            const int b = inf[0], g = inf[1], dest = inf[2], part = inf[3];
+            const float den = gl_s[e][h];
+            const float o = den > 0.f ? num / den : 0.f;
+            const int64_t row = static_cast<int64_t>(b) * a.Hq + static_cast<int64_t>(g) * G + h;
+            if (dest == 0) {
+              a.out[row * D + d] = o;
+            } else {
+              const int64_t slot = static_cast<int64_t>(part) * G + h;
+              a.ws_o[slot * D + d] = o;
+              if (d == 0) {
+                a.ws_m[slot] = gm_s[e][h];
+                a.ws_l[slot] = den;
+              }
+            }
+            num = 0.f;
           }
         }
       }
