@@ -362,6 +362,10 @@ decode_mfma_kernel(DecodeArgs a) {
       const float m_new = fmaxf(m_run, bmax);
       const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+      // quantised caches spend their issue slots on ALU work, so they skip the accumulator
+      // rescale (alpha is exactly 1) on pairs where no column's maximum grew, most pairs once a
+      // few hundred tokens are in; bf16 waits on memory and rescales unconditionally
+      const bool rescale = !kI8 || __ballot(m_new != m_run) != 0;
       m_run = m_new;
       f32x8 pv;
       float psum = 0.f;
@@ -386,18 +390,19 @@ decode_mfma_kernel(DecodeArgs a) {
         for (int e = 0; e < 8; ++e) csum += pr[e];
         c_run = c_run * alpha + csum;
       }
-      // rescale the accumulators: rows 4 qg + j hold head (4 qg + j) % G (unconditionally: a
-      // wave-wide test for alpha == 1 costs more than the multiplies it saves)
+      // rescale the accumulators: rows 4 qg + j hold head (4 qg + j) % G
+      if (rescale) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        float aj;
-        if constexpr (G <= 4) {
-          aj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), j % G));
-        } else {
-          aj = __shfl(alpha, (4 * qg + j) % G, 64);
+        for (int j = 0; j < 4; ++j) {
+          float aj;
+          if constexpr (G <= 4) {
+            aj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), j % G));
+          } else {
+            aj = __shfl(alpha, (4 * qg + j) % G, 64);
+          }
+#pragma unroll
+          for (int n = 0; n < kTiles; ++n) acc[n][j] *= aj;
         }
-#pragma unroll
-        for (int n = 0; n < kTiles; ++n) acc[n][j] *= aj;
       }
       if constexpr (kI8) {
         // P as one fp16 operand (11-bit significand: its rounding stays far inside the int8 /
