@@ -35,6 +35,22 @@ __global__ void __launch_bounds__(256) kv_append_kernel(const T* __restrict__ k_
   const int32_t b = blockIdx.x;
   __shared__ int64_t slot_s;
   __shared__ int32_t index_s;
+  // the new token's values do not depend on the slot: request them before the slot, so the
+  // HBM read overlaps the bus round trip to the step's arrays (at most 4 elements per thread
+  // for Hkv * D <= 1024; larger rows take the loop below)
+  constexpr int kPre = 4;
+  const int32_t n = Hkv * D;
+  const T* kn = k_new + static_cast<int64_t>(b) * n;
+  const T* vn = v_new + static_cast<int64_t>(b) * n;
+  T kv[kPre], vv[kPre];
+#pragma unroll
+  for (int i = 0; i < kPre; ++i) {
+    const int32_t e = threadIdx.x + i * static_cast<int32_t>(blockDim.x);
+    if (e < n) {
+      kv[i] = kn[e];
+      vv[i] = vn[e];
+    }
+  }
   // three threads issue the three reads at once: one bus round trip
   if (threadIdx.x == 0) {
     const int64_t slot = slots[b];
@@ -51,10 +67,18 @@ __global__ void __launch_bounds__(256) kv_append_kernel(const T* __restrict__ k_
     tables[static_cast<int64_t>(b) * max_blocks + index_s] = static_cast<int32_t>(slot / kBlockSize);
   const int64_t blk = slot / kBlockSize;
   const int32_t off = static_cast<int32_t>(slot % kBlockSize);
-  const int32_t n = Hkv * D;
-  const T* kn = k_new + static_cast<int64_t>(b) * n;
-  const T* vn = v_new + static_cast<int64_t>(b) * n;
-  for (int32_t e = threadIdx.x; e < n; e += blockDim.x) {
+#pragma unroll
+  for (int i = 0; i < kPre; ++i) {
+    const int32_t e = threadIdx.x + i * static_cast<int32_t>(blockDim.x);
+    if (e < n) {
+      const int32_t g = e / D, d = e % D;
+      const int64_t tile = blk * Hkv + g;
+      k_cache[(tile * kBlockSize + off) * D + d] = kv[i];
+      v_cache[(tile * D + d) * kBlockSize + off] = vv[i];
+    }
+  }
+  for (int32_t e = threadIdx.x + kPre * static_cast<int32_t>(blockDim.x); e < n;
+       e += blockDim.x) {
     const int32_t g = e / D, d = e % D;
     const int64_t tile = blk * Hkv + g;
     k_cache[(tile * kBlockSize + off) * D + d] = kn[e];
