@@ -36,8 +36,8 @@
 // Quantised caches run v_mfma_f32_16x16x32_f16 instead: codes expand to fp16 values offset + c
 // (a byte permute for int8, a nibble mask and permute for int4), q enters once as fp16, P as one
 // fp16 operand, and the offset is taken out of both sums using the same rounded q and P values
-// the matrix cores saw, so it cancels exactly.  Loads of kDepth pairs are in flight per wave
-// (more for the narrower caches, whose pairs are fewer bytes).
+// the matrix cores saw, so it cancels exactly.  Loads of up to kDepth pairs are in flight per
+// wave.
 #include <cmath>
 #include <type_traits>
 
@@ -109,8 +109,10 @@ struct PairRegsI4 {
   float ks_a, ks_b, vs_a, vs_b;
 };
 
-// Pairs each cache kind keeps in flight per wave.
-constexpr int kDepthBf16 = 2, kDepthI8 = 3, kDepthI4 = 4;
+// Pairs each cache kind keeps in flight per wave.  Eight waves per CU already keep enough bytes
+// in flight; the quantised kinds are bound by issue slots, and deeper look-ahead only adds
+// register pressure (measured: bf16 1 and 2 equal, int8 best at 1, int4 best at 2).
+constexpr int kDepthBf16 = 2, kDepthI8 = 1, kDepthI4 = 2;
 
 template <int G, int D, bool kStream, int kKV>
 __global__ void __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -437,8 +439,9 @@ decode_mfma_kernel(DecodeArgs a) {
     };
 
     // software pipeline: the loads of the next kDepth - 1 pairs are in flight while the
-    // current pair is computed (narrower codes carry fewer bytes per pair, so they keep more
-    // pairs in flight).  The loop is unrolled kDepth times so every buffer index is static.
+    // current pair is computed (kDepth 1: the wave waits for each pair; the other waves of the
+    // CU keep the memory busy).  The loop is unrolled kDepth times so every buffer index is
+    // static.
     // Every iteration issues the same loads: near the end of the piece the look-ahead reloads
     // the wave's last pair (a cache hit) instead of skipping, because a path without loads
     // would make the wait before each compute cover the look-ahead loads as well (vector
