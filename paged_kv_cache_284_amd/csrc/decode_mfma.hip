@@ -119,7 +119,9 @@ __global__ void __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_e
 decode_mfma_kernel(DecodeArgs a) {
   constexpr bool kI4 = kKV == kKvI4;
   constexpr bool kI8 = kKV == kKvI8 || kI4;  // a quantised cache (scales, offset codes)
-  constexpr float kOffset = kI4 ? kNibbleOffset : kCodeOffset;
+  // code offset removed from the sums; int4 carries it inside its weighted sums (two offsets,
+  // one per half of each 8-element operand group)
+  constexpr float kOffset = kI4 ? 1.f : kCodeOffset;
   using Regs = std::conditional_t<kI4, PairRegsI4<D>,
                                   std::conditional_t<kI8, PairRegsI8<D>, PairRegs<D>>>;
   constexpr int kDepth = kI4 ? kDepthI4 : (kI8 ? kDepthI8 : kDepthBf16);  // pairs in flight
@@ -170,7 +172,9 @@ decode_mfma_kernel(DecodeArgs a) {
     // cache: step s covers dims 16 (qg + 4 (s / 2)) + 8 (s % 2) .. +8, matching the 16-byte K
     // loads (16 dims of a row serve two steps).
     u32x4 qv[kSteps];
-    float qsum = 0.f;  // int8: sum of this head's q, reduced over the four lane groups
+    // quantised caches: sum of this head's q operands, reduced over the four lane groups
+    // (int4: weighted by each element's code offset)
+    float qsum = 0.f;
     {
       const uint16_t* q = static_cast<const uint16_t*>(a.q) +
                           (static_cast<int64_t>(b) * a.Hq + static_cast<int64_t>(g) * G + r % G) * D;
@@ -188,11 +192,17 @@ decode_mfma_kernel(DecodeArgs a) {
             f[2 * c] = __uint_as_float(raw[c] << 16);
             f[2 * c + 1] = __uint_as_float(raw[c] & 0xffff0000u);
           }
-          const f16x8 h = __builtin_convertvector(f, f16x8);
+          f16x8 h = __builtin_convertvector(f, f16x8);
+          if constexpr (kI4) {
+            // elements 4..7 meet codes expanded at 16 times their value
+#pragma unroll
+            for (int e = 4; e < 8; ++e) h[e] *= static_cast<_Float16>(0.0625f);
+          }
           qv[s] = __builtin_bit_cast(u32x4, h);
           const f32x8 back = __builtin_convertvector(h, f32x8);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) qsum += back[e];
+          for (int e = 0; e < 8; ++e)
+            qsum += kI4 ? back[e] * (e < 4 ? kNibbleOffset : kNibbleOffsetHi16) : back[e];
         } else {
           qv[s] = load16(q + 32 * s + 8 * qg);
         }
@@ -289,8 +299,8 @@ decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
         for (int c = 0; c < kSteps; ++c) {
           const f16x8 qc = __builtin_bit_cast(f16x8, qv[c]);
-          s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(nibbles_to_f16(R.k1[c]), qc, s1, 0, 0, 0);
-          s2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(nibbles_to_f16(R.k2[c]), qc, s2, 0, 0, 0);
+          s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(nibbles_to_f16_hi16(R.k1[c]), qc, s1, 0, 0, 0);
+          s2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(nibbles_to_f16_hi16(R.k2[c]), qc, s2, 0, 0, 0);
         }
       } else if constexpr (kI8) {
 #pragma unroll
@@ -383,13 +393,16 @@ decode_mfma_kernel(DecodeArgs a) {
         // offset is taken out with the sum of exactly those operands, so it cancels exactly
         // (a sum of unrounded P would leave the rounding error times the offset)
         const float vs = vblk_sel ? R.vs_b : R.vs_a;
+        // int4: elements 4..7 meet codes expanded at 16 times their value
+        const float vs_hi = kI4 ? vs * 0.0625f : vs;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) pv[e] *= vs;
+        for (int e = 0; e < 8; ++e) pv[e] *= e < 4 ? vs : vs_hi;
         p16 = __builtin_convertvector(pv, f16x8);
         const f32x8 pr = __builtin_convertvector(p16, f32x8);
         float csum = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) csum += pr[e];
+        for (int e = 0; e < 8; ++e)
+          csum += kI4 ? pr[e] * (e < 4 ? kNibbleOffset : kNibbleOffsetHi16) : pr[e];
         c_run = c_run * alpha + csum;
       }
       // rescale the accumulators: rows 4 qg + j hold head (4 qg + j) % G
@@ -413,7 +426,7 @@ decode_mfma_kernel(DecodeArgs a) {
         for (int n = 0; n < kTiles; ++n) {
           f16x8 vop;
           if constexpr (kI4) {
-            vop = nibbles_to_f16(R.v[n]);
+            vop = nibbles_to_f16_hi16(R.v[n]);
           } else {
             vop = codes_to_f16(R.v[n][0], R.v[n][1]);
           }

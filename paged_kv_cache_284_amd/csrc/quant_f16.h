@@ -45,4 +45,22 @@ __device__ __forceinline__ qf16x8 nibbles_to_f16(uint32_t x) {
 }
 constexpr float kNibbleOffset = 1032.f;  // nibbles_to_f16(c) = kNibbleOffset + c
 
+// The same eight packed codes in six ALU ops instead of seven: a byte permute puts each byte
+// (both of its nibbles) under the fp16 exponent of 1024, and two masks keep either the low
+// nibble (1024 + n) or the high one in place (1024 + 16 n).  Elements 0..3 come out as
+// kNibbleOffset + c, elements 4..7 as kNibbleOffsetHi16 + 16 c (exact); the caller divides the
+// other operand's elements 4..7 by 16 (exact) and removes each half's offset.
+__device__ __forceinline__ qf16x8 nibbles_to_f16_hi16(uint32_t x) {
+  constexpr uint32_t kExp = 0x64646464u;
+  const uint32_t p01 = __builtin_amdgcn_perm(x, kExp, 0x00050004u);  // {b0, 0x64, b1, 0x64}
+  const uint32_t p23 = __builtin_amdgcn_perm(x, kExp, 0x00070006u);  // {b2, 0x64, b3, 0x64}
+  qu32x4 r;
+  r[0] = p01 & 0x640f640fu;  // elements 0, 1
+  r[1] = p23 & 0x640f640fu;  // 2, 3
+  r[2] = p01 & 0x64f064f0u;  // 4, 5, times 16
+  r[3] = p23 & 0x64f064f0u;  // 6, 7, times 16
+  return __builtin_bit_cast(qf16x8, r);
+}
+constexpr float kNibbleOffsetHi16 = 1152.f;  // 1024 + 16 (c + 8)
+
 }  // namespace pa
