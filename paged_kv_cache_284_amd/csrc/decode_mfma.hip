@@ -41,6 +41,7 @@
 #include <cmath>
 #include <type_traits>
 
+#include "device_load.h"
 #include "internal.h"
 #include "pagedkv.h"
 #include "quant_f16.h"
@@ -59,16 +60,6 @@ constexpr int kWaves = 8;
 constexpr int kPair = 2 * kBlockSize;  // tokens per wave iteration
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
-
-// Wave-uniform read of memory that no launch of this kernel writes (block tables, int8/int4
-// scales), through the scalar cache.  Going through the constant address space keeps these reads
-// off the vector-memory counter, so waiting for a table entry never waits for the K/V tiles
-// requested before it (vector loads complete in order).
-template <typename T>
-__device__ __forceinline__ T uniform_load(const T* base, int64_t idx) {
-  const __attribute__((address_space(4))) T* p = (const __attribute__((address_space(4))) T*)base;
-  return p[idx];
-}
 
 __device__ __forceinline__ u32x4 load16(const uint16_t* p) {
   return *reinterpret_cast<const u32x4*>(p);

@@ -23,6 +23,7 @@
 #include <climits>
 #include <cmath>
 
+#include "device_load.h"
 #include "internal.h"
 #include "pagedkv.h"
 #include "quant_f16.h"
@@ -229,7 +230,7 @@ prefill_mfma_kernel(PrefillArgs a) {
   constexpr bool kQ = kKV != kKvBf16;  // quantised cache: fp16 matrix-core operands
   constexpr float kOffset = kKV == kKvI4 ? kNibbleOffset : kCodeOffset;
   const int lane = threadIdx.x % 64;
-  const int w = threadIdx.x / 64;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
   const int r = lane % 16, qg = lane / 16;
   // blockIdx.x = (rank of the query group) x (KV head, block of kH heads) with the KV heads
   // innermost: with 8 | Hkv, the workgroups of one KV head share an XCD and its L2
@@ -240,12 +241,16 @@ prefill_mfma_kernel(PrefillArgs a) {
 
   int b, jg;
   group_of_rank<kGroupQueries>(a, blockIdx.x / per_group, &b, &jg);
+  // wave-uniform from here on (the compiler cannot see it through the search): the block
+  // table then is read through the scalar cache and the loop bounds stay scalar
+  b = __builtin_amdgcn_readfirstlane(b);
+  jg = __builtin_amdgcn_readfirstlane(jg);
   if (b < 0) return;
-  const int row0 = a.cu_q[b];
-  const int n = a.cu_q[b + 1] - row0;
+  const int row0 = __builtin_amdgcn_readfirstlane(a.cu_q[b]);
+  const int n = __builtin_amdgcn_readfirstlane(a.cu_q[b + 1]) - row0;
   const int qi0 = jg * kGroupQueries + w * kTile;
   if (qi0 >= n) return;                           // no barrier follows: idle waves just leave
-  const int L = min(max(a.seq_lens[b], 0), a.max_seq_len);
+  const int L = __builtin_amdgcn_readfirstlane(min(max(a.seq_lens[b], 0), a.max_seq_len));
   const int q_last = min(qi0 + kTile, n) - 1;    // last query of the tile
   const int p_max = L - n + q_last;               // its position: the tile's causal reach
   const int kv_end = min(L, p_max + 1);
@@ -306,10 +311,10 @@ prefill_mfma_kernel(PrefillArgs a) {
 
   // Blocks of pair i (two consecutive table entries; -1 marks a missing or unused block).
   auto blocks_of = [&](int i) -> Pair {
-    const int tok0 = i * kPairTok;
+    const int tok0 = __builtin_amdgcn_readfirstlane(i * kPairTok);
     const int jb = tok0 / kBlockSize;
-    int32_t ba = table[jb];
-    int32_t bb = (tok0 + kBlockSize < kv_end) ? table[jb + 1] : -1;
+    int32_t ba = uniform_load(table, jb);
+    int32_t bb = (tok0 + kBlockSize < kv_end) ? uniform_load(table, jb + 1) : -1;
     return Pair{(ba >= 0 && ba < NB) ? ba : -1, (bb >= 0 && bb < NB) ? bb : -1};
   };
   auto tile_idx = [&](int32_t blk) {  // (block, KV head) tile number
@@ -329,8 +334,8 @@ prefill_mfma_kernel(PrefillArgs a) {
         ko.k2[s] = ld16(p2 + 32 * s);
       }
     } else {
-      ko.ks_a = a.k_scale[ia];
-      ko.ks_b = a.k_scale[ib];
+      ko.ks_a = uniform_load(a.k_scale, ia);
+      ko.ks_b = uniform_load(a.k_scale, ib);
       const uint8_t* kc = static_cast<const uint8_t*>(a.k);
       if constexpr (kKV == kKvI8) {
         const uint8_t* p1 = kc + (tok1 < 16 ? ia : ib) * (kBlockSize * D) + (tok1 % 16) * D + 16 * qg;
@@ -361,8 +366,8 @@ prefill_mfma_kernel(PrefillArgs a) {
 #pragma unroll
       for (int t = 0; t < kTiles; ++t) vo.v[t] = ld16(pv + 16 * t * kBlockSize);
     } else {
-      vo.vs_a = a.v_scale[tile_idx(bl.a)];
-      vo.vs_b = a.v_scale[tile_idx(bl.b)];
+      vo.vs_a = uniform_load(a.v_scale, tile_idx(bl.a));
+      vo.vs_b = uniform_load(a.v_scale, tile_idx(bl.b));
       const uint8_t* vc = static_cast<const uint8_t*>(a.v);
       if constexpr (kKV == kKvI8) {
         const uint8_t* pv = vc + it * (kBlockSize * D) + r * kBlockSize + vtok;
@@ -461,10 +466,9 @@ prefill_mfma_kernel(PrefillArgs a) {
     Pair cur = blocks_of(0);
     load_k(cur);
     for (int i = 0; i < n_pairs; ++i) {
-      const bool more = i + 1 < n_pairs;
-      const Pair nxt = more ? blocks_of(i + 1) : Pair{-1, -1};
+      const Pair nxt = blocks_of(min(i + 1, n_pairs - 1));
       scores();
-      if (more) load_k(nxt);
+      load_k(nxt);
       if (is_edge(i * kPairTok, cur)) mask_scores(i * kPairTok, vsel ? cur.b : cur.a);
 #pragma unroll
       for (int hh = 0; hh < kH; ++hh) ref[hh] = fmaxf(ref[hh], pair_max(hh));
@@ -498,14 +502,16 @@ prefill_mfma_kernel(PrefillArgs a) {
     }
     // One pair of blocks per step, single-buffered: the next pair's K is requested once every
     // head's scores have consumed this pair's K, and its V once P . V has consumed this V.
+    // Every step requests the same loads (the last pair requests itself again, a cache hit):
+    // vector loads complete in order, and a step without them would make the waits after the
+    // join cover the next pair's loads too.
     for (int i = 0; i < n_pairs; ++i) {
       const int tok0 = i * kPairTok;
       const int t_first = tok0 + 8 * qg;
-      const bool more = i + 1 < n_pairs;
-      const Pair nxt = more ? blocks_of(i + 1) : Pair{-1, -1};
+      const Pair nxt = blocks_of(min(i + 1, n_pairs - 1));
       const int32_t my_blk = vsel ? cur.b : cur.a;
       scores();
-      if (more) load_k(nxt);
+      load_k(nxt);
       if constexpr (kKV == kKvBf16) {
         if (tok0 + kPairTok > L || cur.a < 0 || cur.b < 0) {
           // tokens past the context (or of a missing block) must not reach P.V even with
@@ -575,7 +581,7 @@ prefill_mfma_kernel(PrefillArgs a) {
           }
         }
       }
-      if (more) load_v(nxt);
+      load_v(nxt);
       cur = nxt;
     }
     if (pass == 1) break;
