@@ -228,7 +228,9 @@ prefill_mfma_kernel(PrefillArgs a) {
   constexpr int kTiles = D / 16;
   constexpr int kH = kHeadsPerWave<G>;
   constexpr bool kQ = kKV != kKvBf16;  // quantised cache: fp16 matrix-core operands
-  constexpr float kOffset = kKV == kKvI4 ? kNibbleOffset : kCodeOffset;
+  // code offset removed from the sums; int4 carries it inside its weighted sums (two offsets,
+  // one per half of each 8-element operand group)
+  constexpr float kOffset = kKV == kKvI4 ? 1.f : kCodeOffset;
   const int lane = threadIdx.x % 64;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
   const int r = lane % 16, qg = lane / 16;
@@ -292,11 +294,17 @@ prefill_mfma_kernel(PrefillArgs a) {
             f[2 * cc] = __uint_as_float((raw[cc] << 16) ^ (q_neg ? 0x80000000u : 0u));
             f[2 * cc + 1] = __uint_as_float((raw[cc] & 0xffff0000u) ^ (q_neg ? 0x80000000u : 0u));
           }
-          const f16x8 h = __builtin_convertvector(f, f16x8);
+          f16x8 h = __builtin_convertvector(f, f16x8);
+          if constexpr (kKV == kKvI4) {
+            // elements 4..7 meet codes expanded at 16 times their value
+#pragma unroll
+            for (int e = 4; e < 8; ++e) h[e] *= static_cast<_Float16>(0.0625f);
+          }
           qv[hh][s] = __builtin_bit_cast(u32x4, h);
           const f32x8 back = __builtin_convertvector(h, f32x8);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) part += back[e];
+          for (int e = 0; e < 8; ++e)
+            part += kKV == kKvI4 ? back[e] * (e < 4 ? kNibbleOffset : kNibbleOffsetHi16) : back[e];
         } else {
           qv[hh][s] = ld16(q + 32 * s + 8 * qg) ^ (q_neg ? 0x80008000u : 0u);
         }
@@ -419,8 +427,8 @@ prefill_mfma_kernel(PrefillArgs a) {
             a1 = codes_to_f16(ko.k1[s / 2][2 * (s % 2)], ko.k1[s / 2][2 * (s % 2) + 1]);
             a2 = codes_to_f16(ko.k2[s / 2][2 * (s % 2)], ko.k2[s / 2][2 * (s % 2) + 1]);
           } else {
-            a1 = nibbles_to_f16(ko.k1[s]);
-            a2 = nibbles_to_f16(ko.k2[s]);
+            a1 = nibbles_to_f16_hi16(ko.k1[s]);
+            a2 = nibbles_to_f16_hi16(ko.k2[s]);
           }
           const f16x8 qh = __builtin_bit_cast(f16x8, qv[hh][s]);
           s1[hh] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, qh, s1[hh], 0, 0, 0);
@@ -564,18 +572,25 @@ prefill_mfma_kernel(PrefillArgs a) {
           over = over || !(psum * vsc <= kOverPQ);
           // P times the block's V scale as one fp16 operand next to the fp16 codes; the code
           // offset comes out with the sum of exactly these rounded operands, so it cancels
+          // int4: elements 4..7 meet codes expanded at 16 times their value
+          const float vsc_hi = kKV == kKvI4 ? vsc * 0.0625f : vsc;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) pv[e] *= vsc;
+          for (int e = 0; e < 8; ++e) pv[e] *= e < 4 ? vsc : vsc_hi;
           const f16x8 p16 = __builtin_convertvector(pv, f16x8);
           const f32x8 pr = __builtin_convertvector(p16, f32x8);
-          c_run[hh] += ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
+          if constexpr (kKV == kKvI4) {
+            c_run[hh] += ((pr[0] + pr[1]) + (pr[2] + pr[3])) * kNibbleOffset +
+                         ((pr[4] + pr[5]) + (pr[6] + pr[7])) * kNibbleOffsetHi16;
+          } else {
+            c_run[hh] += ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
+          }
 #pragma unroll
           for (int t = 0; t < kTiles; ++t) {
             f16x8 vop;
             if constexpr (kKV == kKvI8) {
               vop = codes_to_f16(vo.v[t][0], vo.v[t][1]);
             } else {
-              vop = nibbles_to_f16(vo.v[t]);
+              vop = nibbles_to_f16_hi16(vo.v[t]);
             }
             acc[hh][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop, p16, acc[hh][t], 0, 0, 0);
           }

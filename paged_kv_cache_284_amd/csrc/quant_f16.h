@@ -30,26 +30,11 @@ __device__ __forceinline__ qf16x8 codes_to_f16(uint32_t x0, uint32_t x1) {
 constexpr float kCodeOffset = 1152.f;  // codes_to_f16(c) = kCodeOffset + c
 
 // int4 cache: eight packed codes (elements 0..3 in the low nibbles of the four bytes, 4..7 in
-// the high nibbles, each nibble c + 8) -> eight fp16 values 1032 + c, in element order.  The
-// nibbles are split into bytes by a mask and a shift; the same byte permute as for int8 then
-// sets each under the exponent of 1024.
-__device__ __forceinline__ qf16x8 nibbles_to_f16(uint32_t x) {
-  constexpr uint32_t kExp = 0x64646464u;
-  const uint32_t lo = x & 0x0f0f0f0fu, hi = (x >> 4) & 0x0f0f0f0fu;
-  qu32x4 r;
-  r[0] = __builtin_amdgcn_perm(lo, kExp, 0x00050004u);  // elements 0, 1
-  r[1] = __builtin_amdgcn_perm(lo, kExp, 0x00070006u);  // 2, 3
-  r[2] = __builtin_amdgcn_perm(hi, kExp, 0x00050004u);  // 4, 5
-  r[3] = __builtin_amdgcn_perm(hi, kExp, 0x00070006u);  // 6, 7
-  return __builtin_bit_cast(qf16x8, r);
-}
-constexpr float kNibbleOffset = 1032.f;  // nibbles_to_f16(c) = kNibbleOffset + c
-
-// The same eight packed codes in six ALU ops instead of seven: a byte permute puts each byte
-// (both of its nibbles) under the fp16 exponent of 1024, and two masks keep either the low
-// nibble (1024 + n) or the high one in place (1024 + 16 n).  Elements 0..3 come out as
-// kNibbleOffset + c, elements 4..7 as kNibbleOffsetHi16 + 16 c (exact); the caller divides the
-// other operand's elements 4..7 by 16 (exact) and removes each half's offset.
+// the high nibbles, each nibble c + 8) -> eight fp16 operands in six ALU ops.  A byte permute
+// puts each byte (both of its nibbles) under the fp16 exponent of 1024, and two masks keep
+// either the low nibble (1024 + n) or the high one in place (1024 + 16 n).  Elements 0..3 come
+// out as kNibbleOffset + c, elements 4..7 as kNibbleOffsetHi16 + 16 c (exact); the caller
+// divides the other operand's elements 4..7 by 16 (exact) and removes each half's offset.
 __device__ __forceinline__ qf16x8 nibbles_to_f16_hi16(uint32_t x) {
   constexpr uint32_t kExp = 0x64646464u;
   const uint32_t p01 = __builtin_amdgcn_perm(x, kExp, 0x00050004u);  // {b0, 0x64, b1, 0x64}
@@ -61,6 +46,7 @@ __device__ __forceinline__ qf16x8 nibbles_to_f16_hi16(uint32_t x) {
   r[3] = p23 & 0x64f064f0u;  // 6, 7, times 16
   return __builtin_bit_cast(qf16x8, r);
 }
+constexpr float kNibbleOffset = 1032.f;      // 1024 + (c + 8)
 constexpr float kNibbleOffsetHi16 = 1152.f;  // 1024 + 16 (c + 8)
 
 }  // namespace pa
