@@ -573,7 +573,7 @@ def traffic_from_profiles(kernel_src_hash: str):
     return d.get("hbm_bytes_per_launch")
 
 
-DECODE_SOURCES = ("decode_mfma.hip", "internal.h", "quant_f16.h")
+DECODE_SOURCES = ("decode_mfma.hip", "device_load.h", "internal.h", "quant_f16.h")
 # the balanced bf16 decode kernel of the Llama-3.1-8B-shaped batch (G = 4, D = 128)
 DECODE_KERNEL = "decode_mfma_kernel<4, 128, true, 0>"
 TRAFFIC_WORKLOAD = "llama8b_decode"
