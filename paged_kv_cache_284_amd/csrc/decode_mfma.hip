@@ -791,34 +791,61 @@ __global__ void __launch_bounds__(256) streamk_reduce_kernel(DecodeArgs a) {
   }
   if (rec.x < 0) return;
   const int b = rec.x, g = rec.y, wb = rec.z, first = rec.w;
+  float M[kPer], num[kPer], den[kPer];
+  auto add = [&](int k, float m, float l, float o) {
+    if (!(l > 0.f)) return;
+    const float m_new = fmaxf(M[k], m);
+    const float c = __builtin_amdgcn_exp2f(M[k] - m_new);  // 0 for the first piece
+    const float f = l * __builtin_amdgcn_exp2f(m - m_new);
+    den[k] = den[k] * c + f;
+    num[k] = num[k] * c + f * o;
+    M[k] = m_new;
+  };
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    M[k] = -INFINITY;
+    num[k] = 0.f;
+    den[k] = 0.f;
+    if (threadIdx.x + 256 * k >= G * D) continue;
+    // a record always has wb > wa, so wa + 1 exists
+    if (first == 0) {
+      add(k, pm[0][k], pl[0][k], po[0][k]);
+    } else {
+      add(k, pm[1][k], pl[1][k], po[1][k]);
+    }
+    add(k, pm[2][k], pl[2][k], po[2][k]);
+  }
+  // segments longer than a span have pieces in more workgroups: request them 16 at a time
+  constexpr int kBatch = 16;
+  for (int v0 = wa + 2; v0 <= wb; v0 += kBatch) {
+    float mm[kBatch][kPer], ll[kBatch][kPer], oo[kBatch][kPer];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+#pragma unroll
+      for (int k = 0; k < kPer; ++k) {
+        const int idx = threadIdx.x + 256 * k;
+        ll[u][k] = 0.f;
+        if (v0 + u <= wb && idx < G * D) {
+          const int h = idx / D, d = idx % D;
+          const int64_t slot = static_cast<int64_t>(2 * (v0 + u)) * G + h;
+          mm[u][k] = a.ws_m[slot];
+          ll[u][k] = a.ws_l[slot];
+          oo[u][k] = a.ws_o[slot * D + d];
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u)
+#pragma unroll
+      for (int k = 0; k < kPer; ++k) add(k, mm[u][k], ll[u][k], oo[u][k]);
+  }
 #pragma unroll
   for (int k = 0; k < kPer; ++k) {
     const int idx = threadIdx.x + 256 * k;
     if (idx >= G * D) break;
     const int h = idx / D, d = idx % D;
-    float M = -INFINITY, num = 0.f, den = 0.f;
-    auto add = [&](float m, float l, float o) {
-      if (!(l > 0.f)) return;
-      const float m_new = fmaxf(M, m);
-      const float c = __builtin_amdgcn_exp2f(M - m_new);  // 0 for the first piece
-      const float f = l * __builtin_amdgcn_exp2f(m - m_new);
-      den = den * c + f;
-      num = num * c + f * o;
-      M = m_new;
-    };
-    if (first == 0) {
-      add(pm[0][k], pl[0][k], po[0][k]);
-    } else {
-      add(pm[1][k], pl[1][k], po[1][k]);
-    }
-    // a record always has wb > wa, so wa + 1 exists
-    add(pm[2][k], pl[2][k], po[2][k]);
-    for (int v = wa + 2; v <= wb; ++v) {
-      const int64_t slot = static_cast<int64_t>(2 * v) * G + h;
-      add(a.ws_m[slot], a.ws_l[slot], a.ws_o[slot * D + d]);
-    }
     const int64_t row = static_cast<int64_t>(b) * a.Hq + static_cast<int64_t>(g) * G + h;
-    a.out[row * D + d] = den > 0.f ? num / den : 0.f;
+    a.out[row * D + d] = den[k] > 0.f ? num[k] / den[k] : 0.f;
   }
 }
 
