@@ -713,8 +713,9 @@ decode_mfma_kernel(DecodeArgs a) {
       gm_s[e][h] = M;
       gl_s[e][h] = den;
     }
-    if (w == 0) {
-      // used entries, and the last entry of each group
+    if (w == kWaves - 1) {
+      // used entries, and the last entry of each group (on the last wave, which the weights
+      // above leave idle for G <= 8, so the two run side by side)
       const int64_t mine = lane < kE ? tag_s[lane / 2][lane % 2] : -1;
       bool last = mine >= 0;
 #pragma unroll
