@@ -574,6 +574,7 @@ decode_mfma_kernel(DecodeArgs a) {
     // pair counts -> prefix sums cum_s[0..B]
     const int B = a.B;
     int carry = 0;
+    if (threadIdx.x == 0) cum_s[0] = 0;
     for (int base = 0; base < B; base += 64 * kWaves) {
       const int i = base + threadIdx.x;
       const int L = i < B ? min(max(a.seq_lens[i], 0), a.max_seq_len) : 0;
@@ -590,10 +591,9 @@ decode_mfma_kernel(DecodeArgs a) {
       if (i < B) cum_s[i + 1] = add + x;
       int tot = 0;
       for (int v = 0; v < kWaves; ++v) tot += wave_tot[v];
-      __syncthreads();
+      if (base + 64 * kWaves < B) __syncthreads();  // wave_tot is rewritten next round
       carry += tot;
     }
-    if (threadIdx.x == 0) cum_s[0] = 0;
     __syncthreads();
     const int64_t T = carry;              // pairs per KV head
     const int64_t U = T * Hkv;            // all units
@@ -641,13 +641,18 @@ decode_mfma_kernel(DecodeArgs a) {
     while (u < v1) {
       const int g = static_cast<int>(u / T);
       const int rem = static_cast<int>(u - static_cast<int64_t>(g) * T);
-      // first sequence b with cum_s[b + 1] > rem
-      int lo = 0, hi = B - 1;
-      while (lo < hi) {
-        const int mid = (lo + hi) / 2;
-        if (cum_s[mid + 1] > rem) hi = mid; else lo = mid + 1;
+      // first sequence b with cum_s[b + 1] > rem: 64 candidates per LDS read and ballot (rem is
+      // below cum_s[B], so a window below B holds it)
+      int b = B - 1;
+      for (int base = 0; base < B; base += 64) {
+        const int i = base + lane;
+        const uint64_t hit = __ballot(i < B && cum_s[i + 1] > rem);
+        if (hit != 0) {
+          b = base + __builtin_ctzll(hit);
+          break;
+        }
       }
-      const int b = lo;
+      b = __builtin_amdgcn_readfirstlane(b);
       const int n_b = cum_s[b + 1] - cum_s[b];
       const int i0 = rem - cum_s[b];
       const int take = static_cast<int>(min(static_cast<int64_t>(n_b - i0), v1 - u));
