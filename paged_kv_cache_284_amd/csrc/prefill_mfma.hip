@@ -503,11 +503,12 @@ prefill_mfma_kernel(PrefillArgs a) {
       for (int t = 0; t < kTiles; ++t) acc[hh][t] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
     bool over = false;
-    Pair cur = n_pairs > 0 ? blocks_of(0) : Pair{-1, -1};
-    if (n_pairs > 0) {
-      load_k(cur);
-      load_v(cur);
-    }
+    // requested even when the tile has no pairs (block ids are clamped, so the loads stay in
+    // bounds): the loop below is then entered only with these loads outstanding, which keeps
+    // its first wait to this pair's K
+    Pair cur = blocks_of(0);
+    load_k(cur);
+    load_v(cur);
     // One pair of blocks per step, single-buffered: the next pair's K is requested once every
     // head's scores have consumed this pair's K, and its V once P . V has consumed this V.
     // Every step requests the same loads (the last pair requests itself again, a cache hit):
