@@ -321,8 +321,9 @@ prefill_mfma_kernel(PrefillArgs a) {
   auto blocks_of = [&](int i) -> Pair {
     const int tok0 = __builtin_amdgcn_readfirstlane(i * kPairTok);
     const int jb = tok0 / kBlockSize;
-    int32_t ba = uniform_load(table, jb);
-    int32_t bb = (tok0 + kBlockSize < kv_end) ? uniform_load(table, jb + 1) : -1;
+    // entries past the row are never read (a table with no columns may be NULL)
+    int32_t ba = jb < a.max_blocks ? uniform_load(table, jb) : -1;
+    int32_t bb = (tok0 + kBlockSize < kv_end && jb + 1 < a.max_blocks) ? uniform_load(table, jb + 1) : -1;
     return Pair{(ba >= 0 && ba < NB) ? ba : -1, (bb >= 0 && bb < NB) ? bb : -1};
   };
   auto tile_idx = [&](int32_t blk) {  // (block, KV head) tile number

@@ -102,6 +102,22 @@ def test_chunk_longer_than_context():
     _run(w, [8, 40, 3, 70])
 
 
+def test_no_table_columns():
+    """Sequences with no cached keys may pass a block table with no columns (NULL): the kernel
+    reads no table entry and every row comes out zero."""
+    w = _workload(4, 128, [5, 3], cid=82)  # for the cache geometry only
+    case = Case(w)
+    B, T = 2, 8
+    say(f"prefill with an empty table: B={B} T={T}")
+    cu = torch.tensor([0, 5, 8], dtype=torch.int32, device="cuda")
+    lens = torch.zeros(B, dtype=torch.int32, device="cuda")
+    tables = torch.empty((B, 0), dtype=torch.int32, device="cuda")
+    q = to_device(inputs.chunk_queries(w, T), "bf16")
+    out = torch.full((T, w.Hq, w.D), float("nan"), dtype=torch.float32, device="cuda")
+    pkv.prefill(q, case.k, case.v, tables, lens, cu, 0, w.scale, out=out)
+    assert bool(torch.all(out == 0))
+
+
 def test_bench_prefill_workload_sampled():
     """The chunked-prefill batch bench.py times (B 8, 512-query chunks after 1.5-3.6 K cached
     tokens), through the same launch configuration, checked on sampled (row, head) pairs."""
