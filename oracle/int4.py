@@ -1,7 +1,7 @@
 """The packed int4 KV layout, read and written element by element.  TEST INFRASTRUCTURE ONLY.
 
-INT4 keeps half a byte per element ([W] "Step 1": the KV bytes per element set the cache size;
-narrower KV is the survey's next step after INT8).  A (block, KV head) tile holds codes c in
+INT4 keeps half a byte per element ([W] "Step 1": the KV bytes per element set the cache size,
+so four bits halve INT8's cache again).  A (block, KV head) tile holds codes c in
 [-7, 7] stored as the nibble u = c + 8, one fp32 scale per tile (K and V apart), x = c * scale.
 
 Packing (the pages fix none): every group of 4 bytes holds 8 consecutive elements of a row --
