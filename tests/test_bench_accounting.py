@@ -39,3 +39,18 @@ def test_prefill_flops_brute_force():
         for i in range(n):
             keys += (L - n + i) + 1          # keys 0..p of the query at position p
     assert bench.prefill_flops(w, lens, chunks) == 4 * w.D * w.Hq * keys
+
+
+def test_more_than_one_gpu_is_refused_before_any_gpu_work():
+    """bench.py measures one GPU: --gpus 2 (or a multi-rank launch) exits with status 2 and says
+    why, without importing torch."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    for args, env in ((["--gpus", "2"], {}), ([], {"WORLD_SIZE": "2"})):
+        r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), *args],
+                           capture_output=True, text=True, timeout=120,
+                           env={**os.environ, **env})
+        assert r.returncode == 2
+        assert "one GPU" in r.stderr and r.stdout == ""
