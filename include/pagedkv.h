@@ -297,12 +297,20 @@ size_t pa_decode_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
  *   Hq % Hkv == 0, Hq/Hkv <= 16, D in {64, 128}, bs == 16.
  *   max_seq_len: host bound on every seq_lens[b], 0 <= max_seq_len <= max_blocks*bs.
  *   partition_tokens: 0 = balanced schedule: the block pairs of all (sequence, KV head)
- *     segments are split into equal spans, one per resident workgroup, whatever the length mix
- *     (bf16 caches; other dtypes fall back to fixed 512-token partitions).  Otherwise a multiple
- *     of 64 in [64, 8192]: one workgroup per partition of that many tokens.  Either way a
- *     segment cut into several pieces ("split-K") is merged with the log-sum-exp identity.
+ *     segments are split into equal spans, one per resident workgroup, whatever the length
+ *     mix.  It runs for a PA_BF16 q over PA_BF16, PA_I8 or PA_I4 caches with Hq/Hkv <= 8 and
+ *     B <= 8192; everything else (PA_F32 q or cache, Hq/Hkv == 16, larger B) falls back to
+ *     fixed 512-token partitions.  Otherwise a multiple of 64 in [64, 8192]: one workgroup per
+ *     partition of that many tokens.  Either way a segment cut into several pieces ("split-K")
+ *     is merged with the log-sum-exp identity, in a fixed order: repeated calls on the same
+ *     inputs give bit-identical outputs.
  *   workspace: device buffer of workspace_bytes >= pa_decode_workspace_size(...); its contents
- *     need no initialisation and are scratch after the call.
+ *     need no initialisation and are scratch after the call.  Calls that overlap in time must
+ *     not share a workspace.
+ *   Quantised caches (PA_I8, PA_I4) run the products in fp16: q and P * v_scale are rounded to
+ *   fp16, so |q| must stay below 65504 and v_scale below 2^14; beyond that the result is not
+ *   finite.  The scales of blocks a sequence does not read (table entries past its length or
+ *   outside [0, NB)) never enter its result, whatever they hold (NaN included).
  * The softmax runs in fp32 with exp computed as exp2 of a log2(e)-scaled argument. */
 int pa_decode(float* out, const void* q, int32_t q_dtype, const void* k_cache,
               const void* v_cache, int32_t kv_dtype, const float* k_scale, const float* v_scale,

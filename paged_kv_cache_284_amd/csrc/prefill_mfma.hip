@@ -343,8 +343,9 @@ prefill_mfma_kernel(PrefillArgs a) {
         ko.k2[s] = ld16(p2 + 32 * s);
       }
     } else {
-      ko.ks_a = uniform_load(a.k_scale, ia);
-      ko.ks_b = uniform_load(a.k_scale, ib);
+      // a missing block's scale is never read as a number (0 * scale stays 0)
+      ko.ks_a = bl.a >= 0 ? uniform_load(a.k_scale, ia) : 0.f;
+      ko.ks_b = bl.b >= 0 ? uniform_load(a.k_scale, ib) : 0.f;
       const uint8_t* kc = static_cast<const uint8_t*>(a.k);
       if constexpr (kKV == kKvI8) {
         const uint8_t* p1 = kc + (tok1 < 16 ? ia : ib) * (kBlockSize * D) + (tok1 % 16) * D + 16 * qg;
@@ -375,8 +376,8 @@ prefill_mfma_kernel(PrefillArgs a) {
 #pragma unroll
       for (int t = 0; t < kTiles; ++t) vo.v[t] = ld16(pv + 16 * t * kBlockSize);
     } else {
-      vo.vs_a = uniform_load(a.v_scale, tile_idx(bl.a));
-      vo.vs_b = uniform_load(a.v_scale, tile_idx(bl.b));
+      vo.vs_a = bl.a >= 0 ? uniform_load(a.v_scale, tile_idx(bl.a)) : 0.f;
+      vo.vs_b = bl.b >= 0 ? uniform_load(a.v_scale, tile_idx(bl.b)) : 0.f;
       const uint8_t* vc = static_cast<const uint8_t*>(a.v);
       if constexpr (kKV == kKvI8) {
         const uint8_t* pv = vc + it * (kBlockSize * D) + r * kBlockSize + vtok;
