@@ -59,7 +59,8 @@ enum pa_status {
   PA_ERR_OOM = -2,         /* allocator: not enough free blocks; state left unchanged */
   PA_ERR_DEVICE = -3,      /* a HIP call or kernel launch failed */
   PA_ERR_UNSUPPORTED = -4, /* valid arguments, combination not implemented */
-  PA_ERR_STATE = -5        /* allocator: unknown or released sequence id */
+  PA_ERR_STATE = -5,       /* allocator: unknown or released sequence id */
+  PA_ERR_TOO_LARGE = -6    /* pa_decode_no_alloc: the call needs more than its fixed scratch */
 };
 
 enum pa_dtype { PA_F32 = 0, PA_BF16 = 1, PA_I8 = 2, PA_I4 = 3 };
@@ -318,6 +319,24 @@ int pa_decode(float* out, const void* q, int32_t q_dtype, const void* k_cache,
               int32_t max_seq_len, int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t bs,
               int32_t NB, float scale, int32_t partition_tokens, void* workspace,
               size_t workspace_bytes, void* stream);
+
+/* pa_decode for callers that cannot allocate device memory: code being captured into a HIP
+ * graph, tight serving loops, harnesses that forbid allocation.  Same arguments, results and
+ * schedules as pa_decode, without the workspace: the partial states of split segments live in
+ * one fixed buffer of PA_DECODE_SCRATCH_BYTES per GPU, a file-scope device array of the library
+ * (held until the process ends).  Nothing is allocated or freed.  A call whose schedule needs
+ * more scratch than that (the balanced schedule needs at most ~8.4 MiB; fixed partitions need
+ * B*Hq*ceil(max_seq_len/partition)*(D+2)*4 bytes) returns PA_ERR_TOO_LARGE and enqueues
+ * nothing.  Every call on one GPU shares that GPU's buffer: calls that overlap in time on one
+ * GPU (other streams, other threads) race and must be serialised by the caller.  The buffer's
+ * contents need no initialisation and carry nothing from one call to the next. */
+#define PA_DECODE_SCRATCH_BYTES (16u << 20)
+int pa_decode_no_alloc(float* out, const void* q, int32_t q_dtype, const void* k_cache,
+                       const void* v_cache, int32_t kv_dtype, const float* k_scale,
+                       const float* v_scale, const int32_t* block_tables, int32_t max_blocks,
+                       const int32_t* seq_lens, int32_t max_seq_len, int32_t B, int32_t Hq,
+                       int32_t Hkv, int32_t D, int32_t bs, int32_t NB, float scale,
+                       int32_t partition_tokens, void* stream);
 
 /* Chunked-prefill attention over the paged cache ([Serving] "Two Phases: Prefill and Decode":
  * prefill runs a prompt's tokens in parallel, each attending to all earlier ones; "Prefix

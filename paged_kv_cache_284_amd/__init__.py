@@ -27,6 +27,8 @@ LIB_PATH = os.path.join(_HERE, "libpagedkv.so")
 
 PA_OK, PA_ERR_INVALID, PA_ERR_OOM, PA_ERR_DEVICE, PA_ERR_UNSUPPORTED, PA_ERR_STATE = \
     0, -1, -2, -3, -4, -5
+PA_ERR_TOO_LARGE = -6
+DECODE_SCRATCH_BYTES = 16 << 20
 PA_F32, PA_BF16, PA_I8, PA_I4 = 0, 1, 2, 3
 BLOCK_SIZE = 16
 
@@ -77,6 +79,8 @@ _SIGNATURES = {
                              _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _vp]),
     "pa_decode": (C.c_int, [_vp, _vp, _i32, _vp, _vp, _i32, _vp, _vp, _vp, _i32, _vp, _i32,
                             _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz, _vp]),
+    "pa_decode_no_alloc": (C.c_int, [_vp, _vp, _i32, _vp, _vp, _i32, _vp, _vp, _vp, _i32, _vp,
+                                     _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp]),
 }
 
 _lib_handle = None
@@ -553,6 +557,30 @@ def decode(q, k_cache, v_cache, block_tables, seq_lens, max_seq_len: int, scale:
                            bs, NB, float(scale), partition_tokens, _dev(workspace, "workspace"),
                            workspace.numel() * workspace.element_size(), _stream(stream)),
            "pa_decode")
+    return out
+
+
+def decode_no_alloc(q, k_cache, v_cache, block_tables, seq_lens, max_seq_len: int, scale: float,
+                    out, k_scale=None, v_scale=None, partition_tokens: int = 0, stream=None):
+    """pa_decode_no_alloc: decode into the caller's ``out`` with the library's fixed device
+    scratch instead of a workspace; allocates nothing."""
+    B, Hq, D = q.shape
+    NB, Hkv, bs, Dk = cache_geometry(k_cache, v_cache)
+    if Dk != D:
+        raise ValueError("cache shapes do not match q")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or tuple(seq_lens.shape) != (B,):
+        raise ValueError("block_tables must be [B][max_blocks] and seq_lens [B]")
+    if tuple(out.shape) != (B, Hq, D):
+        raise ValueError("out must be [B][Hq][D]")
+    torch = _torch()
+    _check(lib().pa_decode_no_alloc(_dev(out, "out", torch.float32), _dev(q, "q"), _dtype_code(q),
+                                    _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+                                    _dtype_code(k_cache), _dev(k_scale, "k_scale", torch.float32),
+                                    _dev(v_scale, "v_scale", torch.float32),
+                                    _dev(block_tables, "block_tables", torch.int32),
+                                    block_tables.shape[1], _dev(seq_lens, "seq_lens", torch.int32),
+                                    max_seq_len, B, Hq, Hkv, D, bs, NB, float(scale),
+                                    partition_tokens, _stream(stream)), "pa_decode_no_alloc")
     return out
 
 

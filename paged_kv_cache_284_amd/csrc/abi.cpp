@@ -217,12 +217,17 @@ size_t pa_decode_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
   return static_cast<size_t>(bytes < 256 ? 256 : bytes);
 }
 
-int pa_decode(float* out, const void* q, int32_t q_dtype, const void* k_cache,
-              const void* v_cache, int32_t kv_dtype, const float* k_scale, const float* v_scale,
-              const int32_t* block_tables, int32_t max_blocks, const int32_t* seq_lens,
-              int32_t max_seq_len, int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t bs,
-              int32_t NB, float scale, int32_t partition_tokens, void* workspace,
-              size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace pa {
+
+int decode_check(const float* out, const void* q, int32_t q_dtype, const void* k_cache,
+                 const void* v_cache, int32_t kv_dtype, const float* k_scale,
+                 const float* v_scale, const int32_t* block_tables, int32_t max_blocks,
+                 const int32_t* seq_lens, int32_t max_seq_len, int32_t B, int32_t Hq,
+                 int32_t Hkv, int32_t D, int32_t bs, int32_t NB, float scale,
+                 int32_t partition_tokens, bool* nothing) {
+  *nothing = false;
   if (B < 0 || Hq < 1 || Hkv < 1 || NB < 1 || max_blocks < 0 || max_seq_len < 0)
     return PA_ERR_INVALID;
   if (Hq % Hkv != 0 || (D != 64 && D != 128)) return PA_ERR_INVALID;
@@ -236,11 +241,25 @@ int pa_decode(float* out, const void* q, int32_t q_dtype, const void* k_cache,
       (partition_tokens < 64 || partition_tokens > 8192 || partition_tokens % 64 != 0))
     return PA_ERR_INVALID;
   if (!(scale == scale)) return PA_ERR_INVALID;
-  if (B == 0) return PA_OK;
+  if (B == 0) {
+    *nothing = true;
+    return PA_OK;
+  }
   if (!out || !q || !k_cache || !v_cache || !seq_lens || (max_blocks > 0 && !block_tables))
     return PA_ERR_INVALID;
   if (quantised(kv_dtype) && (!k_scale || !v_scale)) return PA_ERR_INVALID;
+  const int32_t G = Hq / Hkv;  // int4 runs on the matrix-core kernel only
+  const bool mfma_group = G == 1 || G == 2 || G == 4 || G == 8 || G == 16;
+  if (kv_dtype == PA_I4 && (q_dtype != PA_BF16 || !mfma_group)) return PA_ERR_UNSUPPORTED;
+  return PA_OK;
+}
 
+int decode_run(float* out, const void* q, int32_t q_dtype, const void* k_cache,
+               const void* v_cache, int32_t kv_dtype, const float* k_scale, const float* v_scale,
+               const int32_t* block_tables, int32_t max_blocks, const int32_t* seq_lens,
+               int32_t max_seq_len, int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t NB,
+               float scale, int32_t partition_tokens, void* workspace, size_t workspace_bytes,
+               bool exact_size, void* stream) {
   pa::DecodeArgs a{};
   a.out = out;
   a.q = q;
@@ -261,9 +280,6 @@ int pa_decode(float* out, const void* q, int32_t q_dtype, const void* k_cache,
   const int64_t np = (static_cast<int64_t>(max_seq_len) + a.partition - 1) / a.partition;
   a.np_max = static_cast<int32_t>(np < 1 ? 1 : np);
   a.scale_log2 = scale * kLog2e;
-  if (!workspace || workspace_bytes < pa_decode_workspace_size(B, Hq, Hkv, D, max_seq_len,
-                                                               partition_tokens))
-    return PA_ERR_INVALID;
 
   const int G = Hq / Hkv;
   const bool mfma = q_dtype == PA_BF16 &&
@@ -271,16 +287,28 @@ int pa_decode(float* out, const void* q, int32_t q_dtype, const void* k_cache,
                     (G == 1 || G == 2 || G == 4 || G == 8 || G == 16);
   const bool balanced = mfma && partition_tokens == 0 && B <= pa::kMaxBalancedBatch &&
                         G <= pa::kMaxBalancedGroup;
-  char* base = static_cast<char*>(workspace);
+  int64_t nw = 0;
   if (balanced) {
     const int cus = cu_count();
     if (cus <= 0) return PA_ERR_DEVICE;
-    int64_t nw = static_cast<int64_t>(cus) * pa::mfma_workgroups_per_cu();
+    nw = static_cast<int64_t>(cus) * pa::mfma_workgroups_per_cu();
     if (nw > pa::kMaxBalancedWorkgroups) nw = pa::kMaxBalancedWorkgroups;
     const int64_t units = static_cast<int64_t>(Hkv) * B * ((max_seq_len + 31) / 32);
     if (nw > units) nw = units;
     if (nw >= 8) nw -= nw % 8;
     if (nw < 1) nw = 1;
+  }
+  if (exact_size) {
+    // a fixed buffer: exactly what this call's schedule uses must fit
+    const int64_t need = balanced ? balanced_bytes(G, D, nw) : fixed_bytes(B, Hq, D, a.np_max);
+    if (static_cast<uint64_t>(need) > workspace_bytes) return PA_ERR_TOO_LARGE;
+  } else if (!workspace ||
+             workspace_bytes < pa_decode_workspace_size(B, Hq, Hkv, D, max_seq_len,
+                                                        partition_tokens)) {
+    return PA_ERR_INVALID;
+  }
+  char* base = static_cast<char*>(workspace);
+  if (balanced) {
     a.nw = static_cast<int32_t>(nw);
     const int64_t rows = nw * 2 * G;
     a.ws_m = reinterpret_cast<float*>(base);
@@ -295,12 +323,31 @@ int pa_decode(float* out, const void* q, int32_t q_dtype, const void* k_cache,
     a.ws_o = reinterpret_cast<float*>(base + 2 * align256(rows * 4));
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (!mfma && kv_dtype == PA_I4) return PA_ERR_UNSUPPORTED;  // int4: matrix-core kernel only
   hipError_t e = mfma ? pa::launch_decode_mfma(a, kv_dtype, s)
                       : pa::launch_decode_generic(a, q_dtype, kv_dtype, s);
   if (e != hipSuccess) return status_of(e);
   if (balanced) return PA_OK;
   return status_of(pa::launch_splitk_reduce(a, s));
+}
+
+}  // namespace pa
+
+extern "C" {
+
+int pa_decode(float* out, const void* q, int32_t q_dtype, const void* k_cache,
+              const void* v_cache, int32_t kv_dtype, const float* k_scale, const float* v_scale,
+              const int32_t* block_tables, int32_t max_blocks, const int32_t* seq_lens,
+              int32_t max_seq_len, int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t bs,
+              int32_t NB, float scale, int32_t partition_tokens, void* workspace,
+              size_t workspace_bytes, void* stream) {
+  bool nothing = false;
+  const int st = pa::decode_check(out, q, q_dtype, k_cache, v_cache, kv_dtype, k_scale, v_scale,
+                                  block_tables, max_blocks, seq_lens, max_seq_len, B, Hq, Hkv,
+                                  D, bs, NB, scale, partition_tokens, &nothing);
+  if (st != PA_OK || nothing) return st;
+  return pa::decode_run(out, q, q_dtype, k_cache, v_cache, kv_dtype, k_scale, v_scale,
+                        block_tables, max_blocks, seq_lens, max_seq_len, B, Hq, Hkv, D, NB,
+                        scale, partition_tokens, workspace, workspace_bytes, false, stream);
 }
 
 int pa_prefill(float* out, const void* q, int32_t q_dtype, const void* k_cache,

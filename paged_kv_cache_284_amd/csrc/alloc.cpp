@@ -626,10 +626,11 @@ const char* pa_status_string(int status) {
     case PA_ERR_DEVICE: return "device error";
     case PA_ERR_UNSUPPORTED: return "unsupported combination";
     case PA_ERR_STATE: return "unknown or released sequence";
+    case PA_ERR_TOO_LARGE: return "needs more scratch than the library's fixed buffer holds";
     default: return "unknown status";
   }
 }
 
-int pa_abi_version(void) { return 4; }
+int pa_abi_version(void) { return 5; }
 
 }  // extern "C"

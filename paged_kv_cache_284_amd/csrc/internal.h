@@ -62,6 +62,23 @@ constexpr int kMaxBalancedGroup = 8;
 // Resident workgroups of the balanced MFMA kernel per compute unit.
 int mfma_workgroups_per_cu();
 
+// pa_decode in two steps.  decode_check: the host-side argument checks (no HIP call); *nothing
+// is set when the call has no work (B == 0).  decode_run: schedule, workspace layout and
+// launches; exact_size: the workspace is a fixed buffer that must hold what this call's schedule
+// uses (PA_ERR_TOO_LARGE otherwise), else it must hold pa_decode_workspace_size().
+int decode_check(const float* out, const void* q, int32_t q_dtype, const void* k_cache,
+                 const void* v_cache, int32_t kv_dtype, const float* k_scale,
+                 const float* v_scale, const int32_t* block_tables, int32_t max_blocks,
+                 const int32_t* seq_lens, int32_t max_seq_len, int32_t B, int32_t Hq,
+                 int32_t Hkv, int32_t D, int32_t bs, int32_t NB, float scale,
+                 int32_t partition_tokens, bool* nothing);
+int decode_run(float* out, const void* q, int32_t q_dtype, const void* k_cache,
+               const void* v_cache, int32_t kv_dtype, const float* k_scale, const float* v_scale,
+               const int32_t* block_tables, int32_t max_blocks, const int32_t* seq_lens,
+               int32_t max_seq_len, int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t NB,
+               float scale, int32_t partition_tokens, void* workspace, size_t workspace_bytes,
+               bool exact_size, void* stream);
+
 // Partition length the library picks when the caller passes 0.
 int32_t auto_partition(int32_t B, int32_t Hq, int32_t max_seq_len);
 
