@@ -495,13 +495,15 @@ def host_threads() -> int:
     return min(n, int(env)) if env.isdigit() and int(env) > 0 else n
 
 
-def cpu_baseline(name: str, min_seconds: float = 10.0, threads: int = 1) -> dict:
-    """Time the fp64 oracle on one decode step of the same workload with `threads` BLAS threads,
-    in a child process (input generation excluded)."""
-    t = str(threads)
-    env = dict(os.environ, OMP_NUM_THREADS=t, OPENBLAS_NUM_THREADS=t, MKL_NUM_THREADS=t)
+def cpu_baseline(name: str, min_seconds: float = 10.0, workers: int = 1) -> dict:
+    """Time the fp64 oracle on decode steps of the same workload on the host cores, in a child
+    process with one BLAS thread per process (input generation excluded).  With workers > 1 the
+    child forks that many processes after the set-up (sharing its arrays), each repeating the
+    decode of its own share of the sequences (b = worker mod workers), and the rates add up."""
+    env = dict(os.environ, OMP_NUM_THREADS="1", OPENBLAS_NUM_THREADS="1", MKL_NUM_THREADS="1")
     code = f"""
 import sys, time, json, numpy as np
+import multiprocessing as mp
 sys.path.insert(0, {ROOT!r})
 import inputs
 from oracle import attention
@@ -514,29 +516,44 @@ seqs = [ids[b] for b in range(w.B)]
 if w.append:
     a.step(seqs)
 tables, lens = a.export(seqs, max(len(a.table(s)) for s in seqs))
+tables, lens = np.asarray(tables), np.asarray(lens)
 pool = inputs.pool(w)
 q = inputs.queries(w, 0)
-reps, t0 = 0, time.perf_counter()
-while True:
-    attention.decode_paged(q, w.q_dtype, pool["k"], pool["v"], w.kv_dtype, tables, lens, w.bs,
-                           w.scale, pool.get("k_scale"), pool.get("v_scale"))
-    reps += 1
-    el = time.perf_counter() - t0
-    if el >= {min_seconds}:
-        break
-print(json.dumps({{"reps": reps, "seconds": el, "B": w.B}}))
+N = {workers}
+def work(i):
+    idx = np.arange(i, w.B, N)
+    if len(idx) == 0:
+        return (0, 0, 1.0)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        attention.decode_paged(q[idx], w.q_dtype, pool["k"], pool["v"], w.kv_dtype, tables[idx],
+                               lens[idx], w.bs, w.scale, pool.get("k_scale"), pool.get("v_scale"))
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= {min_seconds}:
+            return (len(idx), reps, el)
+if N == 1:
+    res = [work(0)]
+else:
+    with mp.get_context("fork").Pool(N) as p:
+        res = p.map(work, range(N))
+print(json.dumps({{"res": res, "B": w.B}}))
 """
     r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True,
                        cwd=ROOT)
     if r.returncode != 0:
-        return {"value": None, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+        return {"value": None, "unit": "tokens/s", "cores": workers, "kind": "oracle",
                 "sample": f"failed: {r.stderr[-300:]}"}
     d = json.loads(r.stdout.strip().splitlines()[-1])
-    tps = d["B"] * d["reps"] / d["seconds"]
-    return {"value": round(tps, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{d['reps']} full decode step(s) of the workload (B={d['B']}, all heads, "
-                      f"fp64 numpy, {threads} thread{'s' if threads > 1 else ''}) in "
-                      f"{d['seconds']:.1f} s"}
+    tps = sum(n * reps / el for n, reps, el in d["res"] if n)
+    steps = sum(n * reps for n, reps, _ in d["res"]) / d["B"]
+    secs = max(el for _, _, el in d["res"])
+    what = ("1 process" if workers == 1 else
+            f"{workers} processes of one thread, each over every {workers}th sequence")
+    return {"value": round(tps, 3), "unit": "tokens/s", "cores": workers, "kind": "oracle",
+            "cpu_model": cpu_model(),
+            "sample": f"{steps:.1f} full decode step(s) of the workload (B={d['B']}, all heads, "
+                      f"fp64 numpy, {what}) in {secs:.1f} s"}
 
 
 def stream_copy_gbps(nbytes: int = 1 << 30, reps: int = 5) -> float:
@@ -632,9 +649,9 @@ def summarize_counters(d: str, copy_mib: int = 512) -> dict:
         "kernel_sources_sha256": kernel_sources_hash(),
         "commands": [
             "rocprofv3 --pmc FETCH_SIZE --output-format csv -d prof_out/pmc_FETCH_SIZE -o dec -- "
-            "python3 -u bench.py --steps 3 --warmup 1 --no-cpu-baseline",
+            "python3 -u bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-configs",
             "rocprofv3 --pmc WRITE_SIZE --output-format csv -d prof_out/pmc_WRITE_SIZE -o dec -- "
-            "python3 -u bench.py --steps 3 --warmup 1 --no-cpu-baseline",
+            "python3 -u bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-configs",
             "rocprofv3 --pmc FETCH_SIZE --output-format csv -d prof_out/pmc_copy_FETCH_SIZE -o cp "
             f"-- python3 -u bench.py --copy-reference {copy_mib}",
             "rocprofv3 --pmc WRITE_SIZE --output-format csv -d prof_out/pmc_copy_WRITE_SIZE -o cp "
@@ -645,6 +662,96 @@ def summarize_counters(d: str, copy_mib: int = 512) -> dict:
     return out
 
 
+def release_device_memory():
+    import gc
+    import torch
+    gc.collect()
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def measure_decode(name: str, steps: int, warmup: int, cold_reps: int, partition: int = 0):
+    """Run warmup + steps decode steps of a workload through the library (each step: allocator
+    step, copy-on-write copies, append, decode, for workloads that append) and time them."""
+    import torch
+    total = warmup + steps
+    w = build_workload(name, total)
+    runner = StepRunner(w, total, partition)
+    torch.cuda.synchronize()
+    for _ in range(warmup):
+        runner.step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        runner.step(time_decode=True)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    timed = runner.decode_ms()
+    ms = [t for t, _ in timed]
+    # the tables after the last step serve every timed step: a copy-on-write only ever replaces
+    # a shared block by a private copy, and blocks a later step adds hold no token of an earlier
+    tables_now, _ = runner.alloc.export(runner.seqs, runner.MB)
+    logical = [algorithmic_bytes(w, lens) for _, lens in timed]
+    byts = [algorithmic_bytes(w, lens, tables_now) for _, lens in timed]
+    mean_ms = float(np.mean(ms))
+    out = {"w": w, "elapsed": elapsed, "ms": ms, "mean_ms": mean_ms, "bytes": byts,
+           "logical": logical, "achieved": float(np.mean(byts)) / (mean_ms * 1e-3) / 1e9,
+           "append": runner.append_ms(),
+           "cold": runner.cold_decode_ms(cold_reps) if cold_reps else []}
+    del runner
+    return out
+
+
+# The decode configurations of the workload list, measured after the headline and reported
+# beside it.  Workloads that append run from their first step (warm-up 0), so that the shared-
+# prefix batch's copy-on-write step is inside the timed steps.
+CONFIG_WORKLOADS = ("tiny_fp32", "llama8b_decode", "long_context", "shared_prefix_batch",
+                    "int8_mha", "int4_mha")
+CONFIG_STEPS = {"tiny_fp32": (0, 10), "llama8b_decode": (2, 10), "long_context": (2, 8),
+                "shared_prefix_batch": (0, 12), "int8_mha": (3, 12), "int4_mha": (3, 12)}
+
+
+def config_record(name: str) -> dict:
+    """One configuration's decode figures: HIP-event time of each pa_decode (both kernels),
+    unique and logical algorithmic bytes, rate and fraction of the HBM peak (the tiny batch is
+    latency-bound: time only), the decode after a 1 GiB read of other memory, and the append."""
+    warmup, steps = CONFIG_STEPS[name]
+    m = measure_decode(name, steps, warmup, 5)
+    w = m["w"]
+    med = float(np.median(m["ms"]))
+    ub, lb = float(np.mean(m["bytes"])), float(np.mean(m["logical"]))
+    r = {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "head_dim": w.D,
+         "kv_dtype": w.kv_dtype, "warmup": warmup, "steps": steps,
+         "decode_us_median": round(med * 1e3, 2), "decode_us_mean": round(m["mean_ms"] * 1e3, 2),
+         "unique_bytes": int(ub), "logical_bytes": int(lb)}
+    if w.name != "tiny_fp32":
+        r["unique_gbps"] = round(m["achieved"], 1)
+        r["logical_gbps"] = round(lb / (m["mean_ms"] * 1e-3) / 1e9, 1)
+        r["frac"] = round(m["achieved"] / PEAK_HBM_GBPS, 4)
+        r["tokens_per_s"] = round(w.B / (m["mean_ms"] * 1e-3), 1)
+    if m["cold"]:
+        r["cold_us_median"] = round(float(np.median(m["cold"])) * 1e3, 2)
+    if m["append"]:
+        r["append_us_mean"] = round(float(np.mean([t for t, _ in m["append"]])) * 1e3, 2)
+        r["append_us_first_step"] = round(m["append"][0][0] * 1e3, 2)
+        r["cow_pairs_first_step"] = int(m["append"][0][1])
+        r["cow_pairs_timed"] = int(sum(n for _, n in m["append"]))
+    m = None
+    release_device_memory()
+    return r
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -653,6 +760,8 @@ def main():
     ap.add_argument("--workload", default="llama8b_decode")
     ap.add_argument("--partition", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-configuration records after the headline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--cold-reps", type=int, default=10,
                     help="decode launches timed alone after a 1 GiB read of other memory "
@@ -695,43 +804,19 @@ def main():
         run_prefill(args)
         return
 
-    total = args.warmup + args.steps
-    w = build_workload(args.workload, total)
-    runner = StepRunner(w, total, args.partition)
-    torch.cuda.synchronize()
-    for _ in range(args.warmup):
-        runner.step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        runner.step(time_decode=True)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-
-    timed = runner.decode_ms()
-    ms = [t for t, _ in timed]
-    # the tables after the last step serve every timed step: warm-up has made every
-    # copy-on-write, and blocks a later step adds hold no token of an earlier one
-    tables_now, _ = runner.alloc.export(runner.seqs, runner.MB)
-    logical = [algorithmic_bytes(w, lens) for _, lens in timed]
-    byts = [algorithmic_bytes(w, lens, tables_now) for _, lens in timed]
-    mean_ms = float(np.mean(ms))
-    achieved = float(np.mean(byts)) / (mean_ms * 1e-3) / 1e9
-    tokens_per_s = w.B * args.steps / elapsed
-    app = runner.append_ms()
-    cold = runner.cold_decode_ms(args.cold_reps) if args.cold_reps else []
+    m = measure_decode(args.workload, args.steps, args.warmup, args.cold_reps, args.partition)
+    w = m["w"]
     # the committed counters cover the headline batch only
     traffic = (traffic_from_profiles(kernel_sources_hash())
                if args.workload == TRAFFIC_WORKLOAD else None)
-
     rec = {
         "metric": METRIC,
-        "value": round(tokens_per_s, 1),
+        "value": round(w.B * args.steps / m["elapsed"], 1),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(elapsed / args.steps * 1e3, 4),
+        "ms_per_step": round(m["elapsed"] / args.steps * 1e3, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -741,30 +826,35 @@ def main():
                    "block_size": w.bs, "kv_dtype": w.kv_dtype, "q_dtype": w.q_dtype,
                    "context_tokens_first_step": int(w.lengths.sum()), "pool_blocks": w.NB,
                    "partition_tokens": args.partition or "auto"},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
-                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
+        "roofline": {"bound": "hbm", "achieved": round(m["achieved"], 1), "peak": PEAK_HBM_GBPS,
+                     "unit": "GB/s", "frac": round(m["achieved"] / PEAK_HBM_GBPS, 4),
                      "traffic": traffic},
-        "decode_ms_mean": round(mean_ms, 5),
-        "decode_ms_median": round(float(np.median(ms)), 5),
-        "decode_ms_p10_p90": [round(float(np.percentile(ms, 10)), 5),
-                              round(float(np.percentile(ms, 90)), 5)],
-        "decode_algorithmic_bytes_mean": int(np.mean(byts)),
-        "decode_logical_bytes_mean": int(np.mean(logical)),
-        "decode_tokens_per_s": round(w.B / (mean_ms * 1e-3), 1),
+        "decode_ms_mean": round(m["mean_ms"], 5),
+        "decode_ms_median": round(float(np.median(m["ms"])), 5),
+        "decode_ms_p10_p90": [round(float(np.percentile(m["ms"], 10)), 5),
+                              round(float(np.percentile(m["ms"], 90)), 5)],
+        "decode_algorithmic_bytes_mean": int(np.mean(m["bytes"])),
+        "decode_logical_bytes_mean": int(np.mean(m["logical"])),
+        "decode_tokens_per_s": round(w.B / (m["mean_ms"] * 1e-3), 1),
     }
-    if app:
-        rec["append_ms_mean"] = round(float(np.mean([t for t, _ in app])), 5)
-        rec["append_cow_pairs_timed"] = int(sum(n for _, n in app))
-    if cold:
-        cmed = float(np.median(cold))
+    if m["append"]:
+        rec["append_ms_mean"] = round(float(np.mean([t for t, _ in m["append"]])), 5)
+        rec["append_cow_pairs_timed"] = int(sum(n for _, n in m["append"]))
+    if m["cold"]:
+        cmed = float(np.median(m["cold"]))
         rec["decode_cold_ms_median"] = round(cmed, 5)
-        rec["decode_cold_gbps"] = round(float(np.mean(byts)) / (cmed * 1e-3) / 1e9, 1)
+        rec["decode_cold_gbps"] = round(float(np.mean(m["bytes"])) / (cmed * 1e-3) / 1e9, 1)
+    m = None
+    release_device_memory()
     rec["stream_copy_gbps"] = stream_copy_gbps()
+    if not args.no_configs:
+        rec["configs"] = [config_record(name) for name in CONFIG_WORKLOADS]
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_seconds)
         n = host_threads()
         if n > 1:
-            rec["cpu_baseline_all_cores"] = cpu_baseline(args.workload, args.cpu_seconds / 2, n)
+            rec["cpu_baseline_all_cores"] = cpu_baseline(args.workload, args.cpu_seconds / 2,
+                                                         workers=n)
     print(json.dumps(rec), flush=True)
 
 
