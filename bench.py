@@ -126,12 +126,13 @@ def build_workload(name: str, total_steps: int):
 class StepRunner:
     """Holds the device state of one workload and runs decode steps through the library."""
 
-    def __init__(self, w, total_steps: int, partition: int = 0):
+    def __init__(self, w, total_steps: int, partition: int = 0, shared: bool = False):
         import torch
         import inputs
         import paged_kv_cache_284_amd as pkv
         self.torch, self.pkv, self.w = torch, pkv, w
         self.partition = partition
+        self.shared = shared  # decode with pa_decode_shared_prefix
         order = inputs.free_order(w)
         self.alloc = pkv.Allocator(w.NB, w.bs, order)
         ids = pkv.run_script(self.alloc, inputs.setup_script(w))
@@ -165,8 +166,9 @@ class StepRunner:
                 kn, vn = inputs.new_tokens(w, s)
                 self.new.append((up(kn, w.kv_dtype), up(vn, w.kv_dtype)))
         max_len = int(self.lens.max()) + (total_steps if w.append else 0)
-        self.ws = torch.empty(pkv.decode_workspace_size(w.B, w.Hq, w.Hkv, w.D, max_len, partition),
-                              dtype=torch.uint8, device=dev)
+        ws = (pkv.decode_shared_prefix_workspace_size(w.B, w.Hq, w.Hkv, w.D, max_len) if shared
+              else pkv.decode_workspace_size(w.B, w.Hq, w.Hkv, w.D, max_len, partition))
+        self.ws = torch.empty(ws, dtype=torch.uint8, device=dev)
         self.out = torch.empty((w.B, w.Hq, w.D), dtype=torch.float32, device=dev)
         # the per-step host arrays, written by pa_step straight into pinned memory and read there
         # by the kernels: slots int64[B] | seq_lens int32[B] | table_index int32[B] | cow pairs
@@ -249,8 +251,18 @@ class StepRunner:
         self.step_no += 1
 
     def decode(self, q):
-        """pa_decode over the current cache state (no allocator or cache change)."""
+        """pa_decode (or pa_decode_shared_prefix) over the current cache state (no allocator or
+        cache change)."""
         w = self.w
+        if self.shared:
+            st = self.L.pa_decode_shared_prefix(
+                self.out.data_ptr(), q.data_ptr(), self.q_code, self.k.data_ptr(),
+                self.v.data_ptr(), self.kv_code, self.ks_p, self.vs_p, self.tables.data_ptr(),
+                self.MB, self.lens_d, self.max_len, w.B, w.Hq, w.Hkv, w.D, w.bs, w.NB, w.scale,
+                self.ws.data_ptr(), self.ws.numel(), self.stream)
+            if st != 0:
+                raise self.pkv.PagedKVError(st, "pa_decode_shared_prefix")
+            return
         st = self.L.pa_decode(self.out.data_ptr(), q.data_ptr(), self.q_code, self.k.data_ptr(),
                               self.v.data_ptr(), self.kv_code, self.ks_p, self.vs_p,
                               self.tables.data_ptr(), self.MB, self.lens_d, self.max_len, w.B,
@@ -670,13 +682,15 @@ def release_device_memory():
     torch.cuda.empty_cache()
 
 
-def measure_decode(name: str, steps: int, warmup: int, cold_reps: int, partition: int = 0):
+def measure_decode(name: str, steps: int, warmup: int, cold_reps: int, partition: int = 0,
+                   shared: bool = False):
     """Run warmup + steps decode steps of a workload through the library (each step: allocator
-    step, copy-on-write copies, append, decode, for workloads that append) and time them."""
+    step, copy-on-write copies, append, decode, for workloads that append) and time them.
+    shared: decode with pa_decode_shared_prefix."""
     import torch
     total = warmup + steps
     w = build_workload(name, total)
-    runner = StepRunner(w, total, partition)
+    runner = StepRunner(w, total, partition, shared)
     torch.cuda.synchronize()
     for _ in range(warmup):
         runner.step()
@@ -711,19 +725,36 @@ CONFIG_STEPS = {"tiny_fp32": (0, 10), "llama8b_decode": (2, 10), "long_context":
                 "shared_prefix_batch": (0, 12), "int8_mha": (3, 12), "int4_mha": (3, 12)}
 
 
+# Workloads whose sequences share prefixes: their record is the shared-prefix decode's, with
+# pa_decode's time on the same steps beside it.
+SHARED_PREFIX_WORKLOADS = ("shared_prefix_batch",)
+
+
 def config_record(name: str) -> dict:
-    """One configuration's decode figures: HIP-event time of each pa_decode (both kernels),
-    unique and logical algorithmic bytes, rate and fraction of the HBM peak (the tiny batch is
-    latency-bound: time only), the decode after a 1 GiB read of other memory, and the append."""
+    """One configuration's decode figures: HIP-event time of each decode call (all its
+    kernels), unique and logical algorithmic bytes, rate and fraction of the HBM peak (the tiny
+    batch is latency-bound: time only), the decode after a 1 GiB read of other memory, and the
+    append."""
     warmup, steps = CONFIG_STEPS[name]
-    m = measure_decode(name, steps, warmup, 5)
+    shared = name in SHARED_PREFIX_WORKLOADS
+    plain = None
+    if shared:
+        p = measure_decode(name, steps, warmup, 0)
+        plain = (float(np.median(p["ms"])), p["achieved"])
+        p = None
+        release_device_memory()
+    m = measure_decode(name, steps, warmup, 5, shared=shared)
     w = m["w"]
     med = float(np.median(m["ms"]))
     ub, lb = float(np.mean(m["bytes"])), float(np.mean(m["logical"]))
     r = {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "head_dim": w.D,
          "kv_dtype": w.kv_dtype, "warmup": warmup, "steps": steps,
+         "decode": "pa_decode_shared_prefix" if shared else "pa_decode",
          "decode_us_median": round(med * 1e3, 2), "decode_us_mean": round(m["mean_ms"] * 1e3, 2),
          "unique_bytes": int(ub), "logical_bytes": int(lb)}
+    if plain is not None:
+        r["pa_decode_us_median"] = round(plain[0] * 1e3, 2)
+        r["pa_decode_frac"] = round(plain[1] / PEAK_HBM_GBPS, 4)
     if w.name != "tiny_fp32":
         r["unique_gbps"] = round(m["achieved"], 1)
         r["logical_gbps"] = round(lb / (m["mean_ms"] * 1e-3) / 1e9, 1)
@@ -759,6 +790,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llama8b_decode")
     ap.add_argument("--partition", type=int, default=0)
+    ap.add_argument("--shared-prefix", action="store_true",
+                    help="decode with pa_decode_shared_prefix")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the per-configuration records after the headline")
@@ -804,7 +837,8 @@ def main():
         run_prefill(args)
         return
 
-    m = measure_decode(args.workload, args.steps, args.warmup, args.cold_reps, args.partition)
+    m = measure_decode(args.workload, args.steps, args.warmup, args.cold_reps, args.partition,
+                       args.shared_prefix)
     w = m["w"]
     # the committed counters cover the headline batch only
     traffic = (traffic_from_profiles(kernel_sources_hash())
@@ -825,7 +859,8 @@ def main():
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "head_dim": w.D,
                    "block_size": w.bs, "kv_dtype": w.kv_dtype, "q_dtype": w.q_dtype,
                    "context_tokens_first_step": int(w.lengths.sum()), "pool_blocks": w.NB,
-                   "partition_tokens": args.partition or "auto"},
+                   "partition_tokens": args.partition or "auto",
+                   "decode": "pa_decode_shared_prefix" if args.shared_prefix else "pa_decode"},
         "roofline": {"bound": "hbm", "achieved": round(m["achieved"], 1), "peak": PEAK_HBM_GBPS,
                      "unit": "GB/s", "frac": round(m["achieved"] / PEAK_HBM_GBPS, 4),
                      "traffic": traffic},

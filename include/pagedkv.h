@@ -338,6 +338,39 @@ int pa_decode_no_alloc(float* out, const void* q, int32_t q_dtype, const void* k
                        int32_t Hkv, int32_t D, int32_t bs, int32_t NB, float scale,
                        int32_t partition_tokens, void* stream);
 
+/* Bytes of scratch that pa_decode_shared_prefix needs for these sizes; 0 for invalid sizes.
+ * At least pa_decode_workspace_size(B, Hq, Hkv, D, max_seq_len, 0). */
+size_t pa_decode_shared_prefix_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                                              int32_t max_seq_len);
+
+/* pa_decode (balanced schedule) that reads a shared prefix once per group instead of once per
+ * sequence ([Serving] "Sharing comes for free": sequences that share a prompt point their block
+ * tables at the same physical blocks; [Walkthrough] "Step 8": a shared prefix is stored once).
+ * Same arguments and result as pa_decode with partition_tokens = 0; the sums are taken in a
+ * different order, so outputs agree with pa_decode's to rounding, not bit for bit (repeated
+ * calls are bit-identical).
+ *   Groups: a run of consecutive batch entries, inside an aligned window of 64, whose tables
+ *     start with the same block in [0, NB).  The library finds them on the device: callers
+ *     that want the saving put sequences that share a prefix next to each other.  Within a
+ *     group, member b shares with the longest member (the first on ties) the tokens below
+ *     min(seq_lens[b], 16 k), k = leading table entries equal in both; those are read once per
+ *     KV head for up to 16 query heads (of several members) at a time, and b's other tokens
+ *     as in pa_decode.  The tables alone decide: a run of unrelated sequences costs nothing
+ *     but the detection.
+ *   Runs its own schedule for a PA_BF16 q over PA_BF16, PA_I8 or PA_I4 caches with Hq/Hkv in
+ *     {1, 2, 4, 8} and B <= 8192; any other valid call is pa_decode(..., 0, ...).
+ *   workspace: device buffer of workspace_bytes >= pa_decode_shared_prefix_workspace_size();
+ *     needs no initialisation; calls that overlap in time must not share it.
+ *   Four launches on `stream`: the group plan, the prefix pass, the decode of every sequence
+ *   past its prefix with the prefix's states folded in (log-sum-exp), and the merge of split
+ *   segments.  Errors as for pa_decode. */
+int pa_decode_shared_prefix(float* out, const void* q, int32_t q_dtype, const void* k_cache,
+                            const void* v_cache, int32_t kv_dtype, const float* k_scale,
+                            const float* v_scale, const int32_t* block_tables, int32_t max_blocks,
+                            const int32_t* seq_lens, int32_t max_seq_len, int32_t B, int32_t Hq,
+                            int32_t Hkv, int32_t D, int32_t bs, int32_t NB, float scale,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
 /* Chunked-prefill attention over the paged cache ([Serving] "Two Phases: Prefill and Decode":
  * prefill runs a prompt's tokens in parallel, each attending to all earlier ones; "Prefix
  * Caching and Chunked Prefill" / "Chunked prefill": a long prefill runs as a series of chunks).

@@ -81,6 +81,10 @@ _SIGNATURES = {
                             _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz, _vp]),
     "pa_decode_no_alloc": (C.c_int, [_vp, _vp, _i32, _vp, _vp, _i32, _vp, _vp, _vp, _i32, _vp,
                                      _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp]),
+    "pa_decode_shared_prefix_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32]),
+    "pa_decode_shared_prefix": (C.c_int, [_vp, _vp, _i32, _vp, _vp, _i32, _vp, _vp, _vp, _i32,
+                                          _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32,
+                                          _vp, _sz, _vp]),
 }
 
 _lib_handle = None
@@ -581,6 +585,40 @@ def decode_no_alloc(q, k_cache, v_cache, block_tables, seq_lens, max_seq_len: in
                                     block_tables.shape[1], _dev(seq_lens, "seq_lens", torch.int32),
                                     max_seq_len, B, Hq, Hkv, D, bs, NB, float(scale),
                                     partition_tokens, _stream(stream)), "pa_decode_no_alloc")
+    return out
+
+
+def decode_shared_prefix_workspace_size(B: int, Hq: int, Hkv: int, D: int,
+                                        max_seq_len: int) -> int:
+    return int(lib().pa_decode_shared_prefix_workspace_size(B, Hq, Hkv, D, max_seq_len))
+
+
+def decode_shared_prefix(q, k_cache, v_cache, block_tables, seq_lens, max_seq_len: int,
+                         scale: float, k_scale=None, v_scale=None, out=None, workspace=None,
+                         stream=None):
+    """pa_decode_shared_prefix: decode that reads the blocks a run of adjacent sequences
+    shares at the start of their tables once per group; returns out [B][Hq][D] float32."""
+    torch = _torch()
+    B, Hq, D = q.shape
+    NB, Hkv, bs, Dk = cache_geometry(k_cache, v_cache)
+    if Dk != D:
+        raise ValueError("cache shapes do not match q")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or tuple(seq_lens.shape) != (B,):
+        raise ValueError("block_tables must be [B][max_blocks] and seq_lens [B]")
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+    elif tuple(out.shape) != (B, Hq, D):
+        raise ValueError("out must be [B][Hq][D]")
+    if workspace is None:
+        need = decode_shared_prefix_workspace_size(B, Hq, Hkv, D, max_seq_len)
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    _check(lib().pa_decode_shared_prefix(
+        _dev(out, "out", torch.float32), _dev(q, "q"), _dtype_code(q), _dev(k_cache, "k_cache"),
+        _dev(v_cache, "v_cache"), _dtype_code(k_cache), _dev(k_scale, "k_scale", torch.float32),
+        _dev(v_scale, "v_scale", torch.float32), _dev(block_tables, "block_tables", torch.int32),
+        block_tables.shape[1], _dev(seq_lens, "seq_lens", torch.int32), max_seq_len, B, Hq, Hkv,
+        D, bs, NB, float(scale), _dev(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(), _stream(stream)), "pa_decode_shared_prefix")
     return out
 
 

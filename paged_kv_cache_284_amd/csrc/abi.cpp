@@ -197,6 +197,53 @@ int cu_count() {
   return n;
 }
 
+// Workgroups of the balanced schedule: the resident ones, no more than there are units, a
+// multiple of 8 (one per XCD) when there are 8 or more; 0 when the device cannot be queried.
+int64_t balanced_workgroups(int32_t B, int32_t Hkv, int32_t max_seq_len) {
+  const int cus = cu_count();
+  if (cus <= 0) return 0;
+  int64_t nw = static_cast<int64_t>(cus) * pa::mfma_workgroups_per_cu();
+  if (nw > pa::kMaxBalancedWorkgroups) nw = pa::kMaxBalancedWorkgroups;
+  const int64_t units = static_cast<int64_t>(Hkv) * B * ((max_seq_len + 31) / 32);
+  if (nw > units) nw = units;
+  if (nw >= 8) nw -= nw % 8;
+  if (nw < 1) nw = 1;
+  return nw;
+}
+
+// Shared-prefix decode: tokens per prefix-pass part and parts per output row.  A part is one
+// workgroup item; at most 8 parts per row keep the states' memory below 8 (D + 2) floats per
+// row.
+void prefix_parts(int32_t max_seq_len, int32_t* tokens, int32_t* parts) {
+  constexpr int64_t kMinPart = 1024, kMaxParts = 8;
+  int64_t np = (static_cast<int64_t>(max_seq_len) + kMinPart - 1) / kMinPart;
+  if (np > kMaxParts) np = kMaxParts;
+  if (np < 1) np = 1;
+  int64_t pt = (static_cast<int64_t>(max_seq_len) + np - 1) / np;
+  pt = (pt + 31) / 32 * 32;
+  if (pt < 32) pt = 32;
+  *tokens = static_cast<int32_t>(pt);
+  *parts = static_cast<int32_t>((max_seq_len + pt - 1) / pt < 1 ? 1 : (max_seq_len + pt - 1) / pt);
+}
+
+// Shared-prefix decode workspace past the balanced schedule's: pstart, ref_p, grp_ref [B]; the
+// prefix states m, l [B][Hq][parts] and o [B][Hq][parts][D].
+int64_t shared_extra_bytes(int32_t B, int32_t Hq, int32_t D, int32_t max_seq_len) {
+  int32_t pt = 0, np = 0;
+  prefix_parts(max_seq_len, &pt, &np);
+  const int64_t rows = static_cast<int64_t>(B) * Hq * np;
+  return 3 * align256(static_cast<int64_t>(B) * 4) + 2 * align256(rows * 4) +
+         align256(rows * D * 4);
+}
+
+// Whether pa_decode_shared_prefix runs its own schedule (else it is pa_decode).
+bool shared_schedule(int32_t q_dtype, int32_t kv_dtype, int32_t B, int32_t Hq, int32_t Hkv) {
+  const int G = Hq / Hkv;
+  return q_dtype == PA_BF16 &&
+         (kv_dtype == PA_BF16 || kv_dtype == PA_I8 || kv_dtype == PA_I4) &&
+         (G == 1 || G == 2 || G == 4 || G == 8) && B <= pa::kMaxBalancedBatch;
+}
+
 }  // namespace
 
 extern "C" {
@@ -289,14 +336,8 @@ int decode_run(float* out, const void* q, int32_t q_dtype, const void* k_cache,
                         G <= pa::kMaxBalancedGroup;
   int64_t nw = 0;
   if (balanced) {
-    const int cus = cu_count();
-    if (cus <= 0) return PA_ERR_DEVICE;
-    nw = static_cast<int64_t>(cus) * pa::mfma_workgroups_per_cu();
-    if (nw > pa::kMaxBalancedWorkgroups) nw = pa::kMaxBalancedWorkgroups;
-    const int64_t units = static_cast<int64_t>(Hkv) * B * ((max_seq_len + 31) / 32);
-    if (nw > units) nw = units;
-    if (nw >= 8) nw -= nw % 8;
-    if (nw < 1) nw = 1;
+    nw = balanced_workgroups(B, Hkv, max_seq_len);
+    if (nw <= 0) return PA_ERR_DEVICE;
   }
   if (exact_size) {
     // a fixed buffer: exactly what this call's schedule uses must fit
@@ -348,6 +389,77 @@ int pa_decode(float* out, const void* q, int32_t q_dtype, const void* k_cache,
   return pa::decode_run(out, q, q_dtype, k_cache, v_cache, kv_dtype, k_scale, v_scale,
                         block_tables, max_blocks, seq_lens, max_seq_len, B, Hq, Hkv, D, NB,
                         scale, partition_tokens, workspace, workspace_bytes, false, stream);
+}
+
+size_t pa_decode_shared_prefix_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                                              int32_t max_seq_len) {
+  const size_t plain = pa_decode_workspace_size(B, Hq, Hkv, D, max_seq_len, 0);
+  if (plain == 0 || B > pa::kMaxBalancedBatch || Hq / Hkv > pa::kMaxBalancedGroup) return plain;
+  const int64_t bytes = balanced_bytes(Hq / Hkv, D, pa::kMaxBalancedWorkgroups) +
+                        shared_extra_bytes(B, Hq, D, max_seq_len);
+  return static_cast<size_t>(bytes) > plain ? static_cast<size_t>(bytes) : plain;
+}
+
+int pa_decode_shared_prefix(float* out, const void* q, int32_t q_dtype, const void* k_cache,
+                            const void* v_cache, int32_t kv_dtype, const float* k_scale,
+                            const float* v_scale, const int32_t* block_tables, int32_t max_blocks,
+                            const int32_t* seq_lens, int32_t max_seq_len, int32_t B, int32_t Hq,
+                            int32_t Hkv, int32_t D, int32_t bs, int32_t NB, float scale,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  bool nothing = false;
+  const int st = pa::decode_check(out, q, q_dtype, k_cache, v_cache, kv_dtype, k_scale, v_scale,
+                                  block_tables, max_blocks, seq_lens, max_seq_len, B, Hq, Hkv,
+                                  D, bs, NB, scale, 0, &nothing);
+  if (st != PA_OK || nothing) return st;
+  if (!workspace ||
+      workspace_bytes < pa_decode_shared_prefix_workspace_size(B, Hq, Hkv, D, max_seq_len))
+    return PA_ERR_INVALID;
+  if (!shared_schedule(q_dtype, kv_dtype, B, Hq, Hkv))
+    return pa::decode_run(out, q, q_dtype, k_cache, v_cache, kv_dtype, k_scale, v_scale,
+                          block_tables, max_blocks, seq_lens, max_seq_len, B, Hq, Hkv, D, NB,
+                          scale, 0, workspace, workspace_bytes, false, stream);
+  const int64_t nw = balanced_workgroups(B, Hkv, max_seq_len);
+  if (nw <= 0) return PA_ERR_DEVICE;
+  pa::DecodeArgs a{};
+  a.out = out;
+  a.q = q;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.tables = block_tables;
+  a.seq_lens = seq_lens;
+  a.max_blocks = max_blocks;
+  a.max_seq_len = max_seq_len;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.D = D;
+  a.NB = NB;
+  a.partition = 512;  // unused by the balanced schedule
+  a.np_max = 1;
+  a.scale_log2 = scale * kLog2e;
+  a.nw = static_cast<int32_t>(nw);
+  const int G = Hq / Hkv;
+  char* base = static_cast<char*>(workspace);
+  const int64_t rows = nw * 2 * G;
+  a.ws_m = reinterpret_cast<float*>(base);
+  a.ws_l = reinterpret_cast<float*>(base + align256(rows * 4));
+  a.ws_o = reinterpret_cast<float*>(base + 2 * align256(rows * 4));
+  a.ws_merge =
+      reinterpret_cast<int32_t*>(base + 2 * align256(rows * 4) + align256(rows * D * 4));
+  char* p = base + balanced_bytes(G, D, nw);
+  const int64_t bb = align256(static_cast<int64_t>(B) * 4);
+  a.pstart = reinterpret_cast<int32_t*>(p);
+  a.ref_p = reinterpret_cast<int32_t*>(p + bb);
+  a.grp_ref = reinterpret_cast<int32_t*>(p + 2 * bb);
+  prefix_parts(max_seq_len, &a.pf_tokens, &a.pf_parts);
+  const int64_t prow = static_cast<int64_t>(B) * Hq * a.pf_parts;
+  a.pf_m = reinterpret_cast<float*>(p + 3 * bb);
+  a.pf_l = reinterpret_cast<float*>(p + 3 * bb + align256(prow * 4));
+  a.pf_o = reinterpret_cast<float*>(p + 3 * bb + 2 * align256(prow * 4));
+  a.pf_gmax = B / 2 + 1;
+  return status_of(pa::launch_decode_shared_prefix(a, kv_dtype, static_cast<hipStream_t>(stream)));
 }
 
 int pa_prefill(float* out, const void* q, int32_t q_dtype, const void* k_cache,

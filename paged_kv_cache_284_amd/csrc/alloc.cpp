@@ -631,6 +631,6 @@ const char* pa_status_string(int status) {
   }
 }
 
-int pa_abi_version(void) { return 5; }
+int pa_abi_version(void) { return 6; }
 
 }  // extern "C"

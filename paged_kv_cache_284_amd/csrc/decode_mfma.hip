@@ -115,9 +115,64 @@ struct PairRegsI4 {
 // register pressure (measured: bf16 1 and 2 equal, int8 best at 1, int4 best at 2).
 constexpr int kDepthBf16 = 2, kDepthI8 = 1, kDepthI4 = 2;
 
-template <int G, int D, bool kStream, int kKV>
+// Schedules of decode_mfma_kernel.
+constexpr int kFixed = 0;     // one workgroup per (partition, KV head, sequence)
+constexpr int kBalanced = 1;  // equal spans of block pairs per workgroup
+constexpr int kSuffix = 2;    // kBalanced over the pairs past each sequence's shared prefix, with
+                              // the prefix pass's states folded into every final output
+constexpr int kPrefix = 3;    // the shared-prefix pass (16 query columns of a group's members)
+
+// Tokens of sequence b that the prefix pass covered (0 when it has no shared prefix).
+__device__ __forceinline__ int prefix_tokens(const DecodeArgs& a, int b, int L) {
+  const int ps = a.pstart[b] + a.ref_p[b];
+  return min(max(ps, 0), L) & ~(2 * kBlockSize - 1);
+}
+
+// Prefix-pass parts that output rows of a sequence with ps prefix tokens fold in.
+__device__ __forceinline__ int prefix_parts_of(const DecodeArgs& a, int ps) {
+  return ps > 0 ? min((ps + a.pf_tokens - 1) / a.pf_tokens, a.pf_parts) : 0;
+}
+
+// One prefix-pass state of element d of output row `row`, part k: (m, l, o).
+struct PrefixState {
+  float m, l, o;
+};
+__device__ __forceinline__ PrefixState load_prefix(const DecodeArgs& a, int64_t row, int k,
+                                                   int d) {
+  const int64_t slot = row * a.pf_parts + k;
+  return {a.pf_m[slot], a.pf_l[slot], a.pf_o[slot * a.D + d]};
+}
+
+// Folds a prefix state into the running state (M, num, den) of one element: M the max (log2
+// domain), num the weighted sum of values and den the sum of weights, both relative to M.
+// Callers load the states of all their elements first and fold them after, so one round trip
+// to memory serves them all.
+__device__ __forceinline__ void fold_state(float& M, float& num, float& den, PrefixState p) {
+  if (!(p.l > 0.f)) return;
+  const float mn = fmaxf(M, p.m);
+  const float c = __builtin_amdgcn_exp2f(M - mn);  // 0 while the running state is empty
+  const float f = p.l * __builtin_amdgcn_exp2f(p.m - mn);
+  num = num * c + f * p.o;
+  den = den * c + f;
+  M = mn;
+}
+
+// Plain (cached) loads: the prefix pass reads each shared tile once per column block, and the
+// column blocks of one tile run side by side on one XCD, so the second read comes from its L2.
+struct CachedLoad {
+  template <typename T>
+  __device__ __forceinline__ T get(const void* p) const {
+    return *reinterpret_cast<const T*>(p);
+  }
+};
+
+template <int G, int D, int kMode, int kKV>
 __global__ void __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
 decode_mfma_kernel(DecodeArgs a) {
+  constexpr bool kStream = kMode == kBalanced || kMode == kSuffix;  // balanced schedule
+  constexpr bool kFold = kMode == kSuffix;
+  constexpr bool kPre = kMode == kPrefix;
+  static_assert(!kPre || G == 16, "the prefix pass fills all 16 columns of its tiles");
   constexpr bool kI4 = kKV == kKvI4;
   constexpr bool kI8 = kKV == kKvI8 || kI4;  // a quantised cache (scales, offset codes)
   // code offset removed from the sums; int4 carries it inside its weighted sums (two offsets,
@@ -139,6 +194,8 @@ decode_mfma_kernel(DecodeArgs a) {
   __shared__ float l_s[kWaves][kSlots][G];
   __shared__ float o_s[kWaves][kSlots][G][D];
   __shared__ int32_t wave_tot[kWaves];
+  // prefix pass: output row (-1: unused) and token limit of each query column of the item
+  __shared__ int32_t colrow_s[kPre ? 16 : 1], collim_s[kPre ? 16 : 1];
 
   const int lane = threadIdx.x % 64;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
@@ -164,8 +221,12 @@ decode_mfma_kernel(DecodeArgs a) {
   //   solo = true: the calling wave takes every pair itself; with lds_slot >= 0 it leaves its
   //     state in LDS slot (w, lds_slot), otherwise it writes the result: dest 0 = final output,
   //     2 = balanced-schedule slot `part`.
+  //   ps (kSuffix): tokens of b the prefix pass covered; a final output folds in its states.
+  //   kPrefix: b is the group's reference sequence (its table is read), the query columns and
+  //     their token limits come from colrow_s / collim_s, and the merged states go to prefix
+  //     part `part` of each column's row.
   auto run_piece = [&](int b, int g, int L, int i0, int i1, bool solo, int dest, int64_t part,
-                       int lds_slot) {
+                       int lds_slot, int ps) {
     const int32_t* __restrict__ table = a.tables + static_cast<int64_t>(b) * a.max_blocks;
     const int end = L;
 
@@ -176,9 +237,15 @@ decode_mfma_kernel(DecodeArgs a) {
     // quantised caches: sum of this head's q operands, reduced over the four lane groups
     // (int4: weighted by each element's code offset)
     float qsum = 0.f;
+    int lim_tok = 0;  // kPrefix: tokens of this lane's column (its pairs from lim_tok on are masked)
     {
-      const uint16_t* q = static_cast<const uint16_t*>(a.q) +
-                          (static_cast<int64_t>(b) * a.Hq + static_cast<int64_t>(g) * G + r % G) * D;
+      int64_t qrow = static_cast<int64_t>(b) * a.Hq + static_cast<int64_t>(g) * G + r % G;
+      if constexpr (kPre) {
+        const int cr = colrow_s[r];
+        qrow = cr >= 0 ? cr : colrow_s[0];  // an unused column computes on a valid row
+        lim_tok = collim_s[r];
+      }
+      const uint16_t* q = static_cast<const uint16_t*>(a.q) + qrow * D;
 #pragma unroll
       for (int s = 0; s < kSteps; ++s) {
         if constexpr (kI8) {
@@ -235,22 +302,22 @@ decode_mfma_kernel(DecodeArgs a) {
         R.vs_a = ba >= 0 ? uniform_load(a.v_scale, ta) : 0.f;
         R.vs_b = bb >= 0 ? uniform_load(a.v_scale, tb) : 0.f;
       }
-      const StreamLoad ld;
+      const std::conditional_t<kPre, CachedLoad, StreamLoad> ld;
       if constexpr (kI4) {
         const int64_t h_a = tile_a / 2, h_b = tile_b / 2;  // tiles of bs * D / 2 bytes
         const uint8_t* k1 = kc8 + (tok1 < 16 ? h_a : h_b) + (tok1 % 16) * (D / 2) + 4 * kSteps * qg;
         const uint8_t* k2 = kc8 + (tok2 < 16 ? h_a : h_b) + (tok2 % 16) * (D / 2) + 4 * kSteps * qg;
         if constexpr (kSteps == 4) {
-          const u32x4 x1 = ld.get<u32x4>(k1);
-          const u32x4 x2 = ld.get<u32x4>(k2);
+          const u32x4 x1 = ld.template get<u32x4>(k1);
+          const u32x4 x2 = ld.template get<u32x4>(k2);
 #pragma unroll
           for (int c = 0; c < 4; ++c) {
             R.k1[c] = x1[c];
             R.k2[c] = x2[c];
           }
         } else {
-          const u32x2 x1 = ld.get<u32x2>(k1);
-          const u32x2 x2 = ld.get<u32x2>(k2);
+          const u32x2 x1 = ld.template get<u32x2>(k1);
+          const u32x2 x2 = ld.template get<u32x2>(k2);
 #pragma unroll
           for (int c = 0; c < 2; ++c) {
             R.k1[c] = x1[c];
@@ -260,30 +327,30 @@ decode_mfma_kernel(DecodeArgs a) {
         const uint8_t* v = vc8 + (vblk_sel ? h_b : h_a) + r * (kBlockSize / 2) + 4 * (qg % 2);
 #pragma unroll
         for (int n = 0; n < kTiles; ++n)
-          R.v[n] = ld.get<uint32_t>(v + 16 * n * (kBlockSize / 2));
+          R.v[n] = ld.template get<uint32_t>(v + 16 * n * (kBlockSize / 2));
       } else if constexpr (kI8) {
         const uint8_t* k1 = kc8 + (tok1 < 16 ? tile_a : tile_b) + (tok1 % 16) * D + 16 * qg;
         const uint8_t* k2 = kc8 + (tok2 < 16 ? tile_a : tile_b) + (tok2 % 16) * D + 16 * qg;
 #pragma unroll
         for (int c = 0; c < kSteps / 2; ++c) {
-          R.k1[c] = ld.get<u32x4>(k1 + 64 * c);
-          R.k2[c] = ld.get<u32x4>(k2 + 64 * c);
+          R.k1[c] = ld.template get<u32x4>(k1 + 64 * c);
+          R.k2[c] = ld.template get<u32x4>(k2 + 64 * c);
         }
         const uint8_t* v = vc8 + (vblk_sel ? tile_b : tile_a) + r * kBlockSize + vtok;
 #pragma unroll
         for (int n = 0; n < kTiles; ++n)
-          R.v[n] = ld.get<u32x2>(v + 16 * n * kBlockSize);
+          R.v[n] = ld.template get<u32x2>(v + 16 * n * kBlockSize);
       } else {
         const uint16_t* k1 = kc + (tok1 < 16 ? tile_a : tile_b) + (tok1 % 16) * D + 8 * qg;
         const uint16_t* k2 = kc + (tok2 < 16 ? tile_a : tile_b) + (tok2 % 16) * D + 8 * qg;
 #pragma unroll
         for (int s = 0; s < kSteps; ++s) {
-          R.k1[s] = ld.get<u32x4>(k1 + 32 * s);
-          R.k2[s] = ld.get<u32x4>(k2 + 32 * s);
+          R.k1[s] = ld.template get<u32x4>(k1 + 32 * s);
+          R.k2[s] = ld.template get<u32x4>(k2 + 32 * s);
         }
         const uint16_t* v = vc + (vblk_sel ? tile_b : tile_a) + r * kBlockSize + vtok;
 #pragma unroll
-        for (int n = 0; n < kTiles; ++n) R.v[n] = ld.get<u32x4>(v + 16 * n * kBlockSize);
+        for (int n = 0; n < kTiles; ++n) R.v[n] = ld.template get<u32x4>(v + 16 * n * kBlockSize);
       }
     };
 
@@ -350,6 +417,14 @@ decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e)
           if (t_first + e >= end || my_blk < 0) sc[e] = -INFINITY;
+      }
+      if constexpr (kPre) {
+        // column limits are multiples of a pair; the reference's tokens below the group's
+        // prefix length are all live, so p = 0 keeps a masked column's values out
+        if (tok0 >= lim_tok) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) sc[e] = -INFINITY;
+        }
       }
       if (tail && !kI8) {
         // masked tokens must not reach P.V even with p = 0 (their V may be anything); int8
@@ -513,6 +588,57 @@ decode_mfma_kernel(DecodeArgs a) {
         to_lds(lds_slot);
         return;
       }
+      if constexpr (kFold) {
+        if (dest == 0 && ps > 0) {
+          // the whole segment past the prefix: fold the prefix states into this state.  Rows
+          // 4 qg + j (< G) of this lane, elements 16 n + r; each part's states are loaded
+          // for all of them before any is folded.
+          float M[4], den[4], num[4][kTiles];
+          int64_t row[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int h = 4 * qg + j;
+            M[j] = __shfl(m_run, h % G, 64);
+            den[j] = __shfl(l_tot, h % G, 64);
+            const float cj = kI8 ? __shfl(c_tot, h % G, 64) : 0.f;
+            row[j] = static_cast<int64_t>(b) * a.Hq + static_cast<int64_t>(g) * G + min(h, G - 1);
+#pragma unroll
+            for (int n = 0; n < kTiles; ++n) num[j][n] = acc[n][j] - kOffset * cj;
+          }
+          const int np = prefix_parts_of(a, ps);
+          for (int k = 0; k < np; ++k) {
+            PrefixState st[4][kTiles];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+              for (int n = 0; n < kTiles; ++n)
+                if (4 * qg + j < G) st[j][n] = load_prefix(a, row[j], k, 16 * n + r);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              if (4 * qg + j >= G) continue;
+              // the row's (m, l) are the same for every element: fold them once
+              const float m0 = M[j], d0 = den[j];
+#pragma unroll
+              for (int n = 0; n < kTiles; ++n) {
+                float mm = m0, dd = d0;
+                fold_state(mm, num[j][n], dd, st[j][n]);
+                if (n == kTiles - 1) {
+                  M[j] = mm;
+                  den[j] = dd;
+                }
+              }
+            }
+          }
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            if (4 * qg + j >= G) continue;
+#pragma unroll
+            for (int n = 0; n < kTiles; ++n)
+              a.out[row[j] * D + 16 * n + r] = den[j] > 0.f ? num[j][n] / den[j] : 0.f;
+          }
+          return;
+        }
+      }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int h = 4 * qg + j;
@@ -558,6 +684,19 @@ decode_mfma_kernel(DecodeArgs a) {
         }
       }
       const float o = den > 0.f ? num / den : 0.f;
+      if constexpr (kPre) {
+        // a column with no tokens in this part writes nothing: its row folds in only the
+        // parts below its limit
+        const int64_t row = colrow_s[h];
+        if (row < 0 || collim_s[h] <= i0 * kPair) continue;
+        const int64_t slot = row * a.pf_parts + part;
+        a.pf_o[slot * D + d] = o;
+        if (d == 0) {
+          a.pf_m[slot] = M;
+          a.pf_l[slot] = den;
+        }
+        continue;
+      }
       const int64_t row = static_cast<int64_t>(b) * a.Hq + static_cast<int64_t>(g) * G + h;
       if (dest == 0) {
         a.out[row * D + d] = o;
@@ -573,14 +712,156 @@ decode_mfma_kernel(DecodeArgs a) {
     __syncthreads();  // LDS is reused by the next piece
   };
 
-  if constexpr (!kStream) {
+  if constexpr (kMode == kFixed) {
     const int p = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
     const int L = min(max(a.seq_lens[b], 0), a.max_seq_len);
     const int nparts = max(1, (L + a.partition - 1) / a.partition);
     if (p >= nparts) return;
     const int ppp = a.partition / kPair;  // pairs per partition
     const int n_b = (L + kPair - 1) / kPair;
-    run_piece(b, g, L, p * ppp, min(n_b, (p + 1) * ppp), false, nparts == 1 ? 0 : 1, p, -1);
+    run_piece(b, g, L, p * ppp, min(n_b, (p + 1) * ppp), false, nparts == 1 ? 0 : 1, p, -1, 0);
+  } else if constexpr (kPre) {
+    // The shared-prefix pass.  Every workgroup first lists the groups with a prefix from the
+    // plan (groups are runs of equal grp_ref inside aligned windows of 64 sequences), in batch
+    // order.  A group of M members with a prefix of P tokens splits into items (KV head g,
+    // part of pf_tokens tokens, column block cb of 16 query columns = member-major (member,
+    // head) pairs); its items are numbered in runs of 8 (g, part) items per column block, so
+    // the column blocks of one (g, part) sit 8 item numbers apart and, with a grid that is a
+    // multiple of 8, run at the same time on the same XCD: the second read of the shared
+    // blocks is served by that XCD's L2.  Items go to workgroups round-robin; the 8 waves of a
+    // workgroup take an item's pairs in turn and merge in LDS.
+    const int B = a.B;
+    const int Gs = a.Hq / Hkv;  // query heads per KV head of the sequences
+    const int PT = a.pf_tokens;
+    const int nwin = (B + 63) / 64;
+    int32_t* grp_off = cum_s;                     // [gmax + 1] first item of each group
+    int32_t* grp_s = cum_s + a.pf_gmax + 1;       // [gmax] first member | members << 16
+    int32_t* grp_p = grp_s + a.pf_gmax;           // [gmax] prefix tokens
+    constexpr int kMaxWindows = kMaxBalancedBatch / 64;
+    __shared__ int32_t win_g[kMaxWindows + 1], win_i[kMaxWindows + 1];
+    // Lane values of window win: is the lane the first member of a group with a prefix; if so
+    // its members, prefix tokens (the longest member prefix: the reference's entry is 0) and
+    // items.
+    auto scan_window = [&](int win, int& members, int& ptok, int& items) -> bool {
+      const int i = win * 64 + lane;
+      const int gr = i < B ? a.grp_ref[i] : -1;
+      const int ps = i < B ? a.pstart[i] : 0;
+      const int gr_up = __shfl_up(gr, 1, 64);
+      const int gr_dn = __shfl_down(gr, 1, 64);
+      const bool start = gr >= 0 && (lane == 0 || gr_up != gr);
+      const bool end = gr >= 0 && (lane == 63 || gr_dn != gr);
+      int P = ps;  // max over this lane and the later lanes of its group (members are contiguous)
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int v = __shfl_down(P, o, 64);
+        const int g2 = __shfl_down(gr, o, 64);
+        if (lane + o < 64 && g2 == gr) P = max(P, v);
+      }
+      const uint64_t em = __ballot(end);
+      const int M = start ? __builtin_ctzll(em >> lane) + 1 : 0;
+      const bool act = start && P > 0;
+      const int np = (P + PT - 1) / PT, ncb = (M * Gs + 15) / 16;
+      members = M;
+      ptok = P;
+      items = act ? (Hkv * np + 7) / 8 * 8 * ncb : 0;
+      return act;
+    };
+    for (int win = w; win < nwin; win += kWaves) {
+      int m, pt, it;
+      const bool act = scan_window(win, m, pt, it);
+      int isum = it;
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) isum += __shfl_xor(isum, o, 64);
+      const uint64_t am = __ballot(act);
+      if (lane == 0) {
+        win_g[win] = __popcll(am);
+        win_i[win] = isum;
+      }
+    }
+    __syncthreads();
+    if (w == 0) {
+      // exclusive prefix sums over the windows (at most 128: two per lane)
+      int g0 = lane < nwin ? win_g[lane] : 0, i0 = lane < nwin ? win_i[lane] : 0;
+      int g1 = lane + 64 < nwin ? win_g[lane + 64] : 0, i1 = lane + 64 < nwin ? win_i[lane + 64] : 0;
+      int sg0 = g0, si0 = i0, sg1 = g1, si1 = i1;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int a0 = __shfl_up(sg0, o, 64), b0 = __shfl_up(si0, o, 64);
+        const int a1 = __shfl_up(sg1, o, 64), b1 = __shfl_up(si1, o, 64);
+        if (lane >= o) {
+          sg0 += a0;
+          si0 += b0;
+          sg1 += a1;
+          si1 += b1;
+        }
+      }
+      const int tg0 = __shfl(sg0, 63, 64), ti0 = __shfl(si0, 63, 64);
+      if (lane < nwin) {
+        win_g[lane] = sg0 - g0;
+        win_i[lane] = si0 - i0;
+      }
+      if (lane + 64 < nwin) {
+        win_g[lane + 64] = tg0 + sg1 - g1;
+        win_i[lane + 64] = ti0 + si1 - i1;
+      }
+      if (lane == 63) {
+        win_g[nwin] = tg0 + sg1;
+        win_i[nwin] = ti0 + si1;
+      }
+    }
+    __syncthreads();
+    for (int win = w; win < nwin; win += kWaves) {
+      int m, pt, it;
+      const bool act = scan_window(win, m, pt, it);
+      const uint64_t am = __ballot(act);
+      const int rank = __popcll(am & ((1ull << lane) - 1));
+      int x = it;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(x, o, 64);
+        if (lane >= o) x += y;
+      }
+      if (act) {
+        const int k = win_g[win] + rank;
+        grp_off[k] = win_i[win] + x - it;
+        grp_s[k] = (win * 64 + lane) | (m << 16);
+        grp_p[k] = pt;
+      }
+    }
+    const int ngroups = win_g[nwin], nitems = win_i[nwin];
+    if (threadIdx.x == 0) grp_off[ngroups] = nitems;
+    __syncthreads();
+    for (int it = blockIdx.x; it < nitems; it += gridDim.x) {
+      int lo = 0, hi = ngroups - 1;  // the group holding item it: last k with grp_off[k] <= it
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) / 2;
+        if (grp_off[mid] <= it) lo = mid; else hi = mid - 1;
+      }
+      const int first = grp_s[lo] & 0xffff, M = grp_s[lo] >> 16, P = grp_p[lo];
+      const int np = (P + PT - 1) / PT, ncb = (M * Gs + 15) / 16;
+      const int local = it - grp_off[lo];
+      const int cb = local % (8 * ncb) / 8;
+      const int qi = local / (8 * ncb) * 8 + local % 8;
+      if (qi >= Hkv * np) continue;  // padding of the last run of 8
+      const int g = qi / np, part = qi % np;
+      const int ref = a.grp_ref[first];
+      if (threadIdx.x < 16) {
+        const int c = cb * 16 + threadIdx.x;
+        const int mi = c / Gs;
+        int row = -1, lim = 0;
+        if (mi < M) {
+          const int mb = first + mi;
+          row = mb * a.Hq + g * Gs + c % Gs;
+          lim = mb == ref ? P : a.pstart[mb];
+        }
+        colrow_s[threadIdx.x] = row;
+        collim_s[threadIdx.x] = lim;
+      }
+      if (threadIdx.x == 0 && qi == 0 && cb == 0) a.ref_p[ref] = P;
+      __syncthreads();
+      const int ptp = PT / kPair;
+      run_piece(ref, g, P, part * ptp, min(P / kPair, (part + 1) * ptp), false, 3, part, -1, 0);
+    }
   } else {
     // pair counts -> prefix sums cum_s[0..B]
     const int B = a.B;
@@ -590,6 +871,9 @@ decode_mfma_kernel(DecodeArgs a) {
       const int i = base + threadIdx.x;
       const int L = i < B ? min(max(a.seq_lens[i], 0), a.max_seq_len) : 0;
       int x = (L + kPair - 1) / kPair;
+      if constexpr (kFold) {
+        if (i < B) x -= prefix_tokens(a, i, L) / kPair;  // the pairs past the shared prefix
+      }
 #pragma unroll
       for (int o = 1; o < 64; o <<= 1) {
         const int y = __shfl_up(x, o, 64);
@@ -610,11 +894,41 @@ decode_mfma_kernel(DecodeArgs a) {
     const int64_t U = T * Hkv;            // all units
     const int NW = a.nw;
     const int wl = blockIdx.x;
-    // empty sequences produce zeros
+    // empty sequences produce zeros (kSuffix: sequences whose prefix covers every token get
+    // the prefix pass's states alone)
     for (int b = wl; b < B; b += NW) {
       if (cum_s[b + 1] != cum_s[b]) continue;
-      for (int i = threadIdx.x; i < a.Hq * D; i += 64 * kWaves)
-        a.out[static_cast<int64_t>(b) * a.Hq * D + i] = 0.f;
+      const int ps =
+          kFold ? prefix_tokens(a, b, min(max(a.seq_lens[b], 0), a.max_seq_len)) : 0;
+      const int np = kFold ? prefix_parts_of(a, ps) : 0;
+      constexpr int kBatch = 4;  // elements per thread whose states are requested together
+      for (int i0 = threadIdx.x; i0 < a.Hq * D; i0 += kBatch * 64 * kWaves) {
+        float M[kBatch], num[kBatch], den[kBatch];
+#pragma unroll
+        for (int e = 0; e < kBatch; ++e) {
+          M[e] = -INFINITY;
+          num[e] = 0.f;
+          den[e] = 0.f;
+        }
+        for (int k = 0; k < np; ++k) {
+          PrefixState st[kBatch];
+#pragma unroll
+          for (int e = 0; e < kBatch; ++e) {
+            const int i = i0 + e * 64 * kWaves;
+            if (i < a.Hq * D)
+              st[e] = load_prefix(a, static_cast<int64_t>(b) * a.Hq + i / D, k, i % D);
+          }
+#pragma unroll
+          for (int e = 0; e < kBatch; ++e)
+            if (i0 + e * 64 * kWaves < a.Hq * D) fold_state(M[e], num[e], den[e], st[e]);
+        }
+#pragma unroll
+        for (int e = 0; e < kBatch; ++e) {
+          const int i = i0 + e * 64 * kWaves;
+          if (i < a.Hq * D)
+            a.out[static_cast<int64_t>(b) * a.Hq * D + i] = den[e] > 0.f ? num[e] / den[e] : 0.f;
+        }
+      }
     }
     // workgroup span [u0, u1); wave w streams its own eighth [v0, v1) of it with no barriers
     const int64_t u0 = U * wl / NW, u1 = U * (wl + 1) / NW;
@@ -685,7 +999,9 @@ decode_mfma_kernel(DecodeArgs a) {
           info_s[w][slot][3] = static_cast<int32_t>(part);
         }
       }
-      run_piece(b, g, L, i0, i0 + take, true, dest, part, slot);
+      const int ps = kFold ? prefix_tokens(a, b, L) : 0;
+      const int off = ps / kPair;  // kSuffix: units count the pairs past the prefix
+      run_piece(b, g, L, i0 + off, i0 + off + take, true, dest, part, slot, ps);
       u += take;
     }
     __syncthreads();
@@ -699,6 +1015,10 @@ decode_mfma_kernel(DecodeArgs a) {
     __shared__ float gm_s[kE][G];   // at a group's last entry: the group's M and l
     __shared__ float gl_s[kE][G];
     __shared__ uint32_t mask_s[2];  // used entries, last entries of groups
+    // kSuffix: prefix tokens of each entry's sequence when the entry's segment is written out
+    // (dest 0), and the (m, l) of that row's first prefix part
+    __shared__ int32_t eps_s[kFold ? kE : 1];
+    __shared__ float pm_s[kFold ? kE : 1][G], pl_s[kFold ? kE : 1][G];
     const float* mf = &m_s[0][0][0];
     const float* lf = &l_s[0][0][0];
     const float* of = &o_s[0][0][0][0];
@@ -728,6 +1048,20 @@ decode_mfma_kernel(DecodeArgs a) {
       wt_s[e][h] = live ? __builtin_amdgcn_exp2f(me - M) : 0.f;
       gm_s[e][h] = M;
       gl_s[e][h] = den;
+      if constexpr (kFold) {
+        int ps = 0;
+        if (used && info_s[e / 2][e % 2][2] == 0) {
+          const int b = info_s[e / 2][e % 2][0], g = info_s[e / 2][e % 2][1];
+          ps = prefix_tokens(a, b, min(max(a.seq_lens[b], 0), a.max_seq_len));
+          if (ps > 0) {
+            const int64_t slot =
+                (static_cast<int64_t>(b) * a.Hq + static_cast<int64_t>(g) * G + h) * a.pf_parts;
+            pm_s[e][h] = a.pf_m[slot];
+            pl_s[e][h] = a.pf_l[slot];
+          }
+        }
+        if (h == 0) eps_s[e] = ps;
+      }
     }
     if (w == kWaves - 1) {
       // used entries, and the last entry of each group (on the last wave, which the weights
@@ -751,6 +1085,21 @@ decode_mfma_kernel(DecodeArgs a) {
         float ov[kE];
 #pragma unroll
         for (int e = 0; e < kE; ++e) ov[e] = of[e * G * D + idx];  // all reads in flight at once
+        // kSuffix: the first prefix part's value of this element for every group written out,
+        // requested together
+        float pov[kFold ? kE : 1];
+        if constexpr (kFold) {
+#pragma unroll
+          for (int e = 0; e < kE; ++e) {
+            pov[e] = 0.f;
+            if (((em >> e) & 1u) && eps_s[e] > 0) {
+              const int b = info_s[e / 2][e % 2][0], g = info_s[e / 2][e % 2][1];
+              const int64_t slot =
+                  (static_cast<int64_t>(b) * a.Hq + static_cast<int64_t>(g) * G + h) * a.pf_parts;
+              pov[e] = a.pf_o[slot * D + d];
+            }
+          }
+        }
         float num = 0.f;
 #pragma unroll
         for (int e = 0; e < kE; ++e) {
@@ -759,9 +1108,19 @@ decode_mfma_kernel(DecodeArgs a) {
             const int* inf = info_s[e / 2][e % 2];
             const int b = inf[0], g = inf[1], dest = inf[2], part = inf[3];
             const float den = gl_s[e][h];
-            const float o = den > 0.f ? num / den : 0.f;
+            float o = den > 0.f ? num / den : 0.f;
             const int64_t row = static_cast<int64_t>(b) * a.Hq + static_cast<int64_t>(g) * G + h;
             if (dest == 0) {
+              if constexpr (kFold) {
+                const int ps = eps_s[e];
+                if (ps > 0) {
+                  float M = gm_s[e][h], nn = num, dd = den;
+                  fold_state(M, nn, dd, PrefixState{pm_s[e][h], pl_s[e][h], pov[e]});
+                  const int np = prefix_parts_of(a, ps);
+                  for (int k = 1; k < np; ++k) fold_state(M, nn, dd, load_prefix(a, row, k, d));
+                  o = dd > 0.f ? nn / dd : 0.f;
+                }
+              }
               a.out[row * D + d] = o;
             } else {
               const int64_t slot = static_cast<int64_t>(part) * G + h;
@@ -785,7 +1144,8 @@ decode_mfma_kernel(DecodeArgs a) {
 // workgroup order, so the result does not depend on timing.  The states of both slots of wa and
 // slot 0 of wa + 1 (every cut segment has those) are requested together with the record, so
 // the common two-piece merge costs one round trip to memory instead of two.
-template <int G, int D>
+// kFold: the segment's sequence may have a shared prefix whose states are folded in.
+template <int G, int D, bool kFold>
 __global__ void __launch_bounds__(256) streamk_reduce_kernel(DecodeArgs a) {
   const int wa = blockIdx.x;
   const bool has_next = wa + 1 < a.nw;
@@ -856,6 +1216,24 @@ __global__ void __launch_bounds__(256) streamk_reduce_kernel(DecodeArgs a) {
 #pragma unroll
       for (int k = 0; k < kPer; ++k) add(k, mm[u][k], ll[u][k], oo[u][k]);
   }
+  if constexpr (kFold) {
+    const int ps = prefix_tokens(a, b, min(max(a.seq_lens[b], 0), a.max_seq_len));
+    const int np = prefix_parts_of(a, ps);
+    for (int part = 0; part < np; ++part) {
+      PrefixState st[kPer];
+#pragma unroll
+      for (int k = 0; k < kPer; ++k) {
+        const int idx = threadIdx.x + 256 * k;
+        if (idx < G * D) {
+          const int64_t row = static_cast<int64_t>(b) * a.Hq + static_cast<int64_t>(g) * G + idx / D;
+          st[k] = load_prefix(a, row, part, idx % D);
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < kPer; ++k)
+        if (threadIdx.x + 256 * k < G * D) fold_state(M[k], num[k], den[k], st[k]);
+    }
+  }
 #pragma unroll
   for (int k = 0; k < kPer; ++k) {
     const int idx = threadIdx.x + 256 * k;
@@ -866,39 +1244,144 @@ __global__ void __launch_bounds__(256) streamk_reduce_kernel(DecodeArgs a) {
   }
 }
 
+// Shared-prefix plan, one wave per sequence b.  b's group is the run of consecutive sequences
+// around it, inside b's aligned window of 64, whose tables start with the same valid block (a
+// sequence with no tokens has no group).  The reference is the group's longest member (the
+// first on ties).  Every other member b shares with it the tokens below min(L_b, 16 k) where k
+// counts the leading table entries that are equal and valid in both: those tokens sit in the
+// same physical slots, so their keys and values are the same bytes.  The prefix pass takes b's
+// shared tokens rounded down to a pair (pstart[b]); the reference's own prefix length, the
+// largest of its members', is set by the prefix pass (ref_p).  The plan trusts nothing but the
+// tables: any run of sequences gives the same attention as without it.
+__global__ void __launch_bounds__(256) prefix_plan_kernel(DecodeArgs a) {
+  const int lane = threadIdx.x % 64;
+  const int b = blockIdx.x * 4 + static_cast<int>(threadIdx.x / 64);
+  const int B = a.B, NB = a.NB;
+  if (b >= B) return;
+  const int w0 = b & ~63, pos = b - w0;
+  const int i = w0 + lane;
+  int key = -1, Li = 0;
+  if (i < B) {
+    Li = min(max(a.seq_lens[i], 0), a.max_seq_len);
+    if (Li > 0 && a.max_blocks > 0) {
+      const int t = a.tables[static_cast<int64_t>(i) * a.max_blocks];
+      key = (t >= 0 && t < NB) ? t : -1;
+    }
+  }
+  const int kb = __shfl(key, pos, 64);
+  const uint64_t same = __ballot(i < B && key >= 0 && key == kb);
+  auto put = [&](int ps, int gr) {
+    if (lane == 0) {
+      a.pstart[b] = ps;
+      a.grp_ref[b] = gr;
+      a.ref_p[b] = 0;
+    }
+  };
+  if (kb < 0) {
+    put(0, -1);
+    return;
+  }
+  // the maximal run of set bits of `same` through bit pos
+  const uint64_t below = ~same & ((1ull << pos) - 1);
+  const uint64_t above = ~same & ~((2ull << pos) - 1);  // bits above pos (none for pos 63)
+  const int s = below ? 64 - __builtin_clzll(below) : 0;
+  const int e = above ? __builtin_ctzll(above) : 64;
+  if (e - s < 2) {
+    put(0, -1);
+    return;
+  }
+  const bool in = lane >= s && lane < e;
+  int best = in ? Li : -1;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) best = max(best, __shfl_xor(best, o, 64));
+  const int ref = w0 + __builtin_ctzll(__ballot(in && Li == best));
+  if (ref == b) {
+    put(0, ref);
+    return;
+  }
+  const int Lb = __shfl(Li, pos, 64);
+  const int n = min((Lb + kBlockSize - 1) / kBlockSize, (best + kBlockSize - 1) / kBlockSize);
+  const int32_t* tb = a.tables + static_cast<int64_t>(b) * a.max_blocks;
+  const int32_t* tr = a.tables + static_cast<int64_t>(ref) * a.max_blocks;
+  int k = n;  // leading entries equal and valid in both tables
+  for (int c = 0; c < n; c += 64) {
+    const int j = c + lane;
+    bool diff = false;
+    if (j < n) {
+      const int x = tb[j], y = tr[j];
+      diff = x != y || x < 0 || x >= NB;
+    }
+    const uint64_t dm = __ballot(diff);
+    if (dm != 0) {
+      k = c + __builtin_ctzll(dm);
+      break;
+    }
+  }
+  put(min(Lb, kBlockSize * k) & ~(2 * kBlockSize - 1), ref);
+}
+
 template <int G, int D, int kKV>
 hipError_t launch_gd(const DecodeArgs& a, hipStream_t stream) {
   if (a.nw == 0 || G > kMaxBalancedGroup) {
     const dim3 grid(a.np_max, a.Hkv, a.B);
-    hipLaunchKernelGGL((decode_mfma_kernel<G, D, false, kKV>), grid, dim3(64 * kWaves), 0, stream,
+    hipLaunchKernelGGL((decode_mfma_kernel<G, D, kFixed, kKV>), grid, dim3(64 * kWaves), 0, stream,
                        a);
     return hipGetLastError();
   }
   constexpr int Gb = G <= kMaxBalancedGroup ? G : kMaxBalancedGroup;  // never launched for G > 8
   const size_t lds = static_cast<size_t>(a.B + 1) * sizeof(int32_t);
-  hipLaunchKernelGGL((decode_mfma_kernel<Gb, D, true, kKV>), dim3(a.nw), dim3(64 * kWaves), lds,
-                     stream, a);
+  hipLaunchKernelGGL((decode_mfma_kernel<Gb, D, kBalanced, kKV>), dim3(a.nw), dim3(64 * kWaves),
+                     lds, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((streamk_reduce_kernel<Gb, D>), dim3(a.nw), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((streamk_reduce_kernel<Gb, D, false>), dim3(a.nw), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
-template <int G, int kKV>
+// Shared-prefix decode: plan, prefix pass (a.nw workgroups), suffix decode, merge.
+template <int G, int D, int kKV>
+hipError_t launch_gd_shared(const DecodeArgs& a, hipStream_t stream) {
+  if constexpr (G > kMaxBalancedGroup) {
+    return hipErrorNotSupported;
+  } else {
+    hipLaunchKernelGGL(prefix_plan_kernel, dim3((a.B + 3) / 4), dim3(256), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const size_t lds_pre = static_cast<size_t>(3 * a.pf_gmax + 1) * sizeof(int32_t);
+    hipLaunchKernelGGL((decode_mfma_kernel<16, D, kPrefix, kKV>), dim3(a.nw), dim3(64 * kWaves),
+                       lds_pre, stream, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const size_t lds = static_cast<size_t>(a.B + 1) * sizeof(int32_t);
+    hipLaunchKernelGGL((decode_mfma_kernel<G, D, kSuffix, kKV>), dim3(a.nw), dim3(64 * kWaves),
+                       lds, stream, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((streamk_reduce_kernel<G, D, true>), dim3(a.nw), dim3(256), 0, stream, a);
+    return hipGetLastError();
+  }
+}
+
+template <int G, int kKV, bool kShared>
 hipError_t launch_g(const DecodeArgs& a, hipStream_t stream) {
-  if (a.D == 128) return launch_gd<G, 128, kKV>(a, stream);
-  if (a.D == 64) return launch_gd<G, 64, kKV>(a, stream);
+  if constexpr (kShared) {
+    if (a.D == 128) return launch_gd_shared<G, 128, kKV>(a, stream);
+    if (a.D == 64) return launch_gd_shared<G, 64, kKV>(a, stream);
+  } else {
+    if (a.D == 128) return launch_gd<G, 128, kKV>(a, stream);
+    if (a.D == 64) return launch_gd<G, 64, kKV>(a, stream);
+  }
   return hipErrorNotSupported;
 }
 
-template <int kKV>
+template <int kKV, bool kShared = false>
 hipError_t launch_kv(const DecodeArgs& a, hipStream_t stream) {
   switch (a.Hq / a.Hkv) {
-    case 1: return launch_g<1, kKV>(a, stream);
-    case 2: return launch_g<2, kKV>(a, stream);
-    case 4: return launch_g<4, kKV>(a, stream);
-    case 8: return launch_g<8, kKV>(a, stream);
-    case 16: return launch_g<16, kKV>(a, stream);
+    case 1: return launch_g<1, kKV, kShared>(a, stream);
+    case 2: return launch_g<2, kKV, kShared>(a, stream);
+    case 4: return launch_g<4, kKV, kShared>(a, stream);
+    case 8: return launch_g<8, kKV, kShared>(a, stream);
+    case 16: return launch_g<16, kKV, kShared>(a, stream);
     default: return hipErrorNotSupported;
   }
 }
@@ -909,7 +1392,7 @@ int mfma_workgroups_per_cu() {
   static int cached = 0;
   if (cached == 0) {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_mfma_kernel<4, 128, true, kKvBf16>,
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_mfma_kernel<4, 128, kBalanced, kKvBf16>,
                                                      64 * kWaves, 1024) != hipSuccess ||
         n < 1)
       n = 1;
@@ -922,6 +1405,12 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, int kv_dtype, hipStream_t str
   if (kv_dtype == PA_I8) return launch_kv<kKvI8>(a, stream);
   if (kv_dtype == PA_I4) return launch_kv<kKvI4>(a, stream);
   return launch_kv<kKvBf16>(a, stream);
+}
+
+hipError_t launch_decode_shared_prefix(const DecodeArgs& a, int kv_dtype, hipStream_t stream) {
+  if (kv_dtype == PA_I8) return launch_kv<kKvI8, true>(a, stream);
+  if (kv_dtype == PA_I4) return launch_kv<kKvI4, true>(a, stream);
+  return launch_kv<kKvBf16, true>(a, stream);
 }
 
 }  // namespace pa

@@ -30,6 +30,18 @@ struct DecodeArgs {
   int32_t nw;                 // balanced schedule: workgroups (0 = fixed partitions)
   int32_t* ws_merge;          // balanced schedule: per-workgroup merge records [nw][4]
   float scale_log2;           // softmax scale * log2(e)
+  // Shared-prefix decode (all null / 0 otherwise).  A group is a run of consecutive sequences
+  // whose tables start with the same physical block; its reference is its longest member.
+  int32_t* pstart;            // [B] leading tokens of a non-reference member read by the
+                              //     prefix pass (multiple of 32; 0 for references / no group)
+  int32_t* ref_p;             // [B] at a reference: tokens its group's prefix pass covers
+  int32_t* grp_ref;           // [B] reference sequence of each sequence's group, -1 when none
+  float* pf_m;                // [B][Hq][pf_parts] prefix-pass states: max (log2 domain)
+  float* pf_l;                //                   sum of weights
+  float* pf_o;                // [B][Hq][pf_parts][D] normalised output
+  int32_t pf_parts;           // prefix-pass parts per output row (ceil(max_seq_len / pf_tokens))
+  int32_t pf_tokens;          // tokens per prefix-pass part (multiple of 32)
+  int32_t pf_gmax;            // bound on the number of groups (B / 2)
 };
 
 // Everything one chunked-prefill launch needs.  Pointers are device pointers.
@@ -118,6 +130,10 @@ hipError_t launch_decode_generic(const DecodeArgs& a, int q_dtype, int kv_dtype,
 // bf16 query; bf16, int8 or int4 cache (PA_BF16 / PA_I8 / PA_I4; the quantised ones with
 // k_scale / v_scale set); D 64/128; group size 1, 2, 4, 8 or 16.
 hipError_t launch_decode_mfma(const DecodeArgs& a, int kv_dtype, hipStream_t stream);
+// Shared-prefix decode on the matrix cores: the group plan, the prefix pass, then the balanced
+// decode of every sequence past its prefix (a.nw workgroups) folding in the prefix states.
+// bf16 query; bf16, int8 or int4 cache; D 64/128; group size 1, 2, 4 or 8.
+hipError_t launch_decode_shared_prefix(const DecodeArgs& a, int kv_dtype, hipStream_t stream);
 hipError_t launch_splitk_reduce(const DecodeArgs& a, hipStream_t stream);
 // bf16 query and cache; D 64/128; group size 1, 2, 4, 8 or 16.
 hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t stream);

@@ -100,7 +100,7 @@ class Case:
         say(f"{w.describe()} set up in {time.time() - t0:.1f}s")
 
     # one pass of the path: allocator step, CoW copies, table patch, append, decode
-    def step(self, partition_tokens: int = 0, check_pool: bool = True):
+    def step(self, partition_tokens: int = 0, check_pool: bool = True, shared: bool = False):
         w, s = self.w, self.step_index
         if w.append:
             slots, lens_after, tidx, pairs = self.lib.step_arrays(self.seqs)
@@ -149,8 +149,16 @@ class Case:
             assert np.array_equal(self.lens_step.cpu().numpy(), lens_p)
             lens_d = self.lens_step
         max_len = int(lens_p.max())
-        out = pkv.decode(to_device(q, w.q_dtype), self.k, self.v, self.tables, lens_d, max_len,
-                         w.scale, self.ks, self.vs, partition_tokens=partition_tokens)
+        qd = to_device(q, w.q_dtype)
+        if shared:
+            out = pkv.decode_shared_prefix(qd, self.k, self.v, self.tables, lens_d, max_len,
+                                           w.scale, self.ks, self.vs)
+            # the same step through the plain decode, for the comparison of the two paths
+            self.plain = pkv.decode(qd, self.k, self.v, self.tables, lens_d, max_len, w.scale,
+                                    self.ks, self.vs).cpu().numpy()
+        else:
+            out = pkv.decode(qd, self.k, self.v, self.tables, lens_d, max_len, w.scale, self.ks,
+                             self.vs, partition_tokens=partition_tokens)
         torch.cuda.synchronize()
         self.step_index += 1
         return q, out.cpu().numpy(), tables_p, lens_p

@@ -39,7 +39,7 @@ def test_binding_covers_every_declared_symbol():
 def test_status_strings():
     assert pkv.status_string(0) == "ok"
     assert pkv.status_string(-2) == "out of free blocks"
-    assert pkv.lib().pa_abi_version() == 5
+    assert pkv.lib().pa_abi_version() == 6
 
 
 FAKE = C.c_void_p(0x1000)  # never dereferenced: every call below must fail its host checks
