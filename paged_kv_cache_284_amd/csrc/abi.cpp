@@ -227,13 +227,16 @@ void prefix_parts(int32_t max_seq_len, int32_t* tokens, int32_t* parts) {
 }
 
 // Shared-prefix decode workspace past the balanced schedule's: pstart, ref_p, grp_ref [B]; the
-// prefix states m, l [B][Hq][parts] and o [B][Hq][parts][D].
-int64_t shared_extra_bytes(int32_t B, int32_t Hq, int32_t D, int32_t max_seq_len) {
+// prefix states m, l [B][Hq][parts] and o [B][Hq][parts][D]; the whole-segment states m, l
+// [B][Hq], o [B][Hq][D] and their marks [B][Hkv].
+int64_t shared_extra_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t max_seq_len) {
   int32_t pt = 0, np = 0;
   prefix_parts(max_seq_len, &pt, &np);
   const int64_t rows = static_cast<int64_t>(B) * Hq * np;
+  const int64_t srows = static_cast<int64_t>(B) * Hq;
   return 3 * align256(static_cast<int64_t>(B) * 4) + 2 * align256(rows * 4) +
-         align256(rows * D * 4);
+         align256(rows * D * 4) + 2 * align256(srows * 4) + align256(srows * D * 4) +
+         align256(static_cast<int64_t>(B) * Hkv * 4);
 }
 
 // Whether pa_decode_shared_prefix runs its own schedule (else it is pa_decode).
@@ -396,7 +399,7 @@ size_t pa_decode_shared_prefix_workspace_size(int32_t B, int32_t Hq, int32_t Hkv
   const size_t plain = pa_decode_workspace_size(B, Hq, Hkv, D, max_seq_len, 0);
   if (plain == 0 || B > pa::kMaxBalancedBatch || Hq / Hkv > pa::kMaxBalancedGroup) return plain;
   const int64_t bytes = balanced_bytes(Hq / Hkv, D, pa::kMaxBalancedWorkgroups) +
-                        shared_extra_bytes(B, Hq, D, max_seq_len);
+                        shared_extra_bytes(B, Hq, Hkv, D, max_seq_len);
   return static_cast<size_t>(bytes) > plain ? static_cast<size_t>(bytes) : plain;
 }
 
@@ -458,6 +461,12 @@ int pa_decode_shared_prefix(float* out, const void* q, int32_t q_dtype, const vo
   a.pf_m = reinterpret_cast<float*>(p + 3 * bb);
   a.pf_l = reinterpret_cast<float*>(p + 3 * bb + align256(prow * 4));
   a.pf_o = reinterpret_cast<float*>(p + 3 * bb + 2 * align256(prow * 4));
+  char* q2 = p + 3 * bb + 2 * align256(prow * 4) + align256(prow * D * 4);
+  const int64_t srow = static_cast<int64_t>(B) * Hq;
+  a.sf_m = reinterpret_cast<float*>(q2);
+  a.sf_l = reinterpret_cast<float*>(q2 + align256(srow * 4));
+  a.sf_o = reinterpret_cast<float*>(q2 + 2 * align256(srow * 4));
+  a.sf_mark = reinterpret_cast<int32_t*>(q2 + 2 * align256(srow * 4) + align256(srow * D * 4));
   a.pf_gmax = B / 2 + 1;
   return status_of(pa::launch_decode_shared_prefix(a, kv_dtype, static_cast<hipStream_t>(stream)));
 }

@@ -115,6 +115,9 @@ struct PairRegsI4 {
 // register pressure (measured: bf16 1 and 2 equal, int8 best at 1, int4 best at 2).
 constexpr int kDepthBf16 = 2, kDepthI8 = 1, kDepthI4 = 2;
 
+// Cost of a segment start in the balanced schedule, in pairs (see the span computation).
+constexpr int kSegCost = 3;
+
 // Schedules of decode_mfma_kernel.
 constexpr int kFixed = 0;     // one workgroup per (partition, KV head, sequence)
 constexpr int kBalanced = 1;  // equal spans of block pairs per workgroup
@@ -189,7 +192,8 @@ decode_mfma_kernel(DecodeArgs a) {
   // the wave's span, when a neighbouring wave holds the rest of it).  o holds acc - 128 c (the
   // int8 offset already taken out).
   constexpr int kSlots = kStream ? 2 : 1;
-  extern __shared__ int32_t cum_s[];  // balanced schedule: pair-count prefix sums, B + 1 entries
+  // balanced schedule: pair-count prefix sums cum_s[0..B], then cost prefix sums cc_s[0..B]
+  extern __shared__ int32_t cum_s[];
   __shared__ float m_s[kWaves][kSlots][G];
   __shared__ float l_s[kWaves][kSlots][G];
   __shared__ float o_s[kWaves][kSlots][G][D];
@@ -588,57 +592,9 @@ decode_mfma_kernel(DecodeArgs a) {
         to_lds(lds_slot);
         return;
       }
-      if constexpr (kFold) {
-        if (dest == 0 && ps > 0) {
-          // the whole segment past the prefix: fold the prefix states into this state.  Rows
-          // 4 qg + j (< G) of this lane, elements 16 n + r; each part's states are loaded
-          // for all of them before any is folded.
-          float M[4], den[4], num[4][kTiles];
-          int64_t row[4];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int h = 4 * qg + j;
-            M[j] = __shfl(m_run, h % G, 64);
-            den[j] = __shfl(l_tot, h % G, 64);
-            const float cj = kI8 ? __shfl(c_tot, h % G, 64) : 0.f;
-            row[j] = static_cast<int64_t>(b) * a.Hq + static_cast<int64_t>(g) * G + min(h, G - 1);
-#pragma unroll
-            for (int n = 0; n < kTiles; ++n) num[j][n] = acc[n][j] - kOffset * cj;
-          }
-          const int np = prefix_parts_of(a, ps);
-          for (int k = 0; k < np; ++k) {
-            PrefixState st[4][kTiles];
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-#pragma unroll
-              for (int n = 0; n < kTiles; ++n)
-                if (4 * qg + j < G) st[j][n] = load_prefix(a, row[j], k, 16 * n + r);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              if (4 * qg + j >= G) continue;
-              // the row's (m, l) are the same for every element: fold them once
-              const float m0 = M[j], d0 = den[j];
-#pragma unroll
-              for (int n = 0; n < kTiles; ++n) {
-                float mm = m0, dd = d0;
-                fold_state(mm, num[j][n], dd, st[j][n]);
-                if (n == kTiles - 1) {
-                  M[j] = mm;
-                  den[j] = dd;
-                }
-              }
-            }
-          }
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            if (4 * qg + j >= G) continue;
-#pragma unroll
-            for (int n = 0; n < kTiles; ++n)
-              a.out[row[j] * D + 16 * n + r] = den[j] > 0.f ? num[j][n] / den[j] : 0.f;
-          }
-          return;
-        }
-      }
+      // kSuffix: a whole segment of a sequence with a shared prefix leaves its state for the
+      // merge launch, which folds the prefix states in
+      const bool to_sf = kFold && dest == 0 && ps > 0;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int h = 4 * qg + j;
@@ -651,18 +607,26 @@ decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
           for (int n = 0; n < kTiles; ++n) {
             const float o = lj > 0.f ? (acc[n][j] - kOffset * cj) / lj : 0.f;
-            if (dest == 0) {
+            if (to_sf) {
+              a.sf_o[row * D + 16 * n + r] = o;
+            } else if (dest == 0) {
               a.out[row * D + 16 * n + r] = o;
             } else {
               a.ws_o[slot * D + 16 * n + r] = o;
             }
           }
-          if (dest != 0 && r == 0) {
-            a.ws_m[slot] = mj;
-            a.ws_l[slot] = lj;
+          if (r == 0) {
+            if (to_sf) {
+              a.sf_m[row] = mj;
+              a.sf_l[row] = lj;
+            } else if (dest != 0) {
+              a.ws_m[slot] = mj;
+              a.ws_l[slot] = lj;
+            }
           }
         }
       }
+      if (to_sf && lane == 0) a.sf_mark[static_cast<int64_t>(b) * Hkv + g] = 1;
       return;
     }
 
@@ -863,10 +827,22 @@ decode_mfma_kernel(DecodeArgs a) {
       run_piece(ref, g, P, part * ptp, min(P / kPair, (part + 1) * ptp), false, 3, part, -1, 0);
     }
   } else {
-    // pair counts -> prefix sums cum_s[0..B]
+    // pair counts -> prefix sums cum_s[0..B], and costs -> cc_s[0..B]: the spans are cut so that
+    // every workgroup and wave gets the same cost, a nonempty segment costing kSegCost pairs
+    // more than its pairs (the latency of a segment start: its table entries, q and first tiles
+    // come from memory with nothing in flight behind them).  Pieces and merges work on units.
     const int B = a.B;
-    int carry = 0;
-    if (threadIdx.x == 0) cum_s[0] = 0;
+    int32_t* cc_s = cum_s + B + 1;
+    __shared__ int32_t wave_cost[kWaves];
+    // kSuffix: tokens of b the prefix pass covered
+    auto ps_of = [&](int b) {
+      return prefix_tokens(a, b, min(max(a.seq_lens[b], 0), a.max_seq_len));
+    };
+    int carry = 0, carry_c = 0;
+    if (threadIdx.x == 0) {
+      cum_s[0] = 0;
+      cc_s[0] = 0;
+    }
     for (int base = 0; base < B; base += 64 * kWaves) {
       const int i = base + threadIdx.x;
       const int L = i < B ? min(max(a.seq_lens[i], 0), a.max_seq_len) : 0;
@@ -874,64 +850,75 @@ decode_mfma_kernel(DecodeArgs a) {
       if constexpr (kFold) {
         if (i < B) x -= prefix_tokens(a, i, L) / kPair;  // the pairs past the shared prefix
       }
+      int c = x > 0 ? x + kSegCost : 0;
 #pragma unroll
       for (int o = 1; o < 64; o <<= 1) {
         const int y = __shfl_up(x, o, 64);
-        if (lane >= o) x += y;
+        const int yc = __shfl_up(c, o, 64);
+        if (lane >= o) {
+          x += y;
+          c += yc;
+        }
       }
-      if (lane == 63) wave_tot[w] = x;
+      if (lane == 63) {
+        wave_tot[w] = x;
+        wave_cost[w] = c;
+      }
       __syncthreads();
-      int add = carry;
-      for (int v = 0; v < w; ++v) add += wave_tot[v];
-      if (i < B) cum_s[i + 1] = add + x;
-      int tot = 0;
-      for (int v = 0; v < kWaves; ++v) tot += wave_tot[v];
+      int add = carry, add_c = carry_c;
+      for (int v = 0; v < w; ++v) {
+        add += wave_tot[v];
+        add_c += wave_cost[v];
+      }
+      if (i < B) {
+        cum_s[i + 1] = add + x;
+        cc_s[i + 1] = add_c + c;
+      }
+      int tot = 0, tot_c = 0;
+      for (int v = 0; v < kWaves; ++v) {
+        tot += wave_tot[v];
+        tot_c += wave_cost[v];
+      }
       if (base + 64 * kWaves < B) __syncthreads();  // wave_tot is rewritten next round
       carry += tot;
+      carry_c += tot_c;
     }
     __syncthreads();
     const int64_t T = carry;              // pairs per KV head
     const int64_t U = T * Hkv;            // all units
-    const int NW = a.nw;
-    const int wl = blockIdx.x;
-    // empty sequences produce zeros (kSuffix: sequences whose prefix covers every token get
-    // the prefix pass's states alone)
-    for (int b = wl; b < B; b += NW) {
-      if (cum_s[b + 1] != cum_s[b]) continue;
-      const int ps =
-          kFold ? prefix_tokens(a, b, min(max(a.seq_lens[b], 0), a.max_seq_len)) : 0;
-      const int np = kFold ? prefix_parts_of(a, ps) : 0;
-      constexpr int kBatch = 4;  // elements per thread whose states are requested together
-      for (int i0 = threadIdx.x; i0 < a.Hq * D; i0 += kBatch * 64 * kWaves) {
-        float M[kBatch], num[kBatch], den[kBatch];
-#pragma unroll
-        for (int e = 0; e < kBatch; ++e) {
-          M[e] = -INFINITY;
-          num[e] = 0.f;
-          den[e] = 0.f;
-        }
-        for (int k = 0; k < np; ++k) {
-          PrefixState st[kBatch];
-#pragma unroll
-          for (int e = 0; e < kBatch; ++e) {
-            const int i = i0 + e * 64 * kWaves;
-            if (i < a.Hq * D)
-              st[e] = load_prefix(a, static_cast<int64_t>(b) * a.Hq + i / D, k, i % D);
-          }
-#pragma unroll
-          for (int e = 0; e < kBatch; ++e)
-            if (i0 + e * 64 * kWaves < a.Hq * D) fold_state(M[e], num[e], den[e], st[e]);
-        }
-#pragma unroll
-        for (int e = 0; e < kBatch; ++e) {
-          const int i = i0 + e * 64 * kWaves;
-          if (i < a.Hq * D)
-            a.out[static_cast<int64_t>(b) * a.Hq * D + i] = den[e] > 0.f ? num[e] / den[e] : 0.f;
+    const int64_t CT = carry_c;           // cost per KV head
+    const int64_t CU = CT * Hkv;          // all costs
+    // the first unit at or after cost position x (a segment's start costs come before its first
+    // pair)
+    auto unit_at = [&](int64_t x) -> int64_t {
+      if (x >= CU) return U;
+      const int g = static_cast<int>(x / CT);
+      const int r = static_cast<int>(x - static_cast<int64_t>(g) * CT);
+      int b = B - 1;
+      for (int base = 0; base < B; base += 64) {
+        const int i = base + lane;
+        const uint64_t hit = __ballot(i < B && cc_s[i + 1] > r);
+        if (hit != 0) {
+          b = base + __builtin_ctzll(hit);
+          break;
         }
       }
+      b = __builtin_amdgcn_readfirstlane(b);
+      return static_cast<int64_t>(g) * T + cum_s[b] + max(r - cc_s[b] - kSegCost, 0);
+    };
+    const int NW = a.nw;
+    const int wl = blockIdx.x;
+    // empty sequences produce zeros (kSuffix: a sequence whose prefix covers every token is
+    // written by the merge launch, from the prefix pass's states alone)
+    for (int b = wl; b < B; b += NW) {
+      if (cum_s[b + 1] != cum_s[b]) continue;
+      if (kFold && ps_of(b) > 0) continue;  // only the prefix: the merge launch writes it
+      for (int i = threadIdx.x; i < a.Hq * D; i += 64 * kWaves)
+        a.out[static_cast<int64_t>(b) * a.Hq * D + i] = 0.f;
     }
     // workgroup span [u0, u1); wave w streams its own eighth [v0, v1) of it with no barriers
-    const int64_t u0 = U * wl / NW, u1 = U * (wl + 1) / NW;
+    const int64_t X0 = CU * wl / NW, X1 = CU * (wl + 1) / NW;
+    const int64_t u0 = unit_at(X0), u1 = unit_at(X1);
     // Merge record for the reduce kernel: the segment that starts in this span and runs past
     // its end (at most one), as {b, g, last workgroup holding a piece, slot of the piece here}.
     // An empty span marks its slot 0 as holding nothing.
@@ -948,7 +935,9 @@ decode_mfma_kernel(DecodeArgs a) {
         const int64_t s0 = static_cast<int64_t>(g) * T + cum_s[lo];
         const int64_t s1 = s0 + (cum_s[lo + 1] - cum_s[lo]);
         if (s0 >= u0 && s1 > u1) {
-          const int64_t wb = (s1 * NW + U - 1) / U - 1;  // workgroup holding unit s1 - 1
+          // the workgroup holding unit s1 - 1: the one whose cost span holds its cost
+          const int64_t xl = static_cast<int64_t>(g) * CT + cc_s[lo + 1] - 1;
+          const int64_t wb = ((xl + 1) * NW + CU - 1) / CU - 1;
           rec = int4{lo, g, static_cast<int>(wb), s0 == u0 ? 0 : 1};
         }
       }
@@ -958,16 +947,15 @@ decode_mfma_kernel(DecodeArgs a) {
       a.ws_m[static_cast<int64_t>(wl) * 2 * G + threadIdx.x] = -INFINITY;
       a.ws_l[static_cast<int64_t>(wl) * 2 * G + threadIdx.x] = 0.f;
     }
-    const int64_t v0 = u0 + (u1 - u0) * w / kWaves, v1 = u0 + (u1 - u0) * (w + 1) / kWaves;
+    const int64_t v0 = unit_at(X0 + (X1 - X0) * w / kWaves);
+    const int64_t v1 = unit_at(X0 + (X1 - X0) * (w + 1) / kWaves);
     __shared__ int64_t tag_s[kWaves][2];   // workgroup piece (first unit) held in each LDS slot
     __shared__ int32_t info_s[kWaves][2][4];  // its b, g, destination, partial slot
     if (lane < 2) tag_s[w][lane] = -1;
     int64_t u = v0;
-    while (u < v1) {
-      const int g = static_cast<int>(u / T);
-      const int rem = static_cast<int>(u - static_cast<int64_t>(g) * T);
-      // first sequence b with cum_s[b + 1] > rem: 64 candidates per LDS read and ballot (rem is
-      // below cum_s[B], so a window below B holds it)
+    // first sequence b with cum_s[b + 1] > rem: 64 candidates per LDS read and ballot (rem is
+    // below cum_s[B], so a window below B holds it)
+    auto seq_at = [&](int rem) {
       int b = B - 1;
       for (int base = 0; base < B; base += 64) {
         const int i = base + lane;
@@ -977,7 +965,12 @@ decode_mfma_kernel(DecodeArgs a) {
           break;
         }
       }
-      b = __builtin_amdgcn_readfirstlane(b);
+      return __builtin_amdgcn_readfirstlane(b);
+    };
+    while (u < v1) {
+      const int g = static_cast<int>(u / T);
+      const int rem = static_cast<int>(u - static_cast<int64_t>(g) * T);
+      const int b = seq_at(rem);
       const int n_b = cum_s[b + 1] - cum_s[b];
       const int i0 = rem - cum_s[b];
       const int take = static_cast<int>(min(static_cast<int64_t>(n_b - i0), v1 - u));
@@ -999,7 +992,7 @@ decode_mfma_kernel(DecodeArgs a) {
           info_s[w][slot][3] = static_cast<int32_t>(part);
         }
       }
-      const int ps = kFold ? prefix_tokens(a, b, L) : 0;
+      const int ps = kFold ? ps_of(b) : 0;
       const int off = ps / kPair;  // kSuffix: units count the pairs past the prefix
       run_piece(b, g, L, i0 + off, i0 + off + take, true, dest, part, slot, ps);
       u += take;
@@ -1016,9 +1009,8 @@ decode_mfma_kernel(DecodeArgs a) {
     __shared__ float gl_s[kE][G];
     __shared__ uint32_t mask_s[2];  // used entries, last entries of groups
     // kSuffix: prefix tokens of each entry's sequence when the entry's segment is written out
-    // (dest 0), and the (m, l) of that row's first prefix part
+    // (dest 0)
     __shared__ int32_t eps_s[kFold ? kE : 1];
-    __shared__ float pm_s[kFold ? kE : 1][G], pl_s[kFold ? kE : 1][G];
     const float* mf = &m_s[0][0][0];
     const float* lf = &l_s[0][0][0];
     const float* of = &o_s[0][0][0][0];
@@ -1049,18 +1041,8 @@ decode_mfma_kernel(DecodeArgs a) {
       gm_s[e][h] = M;
       gl_s[e][h] = den;
       if constexpr (kFold) {
-        int ps = 0;
-        if (used && info_s[e / 2][e % 2][2] == 0) {
-          const int b = info_s[e / 2][e % 2][0], g = info_s[e / 2][e % 2][1];
-          ps = prefix_tokens(a, b, min(max(a.seq_lens[b], 0), a.max_seq_len));
-          if (ps > 0) {
-            const int64_t slot =
-                (static_cast<int64_t>(b) * a.Hq + static_cast<int64_t>(g) * G + h) * a.pf_parts;
-            pm_s[e][h] = a.pf_m[slot];
-            pl_s[e][h] = a.pf_l[slot];
-          }
-        }
-        if (h == 0) eps_s[e] = ps;
+        if (h == 0)
+          eps_s[e] = (used && info_s[e / 2][e % 2][2] == 0) ? ps_of(info_s[e / 2][e % 2][0]) : 0;
       }
     }
     if (w == kWaves - 1) {
@@ -1085,21 +1067,6 @@ decode_mfma_kernel(DecodeArgs a) {
         float ov[kE];
 #pragma unroll
         for (int e = 0; e < kE; ++e) ov[e] = of[e * G * D + idx];  // all reads in flight at once
-        // kSuffix: the first prefix part's value of this element for every group written out,
-        // requested together
-        float pov[kFold ? kE : 1];
-        if constexpr (kFold) {
-#pragma unroll
-          for (int e = 0; e < kE; ++e) {
-            pov[e] = 0.f;
-            if (((em >> e) & 1u) && eps_s[e] > 0) {
-              const int b = info_s[e / 2][e % 2][0], g = info_s[e / 2][e % 2][1];
-              const int64_t slot =
-                  (static_cast<int64_t>(b) * a.Hq + static_cast<int64_t>(g) * G + h) * a.pf_parts;
-              pov[e] = a.pf_o[slot * D + d];
-            }
-          }
-        }
         float num = 0.f;
 #pragma unroll
         for (int e = 0; e < kE; ++e) {
@@ -1108,19 +1075,17 @@ decode_mfma_kernel(DecodeArgs a) {
             const int* inf = info_s[e / 2][e % 2];
             const int b = inf[0], g = inf[1], dest = inf[2], part = inf[3];
             const float den = gl_s[e][h];
-            float o = den > 0.f ? num / den : 0.f;
+            const float o = den > 0.f ? num / den : 0.f;
             const int64_t row = static_cast<int64_t>(b) * a.Hq + static_cast<int64_t>(g) * G + h;
-            if (dest == 0) {
-              if constexpr (kFold) {
-                const int ps = eps_s[e];
-                if (ps > 0) {
-                  float M = gm_s[e][h], nn = num, dd = den;
-                  fold_state(M, nn, dd, PrefixState{pm_s[e][h], pl_s[e][h], pov[e]});
-                  const int np = prefix_parts_of(a, ps);
-                  for (int k = 1; k < np; ++k) fold_state(M, nn, dd, load_prefix(a, row, k, d));
-                  o = dd > 0.f ? nn / dd : 0.f;
-                }
+            if (kFold && dest == 0 && eps_s[e] > 0) {
+              // a whole segment past a shared prefix: its state, for the merge launch
+              a.sf_o[row * D + d] = o;
+              if (d == 0) {
+                a.sf_m[row] = gm_s[e][h];
+                a.sf_l[row] = den;
+                if (h == 0) a.sf_mark[static_cast<int64_t>(b) * Hkv + g] = 1;
               }
+            } else if (dest == 0) {
               a.out[row * D + d] = o;
             } else {
               const int64_t slot = static_cast<int64_t>(part) * G + h;
@@ -1144,9 +1109,20 @@ decode_mfma_kernel(DecodeArgs a) {
 // workgroup order, so the result does not depend on timing.  The states of both slots of wa and
 // slot 0 of wa + 1 (every cut segment has those) are requested together with the record, so
 // the common two-piece merge costs one round trip to memory instead of two.
-// kFold: the segment's sequence may have a shared prefix whose states are folded in.
+// kFold (shared-prefix decode): the segment's sequence may have a shared prefix whose states are
+// folded in; workgroups nw .. nw + B Hkv - 1 then write the segments past a prefix that no cut
+// left to a record (fold_segment).
+template <int G, int D>
+__device__ void fold_segment(const DecodeArgs& a, int seg);
+
 template <int G, int D, bool kFold>
 __global__ void __launch_bounds__(256) streamk_reduce_kernel(DecodeArgs a) {
+  if constexpr (kFold) {
+    if (static_cast<int>(blockIdx.x) >= a.nw) {
+      fold_segment<G, D>(a, blockIdx.x - a.nw);
+      return;
+    }
+  }
   const int wa = blockIdx.x;
   const bool has_next = wa + 1 < a.nw;
   const int4 rec = reinterpret_cast<const int4*>(a.ws_merge)[wa];
@@ -1244,6 +1220,63 @@ __global__ void __launch_bounds__(256) streamk_reduce_kernel(DecodeArgs a) {
   }
 }
 
+// Output of segment (b, g) = seg / Hkv, seg % Hkv of a sequence with a shared prefix that the
+// suffix decode did not cut across workgroups: its whole-segment state (sf_*, when it had pairs
+// past the prefix) folded with the prefix parts in order.  Cut segments are written by their
+// merge record; sequences without a prefix by the decode itself.
+template <int G, int D>
+__device__ void fold_segment(const DecodeArgs& a, int seg) {
+  const int b = seg / a.Hkv, g = seg % a.Hkv;
+  const int L = min(max(a.seq_lens[b], 0), a.max_seq_len);
+  const int ps = prefix_tokens(a, b, L);
+  if (ps == 0) return;
+  const int nb = (L + 2 * kBlockSize - 1) / (2 * kBlockSize) - ps / (2 * kBlockSize);
+  const bool whole = a.sf_mark[seg] != 0;
+  if (nb > 0 && !whole) return;  // cut: its merge record writes it
+  constexpr int kPer = (G * D + 255) / 256;
+  float M[kPer], num[kPer], den[kPer];
+  PrefixState st[kPer];
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    M[k] = -INFINITY;
+    num[k] = 0.f;
+    den[k] = 0.f;
+    const int idx = threadIdx.x + 256 * k;
+    if (whole && idx < G * D) {
+      const int64_t row = static_cast<int64_t>(b) * a.Hq + static_cast<int64_t>(g) * G + idx / D;
+      st[k] = PrefixState{a.sf_m[row], a.sf_l[row], a.sf_o[row * D + idx % D]};
+    }
+  }
+  const int np = prefix_parts_of(a, ps);
+  for (int part = -1; part < np; ++part) {
+    // part -1: the suffix state loaded above; then each prefix part's states, requested for
+    // all of this thread's elements before any is folded
+    if (part >= 0) {
+#pragma unroll
+      for (int k = 0; k < kPer; ++k) {
+        const int idx = threadIdx.x + 256 * k;
+        if (idx < G * D) {
+          const int64_t row =
+              static_cast<int64_t>(b) * a.Hq + static_cast<int64_t>(g) * G + idx / D;
+          st[k] = load_prefix(a, row, part, idx % D);
+        }
+      }
+    } else if (!whole) {
+      continue;
+    }
+#pragma unroll
+    for (int k = 0; k < kPer; ++k)
+      if (threadIdx.x + 256 * k < G * D) fold_state(M[k], num[k], den[k], st[k]);
+  }
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const int idx = threadIdx.x + 256 * k;
+    if (idx >= G * D) break;
+    const int64_t row = static_cast<int64_t>(b) * a.Hq + static_cast<int64_t>(g) * G + idx / D;
+    a.out[row * D + idx % D] = den[k] > 0.f ? num[k] / den[k] : 0.f;
+  }
+}
+
 // Shared-prefix plan, one wave per sequence b.  b's group is the run of consecutive sequences
 // around it, inside b's aligned window of 64, whose tables start with the same valid block (a
 // sequence with no tokens has no group).  The reference is the group's longest member (the
@@ -1270,6 +1303,7 @@ __global__ void __launch_bounds__(256) prefix_plan_kernel(DecodeArgs a) {
   }
   const int kb = __shfl(key, pos, 64);
   const uint64_t same = __ballot(i < B && key >= 0 && key == kb);
+  for (int g = lane; g < a.Hkv; g += 64) a.sf_mark[static_cast<int64_t>(b) * a.Hkv + g] = 0;
   auto put = [&](int ps, int gr) {
     if (lane == 0) {
       a.pstart[b] = ps;
@@ -1329,7 +1363,7 @@ hipError_t launch_gd(const DecodeArgs& a, hipStream_t stream) {
     return hipGetLastError();
   }
   constexpr int Gb = G <= kMaxBalancedGroup ? G : kMaxBalancedGroup;  // never launched for G > 8
-  const size_t lds = static_cast<size_t>(a.B + 1) * sizeof(int32_t);
+  const size_t lds = static_cast<size_t>(2 * a.B + 1) * sizeof(int32_t);
   hipLaunchKernelGGL((decode_mfma_kernel<Gb, D, kBalanced, kKV>), dim3(a.nw), dim3(64 * kWaves),
                      lds, stream, a);
   hipError_t e = hipGetLastError();
@@ -1352,12 +1386,14 @@ hipError_t launch_gd_shared(const DecodeArgs& a, hipStream_t stream) {
                        lds_pre, stream, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const size_t lds = static_cast<size_t>(a.B + 1) * sizeof(int32_t);
+    const size_t lds = static_cast<size_t>(2 * a.B + 1) * sizeof(int32_t);
     hipLaunchKernelGGL((decode_mfma_kernel<G, D, kSuffix, kKV>), dim3(a.nw), dim3(64 * kWaves),
                        lds, stream, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((streamk_reduce_kernel<G, D, true>), dim3(a.nw), dim3(256), 0, stream, a);
+    const int64_t grid = static_cast<int64_t>(a.nw) + static_cast<int64_t>(a.B) * a.Hkv;
+    hipLaunchKernelGGL((streamk_reduce_kernel<G, D, true>), dim3(static_cast<uint32_t>(grid)),
+                       dim3(256), 0, stream, a);
     return hipGetLastError();
   }
 }

@@ -42,6 +42,10 @@ struct DecodeArgs {
   int32_t pf_parts;           // prefix-pass parts per output row (ceil(max_seq_len / pf_tokens))
   int32_t pf_tokens;          // tokens per prefix-pass part (multiple of 32)
   int32_t pf_gmax;            // bound on the number of groups (B / 2)
+  float* sf_m;                // [B][Hq] state of a whole segment past a shared prefix: max,
+  float* sf_l;                //         sum of weights,
+  float* sf_o;                // [B][Hq][D] normalised output (folded with the prefix states and
+  int32_t* sf_mark;           // [B][Hkv] written out by the merge launch); 1 where it was written
 };
 
 // Everything one chunked-prefill launch needs.  Pointers are device pointers.
