@@ -100,6 +100,21 @@ class OutOfBlocks(PagedKVError):
     pass
 
 
+_host_only = False
+
+
+def use_host_library(path: str) -> None:
+    """Bind `path`, a build of the host allocator alone (no device entry points, e.g. the
+    sanitized build of paged_kv_cache_284_amd.build.build_host_sanitized), instead of
+    libpagedkv.so.  Only the symbols it exports are bound and torch is not imported; the device
+    calls are then missing (an AttributeError).  Must come before the first lib() call."""
+    global LIB_PATH, _host_only
+    if _lib_handle is not None:
+        raise RuntimeError("the library is already loaded")
+    LIB_PATH = os.path.abspath(path)
+    _host_only = True
+
+
 def lib() -> C.CDLL:
     """The loaded library; raises if it has not been built."""
     global _lib_handle
@@ -107,12 +122,15 @@ def lib() -> C.CDLL:
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is missing: build it with "
                                "`python -m paged_kv_cache_284_amd.build`")
-        try:  # let torch bring in its HIP runtime first, so the process holds exactly one
-            import torch  # noqa: F401
-        except ImportError:
-            pass
+        if not _host_only:
+            try:  # let torch bring in its HIP runtime first, so the process holds exactly one
+                import torch  # noqa: F401
+            except ImportError:
+                pass
         h = C.CDLL(LIB_PATH)
         for name, (res, args) in _SIGNATURES.items():
+            if _host_only and not hasattr(h, name):
+                continue
             f = getattr(h, name)
             f.restype = res
             f.argtypes = args

@@ -1,6 +1,7 @@
 """Build libpagedkv.so in-tree with hipcc for gfx950.
 
     python -m paged_kv_cache_284_amd.build        # or __graft_entry__.build()
+    python -m paged_kv_cache_284_amd.build --host-sanitized OUT.so   # allocator, ASan + UBSan
 
 Every source under csrc/ is compiled (in parallel) into csrc/../_build and linked into
 paged_kv_cache_284_amd/libpagedkv.so.  The build always recompiles.
@@ -82,5 +83,28 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+# The host allocator alone (csrc/alloc.cpp: plain C++17, no HIP) built with AddressSanitizer and
+# UndefinedBehaviorSanitizer by the host compiler.  The result exports the allocator's C ABI and
+# nothing else; a process loads it with the ASan runtime preloaded (see
+# tests/test_host_sanitizers.py) and binds it with paged_kv_cache_284_amd.use_host_library().
+SANITIZE_FLAGS = [
+    "-std=c++17", "-O1", "-g", "-fno-omit-frame-pointer",
+    "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+]
+
+
+def build_host_sanitized(out: str) -> str:
+    cxx = os.environ.get("CXX", "g++")
+    cmd = [cxx, *SANITIZE_FLAGS, "-shared", "-fPIC", f"-I{os.path.join(ROOT, 'include')}",
+           os.path.join(CSRC, "alloc.cpp"), "-o", out]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"sanitized host build failed:\n{' '.join(cmd)}\n{r.stderr}")
+    return out
+
+
 if __name__ == "__main__":
-    build(verbose=True)
+    if len(sys.argv) > 2 and sys.argv[1] == "--host-sanitized":
+        print("built", build_host_sanitized(os.path.abspath(sys.argv[2])))
+    else:
+        build(verbose=True)

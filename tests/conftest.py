@@ -8,3 +8,9 @@ if ROOT not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (runs through the C-ABI library)")
+    # tests/test_host_sanitizers.py runs the allocator tests in a child process against the
+    # sanitized host-only build of the allocator
+    host = os.environ.get("PKV_HOST_LIBRARY")
+    if host:
+        import paged_kv_cache_284_amd as pkv
+        pkv.use_host_library(host)
