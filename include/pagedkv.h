@@ -206,8 +206,8 @@ int pa_free_list(const pa_allocator* a, int32_t* out, int32_t cap, int32_t* n);
 /* Device entry points                                                                */
 /* ================================================================================== */
 
-/* Append one token per sequence ([Serving] "What the KV Cache Is": each decode step appends one
- * more token's K and V; "The Life of a Request").  k_new, v_new: device [B][Hkv][D] in the
+/* Append one token per sequence ([Serving] "What the KV Cache Is": the cache grows by one
+ * token's K and V per decode step; "The Life of a Request").  k_new, v_new: device [B][Hkv][D] in the
  * cache dtype (PA_F32 or PA_BF16; int8 caches are written by pa_kv_append_int8).
  * slot_mapping: device-readable [B] int64, -1 = skip this sequence.  Writes K into k_cache[slot/bs][g]
  * [slot%bs][:] and V into v_cache[slot/bs][g][:][slot%bs]; nothing else is touched.  Two
@@ -301,7 +301,8 @@ size_t pa_decode_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
  *     segments are split into equal spans, one per resident workgroup, whatever the length
  *     mix.  It runs for a PA_BF16 q over PA_BF16, PA_I8 or PA_I4 caches with Hq/Hkv <= 8 and
  *     B <= 8192; everything else (PA_F32 q or cache, Hq/Hkv == 16, larger B) falls back to
- *     fixed 512-token partitions.  Otherwise a multiple of 64 in [64, 8192]: one workgroup per
+ *     fixed partitions of 512 tokens, or of 8192 when B*Hkv >= 1024 (the batch alone then fills
+ *     the device).  Otherwise a multiple of 64 in [64, 8192]: one workgroup per
  *     partition of that many tokens.  Either way a segment cut into several pieces ("split-K")
  *     is merged with the log-sum-exp identity, in a fixed order: repeated calls on the same
  *     inputs give bit-identical outputs.
@@ -344,8 +345,9 @@ size_t pa_decode_shared_prefix_workspace_size(int32_t B, int32_t Hq, int32_t Hkv
                                               int32_t max_seq_len);
 
 /* pa_decode (balanced schedule) that reads a shared prefix once per group instead of once per
- * sequence ([Serving] "Sharing comes for free": sequences that share a prompt point their block
- * tables at the same physical blocks; [Walkthrough] "Step 8": a shared prefix is stored once).
+ * sequence ([Serving] "Sharing comes for free": the tables of sequences with a common prompt
+ * name the same physical blocks for it; [Walkthrough] "Step 8": a shared prefix is stored
+ * once).
  * Same arguments and result as pa_decode with partition_tokens = 0; the sums are taken in a
  * different order, so outputs agree with pa_decode's to rounding, not bit for bit (repeated
  * calls are bit-identical).

@@ -12,9 +12,10 @@ and the sequence's block table maps that logical block to a physical block of th
 attention kernel follows the table to gather K and V.  Paging changes only where the bytes are,
 not the arithmetic ([Walkthrough] "Quick self-check": the FLOPs are unchanged).
 
-Grouped-query attention ([Serving] "What the KV Cache Is": 32 query heads share 8 KV heads):
-query head h reads KV head h // G with G = Hq / Hkv (contiguous groups; the pages do not say
-which query heads share a KV head, contiguous groups are the plain reading).
+Grouped-query attention ([Serving] "What the KV Cache Is": the Llama 3.1 8B example has four
+query heads per KV head): query head h reads KV head h // G with G = Hq / Hkv (contiguous
+groups; the pages do not say which query heads share a KV head, contiguous groups are the plain
+reading).
 
 Physical layout (the pages fix none; this is the layout both sides use):
     K pool [NB][Hkv][bs][D], V pool [NB][Hkv][D][bs], int8 scales [NB][Hkv] (K and V apart).

@@ -1,12 +1,12 @@
 """Writes into the paged KV cache, defined by their effect on the pool.  TEST INFRASTRUCTURE ONLY.
 
-Append ([Serving] "What the KV Cache Is": each decode step appends one more token's K and V;
-"The Life of a Request": the token goes into the request's current block).  The new token of
+Append ([Serving] "What the KV Cache Is": the cache grows by one token's K and V per decode
+step; "The Life of a Request": that token lands in the last block of the request).  The new token of
 sequence b goes to slot s_b = physical_block * bs + offset chosen by the allocator; a slot of -1
 means "no write".  Every other byte of the pool is left as it was.
 
-Copy-on-write ([Serving] "Sharing comes for free": a shared block is copied only when one
-branch needs to write to it; [Walkthrough] "Step 8").  The whole physical block is copied
+Copy-on-write ([Serving] "Sharing comes for free": a block held by several sequences is
+duplicated at the moment one of them must write into it; [Walkthrough] "Step 8").  The whole physical block is copied
 (all bs slots, K, V and, for int8 caches, both scales); the allocator then points the writer's
 table at the copy.
 

@@ -5,8 +5,8 @@ per layer per KV head, each head_dim values of p bytes:
     bytes/token = 2 * layers * kv_heads * head_dim * p.
 Whole cache ([Walkthrough] "Step 5" and "Feynman retelling"): 2 * B * S * L * d_model * p, where
 d_model = n_head * d_head ("Step 3").  The two agree when every query head has its own KV head;
-with grouped-query attention the KV-head form is the right one ([Serving]: with 32 KV heads
-instead of 8 every figure would be four times larger).
+with grouped-query attention the KV-head form is the right one ([Serving] scales its figures by
+the KV-head count: quadrupling the KV heads quadruples every size).
 
 Waste ([Walkthrough] "Step 6", "Step 7", "Step 8", "Quick self-check"): a contiguous
 reservation of max_len tokens wastes max_len - S slots; paging wastes only the empty tail of the

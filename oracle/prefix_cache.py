@@ -8,9 +8,10 @@ What it does ("How LLM Inference Serving Works", section "Prefix Caching and Chu
     leading blocks and only the rest of its prompt needs prefill;
   * a block that no request uses any more is not freed at once: it stays matchable, and cached
     blocks are evicted in least-recently-used order when memory is needed;
-  * an optional per-request salt is mixed into the first block's hash, so requests with
-    different salts never share cached blocks;
-  * when a request finishes its blocks' counts drop and they become cached-but-evictable.
+  * an optional per-request salt enters the hash of a request's first block, which keeps
+    requests with different salts from matching each other's cached blocks;
+  * a finished request releases its blocks: their reference counts fall, and blocks left
+    unreferenced stay cached until evicted.
 
 Readings where the pages leave a step open (the library follows the same ones):
   * hash: 64-bit FNV-1a (offset basis 0xcbf29ce484222325, prime 0x100000001b3) over

@@ -39,14 +39,14 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 namespace pa {
 
-// Long sequences are split so that the grid holds several workgroups per compute unit even for
-// small batches; short ones stay whole (no merge pass).  Depends only on sizes the workspace
-// query also sees.
-int32_t auto_partition(int32_t B, int32_t Hq, int32_t max_seq_len) {
-  (void)B;
-  (void)Hq;
-  (void)max_seq_len;
-  return 512;
+// Partition length of the fixed-partition schedule when the caller passes 0.  A batch whose
+// (sequence, KV head) pairs alone give every compute unit four workgroups is not split below the
+// largest partition (no merge pass for sequences up to 8192 tokens); a smaller batch is split
+// into 512-token partitions, so long sequences spread over the device.  Depends only on sizes the
+// workspace query also sees.
+int32_t auto_partition(int32_t B, int32_t Hkv) {
+  constexpr int64_t kFillWorkgroups = 4 * 256;
+  return static_cast<int64_t>(B) * Hkv >= kFillWorkgroups ? 8192 : 512;
 }
 
 }  // namespace pa
@@ -257,7 +257,7 @@ size_t pa_decode_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
       partition_tokens < 0)
     return 0;
   const int32_t P =
-      partition_tokens ? partition_tokens : pa::auto_partition(B, Hq, max_seq_len);
+      partition_tokens ? partition_tokens : pa::auto_partition(B, Hkv);
   const int64_t np = (static_cast<int64_t>(max_seq_len) + P - 1) / P;
   int64_t bytes = fixed_bytes(B, Hq, D, np);
   if (partition_tokens == 0 && B <= pa::kMaxBalancedBatch && Hq / Hkv <= pa::kMaxBalancedGroup) {
@@ -326,7 +326,7 @@ int decode_run(float* out, const void* q, int32_t q_dtype, const void* k_cache,
   a.Hkv = Hkv;
   a.D = D;
   a.NB = NB;
-  a.partition = partition_tokens ? partition_tokens : pa::auto_partition(B, Hq, max_seq_len);
+  a.partition = partition_tokens ? partition_tokens : pa::auto_partition(B, Hkv);
   const int64_t np = (static_cast<int64_t>(max_seq_len) + a.partition - 1) / a.partition;
   a.np_max = static_cast<int32_t>(np < 1 ? 1 : np);
   a.scale_log2 = scale * kLog2e;

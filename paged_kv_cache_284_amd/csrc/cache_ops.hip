@@ -1,9 +1,9 @@
 // Writes into the paged cache: token append, copy-on-write block copies, block-table patches.
 //
-// Append ("How LLM Inference Serving Works", "What the KV Cache Is, and How Big It Gets": every
-// decode step appends one token's K and V; "The Life of a Request": into the request's current
-// block).  Copy-on-write ("Sharing comes for free": a shared block is copied only when a branch
-// writes to it).  All three are bit copies; they move a few KiB to a few MiB per step and are
+// Append ("How LLM Inference Serving Works", "What the KV Cache Is, and How Big It Gets": the
+// cache grows by one token's K and V per decode step; "The Life of a Request": that token lands
+// in the request's last block).  Copy-on-write ("Sharing comes for free": a block held by
+// several sequences is duplicated when one of them writes into it).  All three are bit copies; they move a few KiB to a few MiB per step and are
 // bound by launch latency, so they favour simple, fully coalesced addressing over occupancy
 // tuning.
 #include <type_traits>

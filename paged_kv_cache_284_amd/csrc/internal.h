@@ -95,8 +95,8 @@ int decode_run(float* out, const void* q, int32_t q_dtype, const void* k_cache,
                float scale, int32_t partition_tokens, void* workspace, size_t workspace_bytes,
                bool exact_size, void* stream);
 
-// Partition length the library picks when the caller passes 0.
-int32_t auto_partition(int32_t B, int32_t Hq, int32_t max_seq_len);
+// Partition length the fixed-partition schedule uses when the caller passes 0.
+int32_t auto_partition(int32_t B, int32_t Hkv);
 
 // table_index / tables may be NULL; otherwise the launch also patches the block tables.
 // lens_in / lens_out may be NULL; otherwise the launch also copies the sequence lengths.

@@ -81,6 +81,24 @@ def test_edge_lengths(kv, G, D, partition):
     assert lens[0] == 0 and np.array_equal(out[0], np.zeros_like(out[0]))
 
 
+@pytest.mark.parametrize("kv,G", [("f32", 2), ("bf16", 16)])
+def test_fixed_partitions_large_batch(kv, G):
+    """A batch with B * Hkv >= 1024 on the fixed-partition schedule (fp32, or 16 query heads
+    per KV head): the automatic partition is then 8192 tokens, so sequences are not split."""
+    rng = np.random.default_rng(7 + G)
+    lens = [int(x) for x in rng.integers(0, 700, 136)]
+    w = _ragged_case(kv, G, 64, lens=lens)
+    w.Hkv, w.Hq = 8, 8 * G
+    w.cid = 70 + G
+    say(f"fixed partitions large batch kv={kv} G={G} B={w.B}")
+    case = Case(w)
+    q, out, tables, lens = case.step(partition_tokens=0)
+    heads = sample_heads(w, lens, 64, seed=G)
+    ref = case.oracle(q, tables, lens, heads=heads)
+    assert np.all(np.isfinite(out))
+    assert max_err(out, ref, heads) <= TOL[kv]
+
+
 def _empty_pools(kv, NB, Hkv, D, bs=16):
     """Zeroed pools (and unit scales for the quantised kinds) in the library's layouts."""
     if kv == "i4":
