@@ -386,6 +386,8 @@ int pa_decode_shared_prefix(float* out, const void* q, int32_t q_dtype, const vo
  *   PA_ERR_UNSUPPORTED); for PA_I8 / PA_I4 also k_scale / v_scale, device [NB][Hkv] fp32
  *   (element = code * scale), else ignored.  Quantised caches run the products in fp16: q and
  *   P * v_scale are rounded to fp16, and v_scale must stay below 2^14 (|V| below 2^21 for int8).
+ *   A PA_BF16 cache runs P . V in fp16 too: P rounded to fp16, V converted exactly, so |V| must
+ *   stay below 65504 (beyond, the result is not finite); the scores stay in bf16.
  *   out: device [T][Hq][D] fp32; cu_q: device [B + 1] int32, non-decreasing, cu_q[0] = 0,
  *   cu_q[B] = T; seq_lens: device [B] int32; max_seq_len bounds every seq_lens[b];
  *   Hq/Hkv in {1, 2, 4, 8, 16}, D in {64, 128}, bs == 16.  Needs no workspace.  Compute-bound:

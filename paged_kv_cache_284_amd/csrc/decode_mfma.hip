@@ -55,6 +55,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 8;
 constexpr int kPair = 2 * kBlockSize;  // tokens per wave iteration
@@ -178,9 +179,8 @@ decode_mfma_kernel(DecodeArgs a) {
   static_assert(!kPre || G == 16, "the prefix pass fills all 16 columns of its tiles");
   constexpr bool kI4 = kKV == kKvI4;
   constexpr bool kI8 = kKV == kKvI8 || kI4;  // a quantised cache (scales, offset codes)
-  // code offset removed from the sums; int4 carries it inside its weighted sums (two offsets,
-  // one per half of each 8-element operand group)
-  constexpr float kOffset = kI4 ? 1.f : kCodeOffset;
+  // quantised caches: int8 score tiles of 64 dims per v_mfma_i32_16x16x64_i8
+  constexpr int kK8 = D / 64;
   using Regs = std::conditional_t<kI4, PairRegsI4<D>,
                                   std::conditional_t<kI8, PairRegsI8<D>, PairRegs<D>>>;
   constexpr int kDepth = kI4 ? kDepthI4 : (kI8 ? kDepthI8 : kDepthBf16);  // pairs in flight
@@ -234,13 +234,17 @@ decode_mfma_kernel(DecodeArgs a) {
     const int32_t* __restrict__ table = a.tables + static_cast<int64_t>(b) * a.max_blocks;
     const int end = L;
 
-    // q^T operand, head (r % G).  bf16 cache: step s covers dims 32 s + 8 qg .. +8.  int8
-    // cache: step s covers dims 16 (qg + 4 (s / 2)) + 8 (s % 2) .. +8, matching the 16-byte K
-    // loads (16 dims of a row serve two steps).
-    u32x4 qv[kSteps];
-    // quantised caches: sum of this head's q operands, reduced over the four lane groups
-    // (int4: weighted by each element's code offset)
-    float qsum = 0.f;
+    // q^T operand, head (r % G).  bf16 cache: step s covers dims 32 s + 8 qg .. +8.
+    // Quantised caches score with exact integer products (v_mfma_i32_16x16x64_i8): q enters as
+    // two int8 parts on the head's absmax scale sq = max|q| / 127, q ~ sq (hi + lo / 128)
+    // (within sq / 256, about 15 bits of the largest element), the codes as they are (int4:
+    // nibbles unpacked to bytes c + 8).  Lane group qg holds dims of tile t in the order the K
+    // operand has them: int8 16 qg + 64 t + m, int4 (D / 4) qg + 16 t + m, m < 16; both read
+    // as the 8-dim groups s = 2 t, 2 t + 1 of the loads below.
+    u32x4 qv[kI8 ? 1 : kSteps];
+    i32x4 qh[kI8 ? kK8 : 1], ql[kI8 ? kK8 : 1];
+    float qscale = 0.f;  // quantised: sq / 128, the weight of one unit of hi * 128 + lo
+    int q8 = 0;          // int4: 8 * sum_d (128 hi + lo), the nibbles' +8 times q
     int lim_tok = 0;  // kPrefix: tokens of this lane's column (its pairs from lim_tok on are masked)
     {
       int64_t qrow = static_cast<int64_t>(b) * a.Hq + static_cast<int64_t>(g) * G + r % G;
@@ -250,38 +254,59 @@ decode_mfma_kernel(DecodeArgs a) {
         lim_tok = collim_s[r];
       }
       const uint16_t* q = static_cast<const uint16_t*>(a.q) + qrow * D;
+      if constexpr (kI8) {
+        f32x8 f[kSteps];
+        float amax = 0.f;
 #pragma unroll
-      for (int s = 0; s < kSteps; ++s) {
-        if constexpr (kI8) {
-          // quantised cache: the score MFMA runs in fp16 (bf16 -> fp16 is exact in fp16's
-          // normal range), next to fp16 codes.  int4: step s covers dims
-          // 8 kSteps qg + 8 s .. +8, the 4-byte group a lane loads for that step.
-          const u32x4 raw = kI4 ? load16(q + 8 * kSteps * qg + 8 * s)
+        for (int s = 0; s < kSteps; ++s) {
+          const u32x4 raw = kI4 ? load16(q + (D / 4) * qg + 8 * s)
                                 : load16(q + 16 * (qg + 4 * (s / 2)) + 8 * (s % 2));
-          f32x8 f;
 #pragma unroll
           for (int c = 0; c < 4; ++c) {
-            f[2 * c] = __uint_as_float(raw[c] << 16);
-            f[2 * c + 1] = __uint_as_float(raw[c] & 0xffff0000u);
+            f[s][2 * c] = __uint_as_float(raw[c] << 16);
+            f[s][2 * c + 1] = __uint_as_float(raw[c] & 0xffff0000u);
           }
-          f16x8 h = __builtin_convertvector(f, f16x8);
-          if constexpr (kI4) {
-            // elements 4..7 meet codes expanded at 16 times their value
 #pragma unroll
-            for (int e = 4; e < 8; ++e) h[e] *= static_cast<_Float16>(0.0625f);
-          }
-          qv[s] = __builtin_bit_cast(u32x4, h);
-          const f32x8 back = __builtin_convertvector(h, f32x8);
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            qsum += kI4 ? back[e] * (e < 4 ? kNibbleOffset : kNibbleOffsetHi16) : back[e];
-        } else {
-          qv[s] = load16(q + 32 * s + 8 * qg);
+          for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(f[s][e]));
         }
-      }
-      if constexpr (kI8) {
-        qsum += __shfl_xor(qsum, 16, 64);
-        qsum += __shfl_xor(qsum, 32, 64);
+        amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
+        amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+        const float sq = amax > 0.f ? amax / 127.f : 1.f;
+        const float inv = amax > 0.f ? 127.f / amax : 1.f;
+        qscale = sq * (1.f / 128.f);
+        int qtot = 0;
+#pragma unroll
+        for (int t = 0; t < kK8; ++t) {
+          uint32_t hw[4], lw[4];
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {  // 4 dims per word: group s = 2 t + c / 2
+            uint32_t hb = 0, lb = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float x = f[2 * t + c / 2][4 * (c % 2) + e] * inv;
+              const float hi = __builtin_rintf(x);
+              const float lo = __builtin_rintf((x - hi) * 128.f);
+              const int hv = static_cast<int>(hi), lv = static_cast<int>(lo);
+              qtot += 128 * hv + lv;
+              hb |= (static_cast<uint32_t>(hv) & 0xffu) << (8 * e);
+              lb |= (static_cast<uint32_t>(lv) & 0xffu) << (8 * e);
+            }
+            hw[c] = hb;
+            lw[c] = lb;
+          }
+          qh[t] = i32x4{static_cast<int32_t>(hw[0]), static_cast<int32_t>(hw[1]),
+                        static_cast<int32_t>(hw[2]), static_cast<int32_t>(hw[3])};
+          ql[t] = i32x4{static_cast<int32_t>(lw[0]), static_cast<int32_t>(lw[1]),
+                        static_cast<int32_t>(lw[2]), static_cast<int32_t>(lw[3])};
+        }
+        if constexpr (kI4) {
+          qtot += __shfl_xor(qtot, 16, 64);
+          qtot += __shfl_xor(qtot, 32, 64);
+          q8 = 8 * qtot;
+        }
+      } else {
+#pragma unroll
+        for (int s = 0; s < kSteps; ++s) qv[s] = load16(q + 32 * s + 8 * qg);
       }
     }
 
@@ -360,34 +385,46 @@ decode_mfma_kernel(DecodeArgs a) {
 
     float m_run = -INFINITY;  // running max (log2 domain) of head r % G
     float l_run = 0.f;        // lane-partial running sum over this lane's tokens
-    float c_run = 0.f;        // int8: lane-partial running sum of the (scaled) P operand
     f32x4 acc[kTiles];
 #pragma unroll
     for (int n = 0; n < kTiles; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // quantised caches: the codes enter P.V as offset + code (offset 1152 for int8; 1032 for
+    // int4 elements 0..3 and 1152 for 4..7, whose codes come at 16 times their value); accc
+    // collects sum_t P_t offset_t with one more MFMA against a tile of the offsets, rounded and
+    // summed exactly as the value tiles' offset parts, and is taken out at the end
+    f32x4 accc = {0.f, 0.f, 0.f, 0.f};
+    f16x8 offs;
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      offs[e] = static_cast<_Float16>(kI4 && e < 4 ? kNibbleOffset : kCodeOffset);
 
     auto compute_pair = [&](int i, Regs& R) {
       const int tok0 = i * kPair;
       f32x4 s1 = {0.f, 0.f, 0.f, 0.f}, s2 = {0.f, 0.f, 0.f, 0.f};
-      if constexpr (kI4) {
+      i32x4 h1 = {0, 0, 0, 0}, l1 = {0, 0, 0, 0}, h2 = {0, 0, 0, 0}, l2 = {0, 0, 0, 0};
+      if constexpr (kI8) {
 #pragma unroll
-        for (int c = 0; c < kSteps; ++c) {
-          const f16x8 qc = __builtin_bit_cast(f16x8, qv[c]);
-          s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(nibbles_to_f16_hi16(R.k1[c]), qc, s1, 0, 0, 0);
-          s2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(nibbles_to_f16_hi16(R.k2[c]), qc, s2, 0, 0, 0);
-        }
-      } else if constexpr (kI8) {
+        for (int t = 0; t < kK8; ++t) {
+          i32x4 a1, a2;
+          if constexpr (kI4) {
+            // nibble bytes c + 8 of dims (D / 4) qg + 16 t + m: words 2 t, 2 t + 1, each split
+            // into its low nibbles (dims +0..3) and high nibbles (+4..7)
 #pragma unroll
-        for (int c = 0; c < kSteps / 2; ++c) {
-          const f16x8 q0 = __builtin_bit_cast(f16x8, qv[2 * c]);
-          const f16x8 q1 = __builtin_bit_cast(f16x8, qv[2 * c + 1]);
-          s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes_to_f16(R.k1[c][0], R.k1[c][1]), q0,
-                                                       s1, 0, 0, 0);
-          s2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes_to_f16(R.k2[c][0], R.k2[c][1]), q0,
-                                                       s2, 0, 0, 0);
-          s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes_to_f16(R.k1[c][2], R.k1[c][3]), q1,
-                                                       s1, 0, 0, 0);
-          s2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes_to_f16(R.k2[c][2], R.k2[c][3]), q1,
-                                                       s2, 0, 0, 0);
+            for (int c = 0; c < 2; ++c) {
+              const uint32_t x1 = R.k1[2 * t + c], x2 = R.k2[2 * t + c];
+              a1[2 * c] = static_cast<int32_t>(x1 & 0x0f0f0f0fu);
+              a1[2 * c + 1] = static_cast<int32_t>((x1 >> 4) & 0x0f0f0f0fu);
+              a2[2 * c] = static_cast<int32_t>(x2 & 0x0f0f0f0fu);
+              a2[2 * c + 1] = static_cast<int32_t>((x2 >> 4) & 0x0f0f0f0fu);
+            }
+          } else {
+            a1 = __builtin_bit_cast(i32x4, R.k1[t]);
+            a2 = __builtin_bit_cast(i32x4, R.k2[t]);
+          }
+          h1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, qh[t], h1, 0, 0, 0);
+          l1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, ql[t], l1, 0, 0, 0);
+          h2 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a2, qh[t], h2, 0, 0, 0);
+          l2 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a2, ql[t], l2, 0, 0, 0);
         }
       } else {
 #pragma unroll
@@ -402,13 +439,14 @@ decode_mfma_kernel(DecodeArgs a) {
       const bool tail = (tok0 + kPair > end) || R.blk_b < 0 || R.blk_a < 0;
       float sc[8];
       if constexpr (kI8) {
-        // score = k_scale * sum_d q_d c_d = k_scale * (sum_d q_d (1152 + c_d) - 1152 sum_d q_d)
-        const float f = (vblk_sel ? R.ks_b : R.ks_a) * a.scale_log2;
-        const float c0 = -kOffset * qsum * f;
+        // score = k_scale * sq / 128 * sum_d c_d (128 hi_d + lo_d), the sum exact in int32
+        // (int4: the bytes hold c + 8, whose 8 (128 hi + lo) summed over d is q8)
+        const float f = (vblk_sel ? R.ks_b : R.ks_a) * a.scale_log2 * qscale;
+        const float c0 = kI4 ? -static_cast<float>(q8) * f : 0.f;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          sc[e] = fmaf(s1[e], f, c0);
-          sc[4 + e] = fmaf(s2[e], f, c0);
+          sc[e] = fmaf(static_cast<float>((h1[e] << 7) + l1[e]), f, c0);
+          sc[4 + e] = fmaf(static_cast<float>((h2[e] << 7) + l2[e]), f, c0);
         }
       } else {
 #pragma unroll
@@ -470,21 +508,14 @@ decode_mfma_kernel(DecodeArgs a) {
       l_run = l_run * alpha + psum;
       f16x8 p16;
       if constexpr (kI8) {
-        // fold this block's V scale into P and round it to the fp16 operand once; the code
-        // offset is taken out with the sum of exactly those operands, so it cancels exactly
-        // (a sum of unrounded P would leave the rounding error times the offset)
+        // fold this block's V scale into P and round it to the fp16 operand once; the offset
+        // tile meets exactly those operands, so the offsets cancel
         const float vs = vblk_sel ? R.vs_b : R.vs_a;
         // int4: elements 4..7 meet codes expanded at 16 times their value
         const float vs_hi = kI4 ? vs * 0.0625f : vs;
 #pragma unroll
         for (int e = 0; e < 8; ++e) pv[e] *= e < 4 ? vs : vs_hi;
         p16 = __builtin_convertvector(pv, f16x8);
-        const f32x8 pr = __builtin_convertvector(p16, f32x8);
-        float csum = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          csum += kI4 ? pr[e] * (e < 4 ? kNibbleOffset : kNibbleOffsetHi16) : pr[e];
-        c_run = c_run * alpha + csum;
       }
       // rescale the accumulators: rows 4 qg + j hold head (4 qg + j) % G
       if (rescale) {
@@ -498,9 +529,11 @@ decode_mfma_kernel(DecodeArgs a) {
           }
 #pragma unroll
           for (int n = 0; n < kTiles; ++n) acc[n][j] *= aj;
+          if constexpr (kI8) accc[j] *= aj;
         }
       }
       if constexpr (kI8) {
+        accc = __builtin_amdgcn_mfma_f32_16x16x32_f16(p16, offs, accc, 0, 0, 0);
         // P as one fp16 operand (11-bit significand: its rounding stays far inside the int8 /
         // int4 tolerance) next to fp16 codes
 #pragma unroll
@@ -563,14 +596,9 @@ decode_mfma_kernel(DecodeArgs a) {
       }
     }
 
-    // reduce the lane partials over the four lane groups: l_tot, c_tot belong to head r % G
+    // reduce the lane partials over the four lane groups: l_tot belongs to head r % G
     float l_tot = l_run + __shfl_xor(l_run, 16, 64);
     l_tot += __shfl_xor(l_tot, 32, 64);
-    float c_tot = 0.f;
-    if constexpr (kI8) {
-      c_tot = c_run + __shfl_xor(c_run, 16, 64);
-      c_tot += __shfl_xor(c_tot, 32, 64);
-    }
     // accumulator rows 4 qg + j hold head (4 qg + j) % G; the copy with 4 qg + j < G is written
     auto to_lds = [&](int slot) {
       if (qg == 0 && r < G) {
@@ -580,10 +608,10 @@ decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int h = 4 * qg + j;
-        const float cj = kI8 ? __shfl(c_tot, h % G, 64) : 0.f;
+        const float cj = kI8 ? accc[j] : 0.f;  // row 4 qg + j's offset sum
         if (h < G) {
 #pragma unroll
-          for (int n = 0; n < kTiles; ++n) o_s[w][slot][h][16 * n + r] = acc[n][j] - kOffset * cj;
+          for (int n = 0; n < kTiles; ++n) o_s[w][slot][h][16 * n + r] = acc[n][j] - cj;
         }
       }
     };
@@ -600,13 +628,13 @@ decode_mfma_kernel(DecodeArgs a) {
         const int h = 4 * qg + j;
         const float lj = __shfl(l_tot, h % G, 64);
         const float mj = __shfl(m_run, h % G, 64);
-        const float cj = kI8 ? __shfl(c_tot, h % G, 64) : 0.f;
+        const float cj = kI8 ? accc[j] : 0.f;
         if (h < G) {
           const int64_t row = static_cast<int64_t>(b) * a.Hq + static_cast<int64_t>(g) * G + h;
           const int64_t slot = part * G + h;
 #pragma unroll
           for (int n = 0; n < kTiles; ++n) {
-            const float o = lj > 0.f ? (acc[n][j] - kOffset * cj) / lj : 0.f;
+            const float o = lj > 0.f ? (acc[n][j] - cj) / lj : 0.f;
             if (to_sf) {
               a.sf_o[row * D + 16 * n + r] = o;
             } else if (dest == 0) {

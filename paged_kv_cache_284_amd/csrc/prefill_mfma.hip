@@ -65,8 +65,8 @@ __device__ __forceinline__ float sum_across_groups(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-constexpr float kOverP = 2.305843e18f;    // 2^61: a pair's P sum above this asks for a rerun
-constexpr float kOverPQ = 16384.f;         // 2^14: the same bound on P x V scale (fp16 operand)
+constexpr float kOverPQ = 16384.f;         // 2^14: a pair's fp16 P sum (times the V scale) above
+                                           // this asks for a rerun against the exact maximum
 constexpr float kUnderL = 8.6736174e-19f;  // 2^-60: a final l below this asks for a rerun
 
 struct Pair {
@@ -540,6 +540,21 @@ prefill_mfma_kernel(PrefillArgs a) {
       }
       if (is_edge(tok0, cur)) mask_scores(tok0, my_blk);
       const float vsc = kQ ? (vsel ? vo.vs_b : vo.vs_a) : 1.f;
+      // bf16 cache: V tiles as fp16 operands, converted once for all heads of the wave (exact
+      // for |V| in fp16's normal range), so P . V takes one fp16 MFMA per tile
+      f16x8 vh[kKV == kKvBf16 ? kTiles : 1];
+      if constexpr (kKV == kKvBf16) {
+#pragma unroll
+        for (int t = 0; t < kTiles; ++t) {
+          f32x8 vf;
+#pragma unroll
+          for (int cc = 0; cc < 4; ++cc) {
+            vf[2 * cc] = __uint_as_float(vo.v[t][cc] << 16);
+            vf[2 * cc + 1] = __uint_as_float(vo.v[t][cc] & 0xffff0000u);
+          }
+          vh[t] = __builtin_convertvector(vf, f16x8);
+        }
+      }
 #pragma unroll
       for (int hh = 0; hh < kH; ++hh) {
         f32x8 pv;
@@ -553,24 +568,13 @@ prefill_mfma_kernel(PrefillArgs a) {
         // O^T += V^T . P^T: V rows are dims, P^T columns are this lane's query, so the
         // accumulator column of a lane is its own query
         if constexpr (kKV == kKvBf16) {
-          over = over || !(psum <= kOverP);
-          // P enters as a bf16 pair hi + lo, which carries it to about 16 bits
-          const bf16x8 p_hi = __builtin_convertvector(pv, bf16x8);
-          const u32x4 hb = __builtin_bit_cast(u32x4, p_hi);
-          f32x8 rest;
+          // P as one fp16 operand (11-bit significand); its range bound asks for the exact-
+          // maximum pass like the quantised path's
+          over = over || !(psum <= kOverPQ);
+          const f16x8 p16 = __builtin_convertvector(pv, f16x8);
 #pragma unroll
-          for (int cc = 0; cc < 4; ++cc) {
-            rest[2 * cc] = pv[2 * cc] - __uint_as_float(hb[cc] << 16);
-            rest[2 * cc + 1] = pv[2 * cc + 1] - __uint_as_float(hb[cc] & 0xffff0000u);
-          }
-          const bf16x8 p_lo = __builtin_convertvector(rest, bf16x8);
-#pragma unroll
-          for (int t = 0; t < kTiles; ++t) {
-            acc[hh][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vo.v[t]), p_hi,
-                                                                  acc[hh][t], 0, 0, 0);
-            acc[hh][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vo.v[t]), p_lo,
-                                                                  acc[hh][t], 0, 0, 0);
-          }
+          for (int t = 0; t < kTiles; ++t)
+            acc[hh][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vh[t], p16, acc[hh][t], 0, 0, 0);
         } else {
           over = over || !(psum * vsc <= kOverPQ);
           // P times the block's V scale as one fp16 operand next to the fp16 codes; the code
