@@ -33,11 +33,17 @@
 // exactly the 8 tokens it must supply as its P operand (tokens 8*(l/16)..+7 of the pair for head
 // (l%16)%G): softmax and P.V need no cross-lane transposition.  P is fed as a bf16 hi/lo pair
 // (p = hi + lo to ~16 bits) so the rounding of P stays far below the bf16 tolerance.
-// Quantised caches run v_mfma_f32_16x16x32_f16 instead: codes expand to fp16 values offset + c
-// (a byte permute for int8, a nibble mask and permute for int4), q enters once as fp16, P as one
-// fp16 operand, and the offset is taken out of both sums using the same rounded q and P values
-// the matrix cores saw, so it cancels exactly.  Loads of up to kDepth pairs are in flight per
-// wave.
+// Quantised caches score with exact integer products on v_mfma_i32_16x16x64_i8 (the codes as
+// they are, q as two int8 parts on its absmax scale) and run P.V on v_mfma_f32_16x16x32_f16:
+// codes expand to fp16 values offset + c (a byte permute for int8, a nibble mask and permute for
+// int4), P is one fp16 operand, and the offset part of P.V comes out through one more MFMA of
+// the same rounded P against a tile of the offsets, so it cancels exactly.  Loads of up to
+// kDepth pairs are in flight per wave.
+//
+// Shared prefixes (pa_decode_shared_prefix) run the same pair loop in two more modes: a prefix
+// pass whose 16 MFMA columns hold the query heads of up to 16/G members of a group, reading the
+// blocks they share once, and a suffix pass, the balanced schedule over each sequence's tokens
+// past its prefix; the merge launch folds the prefix states into the rows.
 #include <cmath>
 #include <type_traits>
 
@@ -324,12 +330,12 @@ decode_mfma_kernel(DecodeArgs a) {
       const int64_t tile_a = ta * (kBlockSize * D);
       const int64_t tile_b = tb * (kBlockSize * D);
       if constexpr (kI8) {
-        // a masked block's scale is never read as a number: its tokens get weight 0, and
-        // 0 * scale must stay 0 whatever the unused entry holds
-        R.ks_a = ba >= 0 ? uniform_load(a.k_scale, ta) : 0.f;
-        R.ks_b = bb >= 0 ? uniform_load(a.k_scale, tb) : 0.f;
-        R.vs_a = ba >= 0 ? uniform_load(a.v_scale, ta) : 0.f;
-        R.vs_b = bb >= 0 ? uniform_load(a.v_scale, tb) : 0.f;
+        // a masked block reads block 0's entries in its place: its scores become -inf whatever
+        // the K scale gives, and its V scale is zeroed where it is used
+        R.ks_a = uniform_load(a.k_scale, ta);
+        R.ks_b = uniform_load(a.k_scale, tb);
+        R.vs_a = uniform_load(a.v_scale, ta);
+        R.vs_b = uniform_load(a.v_scale, tb);
       }
       const std::conditional_t<kPre, CachedLoad, StreamLoad> ld;
       if constexpr (kI4) {
@@ -510,7 +516,10 @@ decode_mfma_kernel(DecodeArgs a) {
       if constexpr (kI8) {
         // fold this block's V scale into P and round it to the fp16 operand once; the offset
         // tile meets exactly those operands, so the offsets cancel
-        const float vs = vblk_sel ? R.vs_b : R.vs_a;
+        // (a masked block's scale is never read as a number: its P are 0, and 0 * scale must
+        // stay 0 whatever the unused entry holds; chosen here, at the use, so that the wave
+        // does not wait for the look-ahead's scalar loads a pair early)
+        const float vs = my_blk >= 0 ? (vblk_sel ? R.vs_b : R.vs_a) : 0.f;
         // int4: elements 4..7 meet codes expanded at 16 times their value
         const float vs_hi = kI4 ? vs * 0.0625f : vs;
 #pragma unroll

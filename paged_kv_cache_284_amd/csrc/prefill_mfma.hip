@@ -343,9 +343,10 @@ prefill_mfma_kernel(PrefillArgs a) {
         ko.k2[s] = ld16(p2 + 32 * s);
       }
     } else {
-      // a missing block's scale is never read as a number (0 * scale stays 0)
-      ko.ks_a = bl.a >= 0 ? uniform_load(a.k_scale, ia) : 0.f;
-      ko.ks_b = bl.b >= 0 ? uniform_load(a.k_scale, ib) : 0.f;
+      // a missing block reads block 0's scale entry in its place; its scores are replaced by
+      // -inf whatever that scale gives (mask_scores)
+      ko.ks_a = uniform_load(a.k_scale, ia);
+      ko.ks_b = uniform_load(a.k_scale, ib);
       const uint8_t* kc = static_cast<const uint8_t*>(a.k);
       if constexpr (kKV == kKvI8) {
         const uint8_t* p1 = kc + (tok1 < 16 ? ia : ib) * (kBlockSize * D) + (tok1 % 16) * D + 16 * qg;
@@ -376,8 +377,9 @@ prefill_mfma_kernel(PrefillArgs a) {
 #pragma unroll
       for (int t = 0; t < kTiles; ++t) vo.v[t] = ld16(pv + 16 * t * kBlockSize);
     } else {
-      vo.vs_a = bl.a >= 0 ? uniform_load(a.v_scale, tile_idx(bl.a)) : 0.f;
-      vo.vs_b = bl.b >= 0 ? uniform_load(a.v_scale, tile_idx(bl.b)) : 0.f;
+      // block 0's entry for a missing block; zeroed where it is used
+      vo.vs_a = uniform_load(a.v_scale, tile_idx(bl.a));
+      vo.vs_b = uniform_load(a.v_scale, tile_idx(bl.b));
       const uint8_t* vc = static_cast<const uint8_t*>(a.v);
       if constexpr (kKV == kKvI8) {
         const uint8_t* pv = vc + it * (kBlockSize * D) + r * kBlockSize + vtok;
@@ -539,7 +541,11 @@ prefill_mfma_kernel(PrefillArgs a) {
         }
       }
       if (is_edge(tok0, cur)) mask_scores(tok0, my_blk);
-      const float vsc = kQ ? (vsel ? vo.vs_b : vo.vs_a) : 1.f;
+      // a missing block's V scale is never read as a number (its P are 0, and 0 * scale must
+      // stay 0 whatever the unused entry holds).  The choice is made here, at the use, where
+      // the value is waited for anyway: made where the scales are loaded, it would wait for
+      // those loads (and every scalar load in flight) one pair early.
+      const float vsc = kQ ? (my_blk >= 0 ? (vsel ? vo.vs_b : vo.vs_a) : 0.f) : 1.f;
       // bf16 cache: V tiles as fp16 operands, converted once for all heads of the wave (exact
       // for |V| in fp16's normal range), so P . V takes one fp16 MFMA per tile
       f16x8 vh[kKV == kKvBf16 ? kTiles : 1];
