@@ -110,6 +110,8 @@ def build_workload(name: str, total_steps: int):
     import inputs
     if name == "llama8b_decode":
         return inputs.llama8b_decode(steps=total_steps)
+    if name == "llama8b_decode_tp8":
+        return inputs.llama8b_decode_tp8(steps=total_steps)
     if name == "shared_prefix_batch":
         return inputs.shared_prefix_batch(steps=total_steps)
     if name == "long_context":
@@ -727,9 +729,10 @@ def measure_decode(name: str, steps: int, warmup: int, cold_reps: int, partition
 # beside it.  Workloads that append run from their first step (warm-up 0), so that the shared-
 # prefix batch's copy-on-write step is inside the timed steps.
 CONFIG_WORKLOADS = ("tiny_fp32", "llama8b_decode", "long_context", "shared_prefix_batch",
-                    "int8_mha", "int4_mha")
+                    "int8_mha", "int4_mha", "llama8b_decode_tp8")
 CONFIG_STEPS = {"tiny_fp32": (0, 10), "llama8b_decode": (2, 10), "long_context": (2, 8),
-                "shared_prefix_batch": (0, 12), "int8_mha": (3, 12), "int4_mha": (3, 12)}
+                "shared_prefix_batch": (0, 12), "int8_mha": (3, 12), "int4_mha": (3, 12),
+                "llama8b_decode_tp8": (2, 10)}
 
 
 # Workloads whose sequences share prefixes: their record is the shared-prefix decode's, with

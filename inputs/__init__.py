@@ -134,6 +134,14 @@ def llama8b_decode(B: int = 64, lo: int = 512, hi: int = 4096, steps: int = 1,
                     steps=steps)
 
 
+def llama8b_decode_tp8(steps: int = 1, cid: int = 2, name: str = "llama8b_decode_tp8") -> Workload:
+    """One GPU's share of the Llama-3.1-8B decode layer split by KV head over 8 GPUs: the same
+    batch and lengths (same seed), 4 query heads on its one KV head."""
+    w = llama8b_decode(steps=steps, cid=cid, name=name)
+    w.Hq, w.Hkv = w.Hq // 8, w.Hkv // 8
+    return w
+
+
 def long_context(lengths=(8192, 32768, 65536, 131072), cid: int = 3,
                  name: str = "long_context") -> Workload:
     """Split-K stress: Llama-3.1-8B layer shape, few very long sequences, peaked softmax."""
@@ -179,6 +187,7 @@ def int8_mha(B: int = 32, lo: int = 1, hi: int = 2048, Hq: int = 40, cid: int = 
 FULL = {
     "tiny_fp32": tiny_fp32,
     "llama8b_decode": llama8b_decode,
+    "llama8b_decode_tp8": llama8b_decode_tp8,
     "long_context": long_context,
     "shared_prefix_batch": shared_prefix_batch,
     "int8_mha": int8_mha,

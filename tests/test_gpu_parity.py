@@ -35,7 +35,7 @@ def test_small_workload_all_steps(name, partition, fused):
 
 
 @pytest.mark.parametrize("name", ["llama8b_decode", "long_context", "shared_prefix_batch",
-                                  "int8_mha", "int4_mha", "tiny_fp32"])
+                                  "int8_mha", "int4_mha", "tiny_fp32", "llama8b_decode_tp8"])
 def test_full_workload_sampled(name):
     """The full-size workloads in the default launch configuration; the oracle computes sampled
     (sequence, head) rows one by one."""
