@@ -355,17 +355,17 @@ size_t pa_decode_shared_prefix_workspace_size(int32_t B, int32_t Hq, int32_t Hkv
  *     start with the same block in [0, NB).  The library finds them on the device: callers
  *     that want the saving put sequences that share a prefix next to each other.  Within a
  *     group, member b shares with the longest member (the first on ties) the tokens below
- *     min(seq_lens[b], 16 k), k = leading table entries equal in both; those are read once per
- *     KV head for up to 16 query heads (of several members) at a time, and b's other tokens
- *     as in pa_decode.  The tables alone decide: a run of unrelated sequences costs nothing
+ *     min(seq_lens[b], 16 k) rounded down to a multiple of 32, k = leading table entries equal
+ *     and in [0, NB) in both; those are read once per KV head for up to 16 query heads (of
+ *     several members) at a time, and b's other tokens as in pa_decode.  The tables alone decide: a run of unrelated sequences costs nothing
  *     but the detection.
  *   Runs its own schedule for a PA_BF16 q over PA_BF16, PA_I8 or PA_I4 caches with Hq/Hkv in
  *     {1, 2, 4, 8} and B <= 8192; any other valid call is pa_decode(..., 0, ...).
  *   workspace: device buffer of workspace_bytes >= pa_decode_shared_prefix_workspace_size();
  *     needs no initialisation; calls that overlap in time must not share it.
  *   Four launches on `stream`: the group plan, the prefix pass, the decode of every sequence
- *   past its prefix with the prefix's states folded in (log-sum-exp), and the merge of split
- *   segments.  Errors as for pa_decode. */
+ *   past its prefix, and a merge launch that combines split segments and folds the prefix
+ *   states into every row with a shared prefix (log-sum-exp).  Errors as for pa_decode. */
 int pa_decode_shared_prefix(float* out, const void* q, int32_t q_dtype, const void* k_cache,
                             const void* v_cache, int32_t kv_dtype, const float* k_scale,
                             const float* v_scale, const int32_t* block_tables, int32_t max_blocks,
