@@ -1391,6 +1391,12 @@ __global__ void __launch_bounds__(256) prefix_plan_kernel(DecodeArgs a) {
   put(min(Lb, kBlockSize * k) & ~(2 * kBlockSize - 1), ref);
 }
 
+// Dynamic LDS of a balanced-schedule launch: the prefix sums cum_s[0..B] and cc_s[0..B], every
+// entry the kernel touches (sizing it one short left cc_s[B] to the rounding of the allocation).
+size_t balanced_lds(int32_t B) {
+  return static_cast<size_t>(2 * static_cast<int64_t>(B) + 2) * sizeof(int32_t);
+}
+
 template <int G, int D, int kKV>
 hipError_t launch_gd(const DecodeArgs& a, hipStream_t stream) {
   if (a.nw == 0 || G > kMaxBalancedGroup) {
@@ -1400,7 +1406,7 @@ hipError_t launch_gd(const DecodeArgs& a, hipStream_t stream) {
     return hipGetLastError();
   }
   constexpr int Gb = G <= kMaxBalancedGroup ? G : kMaxBalancedGroup;  // never launched for G > 8
-  const size_t lds = static_cast<size_t>(2 * a.B + 1) * sizeof(int32_t);
+  const size_t lds = balanced_lds(a.B);
   hipLaunchKernelGGL((decode_mfma_kernel<Gb, D, kBalanced, kKV>), dim3(a.nw), dim3(64 * kWaves),
                      lds, stream, a);
   hipError_t e = hipGetLastError();
@@ -1423,7 +1429,7 @@ hipError_t launch_gd_shared(const DecodeArgs& a, hipStream_t stream) {
                        lds_pre, stream, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const size_t lds = static_cast<size_t>(2 * a.B + 1) * sizeof(int32_t);
+    const size_t lds = balanced_lds(a.B);
     hipLaunchKernelGGL((decode_mfma_kernel<G, D, kSuffix, kKV>), dim3(a.nw), dim3(64 * kWaves),
                        lds, stream, a);
     e = hipGetLastError();

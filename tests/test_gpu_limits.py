@@ -45,14 +45,16 @@ def _lone(n, rng, hi, zeros=8):
     return [(0, [x]) for x in L]
 
 
-@pytest.mark.parametrize("B", [MAX_BALANCED, MAX_BALANCED + 1])
-def test_decode_at_the_balanced_limit(B):
-    """B = 8192 runs the balanced schedule, B = 8193 the fixed partitions the automatic
-    partition picks; both against the oracle and against 64-token fixed partitions."""
-    rng = np.random.default_rng(B)
-    w, tables, lens, pool, q = _grouped("bf16", 4, 64, _lone(B, rng, 90), Hkv=1, cid=200 + B % 7,
-                                        name="limit")
-    say(f"limit decode B={B}")
+@pytest.mark.parametrize("B,G,D", [(MAX_BALANCED, 4, 64), (MAX_BALANCED, 8, 128),
+                                   (MAX_BALANCED + 1, 4, 64)])
+def test_decode_at_the_balanced_limit(B, G, D):
+    """B = 8192 runs the balanced schedule (G = 8, D = 128 is its largest LDS: the per-wave
+    states beside the 2 B + 2 prefix sums), B = 8193 the fixed partitions the automatic
+    partition picks; each against the oracle and against 64-token fixed partitions."""
+    rng = np.random.default_rng(B + G)
+    w, tables, lens, pool, q = _grouped("bf16", G, D, _lone(B, rng, 90), Hkv=1,
+                                        cid=200 + (B + G) % 7, name="limit")
+    say(f"limit decode B={B} G={G} D={D}")
     qd, dev, tab, ln, max_len = _device(w, tables, lens, pool, q)
     out = pkv.decode(qd, dev["k"], dev["v"], tab, ln, max_len, w.scale)
     other = pkv.decode(qd, dev["k"], dev["v"], tab, ln, max_len, w.scale, partition_tokens=64)
