@@ -359,10 +359,16 @@ decode_mfma_kernel(DecodeArgs a) {
             R.k2[c] = x2[c];
           }
         }
-        const uint8_t* v = vc8 + (vblk_sel ? h_b : h_a) + r * (kBlockSize / 2) + 4 * (qg % 2);
+        // V: two dim rows (16 tokens of 4 bits each) per 16-byte load, 64 dims per load over the
+        // wave: lane group qg reads block qg / 2, dims 64 t + 32 (qg % 2) + 2 r and + 1 (rows of
+        // 8 bytes); compute_pair pairs up the half rows with the neighbouring lane group
+        const uint8_t* v = vc8 + (vblk_sel ? h_b : h_a) + 256 * (qg % 2) + 16 * r;
 #pragma unroll
-        for (int n = 0; n < kTiles; ++n)
-          R.v[n] = ld.template get<uint32_t>(v + 16 * n * (kBlockSize / 2));
+        for (int t = 0; t < kTiles / 4; ++t) {
+          const u32x4 x = ld.template get<u32x4>(v + 512 * t);
+#pragma unroll
+          for (int c = 0; c < 4; ++c) R.v[4 * t + c] = x[c];
+        }
       } else if constexpr (kI8) {
         const uint8_t* k1 = kc8 + (tok1 < 16 ? tile_a : tile_b) + (tok1 % 16) * D + 16 * qg;
         const uint8_t* k2 = kc8 + (tok2 < 16 ? tile_a : tile_b) + (tok2 % 16) * D + 16 * qg;
@@ -545,11 +551,28 @@ decode_mfma_kernel(DecodeArgs a) {
         accc = __builtin_amdgcn_mfma_f32_16x16x32_f16(p16, offs, accc, 0, 0, 0);
         // P as one fp16 operand (11-bit significand: its rounding stays far inside the int8 /
         // int4 tolerance) next to fp16 codes
+        // int4: words 4 t + 2 e and 4 t + 2 e + 1 of a lane hold the token halves 0 and 1 of its
+        // dim row 64 t + 32 (qg % 2) + 2 r + e.  One row swap between the lane groups of a block
+        // (qg = 2 i and 2 i + 1) leaves every lane the half its own group contracts over, of the
+        // even group's row (word 4 t + 2 e) and of the odd group's (word 4 t + 2 e + 1); tile
+        // n = 4 t + 2 s + e takes the even (s = 0) or odd (s = 1) rows, so its column r is dim
+        // 64 t + 32 s + 2 r + e (dim_of).
+        uint32_t vw[kI4 ? kTiles : 1];
+        if constexpr (kI4) {
+#pragma unroll
+          for (int q2 = 0; q2 < kTiles / 2; ++q2) {
+            const auto sw = __builtin_amdgcn_permlane16_swap(R.v[2 * q2], R.v[2 * q2 + 1], false,
+                                                             false);
+            vw[2 * q2] = sw[0];
+            vw[2 * q2 + 1] = sw[1];
+          }
+        }
 #pragma unroll
         for (int n = 0; n < kTiles; ++n) {
           f16x8 vop;
           if constexpr (kI4) {
-            vop = nibbles_to_f16_hi16(R.v[n]);
+            // tile n = 4 t + 2 s + e: word 4 t + 2 e + s after the swap
+            vop = nibbles_to_f16_hi16(vw[4 * (n / 4) + 2 * (n % 2) + (n / 2) % 2]);
           } else {
             vop = codes_to_f16(R.v[n][0], R.v[n][1]);
           }
@@ -605,6 +628,10 @@ decode_mfma_kernel(DecodeArgs a) {
       }
     }
 
+    // the dim of column r of accumulator tile n (int4: see compute_pair)
+    auto dim_of = [&](int n) {
+      return kI4 ? 64 * (n / 4) + 32 * ((n / 2) % 2) + 2 * r + n % 2 : 16 * n + r;
+    };
     // reduce the lane partials over the four lane groups: l_tot belongs to head r % G
     float l_tot = l_run + __shfl_xor(l_run, 16, 64);
     l_tot += __shfl_xor(l_tot, 32, 64);
@@ -620,7 +647,7 @@ decode_mfma_kernel(DecodeArgs a) {
         const float cj = kI8 ? accc[j] : 0.f;  // row 4 qg + j's offset sum
         if (h < G) {
 #pragma unroll
-          for (int n = 0; n < kTiles; ++n) o_s[w][slot][h][16 * n + r] = acc[n][j] - cj;
+          for (int n = 0; n < kTiles; ++n) o_s[w][slot][h][dim_of(n)] = acc[n][j] - cj;
         }
       }
     };
@@ -645,11 +672,11 @@ decode_mfma_kernel(DecodeArgs a) {
           for (int n = 0; n < kTiles; ++n) {
             const float o = lj > 0.f ? (acc[n][j] - cj) / lj : 0.f;
             if (to_sf) {
-              a.sf_o[row * D + 16 * n + r] = o;
+              a.sf_o[row * D + dim_of(n)] = o;
             } else if (dest == 0) {
-              a.out[row * D + 16 * n + r] = o;
+              a.out[row * D + dim_of(n)] = o;
             } else {
-              a.ws_o[slot * D + 16 * n + r] = o;
+              a.ws_o[slot * D + dim_of(n)] = o;
             }
           }
           if (r == 0) {
