@@ -377,10 +377,16 @@ decode_mfma_kernel(DecodeArgs a) {
           R.k1[c] = ld.template get<u32x4>(k1 + 64 * c);
           R.k2[c] = ld.template get<u32x4>(k2 + 64 * c);
         }
-        const uint8_t* v = vc8 + (vblk_sel ? tile_b : tile_a) + r * kBlockSize + vtok;
+        // V: one whole dim row (16 tokens) per 16-byte load, dims 32 t + 16 (qg % 2) + r of
+        // block qg / 2; words 0, 1 are token half 0, words 2, 3 half 1 (compute_pair pairs the
+        // halves up with the neighbouring lane group)
+        const uint8_t* v = vc8 + (vblk_sel ? tile_b : tile_a) + (16 * (qg % 2) + r) * kBlockSize;
 #pragma unroll
-        for (int n = 0; n < kTiles; ++n)
-          R.v[n] = ld.template get<u32x2>(v + 16 * n * kBlockSize);
+        for (int t = 0; t < kTiles / 2; ++t) {
+          const u32x4 x = ld.template get<u32x4>(v + 32 * t * kBlockSize);
+          R.v[2 * t] = u32x2{x[0], x[1]};
+          R.v[2 * t + 1] = u32x2{x[2], x[3]};
+        }
       } else {
         const uint16_t* k1 = kc + (tok1 < 16 ? tile_a : tile_b) + (tok1 % 16) * D + 8 * qg;
         const uint16_t* k2 = kc + (tok2 < 16 ? tile_a : tile_b) + (tok2 % 16) * D + 8 * qg;
@@ -557,6 +563,23 @@ decode_mfma_kernel(DecodeArgs a) {
         // even group's row (word 4 t + 2 e) and of the odd group's (word 4 t + 2 e + 1); tile
         // n = 4 t + 2 s + e takes the even (s = 0) or odd (s = 1) rows, so its column r is dim
         // 64 t + 32 s + 2 r + e (dim_of).
+        // int8: R.v[2 t] / R.v[2 t + 1] hold the token halves 0 / 1 of the lane's dim row
+        // 32 t + 16 (qg % 2) + r; the same swap leaves each lane its group's half of the even
+        // group's row (tile 2 t, dims 32 t + r) and of the odd group's (tile 2 t + 1), so the
+        // tiles keep the plain column map 16 n + r
+        u32x2 v8[kI4 || !kI8 ? 1 : kTiles];
+        if constexpr (kI8 && !kI4) {
+#pragma unroll
+          for (int t = 0; t < kTiles / 2; ++t) {
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+              const auto sw = __builtin_amdgcn_permlane16_swap(R.v[2 * t][c], R.v[2 * t + 1][c],
+                                                               false, false);
+              v8[2 * t][c] = sw[0];
+              v8[2 * t + 1][c] = sw[1];
+            }
+          }
+        }
         uint32_t vw[kI4 ? kTiles : 1];
         if constexpr (kI4) {
 #pragma unroll
@@ -574,7 +597,7 @@ decode_mfma_kernel(DecodeArgs a) {
             // tile n = 4 t + 2 s + e: word 4 t + 2 e + s after the swap
             vop = nibbles_to_f16_hi16(vw[4 * (n / 4) + 2 * (n % 2) + (n / 2) % 2]);
           } else {
-            vop = codes_to_f16(R.v[n][0], R.v[n][1]);
+            vop = codes_to_f16(v8[n][0], v8[n][1]);
           }
           acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(p16, vop, acc[n], 0, 0, 0);
         }
