@@ -64,6 +64,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 8;
+constexpr int kPrefixWaves = 4;  // the shared-prefix pass's workgroup
 constexpr int kPair = 2 * kBlockSize;  // tokens per wave iteration
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
@@ -176,12 +177,17 @@ struct CachedLoad {
   }
 };
 
+// The decode of one workgroup: workgroup wg of the nwg that share the balanced schedule or
+// the prefix pass (the fixed schedule takes its partition, head and sequence from the grid).
 template <int G, int D, int kMode, int kKV>
-__global__ void __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
-decode_mfma_kernel(DecodeArgs a) {
+__device__ __forceinline__ void decode_body(const DecodeArgs& a, const int wg, const int nwg) {
   constexpr bool kStream = kMode == kBalanced || kMode == kSuffix;  // balanced schedule
   constexpr bool kFold = kMode == kSuffix;
   constexpr bool kPre = kMode == kPrefix;
+  constexpr int kW = kPre ? kPrefixWaves : kWaves;  // waves per workgroup
+  // column tiles per wave: the prefix pass takes two column blocks (32 query columns) on every
+  // pair it loads, so each load serves twice the columns
+  constexpr int CT = kPre ? 2 : 1;
   static_assert(!kPre || G == 16, "the prefix pass fills all 16 columns of its tiles");
   constexpr bool kI4 = kKV == kKvI4;
   constexpr bool kI8 = kKV == kKvI8 || kI4;  // a quantised cache (scales, offset codes)
@@ -189,7 +195,8 @@ decode_mfma_kernel(DecodeArgs a) {
   constexpr int kK8 = D / 64;
   using Regs = std::conditional_t<kI4, PairRegsI4<D>,
                                   std::conditional_t<kI8, PairRegsI8<D>, PairRegs<D>>>;
-  constexpr int kDepth = kI4 ? kDepthI4 : (kI8 ? kDepthI8 : kDepthBf16);  // pairs in flight
+  // pairs in flight per wave (the prefix pass, one wave per SIMD, has the registers for four)
+  constexpr int kDepth = kPre ? 4 : (kI4 ? kDepthI4 : (kI8 ? kDepthI8 : kDepthBf16));
   constexpr int kSteps = D / 32;
   constexpr int kTiles = D / 16;
 
@@ -200,12 +207,12 @@ decode_mfma_kernel(DecodeArgs a) {
   constexpr int kSlots = kStream ? 2 : 1;
   // balanced schedule: pair-count prefix sums cum_s[0..B], then cost prefix sums cc_s[0..B]
   extern __shared__ int32_t cum_s[];
-  __shared__ float m_s[kWaves][kSlots][G];
-  __shared__ float l_s[kWaves][kSlots][G];
-  __shared__ float o_s[kWaves][kSlots][G][D];
-  __shared__ int32_t wave_tot[kWaves];
+  __shared__ float m_s[kW][kSlots][G];
+  __shared__ float l_s[kW][kSlots][G];
+  __shared__ float o_s[kW][kSlots][G][D];
+  __shared__ int32_t wave_tot[kW];
   // prefix pass: output row (-1: unused) and token limit of each query column of the item
-  __shared__ int32_t colrow_s[kPre ? 16 : 1], collim_s[kPre ? 16 : 1];
+  __shared__ int32_t colrow_s[kPre ? 16 * CT : 1], collim_s[kPre ? 16 * CT : 1];
 
   const int lane = threadIdx.x % 64;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
@@ -247,17 +254,22 @@ decode_mfma_kernel(DecodeArgs a) {
     // nibbles unpacked to bytes c + 8).  Lane group qg holds dims of tile t in the order the K
     // operand has them: int8 16 qg + 64 t + m, int4 (D / 4) qg + 16 t + m, m < 16; both read
     // as the 8-dim groups s = 2 t, 2 t + 1 of the loads below.
-    u32x4 qv[kI8 ? 1 : kSteps];
-    i32x4 qh[kI8 ? kK8 : 1], ql[kI8 ? kK8 : 1];
-    float qscale = 0.f;  // quantised: sq / 128, the weight of one unit of hi * 128 + lo
-    int q8 = 0;          // int4: 8 * sum_d (128 hi + lo), the nibbles' +8 times q
-    int lim_tok = 0;  // kPrefix: tokens of this lane's column (its pairs from lim_tok on are masked)
-    {
+    // (one set per column tile ct: the prefix pass's lane holds columns r and 16 + r)
+    u32x4 qv[CT][kI8 ? 1 : kSteps];
+    i32x4 qh[CT][kI8 ? kK8 : 1], ql[CT][kI8 ? kK8 : 1];
+    float qscale[CT];  // quantised: sq / 128, the weight of one unit of hi * 128 + lo
+    int q8[CT];        // int4: 8 * sum_d (128 hi + lo), the nibbles' +8 times q
+    int lim_tok[CT];   // kPrefix: tokens of the lane's column (its pairs from lim_tok on are masked)
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      qscale[ct] = 0.f;
+      q8[ct] = 0;
+      lim_tok[ct] = 0;
       int64_t qrow = static_cast<int64_t>(b) * a.Hq + static_cast<int64_t>(g) * G + r % G;
       if constexpr (kPre) {
-        const int cr = colrow_s[r];
+        const int cr = colrow_s[16 * ct + r];
         qrow = cr >= 0 ? cr : colrow_s[0];  // an unused column computes on a valid row
-        lim_tok = collim_s[r];
+        lim_tok[ct] = collim_s[16 * ct + r];
       }
       const uint16_t* q = static_cast<const uint16_t*>(a.q) + qrow * D;
       if constexpr (kI8) {
@@ -279,7 +291,7 @@ decode_mfma_kernel(DecodeArgs a) {
         amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
         const float sq = amax > 0.f ? amax / 127.f : 1.f;
         const float inv = amax > 0.f ? 127.f / amax : 1.f;
-        qscale = sq * (1.f / 128.f);
+        qscale[ct] = sq * (1.f / 128.f);
         int qtot = 0;
 #pragma unroll
         for (int t = 0; t < kK8; ++t) {
@@ -300,19 +312,19 @@ decode_mfma_kernel(DecodeArgs a) {
             hw[c] = hb;
             lw[c] = lb;
           }
-          qh[t] = i32x4{static_cast<int32_t>(hw[0]), static_cast<int32_t>(hw[1]),
+          qh[ct][t] = i32x4{static_cast<int32_t>(hw[0]), static_cast<int32_t>(hw[1]),
                         static_cast<int32_t>(hw[2]), static_cast<int32_t>(hw[3])};
-          ql[t] = i32x4{static_cast<int32_t>(lw[0]), static_cast<int32_t>(lw[1]),
+          ql[ct][t] = i32x4{static_cast<int32_t>(lw[0]), static_cast<int32_t>(lw[1]),
                         static_cast<int32_t>(lw[2]), static_cast<int32_t>(lw[3])};
         }
         if constexpr (kI4) {
           qtot += __shfl_xor(qtot, 16, 64);
           qtot += __shfl_xor(qtot, 32, 64);
-          q8 = 8 * qtot;
+          q8[ct] = 8 * qtot;
         }
       } else {
 #pragma unroll
-        for (int s = 0; s < kSteps; ++s) qv[s] = load16(q + 32 * s + 8 * qg);
+        for (int s = 0; s < kSteps; ++s) qv[ct][s] = load16(q + 32 * s + 8 * qg);
       }
     }
 
@@ -401,16 +413,23 @@ decode_mfma_kernel(DecodeArgs a) {
       }
     };
 
-    float m_run = -INFINITY;  // running max (log2 domain) of head r % G
-    float l_run = 0.f;        // lane-partial running sum over this lane's tokens
-    f32x4 acc[kTiles];
+    float m_run[CT], l_run[CT];  // running max (log2 domain) of the lane's column (head r % G)
+                                 // and the lane-partial running sum over this lane's tokens
+    f32x4 acc[CT][kTiles];
 #pragma unroll
-    for (int n = 0; n < kTiles; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int ct = 0; ct < CT; ++ct) {
+      m_run[ct] = -INFINITY;
+      l_run[ct] = 0.f;
+#pragma unroll
+      for (int n = 0; n < kTiles; ++n) acc[ct][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
     // quantised caches: the codes enter P.V as offset + code (offset 1152 for int8; 1032 for
     // int4 elements 0..3 and 1152 for 4..7, whose codes come at 16 times their value); accc
     // collects sum_t P_t offset_t with one more MFMA against a tile of the offsets, rounded and
     // summed exactly as the value tiles' offset parts, and is taken out at the end
-    f32x4 accc = {0.f, 0.f, 0.f, 0.f};
+    f32x4 accc[CT];
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) accc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
     f16x8 offs;
 #pragma unroll
     for (int e = 0; e < 8; ++e)
@@ -418,74 +437,10 @@ decode_mfma_kernel(DecodeArgs a) {
 
     auto compute_pair = [&](int i, Regs& R) {
       const int tok0 = i * kPair;
-      f32x4 s1 = {0.f, 0.f, 0.f, 0.f}, s2 = {0.f, 0.f, 0.f, 0.f};
-      i32x4 h1 = {0, 0, 0, 0}, l1 = {0, 0, 0, 0}, h2 = {0, 0, 0, 0}, l2 = {0, 0, 0, 0};
-      if constexpr (kI8) {
-#pragma unroll
-        for (int t = 0; t < kK8; ++t) {
-          i32x4 a1, a2;
-          if constexpr (kI4) {
-            // nibble bytes c + 8 of dims (D / 4) qg + 16 t + m: words 2 t, 2 t + 1, each split
-            // into its low nibbles (dims +0..3) and high nibbles (+4..7)
-#pragma unroll
-            for (int c = 0; c < 2; ++c) {
-              const uint32_t x1 = R.k1[2 * t + c], x2 = R.k2[2 * t + c];
-              a1[2 * c] = static_cast<int32_t>(x1 & 0x0f0f0f0fu);
-              a1[2 * c + 1] = static_cast<int32_t>((x1 >> 4) & 0x0f0f0f0fu);
-              a2[2 * c] = static_cast<int32_t>(x2 & 0x0f0f0f0fu);
-              a2[2 * c + 1] = static_cast<int32_t>((x2 >> 4) & 0x0f0f0f0fu);
-            }
-          } else {
-            a1 = __builtin_bit_cast(i32x4, R.k1[t]);
-            a2 = __builtin_bit_cast(i32x4, R.k2[t]);
-          }
-          h1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, qh[t], h1, 0, 0, 0);
-          l1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, ql[t], l1, 0, 0, 0);
-          h2 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a2, qh[t], h2, 0, 0, 0);
-          l2 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a2, ql[t], l2, 0, 0, 0);
-        }
-      } else {
-#pragma unroll
-        for (int s = 0; s < kSteps; ++s) {
-          s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(R.k1[s]), as_bf16x8(qv[s]), s1, 0, 0, 0);
-          s2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(R.k2[s]), as_bf16x8(qv[s]), s2, 0, 0, 0);
-        }
-      }
       // this lane's 8 tokens: pair tokens 8 qg + e, e = 0..7
       const int t_first = tok0 + 8 * qg;
       const int32_t my_blk = vblk_sel ? R.blk_b : R.blk_a;
       const bool tail = (tok0 + kPair > end) || R.blk_b < 0 || R.blk_a < 0;
-      float sc[8];
-      if constexpr (kI8) {
-        // score = k_scale * sq / 128 * sum_d c_d (128 hi_d + lo_d), the sum exact in int32
-        // (int4: the bytes hold c + 8, whose 8 (128 hi + lo) summed over d is q8)
-        const float f = (vblk_sel ? R.ks_b : R.ks_a) * a.scale_log2 * qscale;
-        const float c0 = kI4 ? -static_cast<float>(q8) * f : 0.f;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          sc[e] = fmaf(static_cast<float>((h1[e] << 7) + l1[e]), f, c0);
-          sc[4 + e] = fmaf(static_cast<float>((h2[e] << 7) + l2[e]), f, c0);
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          sc[e] = s1[e] * a.scale_log2;
-          sc[4 + e] = s2[e] * a.scale_log2;
-        }
-      }
-      if (tail) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (t_first + e >= end || my_blk < 0) sc[e] = -INFINITY;
-      }
-      if constexpr (kPre) {
-        // column limits are multiples of a pair; the reference's tokens below the group's
-        // prefix length are all live, so p = 0 keeps a masked column's values out
-        if (tok0 >= lim_tok) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) sc[e] = -INFINITY;
-        }
-      }
       if (tail && !kI8) {
         // masked tokens must not reach P.V even with p = 0 (their V may be anything); int8
         // codes always convert to finite values, so there p = 0 is enough
@@ -503,58 +458,145 @@ decode_mfma_kernel(DecodeArgs a) {
             for (int c = 0; c < 4; ++c) R.v[n][c] &= keep[c];
         }
       }
-      float bmax = sc[0];
-#pragma unroll
-      for (int e = 1; e < 8; ++e) bmax = fmaxf(bmax, sc[e]);
-      bmax = fmaxf(bmax, __shfl_xor(bmax, 16, 64));
-      bmax = fmaxf(bmax, __shfl_xor(bmax, 32, 64));
-      const float m_new = fmaxf(m_run, bmax);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-      // quantised caches spend their issue slots on ALU work, so they skip the accumulator
-      // rescale (alpha is exactly 1) on pairs where no column's maximum grew, most pairs once a
-      // few hundred tokens are in; bf16 waits on memory and rescales unconditionally
-      const bool rescale = !kI8 || __ballot(m_new != m_run) != 0;
-      m_run = m_new;
-      f32x8 pv;
-      float psum = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        pv[e] = __builtin_amdgcn_exp2f(sc[e] - m_use);
-        psum += pv[e];
-      }
-      l_run = l_run * alpha + psum;
-      f16x8 p16;
+      // quantised caches: the K operands of the integer score MFMAs, shared by the column tiles
+      i32x4 ka1[kI8 ? kK8 : 1], ka2[kI8 ? kK8 : 1];
       if constexpr (kI8) {
-        // fold this block's V scale into P and round it to the fp16 operand once; the offset
-        // tile meets exactly those operands, so the offsets cancel
-        // (a masked block's scale is never read as a number: its P are 0, and 0 * scale must
-        // stay 0 whatever the unused entry holds; chosen here, at the use, so that the wave
-        // does not wait for the look-ahead's scalar loads a pair early)
-        const float vs = my_blk >= 0 ? (vblk_sel ? R.vs_b : R.vs_a) : 0.f;
-        // int4: elements 4..7 meet codes expanded at 16 times their value
-        const float vs_hi = kI4 ? vs * 0.0625f : vs;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) pv[e] *= e < 4 ? vs : vs_hi;
-        p16 = __builtin_convertvector(pv, f16x8);
-      }
-      // rescale the accumulators: rows 4 qg + j hold head (4 qg + j) % G
-      if (rescale) {
+        for (int t = 0; t < kK8; ++t) {
+          if constexpr (kI4) {
+            // nibble bytes c + 8 of dims (D / 4) qg + 16 t + m: words 2 t, 2 t + 1, each split
+            // into its low nibbles (dims +0..3) and high nibbles (+4..7)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          float aj;
-          if constexpr (G <= 4) {
-            aj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), j % G));
+            for (int c = 0; c < 2; ++c) {
+              const uint32_t x1 = R.k1[2 * t + c], x2 = R.k2[2 * t + c];
+              ka1[t][2 * c] = static_cast<int32_t>(x1 & 0x0f0f0f0fu);
+              ka1[t][2 * c + 1] = static_cast<int32_t>((x1 >> 4) & 0x0f0f0f0fu);
+              ka2[t][2 * c] = static_cast<int32_t>(x2 & 0x0f0f0f0fu);
+              ka2[t][2 * c + 1] = static_cast<int32_t>((x2 >> 4) & 0x0f0f0f0fu);
+            }
           } else {
-            aj = __shfl(alpha, (4 * qg + j) % G, 64);
+            ka1[t] = __builtin_bit_cast(i32x4, R.k1[t]);
+            ka2[t] = __builtin_bit_cast(i32x4, R.k2[t]);
           }
-#pragma unroll
-          for (int n = 0; n < kTiles; ++n) acc[n][j] *= aj;
-          if constexpr (kI8) accc[j] *= aj;
         }
       }
+      f16x8 p16[CT];
+      bf16x8 p_hi[CT], p_lo[CT];
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) {
+        f32x4 s1 = {0.f, 0.f, 0.f, 0.f}, s2 = {0.f, 0.f, 0.f, 0.f};
+        i32x4 h1 = {0, 0, 0, 0}, l1 = {0, 0, 0, 0}, h2 = {0, 0, 0, 0}, l2 = {0, 0, 0, 0};
+        if constexpr (kI8) {
+#pragma unroll
+          for (int t = 0; t < kK8; ++t) {
+            h1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(ka1[t], qh[ct][t], h1, 0, 0, 0);
+            l1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(ka1[t], ql[ct][t], l1, 0, 0, 0);
+            h2 = __builtin_amdgcn_mfma_i32_16x16x64_i8(ka2[t], qh[ct][t], h2, 0, 0, 0);
+            l2 = __builtin_amdgcn_mfma_i32_16x16x64_i8(ka2[t], ql[ct][t], l2, 0, 0, 0);
+          }
+        } else {
+#pragma unroll
+          for (int s = 0; s < kSteps; ++s) {
+            s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(R.k1[s]), as_bf16x8(qv[ct][s]),
+                                                         s1, 0, 0, 0);
+            s2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(R.k2[s]), as_bf16x8(qv[ct][s]),
+                                                         s2, 0, 0, 0);
+          }
+        }
+        float sc[8];
+        if constexpr (kI8) {
+          // score = k_scale * sq / 128 * sum_d c_d (128 hi_d + lo_d), the sum exact in int32
+          // (int4: the bytes hold c + 8, whose 8 (128 hi + lo) summed over d is q8)
+          const float f = (vblk_sel ? R.ks_b : R.ks_a) * a.scale_log2 * qscale[ct];
+          const float c0 = kI4 ? -static_cast<float>(q8[ct]) * f : 0.f;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            sc[e] = fmaf(static_cast<float>((h1[e] << 7) + l1[e]), f, c0);
+            sc[4 + e] = fmaf(static_cast<float>((h2[e] << 7) + l2[e]), f, c0);
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            sc[e] = s1[e] * a.scale_log2;
+            sc[4 + e] = s2[e] * a.scale_log2;
+          }
+        }
+        if (tail) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (t_first + e >= end || my_blk < 0) sc[e] = -INFINITY;
+        }
+        if constexpr (kPre) {
+          // column limits are multiples of a pair; the reference's tokens below the group's
+          // prefix length are all live, so p = 0 keeps a masked column's values out
+          if (tok0 >= lim_tok[ct]) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sc[e] = -INFINITY;
+          }
+        }
+        float bmax = sc[0];
+#pragma unroll
+        for (int e = 1; e < 8; ++e) bmax = fmaxf(bmax, sc[e]);
+        bmax = fmaxf(bmax, __shfl_xor(bmax, 16, 64));
+        bmax = fmaxf(bmax, __shfl_xor(bmax, 32, 64));
+        const float m_new = fmaxf(m_run[ct], bmax);
+        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+        const float alpha = __builtin_amdgcn_exp2f(m_run[ct] - m_use);
+        // quantised caches spend their issue slots on ALU work, so they skip the accumulator
+        // rescale (alpha is exactly 1) on pairs where no column's maximum grew, most pairs once
+        // a few hundred tokens are in; bf16 waits on memory and rescales unconditionally
+        const bool rescale = !kI8 || __ballot(m_new != m_run[ct]) != 0;
+        m_run[ct] = m_new;
+        f32x8 pv;
+        float psum = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          pv[e] = __builtin_amdgcn_exp2f(sc[e] - m_use);
+          psum += pv[e];
+        }
+        l_run[ct] = l_run[ct] * alpha + psum;
+        if constexpr (kI8) {
+          // fold this block's V scale into P and round it to the fp16 operand once; the offset
+          // tile meets exactly those operands, so the offsets cancel
+          // (a masked block's scale is never read as a number: its P are 0, and 0 * scale must
+          // stay 0 whatever the unused entry holds; chosen here, at the use, so that the wave
+          // does not wait for the look-ahead's scalar loads a pair early)
+          const float vs = my_blk >= 0 ? (vblk_sel ? R.vs_b : R.vs_a) : 0.f;
+          // int4: elements 4..7 meet codes expanded at 16 times their value
+          const float vs_hi = kI4 ? vs * 0.0625f : vs;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) pv[e] *= e < 4 ? vs : vs_hi;
+          p16[ct] = __builtin_convertvector(pv, f16x8);
+        } else {
+          // P as bf16 hi + lo
+          p_hi[ct] = __builtin_convertvector(pv, bf16x8);
+          const u32x4 hi_bits = __builtin_bit_cast(u32x4, p_hi[ct]);
+          f32x8 rest;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            rest[2 * c] = pv[2 * c] - __uint_as_float(hi_bits[c] << 16);
+            rest[2 * c + 1] = pv[2 * c + 1] - __uint_as_float(hi_bits[c] & 0xffff0000u);
+          }
+          p_lo[ct] = __builtin_convertvector(rest, bf16x8);
+        }
+        // rescale the accumulators: rows 4 qg + j hold head (4 qg + j) % G
+        if (rescale) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            float aj;
+            if constexpr (G <= 4) {
+              aj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), j % G));
+            } else {
+              aj = __shfl(alpha, (4 * qg + j) % G, 64);
+            }
+#pragma unroll
+            for (int n = 0; n < kTiles; ++n) acc[ct][n][j] *= aj;
+            if constexpr (kI8) accc[ct][j] *= aj;
+          }
+        }
+        if constexpr (kI8) accc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(p16[ct], offs, accc[ct], 0, 0, 0);
+      }
       if constexpr (kI8) {
-        accc = __builtin_amdgcn_mfma_f32_16x16x32_f16(p16, offs, accc, 0, 0, 0);
         // P as one fp16 operand (11-bit significand: its rounding stays far inside the int8 /
         // int4 tolerance) next to fp16 codes
         // int4: words 4 t + 2 e and 4 t + 2 e + 1 of a lane hold the token halves 0 and 1 of its
@@ -599,23 +641,20 @@ decode_mfma_kernel(DecodeArgs a) {
           } else {
             vop = codes_to_f16(v8[n][0], v8[n][1]);
           }
-          acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(p16, vop, acc[n], 0, 0, 0);
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct)
+            acc[ct][n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(p16[ct], vop, acc[ct][n], 0, 0, 0);
         }
       } else {
-        // P as bf16 hi + lo
-        const bf16x8 p_hi = __builtin_convertvector(pv, bf16x8);
-        const u32x4 hi_bits = __builtin_bit_cast(u32x4, p_hi);
-        f32x8 rest;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          rest[2 * c] = pv[2 * c] - __uint_as_float(hi_bits[c] << 16);
-          rest[2 * c + 1] = pv[2 * c + 1] - __uint_as_float(hi_bits[c] & 0xffff0000u);
-        }
-        const bf16x8 p_lo = __builtin_convertvector(rest, bf16x8);
 #pragma unroll
         for (int n = 0; n < kTiles; ++n) {
-          acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(p_hi, as_bf16x8(R.v[n]), acc[n], 0, 0, 0);
-          acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(p_lo, as_bf16x8(R.v[n]), acc[n], 0, 0, 0);
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct) {
+            acc[ct][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(p_hi[ct], as_bf16x8(R.v[n]),
+                                                                 acc[ct][n], 0, 0, 0);
+            acc[ct][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(p_lo[ct], as_bf16x8(R.v[n]),
+                                                                 acc[ct][n], 0, 0, 0);
+          }
         }
       }
     };
@@ -629,7 +668,7 @@ decode_mfma_kernel(DecodeArgs a) {
     // would make the wait before each compute cover the look-ahead loads as well (vector
     // loads complete in order, and the wait at the join must hold on both paths).
     {
-      const int step = solo ? 1 : kWaves;
+      const int step = solo ? 1 : kW;
       int i = solo ? i0 : i0 + w;
       if (i < i1) {
         const int last = i + (i1 - 1 - i) / step * step;  // the wave's last pair of the piece
@@ -656,27 +695,31 @@ decode_mfma_kernel(DecodeArgs a) {
       return kI4 ? 64 * (n / 4) + 32 * ((n / 2) % 2) + 2 * r + n % 2 : 16 * n + r;
     };
     // reduce the lane partials over the four lane groups: l_tot belongs to head r % G
-    float l_tot = l_run + __shfl_xor(l_run, 16, 64);
-    l_tot += __shfl_xor(l_tot, 32, 64);
+    float l_tot[CT];
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      l_tot[ct] = l_run[ct] + __shfl_xor(l_run[ct], 16, 64);
+      l_tot[ct] += __shfl_xor(l_tot[ct], 32, 64);
+    }
     // accumulator rows 4 qg + j hold head (4 qg + j) % G; the copy with 4 qg + j < G is written
-    auto to_lds = [&](int slot) {
+    auto to_lds = [&](int slot, int ct) {
       if (qg == 0 && r < G) {
-        m_s[w][slot][r] = m_run;
-        l_s[w][slot][r] = l_tot;
+        m_s[w][slot][r] = m_run[ct];
+        l_s[w][slot][r] = l_tot[ct];
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int h = 4 * qg + j;
-        const float cj = kI8 ? accc[j] : 0.f;  // row 4 qg + j's offset sum
+        const float cj = kI8 ? accc[ct][j] : 0.f;  // row 4 qg + j's offset sum
         if (h < G) {
 #pragma unroll
-          for (int n = 0; n < kTiles; ++n) o_s[w][slot][h][dim_of(n)] = acc[n][j] - cj;
+          for (int n = 0; n < kTiles; ++n) o_s[w][slot][h][dim_of(n)] = acc[ct][n][j] - cj;
         }
       }
     };
-    if (solo) {
+    if (solo) {  // (one column tile: CT is 2 only for the prefix pass, which never runs solo)
       if (lds_slot >= 0) {
-        to_lds(lds_slot);
+        to_lds(lds_slot, 0);
         return;
       }
       // kSuffix: a whole segment of a sequence with a shared prefix leaves its state for the
@@ -685,15 +728,15 @@ decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int h = 4 * qg + j;
-        const float lj = __shfl(l_tot, h % G, 64);
-        const float mj = __shfl(m_run, h % G, 64);
-        const float cj = kI8 ? accc[j] : 0.f;
+        const float lj = __shfl(l_tot[0], h % G, 64);
+        const float mj = __shfl(m_run[0], h % G, 64);
+        const float cj = kI8 ? accc[0][j] : 0.f;
         if (h < G) {
           const int64_t row = static_cast<int64_t>(b) * a.Hq + static_cast<int64_t>(g) * G + h;
           const int64_t slot = part * G + h;
 #pragma unroll
           for (int n = 0; n < kTiles; ++n) {
-            const float o = lj > 0.f ? (acc[n][j] - cj) / lj : 0.f;
+            const float o = lj > 0.f ? (acc[0][n][j] - cj) / lj : 0.f;
             if (to_sf) {
               a.sf_o[row * D + dim_of(n)] = o;
             } else if (dest == 0) {
@@ -717,18 +760,21 @@ decode_mfma_kernel(DecodeArgs a) {
       return;
     }
 
-    to_lds(0);
+    // merge the waves and write, one column tile at a time (the LDS states hold one)
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+    if (ct > 0) __syncthreads();  // the previous tile's merge has read LDS
+    to_lds(0, ct);
     __syncthreads();
-    // merge the waves and write
-    for (int idx = threadIdx.x; idx < G * D; idx += 64 * kWaves) {
+    for (int idx = threadIdx.x; idx < G * D; idx += 64 * kW) {
       const int h = idx / D, d = idx % D;
       float M = -INFINITY;
 #pragma unroll
-      for (int v = 0; v < kWaves; ++v) M = fmaxf(M, m_s[v][0][h]);
+      for (int v = 0; v < kW; ++v) M = fmaxf(M, m_s[v][0][h]);
       float num = 0.f, den = 0.f;
       if (M != -INFINITY) {
 #pragma unroll
-        for (int v = 0; v < kWaves; ++v) {
+        for (int v = 0; v < kW; ++v) {
           const float f = __builtin_amdgcn_exp2f(m_s[v][0][h] - M);
           num += f * o_s[v][0][h][d];
           den += f * l_s[v][0][h];
@@ -738,8 +784,8 @@ decode_mfma_kernel(DecodeArgs a) {
       if constexpr (kPre) {
         // a column with no tokens in this part writes nothing: its row folds in only the
         // parts below its limit
-        const int64_t row = colrow_s[h];
-        if (row < 0 || collim_s[h] <= i0 * kPair) continue;
+        const int64_t row = colrow_s[16 * ct + h];
+        if (row < 0 || collim_s[16 * ct + h] <= i0 * kPair) continue;
         const int64_t slot = row * a.pf_parts + part;
         a.pf_o[slot * D + d] = o;
         if (d == 0) {
@@ -760,6 +806,7 @@ decode_mfma_kernel(DecodeArgs a) {
         a.ws_l[slot] = den;
       }
     }
+    }
     __syncthreads();  // LDS is reused by the next piece
   };
 
@@ -775,12 +822,13 @@ decode_mfma_kernel(DecodeArgs a) {
     // The shared-prefix pass.  Every workgroup first lists the groups with a prefix from the
     // plan (groups are runs of equal grp_ref inside aligned windows of 64 sequences), in batch
     // order.  A group of M members with a prefix of P tokens splits into items (KV head g,
-    // part of pf_tokens tokens, column block cb of 16 query columns = member-major (member,
-    // head) pairs); its items are numbered in runs of 8 (g, part) items per column block, so
-    // the column blocks of one (g, part) sit 8 item numbers apart and, with a grid that is a
-    // multiple of 8, run at the same time on the same XCD: the second read of the shared
-    // blocks is served by that XCD's L2.  Items go to workgroups round-robin; the 8 waves of a
-    // workgroup take an item's pairs in turn and merge in LDS.
+    // part of pf_tokens tokens, column block cb of 16 CT = 32 query columns = member-major
+    // (member, head) pairs, two MFMA column tiles that every loaded pair serves); its items are
+    // numbered in runs of 8 (g, part) items per column block, so the column blocks of one
+    // (g, part) sit 8 item numbers apart and, with a grid that is a multiple of 8, run at the
+    // same time on the same XCD: a further read of the shared blocks is served by that XCD's
+    // L2.  Items go to workgroups round-robin; the waves of a workgroup take an item's pairs in
+    // turn and merge in LDS.
     const int B = a.B;
     const int Gs = a.Hq / Hkv;  // query heads per KV head of the sequences
     const int PT = a.pf_tokens;
@@ -811,13 +859,13 @@ decode_mfma_kernel(DecodeArgs a) {
       const uint64_t em = __ballot(end);
       const int M = start ? __builtin_ctzll(em >> lane) + 1 : 0;
       const bool act = start && P > 0;
-      const int np = (P + PT - 1) / PT, ncb = (M * Gs + 15) / 16;
+      const int np = (P + PT - 1) / PT, ncb = (M * Gs + 16 * CT - 1) / (16 * CT);
       members = M;
       ptok = P;
       items = act ? (Hkv * np + 7) / 8 * 8 * ncb : 0;
       return act;
     };
-    for (int win = w; win < nwin; win += kWaves) {
+    for (int win = w; win < nwin; win += kW) {
       int m, pt, it;
       const bool act = scan_window(win, m, pt, it);
       int isum = it;
@@ -861,7 +909,7 @@ decode_mfma_kernel(DecodeArgs a) {
       }
     }
     __syncthreads();
-    for (int win = w; win < nwin; win += kWaves) {
+    for (int win = w; win < nwin; win += kW) {
       int m, pt, it;
       const bool act = scan_window(win, m, pt, it);
       const uint64_t am = __ballot(act);
@@ -882,22 +930,22 @@ decode_mfma_kernel(DecodeArgs a) {
     const int ngroups = win_g[nwin], nitems = win_i[nwin];
     if (threadIdx.x == 0) grp_off[ngroups] = nitems;
     __syncthreads();
-    for (int it = blockIdx.x; it < nitems; it += gridDim.x) {
+    for (int it = wg; it < nitems; it += nwg) {
       int lo = 0, hi = ngroups - 1;  // the group holding item it: last k with grp_off[k] <= it
       while (lo < hi) {
         const int mid = (lo + hi + 1) / 2;
         if (grp_off[mid] <= it) lo = mid; else hi = mid - 1;
       }
       const int first = grp_s[lo] & 0xffff, M = grp_s[lo] >> 16, P = grp_p[lo];
-      const int np = (P + PT - 1) / PT, ncb = (M * Gs + 15) / 16;
+      const int np = (P + PT - 1) / PT, ncb = (M * Gs + 16 * CT - 1) / (16 * CT);
       const int local = it - grp_off[lo];
       const int cb = local % (8 * ncb) / 8;
       const int qi = local / (8 * ncb) * 8 + local % 8;
       if (qi >= Hkv * np) continue;  // padding of the last run of 8
       const int g = qi / np, part = qi % np;
       const int ref = a.grp_ref[first];
-      if (threadIdx.x < 16) {
-        const int c = cb * 16 + threadIdx.x;
+      if (threadIdx.x < 16 * CT) {
+        const int c = cb * 16 * CT + threadIdx.x;
         const int mi = c / Gs;
         int row = -1, lim = 0;
         if (mi < M) {
@@ -920,7 +968,7 @@ decode_mfma_kernel(DecodeArgs a) {
     // come from memory with nothing in flight behind them).  Pieces and merges work on units.
     const int B = a.B;
     int32_t* cc_s = cum_s + B + 1;
-    __shared__ int32_t wave_cost[kWaves];
+    __shared__ int32_t wave_cost[kW];
     // kSuffix: tokens of b the prefix pass covered
     auto ps_of = [&](int b) {
       return prefix_tokens(a, b, min(max(a.seq_lens[b], 0), a.max_seq_len));
@@ -930,7 +978,7 @@ decode_mfma_kernel(DecodeArgs a) {
       cum_s[0] = 0;
       cc_s[0] = 0;
     }
-    for (int base = 0; base < B; base += 64 * kWaves) {
+    for (int base = 0; base < B; base += 64 * kW) {
       const int i = base + threadIdx.x;
       const int L = i < B ? min(max(a.seq_lens[i], 0), a.max_seq_len) : 0;
       int x = (L + kPair - 1) / kPair;
@@ -962,11 +1010,11 @@ decode_mfma_kernel(DecodeArgs a) {
         cc_s[i + 1] = add_c + c;
       }
       int tot = 0, tot_c = 0;
-      for (int v = 0; v < kWaves; ++v) {
+      for (int v = 0; v < kW; ++v) {
         tot += wave_tot[v];
         tot_c += wave_cost[v];
       }
-      if (base + 64 * kWaves < B) __syncthreads();  // wave_tot is rewritten next round
+      if (base + 64 * kW < B) __syncthreads();  // wave_tot is rewritten next round
       carry += tot;
       carry_c += tot_c;
     }
@@ -993,14 +1041,14 @@ decode_mfma_kernel(DecodeArgs a) {
       b = __builtin_amdgcn_readfirstlane(b);
       return static_cast<int64_t>(g) * T + cum_s[b] + max(r - cc_s[b] - kSegCost, 0);
     };
-    const int NW = a.nw;
-    const int wl = blockIdx.x;
+    const int NW = nwg;
+    const int wl = wg;
     // empty sequences produce zeros (kSuffix: a sequence whose prefix covers every token is
     // written by the merge launch, from the prefix pass's states alone)
     for (int b = wl; b < B; b += NW) {
       if (cum_s[b + 1] != cum_s[b]) continue;
       if (kFold && ps_of(b) > 0) continue;  // only the prefix: the merge launch writes it
-      for (int i = threadIdx.x; i < a.Hq * D; i += 64 * kWaves)
+      for (int i = threadIdx.x; i < a.Hq * D; i += 64 * kW)
         a.out[static_cast<int64_t>(b) * a.Hq * D + i] = 0.f;
     }
     // workgroup span [u0, u1); wave w streams its own eighth [v0, v1) of it with no barriers
@@ -1034,10 +1082,10 @@ decode_mfma_kernel(DecodeArgs a) {
       a.ws_m[static_cast<int64_t>(wl) * 2 * G + threadIdx.x] = -INFINITY;
       a.ws_l[static_cast<int64_t>(wl) * 2 * G + threadIdx.x] = 0.f;
     }
-    const int64_t v0 = unit_at(X0 + (X1 - X0) * w / kWaves);
-    const int64_t v1 = unit_at(X0 + (X1 - X0) * (w + 1) / kWaves);
-    __shared__ int64_t tag_s[kWaves][2];   // workgroup piece (first unit) held in each LDS slot
-    __shared__ int32_t info_s[kWaves][2][4];  // its b, g, destination, partial slot
+    const int64_t v0 = unit_at(X0 + (X1 - X0) * w / kW);
+    const int64_t v1 = unit_at(X0 + (X1 - X0) * (w + 1) / kW);
+    __shared__ int64_t tag_s[kW][2];   // workgroup piece (first unit) held in each LDS slot
+    __shared__ int32_t info_s[kW][2][4];  // its b, g, destination, partial slot
     if (lane < 2) tag_s[w][lane] = -1;
     int64_t u = v0;
     // first sequence b with cum_s[b + 1] > rem: 64 candidates per LDS read and ballot (rem is
@@ -1085,12 +1133,12 @@ decode_mfma_kernel(DecodeArgs a) {
       u += take;
     }
     __syncthreads();
-    // Merge the pieces that waves share.  The 2 kWaves LDS entries e = 2 w + slot are in unit
+    // Merge the pieces that waves share.  The 2 kW LDS entries e = 2 w + slot are in unit
     // order, and the entries of one segment (equal tags) are consecutive among the used ones.
     // First the entries' (m, l) become per-entry weights 2^(m - M) and per-group sums (one
     // thread per entry and head); then every thread reads its element of all entries at once
     // and sums each group in entry order, so the result does not depend on timing.
-    constexpr int kE = 2 * kWaves;
+    constexpr int kE = 2 * kW;
     __shared__ float wt_s[kE][G];   // entry weight 2^(m - M_group) (0 for unused entries)
     __shared__ float gm_s[kE][G];   // at a group's last entry: the group's M and l
     __shared__ float gl_s[kE][G];
@@ -1102,7 +1150,7 @@ decode_mfma_kernel(DecodeArgs a) {
     const float* lf = &l_s[0][0][0];
     const float* of = &o_s[0][0][0][0];
     // one thread per (entry, head): the group of an entry is every used entry with its tag
-    for (int t = threadIdx.x; t < kE * G; t += 64 * kWaves) {
+    for (int t = threadIdx.x; t < kE * G; t += 64 * kW) {
       const int e = t / G, h = t % G;
       int64_t tg[kE];
       float mm[kE], ll[kE];
@@ -1132,7 +1180,7 @@ decode_mfma_kernel(DecodeArgs a) {
           eps_s[e] = (used && info_s[e / 2][e % 2][2] == 0) ? ps_of(info_s[e / 2][e % 2][0]) : 0;
       }
     }
-    if (w == kWaves - 1) {
+    if (w == kW - 1) {
       // used entries, and the last entry of each group (on the last wave, which the weights
       // above leave idle for G <= 8, so the two run side by side)
       const int64_t mine = lane < kE ? tag_s[lane / 2][lane % 2] : -1;
@@ -1149,7 +1197,7 @@ decode_mfma_kernel(DecodeArgs a) {
     __syncthreads();
     const uint32_t um = mask_s[0], em = mask_s[1];
     if (um != 0) {
-      for (int idx = threadIdx.x; idx < G * D; idx += 64 * kWaves) {
+      for (int idx = threadIdx.x; idx < G * D; idx += 64 * kW) {
         const int h = idx / D, d = idx % D;
         float ov[kE];
 #pragma unroll
@@ -1188,6 +1236,20 @@ decode_mfma_kernel(DecodeArgs a) {
       }
     }
   }
+}
+
+template <int G, int D, int kMode, int kKV>
+__global__ void __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
+decode_mfma_kernel(DecodeArgs a) {
+  decode_body<G, D, kMode, kKV>(a, blockIdx.x, gridDim.x);
+}
+
+// The shared-prefix pass: four waves per workgroup, one per SIMD, so that each wave has the
+// registers for 32 query columns (two column blocks) and four pairs of loads in flight.
+template <int D, int kKV>
+__global__ void __launch_bounds__(64 * kPrefixWaves) __attribute__((amdgpu_waves_per_eu(1, 1)))
+decode_prefix_kernel(DecodeArgs a) {
+  decode_body<16, D, kPrefix, kKV>(a, blockIdx.x, gridDim.x);
 }
 
 // Merge the partial pieces of the segments the balanced schedule cut: one workgroup per decode
@@ -1475,7 +1537,7 @@ hipError_t launch_gd_shared(const DecodeArgs& a, hipStream_t stream) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const size_t lds_pre = static_cast<size_t>(3 * a.pf_gmax + 1) * sizeof(int32_t);
-    hipLaunchKernelGGL((decode_mfma_kernel<16, D, kPrefix, kKV>), dim3(a.nw), dim3(64 * kWaves),
+    hipLaunchKernelGGL((decode_prefix_kernel<D, kKV>), dim3(a.nw), dim3(64 * kPrefixWaves),
                        lds_pre, stream, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
