@@ -8,8 +8,10 @@
 // Layout of the work: one workgroup per (partition, KV head, sequence).  It walks its
 // partition in chunks of 256 tokens: one thread scores one token for all G heads of the group,
 // a wave per head folds the chunk into the running max / sum (online softmax, exp2 domain), and
-// one thread per (head, dim) accumulates the P.V column.  It is the correctness path for the
-// fp32 cache and for shapes the tuned kernels do not take; it is not tuned for bandwidth.
+// one thread per (head, dim) accumulates the P.V column.  It is the path for the fp32 cache and
+// fp32 queries, where the matrix-core kernels do not apply; it is built for short latency
+// chains rather than bandwidth: a thread requests its whole K row, and its V column a block of
+// 16 tokens at a time, as 16-byte pieces before it uses the first of them.
 #include <cfloat>
 
 #include "internal.h"
@@ -21,22 +23,40 @@ namespace {
 constexpr int kChunk = 256;
 constexpr int kGMax = 16;
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Element loaders: get reads element i; unpack takes element e of a 16-byte piece (kE elements)
 struct F32 {
   using T = float;
+  static constexpr int kE = 4;
   static __device__ __forceinline__ float get(const T* p, int64_t i) { return p[i]; }
+  static __device__ __forceinline__ float unpack(u32x4 x, int e) { return __uint_as_float(x[e]); }
 };
 struct BF16 {
   using T = uint16_t;
+  static constexpr int kE = 8;
   static __device__ __forceinline__ float get(const T* p, int64_t i) {
     return __uint_as_float(static_cast<uint32_t>(p[i]) << 16);
+  }
+  static __device__ __forceinline__ float unpack(u32x4 x, int e) {
+    return __uint_as_float(e % 2 ? x[e / 2] & 0xffff0000u : x[e / 2] << 16);
   }
 };
 struct I8 {
   using T = int8_t;
+  static constexpr int kE = 16;
   static __device__ __forceinline__ float get(const T* p, int64_t i) {
     return static_cast<float>(p[i]);
   }
+  static __device__ __forceinline__ float unpack(u32x4 x, int e) {
+    return static_cast<float>(static_cast<int8_t>((x[e / 4] >> (8 * (e % 4))) & 0xffu));
+  }
 };
+
+template <typename T>
+__device__ __forceinline__ u32x4 piece(const T* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
 
 __device__ __forceinline__ float wave_max(float x) {
   for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
@@ -101,24 +121,24 @@ __global__ void __launch_bounds__(256) decode_generic_kernel(DecodeArgs a, int G
     }
     __syncthreads();
 
-    // scores: thread t <-> token c0 + t
+    // scores: thread t <-> token c0 + t, its K row requested whole
     {
+      constexpr int kE = KL::kE;
       const int t = tid;
       const int32_t blk = t < n ? blk_s[t / kBlockSize] : -1;
       if (blk >= 0) {
         const KT* krow = kc + ((static_cast<int64_t>(blk) * a.Hkv + g) * kBlockSize +
                                t % kBlockSize) * D;
-        float dot[kGMax];
+        u32x4 kp[D / kE];
 #pragma unroll
-        for (int h = 0; h < kGMax; ++h) dot[h] = 0.f;
-        for (int d = 0; d < D; ++d) {
-          const float kv = KL::get(krow, d);
-#pragma unroll
-          for (int h = 0; h < kGMax; ++h)
-            if (h < G) dot[h] = fmaf(q_s[h][d], kv, dot[h]);
-        }
+        for (int c = 0; c < D / kE; ++c) kp[c] = piece(krow + c * kE);
         const float f = a.scale_log2 * (kQuant ? ks_s[t / kBlockSize] : 1.f);
-        for (int h = 0; h < G; ++h) s_s[h][t] = dot[h] * f;
+        for (int h = 0; h < G; ++h) {
+          float dot[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int d = 0; d < D; ++d) dot[d % 4] = fmaf(q_s[h][d], KL::unpack(kp[d / kE], d % kE), dot[d % 4]);
+          s_s[h][t] = ((dot[0] + dot[1]) + (dot[2] + dot[3])) * f;
+        }
       } else {
         for (int h = 0; h < G; ++h) s_s[h][t] = -INFINITY;
       }
@@ -152,22 +172,35 @@ __global__ void __launch_bounds__(256) decode_generic_kernel(DecodeArgs a, int G
     }
     __syncthreads();
 
-    // P.V: thread <-> (head, dim) pairs
+    // P.V: thread <-> (head, dim) pairs; the 16 tokens of dim d in a block are contiguous in
+    // the dim-major V tile, one to four 16-byte pieces
 #pragma unroll
     for (int k = 0; k < kPairs; ++k) {
       const int idx = tid + 256 * k;
       if (idx < G * D) {
+        constexpr int kE = KL::kE;
         const int h = idx / D, d = idx % D;
-        float sum = 0.f;
-        for (int t = 0; t < n; ++t) {
-          const int32_t blk = blk_s[t / kBlockSize];
-          if (blk < 0) continue;
-          float v = KL::get(vc, ((static_cast<int64_t>(blk) * a.Hkv + g) * D + d) * kBlockSize +
-                                    t % kBlockSize);
-          if (kQuant) v *= vs_s[t / kBlockSize];
-          sum = fmaf(s_s[h][t], v, sum);
+        float sum[2] = {0.f, 0.f};
+        const int nb = (n + kBlockSize - 1) / kBlockSize;
+#pragma unroll 2
+        for (int j = 0; j < nb; ++j) {
+          const int32_t blk = blk_s[j];
+          if (blk < 0) continue;  // its P are 0 and its V is not read
+          const KT* vcol = vc + ((static_cast<int64_t>(blk) * a.Hkv + g) * D + d) * kBlockSize;
+          u32x4 vp[kBlockSize / kE];
+#pragma unroll
+          for (int c = 0; c < kBlockSize / kE; ++c) vp[c] = piece(vcol + c * kE);
+          const float vsc = kQuant ? vs_s[j] : 1.f;
+          const int lim = n - j * kBlockSize;  // tokens of the block inside the chunk
+#pragma unroll
+          for (int e = 0; e < kBlockSize; ++e) {
+            // tokens past the chunk's end may hold anything, also NaN: skipped, not weighted
+            if (e < lim)
+              sum[e % 2] = fmaf(s_s[h][j * kBlockSize + e], KL::unpack(vp[e / kE], e % kE) * vsc,
+                                sum[e % 2]);
+          }
         }
-        acc[k] = acc[k] * alpha_s[h] + sum;
+        acc[k] = acc[k] * alpha_s[h] + (sum[0] + sum[1]);
       }
     }
     __syncthreads();

@@ -81,6 +81,25 @@ def test_edge_lengths(kv, G, D, partition):
     assert lens[0] == 0 and np.array_equal(out[0], np.zeros_like(out[0]))
 
 
+@pytest.mark.parametrize("q_dtype,kv,G,D", [("f32", "bf16", 4, 128), ("bf16", "f32", 2, 64),
+                                            ("f32", "i8", 8, 64), ("f32", "f32", 1, 128),
+                                            ("bf16", "f32", 16, 128)])
+@pytest.mark.parametrize("partition", [0, 64])
+def test_portable_path_dtype_pairs(q_dtype, kv, G, D, partition):
+    """The query / cache dtype pairs that only the portable kernel takes (fp32 on either side)
+    over the boundary lengths: empty, one token, block edges, and 1000 tokens, which spans
+    several 256-token chunks and, at 64-token partitions, many partitions."""
+    w = _ragged_case(kv, G, D)
+    w.q_dtype = q_dtype
+    w.cid = 140 + D + G + (q_dtype == "f32")
+    case = Case(w)
+    say(f"portable q={q_dtype} kv={kv} G={G} D={D} partition={partition}")
+    q, out, tables, lens = case.step(partition_tokens=partition)
+    ref = case.oracle(q, tables, lens)
+    assert max_err(out, ref) <= TOL[kv]
+    assert lens[0] == 0 and np.array_equal(out[0], np.zeros_like(out[0]))
+
+
 @pytest.mark.parametrize("kv,G", [("f32", 2), ("bf16", 16)])
 def test_fixed_partitions_large_batch(kv, G):
     """A batch with B * Hkv >= 1024 on the fixed-partition schedule (fp32, or 16 query heads
