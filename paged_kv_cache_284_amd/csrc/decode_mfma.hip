@@ -69,6 +69,27 @@ constexpr int kPair = 2 * kBlockSize;  // tokens per wave iteration
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
 
+// Maximum and integer sum over the four 16-lane groups (lanes r, r + 16, r + 32, r + 48), every
+// lane receiving the result, with the gfx950 half and row swaps: plain VALU work, where a lane
+// shuffle goes through the LDS crossbar and its wait would also cover the scalar loads of the
+// block table and scales that are in flight (used by the quantised kinds)
+__device__ __forceinline__ float group_max(float x) {
+  const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  x = fmaxf(__uint_as_float(h[0]), __uint_as_float(h[1]));
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ int group_sum(int x) {
+  const auto h = __builtin_amdgcn_permlane32_swap(static_cast<uint32_t>(x),
+                                                  static_cast<uint32_t>(x), false, false);
+  x = static_cast<int>(h[0]) + static_cast<int>(h[1]);
+  const auto r = __builtin_amdgcn_permlane16_swap(static_cast<uint32_t>(x),
+                                                  static_cast<uint32_t>(x), false, false);
+  return static_cast<int>(r[0]) + static_cast<int>(r[1]);
+}
+
 __device__ __forceinline__ u32x4 load16(const uint16_t* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
@@ -287,8 +308,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, const int wg, c
 #pragma unroll
           for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(f[s][e]));
         }
-        amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
-        amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+        amax = group_max(amax);
         const float sq = amax > 0.f ? amax / 127.f : 1.f;
         const float inv = amax > 0.f ? 127.f / amax : 1.f;
         qscale[ct] = sq * (1.f / 128.f);
@@ -318,8 +338,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, const int wg, c
                         static_cast<int32_t>(lw[2]), static_cast<int32_t>(lw[3])};
         }
         if constexpr (kI4) {
-          qtot += __shfl_xor(qtot, 16, 64);
-          qtot += __shfl_xor(qtot, 32, 64);
+          qtot = group_sum(qtot);
           q8[ct] = 8 * qtot;
         }
       } else {
@@ -537,8 +556,13 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, const int wg, c
         float bmax = sc[0];
 #pragma unroll
         for (int e = 1; e < 8; ++e) bmax = fmaxf(bmax, sc[e]);
-        bmax = fmaxf(bmax, __shfl_xor(bmax, 16, 64));
-        bmax = fmaxf(bmax, __shfl_xor(bmax, 32, 64));
+        if constexpr (kI8) {
+          bmax = group_max(bmax);
+        } else {
+          // bf16 keeps the lane shuffles: with the swaps it measured 0.6% slower
+          bmax = fmaxf(bmax, __shfl_xor(bmax, 16, 64));
+          bmax = fmaxf(bmax, __shfl_xor(bmax, 32, 64));
+        }
         const float m_new = fmaxf(m_run[ct], bmax);
         const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
         const float alpha = __builtin_amdgcn_exp2f(m_run[ct] - m_use);
