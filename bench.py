@@ -16,7 +16,11 @@ Also reported: the append's time per step (copy-on-write copies included), the d
 alone after reading 1 GiB of other memory (cold caches), a plain device copy's rate for context,
 and the oracle on all host threads.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload llama8b_decode]
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--settle-ms 300]
+                    [--workload llama8b_decode]
+
+Before the warm-up steps, untimed decode calls on the first step's state (they change no state)
+run for --settle-ms so that the GPU's clocks are at their sustained level when timing starts.
 
 --workload prefill_llama8b measures the chunked-prefill path instead: one step appends a
 512-token chunk per sequence (one pa_kv_append entry per token) and runs pa_prefill over it;
@@ -685,14 +689,25 @@ def release_device_memory():
 
 
 def measure_decode(name: str, steps: int, warmup: int, cold_reps: int, partition: int = 0,
-                   shared: bool = False):
+                   shared: bool = False, settle_ms: float = 0.0):
     """Run warmup + steps decode steps of a workload through the library (each step: allocator
     step, copy-on-write copies, append, decode, for workloads that append) and time them.
-    shared: decode with pa_decode_shared_prefix."""
+    shared: decode with pa_decode_shared_prefix.  settle_ms: before the warm-up steps, repeat
+    untimed decode calls on the first step's state (they change no state) for that long, so
+    that the GPU's clocks reach the level they hold under sustained load."""
     import torch
     total = warmup + steps
     w = build_workload(name, total)
     runner = StepRunner(w, total, partition, shared)
+    if settle_ms > 0:
+        runner.lens_d = runner.lens_dev.data_ptr() if not w.append else runner.lens_step.data_ptr()
+        if w.append:
+            runner.lens_step.copy_(torch.from_numpy(runner.lens))
+        t_end = time.perf_counter() + settle_ms * 1e-3
+        while time.perf_counter() < t_end:
+            for _ in range(20):
+                runner.decode(runner.q[0])
+            torch.cuda.synchronize()
     if warmup == 0:
         # timing from the first step (its copy-on-write copies included): one decode call
         # beforehand, which changes no state, loads the kernels' code outside the timed steps
@@ -798,6 +813,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--settle-ms", type=float, default=300.0,
+                    help="untimed decode calls on the first step's state for this long before "
+                         "the warm-up steps (GPU clocks to their sustained level)")
     ap.add_argument("--workload", default="llama8b_decode")
     ap.add_argument("--partition", type=int, default=0)
     ap.add_argument("--shared-prefix", action="store_true",
@@ -848,7 +866,7 @@ def main():
         return
 
     m = measure_decode(args.workload, args.steps, args.warmup, args.cold_reps, args.partition,
-                       args.shared_prefix)
+                       args.shared_prefix, args.settle_ms)
     w = m["w"]
     # the committed counters cover the headline batch only
     traffic = (traffic_from_profiles(kernel_sources_hash())
@@ -860,6 +878,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_ms": args.settle_ms,
         "ms_per_step": round(m["elapsed"] / args.steps * 1e3, 4),
         "higher_is_better": True,
         "scaling": "weak",
