@@ -215,7 +215,7 @@ int64_t balanced_workgroups(int32_t B, int32_t Hkv, int32_t max_seq_len) {
 // workgroup item; at most 8 parts per row keep the states' memory below 8 (D + 2) floats per
 // row.
 void prefix_parts(int32_t max_seq_len, int32_t* tokens, int32_t* parts) {
-  constexpr int64_t kMinPart = 1024, kMaxParts = 8;
+  constexpr int64_t kMinPart = 1024, kMaxParts = pa::kMaxPrefixParts;
   int64_t np = (static_cast<int64_t>(max_seq_len) + kMinPart - 1) / kMinPart;
   if (np > kMaxParts) np = kMaxParts;
   if (np < 1) np = 1;

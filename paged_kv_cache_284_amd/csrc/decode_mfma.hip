@@ -1400,53 +1400,39 @@ __global__ void __launch_bounds__(256) streamk_reduce_kernel(DecodeArgs a) {
 template <int G, int D>
 __device__ void fold_segment(const DecodeArgs& a, int seg) {
   const int b = seg / a.Hkv, g = seg % a.Hkv;
+  // what decides the work is requested in one round trip: length, prefix and the mark
   const int L = min(max(a.seq_lens[b], 0), a.max_seq_len);
   const int ps = prefix_tokens(a, b, L);
+  const bool whole = a.sf_mark[seg] != 0;
   if (ps == 0) return;
   const int nb = (L + 2 * kBlockSize - 1) / (2 * kBlockSize) - ps / (2 * kBlockSize);
-  const bool whole = a.sf_mark[seg] != 0;
   if (nb > 0 && !whole) return;  // cut: its merge record writes it
   constexpr int kPer = (G * D + 255) / 256;
-  float M[kPer], num[kPer], den[kPer];
-  PrefixState st[kPer];
+  const int np = prefix_parts_of(a, ps);
+  // then every state this thread folds (the suffix's, each prefix part's), all requested
+  // before the first is folded
+  PrefixState sf[kPer], pf[kMaxPrefixParts][kPer];
 #pragma unroll
   for (int k = 0; k < kPer; ++k) {
-    M[k] = -INFINITY;
-    num[k] = 0.f;
-    den[k] = 0.f;
     const int idx = threadIdx.x + 256 * k;
-    if (whole && idx < G * D) {
-      const int64_t row = static_cast<int64_t>(b) * a.Hq + static_cast<int64_t>(g) * G + idx / D;
-      st[k] = PrefixState{a.sf_m[row], a.sf_l[row], a.sf_o[row * D + idx % D]};
-    }
-  }
-  const int np = prefix_parts_of(a, ps);
-  for (int part = -1; part < np; ++part) {
-    // part -1: the suffix state loaded above; then each prefix part's states, requested for
-    // all of this thread's elements before any is folded
-    if (part >= 0) {
+    if (idx >= G * D) continue;
+    const int64_t row = static_cast<int64_t>(b) * a.Hq + static_cast<int64_t>(g) * G + idx / D;
+    if (whole) sf[k] = PrefixState{a.sf_m[row], a.sf_l[row], a.sf_o[row * D + idx % D]};
 #pragma unroll
-      for (int k = 0; k < kPer; ++k) {
-        const int idx = threadIdx.x + 256 * k;
-        if (idx < G * D) {
-          const int64_t row =
-              static_cast<int64_t>(b) * a.Hq + static_cast<int64_t>(g) * G + idx / D;
-          st[k] = load_prefix(a, row, part, idx % D);
-        }
-      }
-    } else if (!whole) {
-      continue;
-    }
-#pragma unroll
-    for (int k = 0; k < kPer; ++k)
-      if (threadIdx.x + 256 * k < G * D) fold_state(M[k], num[k], den[k], st[k]);
+    for (int part = 0; part < kMaxPrefixParts; ++part)
+      if (part < np) pf[part][k] = load_prefix(a, row, part, idx % D);
   }
 #pragma unroll
   for (int k = 0; k < kPer; ++k) {
     const int idx = threadIdx.x + 256 * k;
     if (idx >= G * D) break;
+    float M = -INFINITY, num = 0.f, den = 0.f;
+    if (whole) fold_state(M, num, den, sf[k]);
+#pragma unroll
+    for (int part = 0; part < kMaxPrefixParts; ++part)
+      if (part < np) fold_state(M, num, den, pf[part][k]);
     const int64_t row = static_cast<int64_t>(b) * a.Hq + static_cast<int64_t>(g) * G + idx / D;
-    a.out[row * D + idx % D] = den[k] > 0.f ? num[k] / den[k] : 0.f;
+    a.out[row * D + idx % D] = den > 0.f ? num / den : 0.f;
   }
 }
 

@@ -75,6 +75,8 @@ constexpr int kMaxBalancedWorkgroups = 1024;
 // live in LDS).
 constexpr int kMaxBalancedBatch = 8192;
 constexpr int kMaxBalancedGroup = 8;
+// Most prefix-pass parts one output row folds in (parts are at least 1024 tokens).
+constexpr int kMaxPrefixParts = 8;
 // Resident workgroups of the balanced MFMA kernel per compute unit.
 int mfma_workgroups_per_cu();
 
