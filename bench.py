@@ -19,8 +19,9 @@ and the oracle on all host threads.
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--settle-ms 300]
                     [--workload llama8b_decode]
 
-Before the warm-up steps, untimed decode calls on the first step's state (they change no state)
-run for --settle-ms so that the GPU's clocks are at their sustained level when timing starts.
+Before the warm-up steps, untimed decode calls on the first step's state (fixed partitions of
+8192 tokens; they change no state) run for --settle-ms, so that timing starts with the GPU in
+the state it holds under sustained decoding.
 
 --workload prefill_llama8b measures the chunked-prefill path instead: one step appends a
 512-token chunk per sequence (one pa_kv_append entry per token) and runs pa_prefill over it;
@@ -667,9 +668,9 @@ def summarize_counters(d: str, copy_mib: int = 512) -> dict:
         "kernel_sources_sha256": kernel_sources_hash(),
         "commands": [
             "rocprofv3 --pmc FETCH_SIZE --output-format csv -d prof_out/pmc_FETCH_SIZE -o dec -- "
-            "python3 -u bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-configs",
+            "python3 -u bench.py --steps 3 --warmup 1 --settle-ms 0 --no-cpu-baseline --no-configs",
             "rocprofv3 --pmc WRITE_SIZE --output-format csv -d prof_out/pmc_WRITE_SIZE -o dec -- "
-            "python3 -u bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-configs",
+            "python3 -u bench.py --steps 3 --warmup 1 --settle-ms 0 --no-cpu-baseline --no-configs",
             "rocprofv3 --pmc FETCH_SIZE --output-format csv -d prof_out/pmc_copy_FETCH_SIZE -o cp "
             f"-- python3 -u bench.py --copy-reference {copy_mib}",
             "rocprofv3 --pmc WRITE_SIZE --output-format csv -d prof_out/pmc_copy_WRITE_SIZE -o cp "
@@ -688,6 +689,38 @@ def release_device_memory():
     torch.cuda.empty_cache()
 
 
+def settle(ms: float, runner) -> None:
+    """Before timing, decode the workload's first-step state for `ms` of wall time with the
+    fixed-partition schedule at 8192 tokens (pa_decode with partition_tokens 8192: one
+    workgroup per sequence and KV head, no merge launch).  The calls read the same pool pages
+    as the timed decode and change no state; without them the first timed steps ran about 1%
+    slower.  They use other kernel instances than the balanced schedule, so a trace keeps the
+    timed kernels' rows apart from them."""
+    import torch
+    w = runner.w
+    if w.q_dtype != "bf16" or w.kv_dtype not in ("bf16", "i8", "i4"):
+        return  # the portable kernel serves these: no separate instance to settle with
+    runner.lens_d = runner.lens_dev.data_ptr() if not w.append else runner.lens_step.data_ptr()
+    if w.append:
+        runner.lens_step.copy_(torch.from_numpy(runner.lens))
+    pkv = runner.pkv
+    ws = torch.empty(max(pkv.decode_workspace_size(w.B, w.Hq, w.Hkv, w.D, runner.max_len, 8192),
+                         1), dtype=torch.uint8, device="cuda")
+    q = runner.q[0]
+    t_end = time.perf_counter() + ms * 1e-3
+    while time.perf_counter() < t_end:
+        for _ in range(20):
+            st = runner.L.pa_decode(
+                runner.out.data_ptr(), q.data_ptr(), runner.q_code, runner.k.data_ptr(),
+                runner.v.data_ptr(), runner.kv_code, runner.ks_p, runner.vs_p,
+                runner.tables.data_ptr(), runner.MB, runner.lens_d, runner.max_len, w.B, w.Hq,
+                w.Hkv, w.D, w.bs, w.NB, w.scale, 8192, ws.data_ptr(), ws.numel(), runner.stream)
+            if st != 0:
+                raise pkv.PagedKVError(st, "pa_decode")
+        torch.cuda.synchronize()
+    del ws
+
+
 def measure_decode(name: str, steps: int, warmup: int, cold_reps: int, partition: int = 0,
                    shared: bool = False, settle_ms: float = 0.0):
     """Run warmup + steps decode steps of a workload through the library (each step: allocator
@@ -700,14 +733,7 @@ def measure_decode(name: str, steps: int, warmup: int, cold_reps: int, partition
     w = build_workload(name, total)
     runner = StepRunner(w, total, partition, shared)
     if settle_ms > 0:
-        runner.lens_d = runner.lens_dev.data_ptr() if not w.append else runner.lens_step.data_ptr()
-        if w.append:
-            runner.lens_step.copy_(torch.from_numpy(runner.lens))
-        t_end = time.perf_counter() + settle_ms * 1e-3
-        while time.perf_counter() < t_end:
-            for _ in range(20):
-                runner.decode(runner.q[0])
-            torch.cuda.synchronize()
+        settle(settle_ms, runner)
     if warmup == 0:
         # timing from the first step (its copy-on-write copies included): one decode call
         # beforehand, which changes no state, loads the kernels' code outside the timed steps
@@ -815,7 +841,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--settle-ms", type=float, default=300.0,
                     help="untimed decode calls on the first step's state for this long before "
-                         "the warm-up steps (GPU clocks to their sustained level)")
+                         "the warm-up steps (the GPU at its sustained state when timing starts)")
     ap.add_argument("--workload", default="llama8b_decode")
     ap.add_argument("--partition", type=int, default=0)
     ap.add_argument("--shared-prefix", action="store_true",
