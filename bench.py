@@ -689,7 +689,7 @@ def release_device_memory():
     torch.cuda.empty_cache()
 
 
-def settle(ms: float, runner) -> None:
+def settle(ms: float, runner) -> float:
     """Before timing, decode the workload's first-step state for `ms` of wall time with the
     fixed-partition schedule at 8192 tokens (pa_decode with partition_tokens 8192: one
     workgroup per sequence and KV head, no merge launch).  The calls read the same pool pages
@@ -699,7 +699,7 @@ def settle(ms: float, runner) -> None:
     import torch
     w = runner.w
     if w.q_dtype != "bf16" or w.kv_dtype not in ("bf16", "i8", "i4"):
-        return  # the portable kernel serves these: no separate instance to settle with
+        return 0.0  # the portable kernel serves these: no separate instance to settle with
     runner.lens_d = runner.lens_dev.data_ptr() if not w.append else runner.lens_step.data_ptr()
     if w.append:
         runner.lens_step.copy_(torch.from_numpy(runner.lens))
@@ -719,6 +719,7 @@ def settle(ms: float, runner) -> None:
                 raise pkv.PagedKVError(st, "pa_decode")
         torch.cuda.synchronize()
     del ws
+    return ms
 
 
 def measure_decode(name: str, steps: int, warmup: int, cold_reps: int, partition: int = 0,
@@ -732,8 +733,7 @@ def measure_decode(name: str, steps: int, warmup: int, cold_reps: int, partition
     total = warmup + steps
     w = build_workload(name, total)
     runner = StepRunner(w, total, partition, shared)
-    if settle_ms > 0:
-        settle(settle_ms, runner)
+    settled = settle(settle_ms, runner) if settle_ms > 0 else 0.0
     if warmup == 0:
         # timing from the first step (its copy-on-write copies included): one decode call
         # beforehand, which changes no state, loads the kernels' code outside the timed steps
@@ -760,7 +760,7 @@ def measure_decode(name: str, steps: int, warmup: int, cold_reps: int, partition
     mean_ms = float(np.mean(ms))
     out = {"w": w, "elapsed": elapsed, "ms": ms, "mean_ms": mean_ms, "bytes": byts,
            "logical": logical, "achieved": float(np.mean(byts)) / (mean_ms * 1e-3) / 1e9,
-           "append": runner.append_ms(),
+           "append": runner.append_ms(), "settled_ms": settled,
            "cold": runner.cold_decode_ms(cold_reps) if cold_reps else []}
     del runner
     return out
@@ -904,7 +904,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "settle_ms": args.settle_ms,
+        "settle_ms": m["settled_ms"],
         "ms_per_step": round(m["elapsed"] / args.steps * 1e3, 4),
         "higher_is_better": True,
         "scaling": "weak",
