@@ -507,6 +507,87 @@ def run_prefill(args):
     print(json.dumps(rec), flush=True)
 
 
+# host link of an MI355X: PCIe 5.0 x16, 32 GT/s x 16 lanes x 128/130 encoding, per direction
+PEAK_HOST_LINK_GBPS = 63.0
+SWAP_WORKLOAD = "swap_llama8b"
+
+
+def run_swap(args):
+    """Preemption by swapping on the headline layer's pool (bf16, 8 KV heads, D 128, 16-token
+    blocks): the blocks of 8 of its 64 sequences (seeded pick, lengths U[512, 4096]) copied to a
+    pinned host swap pool with one pa_swap_blocks launch (swap-out), then back into other
+    device blocks (swap-in).  Each timed step is one swap-out and one swap-in, timed apart with
+    HIP events on the launch stream; the rate is the blocks' K and V bytes over the launch time,
+    against the host link's per-direction peak."""
+    import torch
+    import paged_kv_cache_284_amd as pkv
+    w = build_workload("llama8b_decode", 1)
+    rng = np.random.default_rng(2024)
+    picked = np.sort(rng.choice(w.B, 8, replace=False))
+    nblk = int(sum((int(w.lengths[b]) + w.bs - 1) // w.bs for b in picked))
+    NB = int(w.NB)
+    dev = torch.device("cuda")
+    k = torch.randn((NB, w.Hkv, w.bs, w.D), dtype=torch.bfloat16, device=dev)
+    v = torch.randn((NB, w.Hkv, w.D, w.bs), dtype=torch.bfloat16, device=dev)
+    hk = torch.empty((nblk, w.Hkv, w.bs, w.D), dtype=torch.bfloat16, pin_memory=True)
+    hv = torch.empty((nblk, w.Hkv, w.D, w.bs), dtype=torch.bfloat16, pin_memory=True)
+    blocks = rng.permutation(NB)
+    out_src, in_dst = blocks[:nblk], blocks[nblk:2 * nblk]
+    host = np.arange(nblk)
+    pairs_out = torch.from_numpy(np.stack([out_src, host], 1).astype(np.int32)).to(dev)
+    pairs_in = torch.from_numpy(np.stack([host, in_dst], 1).astype(np.int32)).to(dev)
+    stream = torch.cuda.current_stream()
+    ev = HipEvents()
+    sid = stream.cuda_stream
+    for _ in range(args.warmup):
+        pkv.swap_blocks(k, v, hk, hv, pairs_out, stream=stream)
+        pkv.swap_blocks(hk, hv, k, v, pairs_in, stream=stream)
+    torch.cuda.synchronize()
+    marks = [ev.create() for _ in range(3 * args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev.record(marks[3 * i], sid)
+        pkv.swap_blocks(k, v, hk, hv, pairs_out, stream=stream)
+        ev.record(marks[3 * i + 1], sid)
+        pkv.swap_blocks(hk, hv, k, v, pairs_in, stream=stream)
+        ev.record(marks[3 * i + 2], sid)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    out_ms = [ev.elapsed_ms(marks[3 * i], marks[3 * i + 1]) for i in range(args.steps)]
+    in_ms = [ev.elapsed_ms(marks[3 * i + 1], marks[3 * i + 2]) for i in range(args.steps)]
+    for e in marks:
+        ev.hip.hipEventDestroy(e)
+    nbytes = nblk * 2 * w.Hkv * w.bs * w.D * 2
+    out_gbps = nbytes / (float(np.mean(out_ms)) * 1e-3) / 1e9
+    in_gbps = nbytes / (float(np.mean(in_ms)) * 1e-3) / 1e9
+    achieved = 2 * nbytes / ((float(np.mean(out_ms)) + float(np.mean(in_ms))) * 1e-3) / 1e9
+    rec = {
+        "metric": "pa_swap_blocks: KV bytes moved per second between HBM and a pinned host pool",
+        "value": round(achieved, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) K/V in the headline layer's pool shape; no weights)",
+        "config": {"workload": SWAP_WORKLOAD, "Hkv": w.Hkv, "head_dim": w.D, "block_size": w.bs,
+                   "kv_dtype": "bf16", "pool_blocks": NB, "sequences": [int(b) for b in picked],
+                   "blocks_per_swap": nblk, "bytes_per_swap": nbytes},
+        "roofline": {"bound": "host link", "achieved": round(achieved, 2),
+                     "peak": PEAK_HOST_LINK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HOST_LINK_GBPS, 4), "traffic": None},
+        "swap_out_ms_mean": round(float(np.mean(out_ms)), 5),
+        "swap_in_ms_mean": round(float(np.mean(in_ms)), 5),
+        "swap_out_gbps": round(out_gbps, 2),
+        "swap_in_gbps": round(in_gbps, 2),
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def host_threads() -> int:
     """Threads this process may use: the CPU affinity, capped by OMP_NUM_THREADS when set."""
     n = len(os.sched_getaffinity(0))
@@ -887,6 +968,9 @@ def main():
 
     import paged_kv_cache_284_amd as pkv
     pkv.lib()
+    if args.workload == SWAP_WORKLOAD:
+        run_swap(args)
+        return
     if args.workload.startswith("prefill"):
         run_prefill(args)
         return
