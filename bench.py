@@ -588,6 +588,89 @@ def run_swap(args):
     print(json.dumps(rec), flush=True)
 
 
+PREFIX_WORKLOAD = "prefix_cache_host"
+
+
+def run_prefix_cache(args):
+    """Automatic prefix caching on the host allocator (no GPU work): a 3,000-token prompt is
+    cached once (created, its slots reserved, its full blocks published), then each request
+    shares it and adds 64 tokens of its own: pa_seq_create_prefix hashes the prompt's blocks
+    (chained FNV-1a over the parent hash and 16 token ids) and finds 187 of them cached (2,992
+    tokens), and pa_seq_reserve takes slots for the other 72.  Requests are released after each
+    round of 64, so their private blocks become evictable (and are evicted, oldest first, once
+    the free list is empty).  Timed: `steps` rounds of create + reserve + release, called through
+    the C ABI with every argument prepared beforehand (Python's own marshalling, several
+    microseconds per call, would otherwise dominate)."""
+    import ctypes as C
+    import paged_kv_cache_284_amd as pkv
+    L = pkv.lib()
+    rng = np.random.default_rng(3000)
+    prompt = rng.integers(0, 128000, 3000).astype(np.int32)
+    rounds = args.warmup + args.steps
+    reqs = [[np.concatenate([prompt, rng.integers(0, 128000, 64).astype(np.int32)])
+             for _ in range(64)] for _ in range(rounds)]
+    ptrs = [[r.ctypes.data_as(C.POINTER(C.c_int32)) for r in rr] for rr in reqs]
+    al = pkv.Allocator(4096, 16)
+    s0, c0 = al.create_prefix(np.concatenate([prompt, np.ones(1, np.int32)]))
+    al.reserve(s0, len(prompt) + 1 - c0)
+    slots = np.zeros(128, np.int64)
+    pairs = np.zeros((128, 2), np.int32)
+    p_slots = slots.ctypes.data_as(C.POINTER(C.c_int64))
+    p_pairs = pairs.ctypes.data_as(C.POINTER(C.c_int32))
+    seq, cached, ncow = C.c_int32(), C.c_int32(), C.c_int32()
+    r_seq, r_cached, r_ncow = C.byref(seq), C.byref(cached), C.byref(ncow)
+    n_req = len(prompt) + 64
+    h = al._h
+
+    def round_(k):
+        live, tot = [], 0
+        for p in ptrs[k]:
+            if L.pa_seq_create_prefix(h, p, n_req, 0, r_seq, r_cached) != 0:
+                raise RuntimeError("pa_seq_create_prefix failed")
+            if L.pa_seq_reserve(h, seq.value, n_req - cached.value, p_slots, p_pairs,
+                                r_ncow) != 0:
+                raise RuntimeError("pa_seq_reserve failed")
+            live.append(seq.value)
+            tot += cached.value
+        for s_ in live:
+            if L.pa_seq_free(h, s_) != 0:
+                raise RuntimeError("pa_seq_free failed")
+        return tot
+
+    for k in range(args.warmup):
+        round_(k)
+    t0 = time.perf_counter()
+    tot = 0
+    for k in range(args.warmup, rounds):
+        tot += round_(k)
+    elapsed = time.perf_counter() - t0
+    n = 64 * args.steps
+    rec = {
+        "metric": "automatic prefix caching: requests created per second on the host allocator",
+        "value": round(n / elapsed, 1),
+        "unit": "requests/s",
+        "n_gpus": 0,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int32 token ids, uint64 hashes",
+        "data": "synthetic (seeded token ids; a 3,000-token shared prompt, 64 private tokens per "
+                "request)",
+        "config": {"workload": PREFIX_WORKLOAD, "block_size": 16, "pool_blocks": 4096,
+                   "prompt_tokens": len(prompt), "private_tokens": 64,
+                   "requests_per_step": 64},
+        "us_per_request": round(elapsed / n * 1e6, 2),
+        "cached_tokens_per_request": tot // n,
+        "token_ids_hashed_per_s": round(n_req * n / elapsed, 1),
+        "host": cpu_model(),
+    }
+    al.close()
+    print(json.dumps(rec), flush=True)
+
+
 def host_threads() -> int:
     """Threads this process may use: the CPU affinity, capped by OMP_NUM_THREADS when set."""
     n = len(os.sched_getaffinity(0))
@@ -946,6 +1029,9 @@ def main():
         with open(os.path.join(ROOT, "profiles", "decode_traffic.json"), "w") as f:
             json.dump(out, f, indent=1)
         print(json.dumps(out))
+        return
+    if args.workload == PREFIX_WORKLOAD:
+        run_prefix_cache(args)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the decode path shards by sequence or KV head with no "
