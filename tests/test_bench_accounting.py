@@ -54,3 +54,17 @@ def test_more_than_one_gpu_is_refused_before_any_gpu_work():
                            env={**os.environ, **env})
         assert r.returncode == 2
         assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_prefix_cache_measurement_reuses_the_shared_prompt(capsys):
+    """The host prefix-cache measurement (no GPU work): every request finds the 3,000-token
+    prompt's 187 full blocks cached (2,992 tokens, the page's example), never its private
+    tokens, and the line reports what it timed."""
+    import json
+    import types
+    bench.run_prefix_cache(types.SimpleNamespace(steps=3, warmup=1))
+    r = json.loads(capsys.readouterr().out.strip().splitlines()[-1])
+    assert r["cached_tokens_per_request"] == 2992
+    assert r["config"]["requests_per_step"] == 64 and r["steps"] == 3
+    assert r["value"] > 0 and r["us_per_request"] > 0
+    assert abs(r["value"] * r["us_per_request"] - 1e6) < 1e-2 * 1e6
