@@ -136,7 +136,8 @@ __global__ void __launch_bounds__(256) decode_generic_kernel(DecodeArgs a, int G
         for (int h = 0; h < G; ++h) {
           float dot[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int d = 0; d < D; ++d) dot[d % 4] = fmaf(q_s[h][d], KL::unpack(kp[d / kE], d % kE), dot[d % 4]);
+          for (int d = 0; d < D; ++d)
+            dot[d % 4] = fmaf(q_s[h][d], KL::unpack(kp[d / kE], d % kE), dot[d % 4]);
           s_s[h][t] = ((dot[0] + dot[1]) + (dot[2] + dot[3])) * f;
         }
       } else {
