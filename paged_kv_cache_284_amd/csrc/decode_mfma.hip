@@ -64,6 +64,11 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 8;
+// Waves per workgroup of the decode kernel.  bf16 caches with up to 4 query heads per KV head
+// keep one pair in flight per wave instead of two, which leaves them at ~160 VGPRs, so three
+// waves share each SIMD (12 per workgroup); the others run two per SIMD.
+template <int G, int kKV>
+constexpr int kWavesOf = (G <= 4 && kKV == kKvBf16) ? 12 : kWaves;
 constexpr int kPrefixWaves = 4;  // the shared-prefix pass's workgroup
 constexpr int kPair = 2 * kBlockSize;  // tokens per wave iteration
 
@@ -205,7 +210,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, const int wg, c
   constexpr bool kStream = kMode == kBalanced || kMode == kSuffix;  // balanced schedule
   constexpr bool kFold = kMode == kSuffix;
   constexpr bool kPre = kMode == kPrefix;
-  constexpr int kW = kPre ? kPrefixWaves : kWaves;  // waves per workgroup
+  constexpr int kW = kPre ? kPrefixWaves : kWavesOf<G, kKV>;  // waves per workgroup
   // column tiles per wave: the prefix pass takes two column blocks (32 query columns) on every
   // pair it loads, so each load serves twice the columns
   constexpr int CT = kPre ? 2 : 1;
@@ -217,7 +222,8 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, const int wg, c
   using Regs = std::conditional_t<kI4, PairRegsI4<D>,
                                   std::conditional_t<kI8, PairRegsI8<D>, PairRegs<D>>>;
   // pairs in flight per wave (the prefix pass, one wave per SIMD, has the registers for four)
-  constexpr int kDepth = kPre ? 4 : (kI4 ? kDepthI4 : (kI8 ? kDepthI8 : kDepthBf16));
+  constexpr int kDepth =
+      kPre ? 4 : (kI4 ? kDepthI4 : (kI8 ? kDepthI8 : (kW == 12 ? 1 : kDepthBf16)));
   constexpr int kSteps = D / 32;
   constexpr int kTiles = D / 16;
 
@@ -1263,7 +1269,8 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, const int wg, c
 }
 
 template <int G, int D, int kMode, int kKV>
-__global__ void __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ void __launch_bounds__((64 * kWavesOf<G, kKV>))
+    __attribute__((amdgpu_waves_per_eu((kWavesOf<G, kKV> / 4), (kWavesOf<G, kKV> / 4))))
 decode_mfma_kernel(DecodeArgs a) {
   decode_body<G, D, kMode, kKV>(a, blockIdx.x, gridDim.x);
 }
@@ -1523,13 +1530,13 @@ template <int G, int D, int kKV>
 hipError_t launch_gd(const DecodeArgs& a, hipStream_t stream) {
   if (a.nw == 0 || G > kMaxBalancedGroup) {
     const dim3 grid(a.np_max, a.Hkv, a.B);
-    hipLaunchKernelGGL((decode_mfma_kernel<G, D, kFixed, kKV>), grid, dim3(64 * kWaves), 0, stream,
+    hipLaunchKernelGGL((decode_mfma_kernel<G, D, kFixed, kKV>), grid, dim3(64 * kWavesOf<G, kKV>), 0, stream,
                        a);
     return hipGetLastError();
   }
   constexpr int Gb = G <= kMaxBalancedGroup ? G : kMaxBalancedGroup;  // never launched for G > 8
   const size_t lds = balanced_lds(a.B);
-  hipLaunchKernelGGL((decode_mfma_kernel<Gb, D, kBalanced, kKV>), dim3(a.nw), dim3(64 * kWaves),
+  hipLaunchKernelGGL((decode_mfma_kernel<Gb, D, kBalanced, kKV>), dim3(a.nw), dim3(64 * kWavesOf<Gb, kKV>),
                      lds, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -1552,7 +1559,7 @@ hipError_t launch_gd_shared(const DecodeArgs& a, hipStream_t stream) {
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const size_t lds = balanced_lds(a.B);
-    hipLaunchKernelGGL((decode_mfma_kernel<G, D, kSuffix, kKV>), dim3(a.nw), dim3(64 * kWaves),
+    hipLaunchKernelGGL((decode_mfma_kernel<G, D, kSuffix, kKV>), dim3(a.nw), dim3(64 * kWavesOf<G, kKV>),
                        lds, stream, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -1594,7 +1601,7 @@ int mfma_workgroups_per_cu() {
   if (cached == 0) {
     int n = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_mfma_kernel<4, 128, kBalanced, kKvBf16>,
-                                                     64 * kWaves, 1024) != hipSuccess ||
+                                                     64 * kWavesOf<4, kKvBf16>, 1024) != hipSuccess ||
         n < 1)
       n = 1;
     cached = n;
