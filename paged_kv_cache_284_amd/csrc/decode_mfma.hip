@@ -68,7 +68,7 @@ constexpr int kWaves = 8;
 // keep one pair in flight per wave instead of two, which leaves them at ~160 VGPRs, so three
 // waves share each SIMD (12 per workgroup); the others run two per SIMD.
 template <int G, int kKV>
-constexpr int kWavesOf = (G <= 4) ? 12 : kWaves;
+constexpr int kWavesOf = (G <= 4 && kKV == kKvBf16) ? 12 : kWaves;
 constexpr int kPrefixWaves = 4;  // the shared-prefix pass's workgroup
 constexpr int kPair = 2 * kBlockSize;  // tokens per wave iteration
 
