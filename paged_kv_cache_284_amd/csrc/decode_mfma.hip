@@ -69,7 +69,7 @@ constexpr int kWaves = 8;
 // waves share each SIMD (12 per workgroup); the others run two per SIMD.
 template <int G, int kKV>
 constexpr int kWavesOf = (G <= 4 && kKV == kKvBf16) ? 12 : kWaves;
-constexpr int kPrefixWaves = 4;  // the shared-prefix pass's workgroup
+constexpr int kPrefixWaves = 8;  // the shared-prefix pass's workgroup
 constexpr int kPair = 2 * kBlockSize;  // tokens per wave iteration
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
@@ -221,9 +221,10 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, const int wg, c
   constexpr int kK8 = D / 64;
   using Regs = std::conditional_t<kI4, PairRegsI4<D>,
                                   std::conditional_t<kI8, PairRegsI8<D>, PairRegs<D>>>;
-  // pairs in flight per wave (the prefix pass, one wave per SIMD, has the registers for four)
+  // pairs in flight per wave (the prefix pass keeps one: two waves per SIMD cover each other's
+  // waits better than one wave with four pairs in flight)
   constexpr int kDepth =
-      kPre ? 4 : (kI4 ? kDepthI4 : (kI8 ? kDepthI8 : (kW == 12 ? 1 : kDepthBf16)));
+      kPre ? 1 : (kI4 ? kDepthI4 : (kI8 ? kDepthI8 : (kW == 12 ? 1 : kDepthBf16)));
   constexpr int kSteps = D / 32;
   constexpr int kTiles = D / 16;
 
@@ -1275,10 +1276,10 @@ decode_mfma_kernel(DecodeArgs a) {
   decode_body<G, D, kMode, kKV>(a, blockIdx.x, gridDim.x);
 }
 
-// The shared-prefix pass: four waves per workgroup, one per SIMD, so that each wave has the
-// registers for 32 query columns (two column blocks) and four pairs of loads in flight.
+// The shared-prefix pass: eight waves per workgroup, two per SIMD, each with 32 query columns
+// (two column blocks) and one pair of loads in flight, which fits two waves' registers.
 template <int D, int kKV>
-__global__ void __launch_bounds__(64 * kPrefixWaves) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ void __launch_bounds__(64 * kPrefixWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
 decode_prefix_kernel(DecodeArgs a) {
   decode_body<16, D, kPrefix, kKV>(a, blockIdx.x, gridDim.x);
 }
