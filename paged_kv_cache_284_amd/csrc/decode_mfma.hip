@@ -149,8 +149,11 @@ struct PairRegsI4 {
 // register pressure (measured: bf16 1 and 2 equal, int8 best at 1, int4 best at 2).
 constexpr int kDepthBf16 = 2, kDepthI8 = 1, kDepthI4 = 2;
 
-// Cost of a segment start in the balanced schedule, in pairs (see the span computation).
-constexpr int kSegCost = 3;
+// Cost of a segment start in the balanced schedule, in pairs of the cache's kind (see the span
+// computation).  A start costs about the same time whatever the kind, so it is worth more of
+// the cheaper int4 pairs (4 KB against 8 KB int8 and 16 KB bf16).
+template <int kKV>
+constexpr int kSegCostOf = kKV == kKvI4 ? 3 : 2;
 
 // Schedules of decode_mfma_kernel.
 constexpr int kFixed = 0;     // one workgroup per (partition, KV head, sequence)
@@ -994,7 +997,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, const int wg, c
     }
   } else {
     // pair counts -> prefix sums cum_s[0..B], and costs -> cc_s[0..B]: the spans are cut so that
-    // every workgroup and wave gets the same cost, a nonempty segment costing kSegCost pairs
+    // every workgroup and wave gets the same cost, a nonempty segment costing kSegCostOf pairs
     // more than its pairs (the latency of a segment start: its table entries, q and first tiles
     // come from memory with nothing in flight behind them).  Pieces and merges work on units.
     const int B = a.B;
@@ -1016,7 +1019,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, const int wg, c
       if constexpr (kFold) {
         if (i < B) x -= prefix_tokens(a, i, L) / kPair;  // the pairs past the shared prefix
       }
-      int c = x > 0 ? x + kSegCost : 0;
+      int c = x > 0 ? x + kSegCostOf<kKV> : 0;
 #pragma unroll
       for (int o = 1; o < 64; o <<= 1) {
         const int y = __shfl_up(x, o, 64);
@@ -1070,7 +1073,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, const int wg, c
         }
       }
       b = __builtin_amdgcn_readfirstlane(b);
-      return static_cast<int64_t>(g) * T + cum_s[b] + max(r - cc_s[b] - kSegCost, 0);
+      return static_cast<int64_t>(g) * T + cum_s[b] + max(r - cc_s[b] - kSegCostOf<kKV>, 0);
     };
     const int NW = nwg;
     const int wl = wg;
